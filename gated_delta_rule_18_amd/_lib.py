@@ -1,0 +1,191 @@
+"""ctypes binding of libkla.so: argument marshalling only.
+
+Every function here checks the torch tensors it is given (device, dtype, shape,
+contiguity), passes their device pointers and the current HIP stream to the C ABI
+declared in include/kla.h, and raises KLAError on a non-zero status. All arithmetic
+happens in the HIP kernels; there is no fallback of any kind. If the shared library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+
+LIB_PATH = pathlib.Path(__file__).resolve().with_name("libkla.so")
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "kla.h"
+
+KLA_OK, KLA_ERR_INVALID_VALUE, KLA_ERR_NOT_SUPPORTED, KLA_ERR_LAUNCH = 0, 1, 2, 3
+KLA_F32, KLA_BF16 = 0, 1
+CHUNK = 64
+
+_lib = None
+
+_c_void_p, _i64, _f32, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_SIGNATURES = {
+    "kla_prepare_beta": (_int, [_c_void_p] * 5 + [_i64] * 5 + [_f32, _int, _c_void_p]),
+    "kla_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
+    "kla_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _c_void_p]),
+    "kla_status_string": (ctypes.c_char_p, [_int]),
+    "kla_last_error": (ctypes.c_char_p, []),
+}
+
+
+class KLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"status {status}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (loaded on first use). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_18_amd.build`")
+        handle = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/kla.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kla_[a-z_]+)\s*\(", text)))
+
+
+def check(status: int) -> None:
+    if status != KLA_OK:
+        L = lib()
+        raise KLAError(status, f"{L.kla_status_string(status).decode()} — {L.kla_last_error().decode()}")
+
+
+# ------------------------------------------------------------------------- torch-facing wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KLA_BF16
+    if t.dtype == torch.float32:
+        return KLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def kla_prepare_beta(k, eta, log_alpha, eps=1e-6, chunk=CHUNK, with_gcum=True, beta_out=None, gcum_out=None,
+                     stream=None):
+    """beta = eta / (||k||^2 + eps) and the chunk-local log-decay prefix, [B, T, H] fp32 each.
+    k [B, T, H, d_k] bf16/fp32 on a GPU; eta, log_alpha [B, T, H] fp32."""
+    torch = _torch()
+    if k.dim() != 4:
+        raise ValueError("k must be [B, T, H, d_k]")
+    B, T, H, dk = k.shape
+    dev = k.device
+    _need(k, "k", (B, T, H, dk), k.dtype, dev)
+    _need(eta, "eta", (B, T, H), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (B, T, H), torch.float32, dev)
+    if beta_out is None:
+        beta_out = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    _need(beta_out, "beta_out", (B, T, H), torch.float32, dev)
+    if with_gcum and gcum_out is None:
+        gcum_out = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    if gcum_out is not None:
+        _need(gcum_out, "gcum_out", (B, T, H), torch.float32, dev)
+    check(lib().kla_prepare_beta(_ptr(k), _ptr(eta), _ptr(log_alpha), _ptr(beta_out), _ptr(gcum_out),
+                                 B, T, H, dk, chunk, float(eps), _dtype_code(k), _stream(dev, stream)))
+    return beta_out, gcum_out
+
+
+def kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16) -> int:
+    return int(lib().kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+
+
+def kla_chunk_fwd(q, k, v, eta, log_alpha, eps=1e-6, state_in=None, return_state=True, o=None, state_out=None,
+                  chunk=CHUNK, workspace=None, stream=None):
+    """Chunkwise KLA forward. q, k [B, T, H, d_k], v [B, T, H, d_v] (bf16 or fp32, one dtype);
+    eta, log_alpha [B, T, H] fp32; state_in [B, H, d_k, d_v] fp32 or None (zeros).
+    Returns (o [B, T, H, d_v] in the input dtype, final state [B, H, d_k, d_v] fp32 or None)."""
+    torch = _torch()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(eta, "eta", (B, T, H), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (B, T, H), torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(o, "o", (B, T, H, dv), dt, dev)
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", (B, H, dk, dv), torch.float32, dev)
+    code = _dtype_code(q)
+    need = kla_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().kla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state_in),
+                              _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, float(eps), code,
+                              _ptr(workspace), ws_bytes, _stream(dev, stream)))
+    return o, state_out
+
+
+def kla_decode_step(q, k, v, eta, log_alpha, state, eps=1e-6, o=None, stream=None):
+    """One decode step, in place on ``state``. q, k [B, H, d_k], v [B, H, d_v] (bf16 or fp32);
+    eta, log_alpha [B, H] fp32; state [B, H, d_k, d_v] fp32. Returns o [B, H, d_v]."""
+    torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, H, dk), dt, dev)
+    _need(k, "k", (B, H, dk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(eta, "eta", (B, H), torch.float32, dev)
+    _need(log_alpha, "log_alpha", (B, H), torch.float32, dev)
+    _need(state, "state", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(o, "o", (B, H, dv), dt, dev)
+    check(lib().kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state), _ptr(o),
+                                B, H, dk, dv, float(eps), _dtype_code(q), _stream(dev, stream)))
+    return o

@@ -1,0 +1,200 @@
+// C ABI of the KLA library: argument checks, then stream-ordered launches.
+// Declarations and the contract of every entry point: include/kla.h.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "kla.h"
+#include "kla_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kla_status_t fail(kla_status_t st, const char* fmt, const char* what) {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, what);
+  return st;
+}
+
+kla_status_t launched(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+  return KLA_ERR_LAUNCH;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool supported_head(int64_t d) { return d == 64 || d == 128; }
+
+// Products of non-negative sizes, refusing anything past 2^62 elements.
+bool mul_ok(int64_t& acc, int64_t x) {
+  if (x < 0) return false;
+  if (x != 0 && acc > (int64_t(1) << 62) / x) return false;
+  acc *= x;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kla_status_string(kla_status_t status) {
+  switch (status) {
+    case KLA_OK: return "KLA_OK";
+    case KLA_ERR_INVALID_VALUE: return "KLA_ERR_INVALID_VALUE: bad argument";
+    case KLA_ERR_NOT_SUPPORTED: return "KLA_ERR_NOT_SUPPORTED: head size or chunk length not provided";
+    case KLA_ERR_LAUNCH: return "KLA_ERR_LAUNCH: HIP launch failed";
+  }
+  return "unknown kla_status_t";
+}
+
+const char* kla_last_error(void) { return g_last_error; }
+
+kla_status_t kla_prepare_beta(const void* k, const float* eta, const float* log_alpha, float* beta_out,
+                              float* gcum_out, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t chunk,
+                              float eps, kla_dtype_t dt, void* stream) {
+  if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", "kla_prepare_beta");
+  if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", "kla_prepare_beta");
+  if (!supported_head(d_k)) return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k must be 64 or 128", "kla_prepare_beta");
+  if (chunk != kla::kChunk) return fail(KLA_ERR_NOT_SUPPORTED, "%s: chunk must be 64", "kla_prepare_beta");
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: eps must be finite and >= 0", "kla_prepare_beta");
+  int64_t n = 1;
+  if (!mul_ok(n, B) || !mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, d_k))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: size overflow", "kla_prepare_beta");
+  if (B == 0 || T == 0 || H == 0) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  if (B * H * ((T + kla::kChunk - 1) / kla::kChunk) > 0x7fffffffLL)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", "kla_prepare_beta");
+  if (!k || !eta || !log_alpha || !beta_out)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", "kla_prepare_beta");
+  if (!aligned(k, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4) || !aligned(beta_out, 4) ||
+      !aligned(gcum_out, 4))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", "kla_prepare_beta");
+  const int64_t tok = B * T * H;
+  const Range outs[2] = {range("beta_out", beta_out, tok * 4), range("gcum_out", gcum_out, tok * 4)};
+  const Range ins[3] = {range("k", k, tok * d_k * (dt == KLA_BF16 ? 2 : 4)), range("eta", eta, tok * 4),
+                        range("log_alpha", log_alpha, tok * 4)};
+  if (overlap(outs[0], outs[1])) return fail(KLA_ERR_INVALID_VALUE, "%s: outputs overlap", "kla_prepare_beta");
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlap(o, i)) return fail(KLA_ERR_INVALID_VALUE, "kla_prepare_beta: %s overlaps an input", o.name);
+  kla::PrepareArgs a{k, eta, log_alpha, beta_out, gcum_out, B, T, H, d_k, eps, dt == KLA_BF16};
+  return launched(kla::launch_prepare_beta(a, static_cast<hipStream_t>(stream)), "kla_prepare_beta");
+}
+
+size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                    kla_dtype_t dt) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
+    return 0;
+  return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+}
+
+kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                           const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
+                           int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const char* fn = "kla_chunk_fwd";
+  if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
+  if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
+  if (!supported_head(d_k) || !supported_head(d_v))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k and d_v must be 64 or 128", fn);
+  if (chunk != kla::kChunk) return fail(KLA_ERR_NOT_SUPPORTED, "%s: chunk must be 64", fn);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(KLA_ERR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+  int64_t n = 1;
+  if (!mul_ok(n, B) || !mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, d_k > d_v ? d_k : d_v))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: size overflow", fn);
+  if (B == 0 || H == 0) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  if (B * H * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  if (T > 0 && (!q || !k || !v || !eta || !log_alpha || !o))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||
+      !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
+  const size_t need = kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+  if (T > 0 && need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
+  const int64_t es = dt == KLA_BF16 ? 2 : 4;
+  const int64_t tok = B * T * H;
+  const int64_t sbytes = B * H * d_k * d_v * 4;
+  const Range rq = range("q", q, tok * d_k * es), rk = range("k", k, tok * d_k * es),
+              rv = range("v", v, tok * d_v * es), re = range("eta", eta, tok * 4),
+              rl = range("log_alpha", log_alpha, tok * 4), rsi = range("state_in", state_in, sbytes),
+              rso = range("state_out", state_out, sbytes), ro = range("o", o, tok * d_v * es),
+              rw = range("workspace", workspace, (int64_t)(need > 0 ? workspace_bytes : 0));
+  const Range* ins[6] = {&rq, &rk, &rv, &re, &rl, &rsi};
+  for (const Range* i : ins) {
+    if (overlap(ro, *i)) return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: o overlaps %s", i->name);
+    if (i != &rsi && overlap(rso, *i))
+      return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: state_out overlaps %s", i->name);
+    if (overlap(rw, *i)) return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: workspace overlaps %s", i->name);
+  }
+  if (overlap(ro, rso) || overlap(rw, ro) || overlap(rw, rso))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: outputs overlap", fn);
+  if (state_in && state_out && state_in != state_out && overlap(rsi, rso))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: state_in and state_out overlap without being equal", fn);
+  if (T == 0 && !state_out) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
+                   workspace, workspace_bytes};
+  return launched(kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                             float* state, void* o, int64_t B, int64_t H, int64_t d_k, int64_t d_v, float eps,
+                             kla_dtype_t dt, void* stream) {
+  const char* fn = "kla_decode_step";
+  if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
+  if (B < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
+  if (!supported_head(d_k) || !supported_head(d_v))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k and d_v must be 64 or 128", fn);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(KLA_ERR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+  int64_t n = 1;
+  if (!mul_ok(n, B) || !mul_ok(n, H) || !mul_ok(n, d_k) || !mul_ok(n, d_v))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: size overflow", fn);
+  if (B == 0 || H == 0) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  if (B * H * 4 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  if (!q || !k || !v || !eta || !log_alpha || !state || !o) return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
+      !aligned(eta, 4) || !aligned(log_alpha, 4))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
+  const int64_t es = dt == KLA_BF16 ? 2 : 4;
+  const Range rs = range("state", state, B * H * d_k * d_v * 4), ro = range("o", o, B * H * d_v * es);
+  const Range ins[5] = {range("q", q, B * H * d_k * es), range("k", k, B * H * d_k * es),
+                        range("v", v, B * H * d_v * es), range("eta", eta, B * H * 4),
+                        range("log_alpha", log_alpha, B * H * 4)};
+  if (overlap(ro, rs)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps state", fn);
+  for (const Range& i : ins) {
+    if (overlap(ro, i)) return fail(KLA_ERR_INVALID_VALUE, "kla_decode_step: o overlaps %s", i.name);
+    if (overlap(rs, i)) return fail(KLA_ERR_INVALID_VALUE, "kla_decode_step: state overlaps %s", i.name);
+  }
+  kla::DecodeArgs a{q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt == KLA_BF16};
+  return launched(kla::launch_decode_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

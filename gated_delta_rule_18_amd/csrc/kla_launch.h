@@ -1,0 +1,58 @@
+// Host-side launch interface between the C ABI (kla_abi.hip) and the kernel files.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kla {
+
+constexpr int kChunk = 64;  // chunk length of the chunkwise algorithm
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* log_alpha;
+  float* state;
+  void* o;
+  int64_t B, H, d_k, d_v;
+  float eps;
+  bool bf16;
+};
+
+struct PrepareArgs {
+  const void* k;
+  const float* eta;
+  const float* log_alpha;
+  float* beta;
+  float* gcum;  // may be null
+  int64_t B, T, H, d_k;
+  float eps;
+  bool bf16;
+};
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* log_alpha;
+  const float* state_in;  // may be null: S_0 = 0
+  float* state_out;       // may be null
+  void* o;
+  int64_t B, T, H, d_k, d_v;
+  float eps;
+  bool bf16;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prepare_beta(const PrepareArgs& a, hipStream_t stream);
+hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
+size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+
+}  // namespace kla

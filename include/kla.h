@@ -1,0 +1,131 @@
+/*
+ * kla.h — C ABI of the Kaczmarz Linear Attention (KLA) hot path for AMD Instinct
+ * MI355X (CDNA4, gfx950).
+ *
+ * The method ("Kaczmarz Linear Attention", Abstract) is Gated DeltaNet's recurrence
+ * ("Deep Dive into KDA", section 2.2) with the Kaczmarz step size
+ *     beta_t = eta_t / (||k_t||_2^2 + eps).
+ * The state of one head is stored as S = M^T with shape [d_k][d_v] (d_v contiguous),
+ * where M is the d_v x d_k map of the pages:
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t.
+ * (The erase acts on the key side so that, with alpha = eta = 1 and eps = 0, the new
+ * state maps k_t to v_t exactly — the projection the pages describe.)
+ * The decay is passed as log(alpha_t); alpha_t = exp(log_alpha_t).
+ *
+ * Conventions shared by every entry point
+ *   Layouts (row-major, contiguous, no strides):
+ *     q, k        [B, T, H, d_k]      (decode: [B, H, d_k])
+ *     v, o        [B, T, H, d_v]      (decode: [B, H, d_v])
+ *     eta, log_alpha, beta, gcum  [B, T, H] fp32   (decode: [B, H])
+ *     state       [B, H, d_k, d_v] fp32
+ *   dt selects the element type of q, k, v and o: KLA_BF16 (bfloat16) or KLA_F32.
+ *   State, gates and all accumulation are fp32 in both cases.
+ *   Pointers are device pointers (HIP device memory of the current device) unless
+ *   stated otherwise; q/k/v/o/state must be 16-byte aligned, gate arrays 4-byte aligned.
+ *   Supported head sizes: d_k, d_v in {64, 128}. The chunk length must be 64.
+ *   eta is used as given (any finite value >= 0; the pages' eta is a sigmoid output).
+ *   eps must be finite and >= 0. With eps = 0 a zero key gives beta = inf and NaNs,
+ *   exactly as the recurrence does.
+ *   stream is a hipStream_t (NULL: the legacy default stream). Every call only
+ *   enqueues work on that stream and returns; nothing waits on the host.
+ *   Ownership: the caller allocates and owns every buffer. The library allocates
+ *   nothing and keeps no pointer after a call returns.
+ *   Errors: arguments are checked before anything is enqueued; on a bad argument the
+ *   call returns KLA_ERR_INVALID_VALUE or KLA_ERR_NOT_SUPPORTED and enqueues nothing.
+ *   A failed launch returns KLA_ERR_LAUNCH; kla_last_error() then holds the HIP text.
+ *   Calls with B, H or (where present) T equal to 0 do no work beyond what is stated.
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kla_status {
+  KLA_OK = 0,
+  KLA_ERR_INVALID_VALUE = 1, /* null/misaligned pointer, negative size, bad eps, overlap */
+  KLA_ERR_NOT_SUPPORTED = 2, /* head size or chunk length this build does not provide */
+  KLA_ERR_LAUNCH = 3         /* the HIP runtime refused a launch; see kla_last_error() */
+} kla_status_t;
+
+typedef enum kla_dtype { KLA_F32 = 0, KLA_BF16 = 1 } kla_dtype_t;
+
+/*
+ * kla_prepare_beta — the prologue on its own.
+ * Source: "Kaczmarz Linear Attention", Abstract (beta_t = eta_t / (||k_t||^2 + eps));
+ * "Deep Dive into KDA", section 3 (intra-chunk accumulated decay computed once by
+ * prefix sums) and section 5 (log-domain prefixes).
+ *   beta_out[b,t,h] = eta[b,t,h] / (sum_i k[b,t,h,i]^2 + eps)        (fp32 accumulation)
+ *   gcum_out[b,t,h] = sum of log_alpha[b,s,h] over s in t's chunk with s <= t,
+ *                     chunks being [0,chunk), [chunk,2 chunk), ... along T.
+ * gcum_out may be NULL (not computed). kla_chunk_fwd computes the same values
+ * internally; this entry point exists for callers who want beta itself.
+ */
+kla_status_t kla_prepare_beta(const void* k, const float* eta, const float* log_alpha,
+                              float* beta_out, float* gcum_out,
+                              int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t chunk,
+                              float eps, kla_dtype_t dt, void* stream);
+
+/*
+ * kla_chunk_fwd_workspace_size — bytes of device workspace kla_chunk_fwd needs for
+ * these sizes (0 when it needs none). Host-only; never fails.
+ */
+size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                    int64_t chunk, kla_dtype_t dt);
+
+/*
+ * kla_chunk_fwd — chunkwise-parallel forward over a whole sequence (prefill / training).
+ * Source: "Kaczmarz Linear Attention", Abstract (KLA keeps GDN's chunkwise parallel
+ * algorithm); "Deep Dive into KDA", section 3 (inter-chunk state update
+ * S[n+1] = Diag(gamma) S[n] + (Gamma o K[n])^T (U[n] - W[n] S[n]) and intra-chunk output
+ * O[n] = (Gamma o Q[n]) S[n] + Tril(...)(U[n] - W[n] S[n])), with a scalar gate.
+ * Computes, for every head, o_t = S_t^T q_t for t = 0..T-1 starting from S_0, and the
+ * final state S_T. Numerically it equals the token recurrence up to rounding.
+ *   state_in   [B,H,d_k,d_v] fp32, or NULL for S_0 = 0.
+ *   state_out  [B,H,d_k,d_v] fp32, or NULL if the final state is not wanted.
+ *              state_out may equal state_in (in-place update); any other overlap is an error.
+ *   o          [B,T,H,d_v] of type dt; must not overlap any input.
+ *   T          any length >= 0; a last partial chunk is handled. T = 0 writes
+ *              state_out = S_0 and no output.
+ *   workspace  device buffer of at least kla_chunk_fwd_workspace_size(...) bytes, or NULL
+ *              when that size is 0.
+ */
+kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* eta, const float* log_alpha,
+                           const float* state_in, float* state_out, void* o,
+                           int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                           float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * kla_decode_step — one recurrent decode step for B x H heads (one new token each).
+ * Source: "Kaczmarz Linear Attention", Abstract (recurrent decoding with a fixed-size
+ * state); "Deep Dive into KDA", section 2.2 (the token update) and section 3 (memory
+ * decoupled from sequence length).
+ * Per head: n = ||k||^2, beta = eta / (n + eps), alpha = exp(log_alpha);
+ *   u = alpha S^T k,  p = alpha S^T q,  delta = beta (v - u),
+ *   o = p + (k.q) delta  (= S_new^T q),   S <- alpha S + k delta^T   (in place).
+ *   q, k [B,H,d_k], v [B,H,d_v], o [B,H,d_v] of type dt; eta, log_alpha [B,H] fp32;
+ *   state [B,H,d_k,d_v] fp32, read and overwritten. o must not overlap the state.
+ */
+kla_status_t kla_decode_step(const void* q, const void* k, const void* v,
+                             const float* eta, const float* log_alpha,
+                             float* state, void* o,
+                             int64_t B, int64_t H, int64_t d_k, int64_t d_v,
+                             float eps, kla_dtype_t dt, void* stream);
+
+/* Static text for a status code. */
+const char* kla_status_string(kla_status_t status);
+
+/* Text of the last error on the calling host thread ("" if none). */
+const char* kla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H */

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports everything include/kla.h
+declares, and rejects bad arguments before it enqueues anything (no compute calls)."""
+import ctypes
+
+import pytest
+
+from gated_delta_rule_18_amd import _lib as K
+
+A16 = 1 << 20  # a 16-byte-aligned fake address; never dereferenced: every call below fails validation
+
+
+def L():
+    return K.lib()
+
+
+def test_exports_every_declared_symbol():
+    names = K.declared_functions()
+    assert set(names) == {"kla_prepare_beta", "kla_chunk_fwd_workspace_size", "kla_chunk_fwd",
+                          "kla_decode_step", "kla_status_string", "kla_last_error"}
+    for n in names:
+        assert hasattr(L(), n), n
+
+
+def test_status_strings():
+    for code in range(4):
+        assert L().kla_status_string(code).startswith(b"KLA_")
+    assert b"unknown" in L().kla_status_string(99)
+
+
+def p(x=A16):
+    return ctypes.c_void_p(x)
+
+
+def chunk(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1,
+          q=A16, k=A16 * 2, v=A16 * 3, eta=A16 * 4, la=A16 * 5, s_in=0, s_out=0, o=A16 * 6, ws=0, ws_bytes=0):
+    return L().kla_chunk_fwd(p(q), p(k), p(v), p(eta), p(la), p(s_in) if s_in else None,
+                             p(s_out) if s_out else None, p(o), B, T, H, dk, dv, chunk_len, eps, dt,
+                             p(ws) if ws else None, ws_bytes, None)
+
+
+def decode(dk=128, dv=128, eps=1e-6, dt=K.KLA_BF16, B=1, H=1, q=A16, k=A16 * 2, v=A16 * 3, eta=A16 * 4,
+           la=A16 * 5, state=A16 * 8, o=A16 * 16):
+    return L().kla_decode_step(p(q), p(k), p(v), p(eta), p(la), p(state) if state else None, p(o) if o else None,
+                               B, H, dk, dv, eps, dt, None)
+
+
+def prep(dk=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, k=A16, eta=A16 * 2, la=A16 * 3,
+         beta=A16 * 4, gcum=A16 * 5):
+    return L().kla_prepare_beta(p(k), p(eta), p(la), p(beta), p(gcum) if gcum else None, B, T, H, dk,
+                                chunk_len, eps, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(dv=256), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(chunk_len=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(eps=-1.0), K.KLA_ERR_INVALID_VALUE),
+    (dict(eps=float("nan")), K.KLA_ERR_INVALID_VALUE),
+    (dict(dt=7), K.KLA_ERR_INVALID_VALUE),
+    (dict(T=-1), K.KLA_ERR_INVALID_VALUE),
+    (dict(q=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(o=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(q=A16 + 2), K.KLA_ERR_INVALID_VALUE),          # misaligned
+    (dict(eta=A16 * 4 + 2), K.KLA_ERR_INVALID_VALUE),    # misaligned gate
+    (dict(o=A16 + 64), K.KLA_ERR_INVALID_VALUE),         # o overlaps q
+    (dict(s_in=A16 * 32, s_out=A16 * 32 + 256), K.KLA_ERR_INVALID_VALUE),  # partial state overlap
+    (dict(B=1 << 40, T=1 << 30), K.KLA_ERR_INVALID_VALUE),  # size overflow
+])
+def test_chunk_fwd_rejects(kw, status):
+    assert chunk(**kw) == status
+    assert L().kla_last_error() != b""
+
+
+def test_chunk_fwd_empty_batch_is_a_no_op():
+    assert chunk(B=0) == K.KLA_OK
+    assert chunk(H=0, q=0, k=0) == K.KLA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(state=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(o=A16 * 8 + 16), K.KLA_ERR_INVALID_VALUE),    # o inside the state
+    (dict(k=A16 * 2 + 8), K.KLA_ERR_INVALID_VALUE),     # misaligned
+    (dict(eps=float("inf")), K.KLA_ERR_INVALID_VALUE),
+    (dict(B=-2), K.KLA_ERR_INVALID_VALUE),
+])
+def test_decode_step_rejects(kw, status):
+    assert decode(**kw) == status
+
+
+def test_decode_empty_is_a_no_op():
+    assert decode(B=0) == K.KLA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=100), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(chunk_len=128), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(beta=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(beta=A16 + 4), K.KLA_ERR_INVALID_VALUE),      # beta overlaps k
+    (dict(gcum=A16 * 4), K.KLA_ERR_INVALID_VALUE),      # gcum == beta
+])
+def test_prepare_beta_rejects(kw, status):
+    assert prep(**kw) == status
+
+
+def test_workspace_size_is_host_only():
+    assert K.lib().kla_chunk_fwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16) >= 0
+    assert K.lib().kla_chunk_fwd_workspace_size(8, 4096, 8, 96, 128, 64, K.KLA_BF16) == 0
+
+
+def test_python_wrapper_rejects_without_gpu_work():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        K.kla_chunk_fwd(q, q, q[..., :32].contiguous(), torch.zeros(1, 4, 2), torch.zeros(1, 4, 1))

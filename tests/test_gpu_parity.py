@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64 oracle on the
+same seeded inputs. Bars: relative L2 <= 1e-4 for fp32 inputs and <= 2e-2 for bf16
+inputs with fp32 accumulation, on o and on the final state."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.kla_testutil import TOL, dev, host, rel_l2, report
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gated_delta_rule_18_amd as kla  # noqa: E402
+
+
+def _sel(x, heads):
+    return np.stack([x[b, :, h] for b, h in heads])
+
+
+def gpu_fwd(w, inp, S0=None, return_state=True):
+    o, S = kla.kla_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                             dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps,
+                             state_in=None if S0 is None else dev(S0), return_state=return_state)
+    torch.cuda.synchronize()
+    return host(o), (None if S is None else host(S))
+
+
+def oracle_fwd(w, inp, heads, S0=None):
+    s0 = None if S0 is None else np.stack([S0[b, h] for b, h in heads])
+    return oracle.kla_recurrent(_sel(inp["q"], heads), _sel(inp["k"], heads), _sel(inp["v"], heads),
+                                _sel(inp["eta"], heads), _sel(inp["log_alpha"], heads), w.eps, s0)
+
+
+def check_fwd(name, w, inp, heads, S0=None, tol=None):
+    tol = TOL[w.dtype] if tol is None else tol
+    o, S = gpu_fwd(w, inp, S0)
+    ro, rS = oracle_fwd(w, inp, heads, S0)
+    eo = rel_l2(_sel(o, heads), ro)
+    eS = rel_l2(np.stack([S[b, h] for b, h in heads]), rS)
+    report(name, o=eo, S_T=eS)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= tol and eS <= tol, (eo, eS)
+    return o, S
+
+
+def all_heads(w):
+    return [(b, h) for b in range(w.B) for h in range(w.H)]
+
+
+# ----------------------------------------------------------------------------- prologue
+
+@pytest.mark.parametrize("dtype,dk,T", [("bf16", 128, 250), ("f32", 64, 130), ("bf16", 64, 64), ("f32", 128, 1)])
+def test_prepare_beta(dtype, dk, T):
+    w = wl.custom("prep", 200, B=2, H=3, dk=dk, dv=dk, T=T, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    beta, G = kla.kla_prepare_beta(dev(inp["k"], dtype), dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps)
+    torch.cuda.synchronize()
+    rb, rG = oracle.kla_prepare_beta(inp["k"], inp["eta"], inp["log_alpha"], w.eps, 64)
+    report(f"prepare_beta {dtype} dk={dk} T={T}", beta=rel_l2(host(beta), rb), G=rel_l2(host(G), rG))
+    np.testing.assert_allclose(host(beta), rb, rtol=2e-6, atol=0)
+    np.testing.assert_allclose(host(G), rG, rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv,B,H", [(128, 128, 2, 3), (64, 64, 2, 3), (128, 64, 1, 5), (64, 128, 3, 1),
+                                       (128, 128, 64, 17)])
+def test_decode_steps_small(dtype, dk, dv, B, H):
+    w = wl.custom("dec", 201, B=B, H=H, dk=dk, dv=dv, steps=12, dtype=dtype, s0_std=0.05)
+    inp = wl.decode_inputs(w)
+    S = dev(inp["S0"])
+    outs = []
+    for s in range(w.steps):
+        o = kla.kla_decode_step(dev(inp["q"][s], dtype), dev(inp["k"][s], dtype), dev(inp["v"][s], dtype),
+                                dev(inp["eta"][s]), dev(inp["log_alpha"][s]), S, eps=w.eps)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    ro, rS = oracle.kla_decode_steps(inp["q"], inp["k"], inp["v"], inp["eta"], inp["log_alpha"], w.eps, inp["S0"])
+    eo, eS = rel_l2(np.stack(outs), ro), rel_l2(host(S), rS)
+    report(f"decode {dtype} dk={dk} dv={dv} B={B} H={H}", o=eo, S=eS)
+    assert eo <= TOL[dtype] and eS <= TOL[dtype]
+
+
+def test_decode_workload_b64h16_1024_steps():
+    """Decode B64 H16 d128, 1024 consecutive steps from S0 ~ N(0, 0.02); oracle on sampled heads."""
+    w = wl.WORKLOADS["decode_b64h16"]
+    inp = wl.decode_inputs(w)
+    S = dev(inp["S0"])
+    q, k, v = dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype)
+    eta, la = dev(inp["eta"]), dev(inp["log_alpha"])
+    o_all = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda:0")
+    for s in range(w.steps):
+        kla.kla_decode_step(q[s], k[s], v[s], eta[s], la[s], S, eps=w.eps, o=o_all[s])
+    torch.cuda.synchronize()
+    heads = [(0, 0), (17, 5), (40, 9), (63, 15)]
+    o_h = host(o_all)
+    S_h = host(S)
+    for i, (b, h) in enumerate(heads):
+        ro, rS = oracle.kla_decode_steps(inp["q"][:, b:b + 1, h:h + 1], inp["k"][:, b:b + 1, h:h + 1],
+                                         inp["v"][:, b:b + 1, h:h + 1], inp["eta"][:, b:b + 1, h:h + 1],
+                                         inp["log_alpha"][:, b:b + 1, h:h + 1], w.eps, inp["S0"][b:b + 1, h:h + 1])
+        eo = rel_l2(o_h[:, b, h], ro[:, 0, 0])
+        eS = rel_l2(S_h[b, h], rS[0, 0])
+        report(f"decode_b64h16 head ({b},{h})", o=eo, S=eS)
+        assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
+    assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
+
+
+# ----------------------------------------------------------------------------- chunked forward
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 15, 63, 64, 65, 250])
+def test_chunk_fwd_small_shapes(dtype, T):
+    w = wl.custom("fwd", 202 + T, B=2, H=3, dk=128, dv=128, T=T, dtype=dtype)
+    check_fwd(f"chunk_fwd {dtype} T={T}", w, wl.prefill_inputs(w), all_heads(w))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64), (64, 128)])
+def test_chunk_fwd_head_sizes(dtype, dk, dv):
+    w = wl.custom("fwd_d", 210 + dk + dv, B=1, H=9, dk=dk, dv=dv, T=200, dtype=dtype)
+    check_fwd(f"chunk_fwd {dtype} dk={dk} dv={dv}", w, wl.prefill_inputs(w), all_heads(w))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_fwd_initial_state_and_aliasing(dtype):
+    w = wl.custom("fwd_s0", 220, B=2, H=2, dk=128, dv=128, T=190, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    S0 = np.random.default_rng(5).normal(0, 0.05, (2, 2, 128, 128)).astype(np.float32)
+    check_fwd(f"chunk_fwd {dtype} with S0", w, inp, all_heads(w), S0=S0)
+    # in place: state_out is state_in
+    S = dev(S0)
+    o, S_out = kla.kla_chunk_fwd(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype),
+                                 dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps, state_in=S, state_out=S)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    _, rS = oracle_fwd(w, inp, all_heads(w), S0)
+    assert rel_l2(host(S).reshape(-1, 128, 128), rS) <= TOL[dtype]
+
+
+def test_chunk_fwd_zero_length_copies_state():
+    S0 = dev(np.random.default_rng(6).normal(0, 1, (2, 3, 64, 64)).astype(np.float32))
+    z = torch.zeros((2, 0, 3, 64), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.zeros((2, 0, 3), dtype=torch.float32, device="cuda:0")
+    o, S = kla.kla_chunk_fwd(z, z, z, g, g, state_in=S0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 64)
+    assert torch.equal(S, S0)
+
+
+def test_chunk_fwd_fwd_tiny_f32_workload():
+    """fp32 B1 H1 T256 d64: the whole output and state against the oracle (bar 1e-4)."""
+    w = wl.WORKLOADS["fwd_tiny_f32"]
+    check_fwd("fwd_tiny_f32", w, wl.prefill_inputs(w), all_heads(w))
+
+
+def test_chunk_fwd_b8h8_t4096_workload():
+    w = wl.WORKLOADS["fwd_b8h8_t4096"]
+    check_fwd("fwd_b8h8_t4096 (sampled heads)", w, wl.prefill_inputs(w), [(0, 0), (3, 5), (7, 7)])
+
+
+def test_chunk_fwd_long_t65536_workload():
+    w = wl.WORKLOADS["fwd_long_t65536"]
+    check_fwd("fwd_long_t65536 (sampled heads)", w, wl.prefill_inputs(w), [(0, 3), (0, 12)])
+
+
+def test_mixed_prefill_then_decode_workload():
+    """Prefill B4 H16 T32768, then 512 decode steps from its final states; sampled heads are
+    checked against one uninterrupted oracle recurrence over T + 512 tokens."""
+    w = wl.WORKLOADS["mixed_b4h16"]
+    inp = wl.prefill_inputs(w)
+    o, S = kla.kla_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                             dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps)
+    dec = wl.decode_inputs(w)
+    q, k, v = dev(dec["q"], w.dtype), dev(dec["k"], w.dtype), dev(dec["v"], w.dtype)
+    eta, la = dev(dec["eta"]), dev(dec["log_alpha"])
+    od = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda:0")
+    for s in range(w.steps):
+        kla.kla_decode_step(q[s], k[s], v[s], eta[s], la[s], S, eps=w.eps, o=od[s])
+    torch.cuda.synchronize()
+    o_h, od_h, S_h = host(o), host(od), host(S)
+    for b, h in [(0, 0), (3, 11)]:
+        cat = lambda a, d: np.concatenate([a[b, :, h], d[:, b, h]])[None]
+        ro, rS = oracle.kla_recurrent(cat(inp["q"], dec["q"]), cat(inp["k"], dec["k"]), cat(inp["v"], dec["v"]),
+                                      cat(inp["eta"], dec["eta"]), cat(inp["log_alpha"], dec["log_alpha"]), w.eps)
+        e_pre = rel_l2(o_h[b, :, h], ro[0, :w.T])
+        e_dec = rel_l2(od_h[:, b, h], ro[0, w.T:])
+        e_S = rel_l2(S_h[b, h], rS[0])
+        report(f"mixed_b4h16 head ({b},{h})", prefill_o=e_pre, decode_o=e_dec, S=e_S)
+        assert max(e_pre, e_dec, e_S) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_eta_zero_is_pure_decay(dtype):
+    w = wl.custom("eta0", 230, B=1, H=2, dk=128, dv=128, T=150, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    inp["eta"][:] = 0.0
+    S0 = np.random.default_rng(7).normal(0, 0.1, (1, 2, 128, 128)).astype(np.float32)
+    check_fwd(f"eta=0 {dtype}", w, inp, all_heads(w), S0=S0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_no_decay_full_step_and_zero_keys(dtype):
+    """alpha = 1 and eta = 1 everywhere, with some all-zero keys (finite, only decay)."""
+    w = wl.custom("edge", 231, B=1, H=3, dk=64, dv=64, T=140, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    inp["log_alpha"][:] = 0.0
+    inp["eta"][:] = 1.0
+    inp["k"][0, [0, 5, 63, 64, 100], :, :] = 0.0
+    check_fwd(f"alpha=1 eta=1 zero keys {dtype}", w, inp, all_heads(w))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_extreme_gates(dtype):
+    """Strong forgetting (log alpha down to -8 per token) and eta near 0 and 1."""
+    w = wl.custom("extreme", 232, B=1, H=4, dk=128, dv=128, T=256, dtype=dtype, eta_std=4.0,
+                  log_alpha_range=(0.0, 8.0))
+    check_fwd(f"extreme gates {dtype}", w, wl.prefill_inputs(w), all_heads(w))
+
+
+# ----------------------------------------------------------------------------- properties
+
+def test_deterministic_bitwise():
+    w = wl.custom("det", 240, B=2, H=4, dk=128, dv=128, T=300)
+    inp = wl.prefill_inputs(w)
+    args = (dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"), dev(inp["eta"]),
+            dev(inp["log_alpha"]))
+    o1, S1 = kla.kla_chunk_fwd(*args)
+    o2, S2 = kla.kla_chunk_fwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_passing_split(dtype):
+    """fwd(T1) then fwd(T2 | S_T1) agrees with fwd(T1 + T2): only the state crosses."""
+    w = wl.custom("split", 241, B=1, H=4, dk=128, dv=128, T=320, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    t1 = 131
+    first = {n: a[:, :t1].copy() for n, a in inp.items()}
+    second = {n: a[:, t1:].copy() for n, a in inp.items()}
+    o1, S1 = gpu_fwd(w.with_(T=t1), first)
+    o2, S2 = gpu_fwd(w.with_(T=w.T - t1), second, S0=S1.astype(np.float32))
+    o, S = gpu_fwd(w, inp)
+    e_o = rel_l2(np.concatenate([o1, o2], 1), o)
+    e_S = rel_l2(S2, S)
+    report(f"state passing {dtype}", o=e_o, S=e_S)
+    assert e_o <= TOL[dtype] and e_S <= TOL[dtype]
+
+
+def test_decode_continues_chunk_fwd():
+    """T decode steps from zero agree with one chunked pass over the same T tokens."""
+    w = wl.custom("dvc", 242, B=2, H=2, dk=128, dv=128, T=70, dtype="f32")
+    inp = wl.prefill_inputs(w)
+    o, S = gpu_fwd(w, inp)
+    St = torch.zeros((2, 2, 128, 128), dtype=torch.float32, device="cuda:0")
+    od = []
+    for t in range(w.T):
+        od.append(host(kla.kla_decode_step(dev(inp["q"][:, t], "f32"), dev(inp["k"][:, t], "f32"),
+                                           dev(inp["v"][:, t], "f32"), dev(inp["eta"][:, t]),
+                                           dev(inp["log_alpha"][:, t]), St, eps=w.eps)))
+    torch.cuda.synchronize()
+    e_o = rel_l2(np.stack(od, 1), o)
+    e_S = rel_l2(host(St), S)
+    report("decode vs chunk_fwd f32", o=e_o, S=e_S)
+    assert e_o <= 1e-4 and e_S <= 1e-4
+    assert math.isfinite(e_o)

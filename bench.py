@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the Kaczmarz Linear Attention hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input. The
+default workload, mixed_b4h16, is a chunkwise prefill over B=4, H=16, T=32768,
+d_k=d_v=128 (bf16 q/k/v/o, fp32 state and gates) followed by 512 recurrent decode
+steps that continue from the prefill's final states, so every stage runs: the
+beta/decay prologue, the chunk products, the triangular solve, the state scan, the
+output and the decode step. Other workloads (--workload) time one part alone.
+
+Inputs are generated (seeded) and copied to HBM before the timed region. Kernels
+are launched through the C ABI with pre-marshalled pointers on torch's current
+stream; HIP events on that stream time each part. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "chunked-fwd tokens/s + decode tokens/s at 1 GPU; % MFMA / HBM roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+
+
+def chunk_flops_per_head_token(dk, dv, C=64):
+    """Dense chunk-product count: K K^T, Q K^T, T (beta K), T (beta V), P Delta (C-wide),
+    W S, Q S, K^T Delta (d_k x d_v-wide)."""
+    return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv
+
+
+def chunk_bytes(w, es):
+    """Algorithmic HBM bytes of one prefill launch: q, k, v, o, eta, log_alpha once, plus the
+    final state written (and the initial one read when given)."""
+    per_tok = (2 * w.dk + 2 * w.dv) * es + 8
+    return w.heads * w.T * per_tok + w.heads * w.dk * w.dv * 4
+
+
+def decode_bytes(w, es):
+    """Algorithmic HBM bytes of one decode launch: the fp32 state read and written once,
+    q, k, v, o, eta, log_alpha."""
+    return w.heads * (2 * w.dk * w.dv * 4 + (2 * w.dk + 2 * w.dv) * es + 8)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, head_tokens):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: every head
+    of the batch over the first head_tokens / (B H) prefill tokens (or decode steps). Single
+    threaded; the recurrence costs the same per token at any position."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    n = max(1, min(head_tokens // w.heads, w.T if w.T else w.steps))
+    if w.T:
+        x = wl.prefill_inputs(w.with_(T=n))
+        args = (x["q"], x["k"], x["v"], x["eta"], x["log_alpha"], w.eps)
+        run = lambda: oracle.kla_forward(*args)
+        what = f"oracle kla_forward on all {w.heads} heads (B={w.B}, H={w.H}) of the first {n} prefill tokens"
+    else:
+        x = wl.decode_inputs(w.with_(steps=n))
+        args = (x["q"], x["k"], x["v"], x["eta"], x["log_alpha"], w.eps, x["S0"])
+        run = lambda: oracle.kla_decode_steps(*args)
+        what = f"oracle decode on all {w.heads} heads (B={w.B}, H={w.H}) for the first {n} steps"
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    if ctx:
+        with ctx:
+            run()
+    else:
+        run()
+    dt = time.perf_counter() - t0
+    tokens = w.B * n
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}: {tokens} tokens in {dt:.2f} s (fp64 numpy, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-head-tokens", type=int, default=131072,
+                    help="size of the oracle's bounded sample, in head-tokens")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no communication). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_18_amd as kla
+    from gated_delta_rule_18_amd import _lib as K
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    es = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
+    L = K.lib()
+
+    log(f"[bench] generating {w.name} ({w.note}) ...")
+    t_gen = time.perf_counter()
+    on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
+    pre = dec = None
+    if w.T:
+        x = wl.prefill_inputs(w)
+        pre = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
+        del x
+        pre["o"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
+    state = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=device)
+    if w.steps:
+        x = wl.decode_inputs(w)
+        dec = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
+        del x
+        dec["o"] = torch.empty((w.steps, w.B, w.H, w.dv), dtype=tdt, device=device)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s)")
+
+    stream = torch.cuda.current_stream(device)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    fwd_args = None
+    if pre is not None:
+        ws_bytes = int(L.kla_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+        fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), P(pre["log_alpha"]), None, P(state),
+                    P(pre["o"]), w.B, w.T, w.H, w.dk, w.dv, 64, ctypes.c_float(w.eps), code, P(workspace),
+                    ws_bytes, sp)
+    dec_args = []
+    if dec is not None:
+        for s in range(w.steps):
+            dec_args.append((P(dec["q"][s]), P(dec["k"][s]), P(dec["v"][s]), P(dec["eta"][s]),
+                             P(dec["log_alpha"][s]), P(state), P(dec["o"][s]), w.B, w.H, w.dk, w.dv,
+                             ctypes.c_float(w.eps), code, sp))
+    fwd_fn, dec_fn = L.kla_chunk_fwd, L.kla_decode_step
+
+    if pre is None:  # decode-only workloads start from their S0 and keep decoding step after step
+        state.copy_(dec["S0"])
+
+    def one_step(ev):
+        if fwd_args is not None:
+            ev["fwd"][0].record(stream)
+            st = fwd_fn(*fwd_args)
+            ev["fwd"][1].record(stream)
+            if st:
+                K.check(st)
+        if dec_args:
+            ev["dec"][0].record(stream)
+            for a in dec_args:
+                st = dec_fn(*a)
+                if st:
+                    K.check(st)
+            ev["dec"][1].record(stream)
+
+    def new_events():
+        return {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for p in ("fwd", "dec")}
+
+    log(f"[bench] warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        one_step(new_events())
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} step(s)")
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed region {elapsed * 1e3:.2f} ms")
+
+    parts = {}
+    fwd_tokens = w.B * w.T
+    dec_tokens = w.B * w.steps
+    if fwd_args is not None:
+        ms = sum(e["fwd"][0].elapsed_time(e["fwd"][1]) for e in evs) / args.steps
+        flops = chunk_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
+        nbytes = chunk_bytes(w, es)
+        parts["chunk_fwd"] = {
+            "kernel": "chunk_fwd_kernel", "launches_per_step": 1, "ms_per_step": ms,
+            "kernel_avg_us": ms * 1e3, "tokens": fwd_tokens, "tokens_per_s": fwd_tokens / (ms * 1e-3),
+            "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
+            "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS),
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if dec_args:
+        ms = sum(e["dec"][0].elapsed_time(e["dec"][1]) for e in evs) / args.steps
+        per = ms / w.steps
+        nbytes = decode_bytes(w, es)
+        parts["decode"] = {
+            "kernel": "decode_step_kernel", "launches_per_step": w.steps, "ms_per_step": ms,
+            "kernel_avg_us": per * 1e3, "tokens": dec_tokens, "tokens_per_s": dec_tokens / (ms * 1e-3),
+            "algorithmic_bytes_per_launch": nbytes,
+            "hbm_gbs": nbytes / (per * 1e-3) / 1e9, "hbm_frac": nbytes / (per * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+    dom_name = max(parts, key=lambda p: parts[p]["ms_per_step"])
+    dom = parts[dom_name]
+    if dom_name == "chunk_fwd":
+        roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None,
+                "mfma_view": {"achieved": dom["mfma_tflops"],
+                              "peak": PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS,
+                              "unit": "TFLOP/s", "frac": dom["mfma_frac"]}}
+    else:
+        roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None}
+
+    tokens_per_step = fwd_tokens + dec_tokens
+    ms_step = elapsed * 1e3 / args.steps
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_step * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; distributions of the workload description)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "decode_steps": w.steps, "d_k": w.dk,
+                   "d_v": w.dv, "chunk": 64, "parallelism": "single GPU"},
+        "parts": parts,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on a bounded sample ({args.cpu_head_tokens} head-tokens)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_head_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,7 +16,7 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkla.so"
-SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_fwd.hip"]
+SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

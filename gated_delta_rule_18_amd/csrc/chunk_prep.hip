@@ -1,0 +1,282 @@
+// Chunkwise forward, part 1 of 2: the state-independent work of every chunk, all chunks in
+// parallel (one workgroup per chunk of one head).
+//
+// Sources: "Kaczmarz Linear Attention", Abstract (beta_t = eta_t / (||k_t||^2 + eps));
+// "Deep Dive into KDA", section 3 (intra-chunk accumulated decays by prefix sums; the
+// intra-chunk part as matrix products; the triangular-masked causal scores) and section 5
+// (decay prefixes in the log domain, never dividing by a decayed quantity).
+//
+// For the chunk's tokens r, s (chunk-local, C = 64), with G the inclusive prefix of log(alpha)
+// and rs_r = 1/sqrt(||k_r||^2 + eps):
+//   A[r][s] = eta_r rs_r rs_s exp(G_r - G_s) k_r.k_s  (s < r)   -- a diagonal similarity of
+//             beta_r exp(G_r - G_s) k_r.k_s that keeps |A| <= eta
+//   T       = (I + A)^-1                                          (fp32)
+//   P[r][s] = exp(G_r - G_s) q_r.k_s                  (s <= r)
+// and the per-token factors the scan needs (see chunk_common.h).
+//
+// T is found blockwise on 16 x 16 blocks: the four diagonal blocks by forward substitution in
+// registers (one wave, a lane per column), then the off-diagonal blocks by two doubling steps
+// on fp32 MFMA: T10 = -T11 A10 T00 and T32 = -T33 A32 T22, then
+// T[2:4, 0:2] = -T[2:4, 2:4] (A[2:4, 0:2] T[0:2, 0:2]). T overwrites A in place.
+#include "chunk_common.h"
+
+namespace kla {
+namespace {
+
+template <typename E, int DK>
+struct PrepSmem {
+  static constexpr int PAD = 16 / sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDP = kChunk + PAD;
+  static constexpr int LDF = kChunk + 4;
+  alignas(16) E Ks[kChunk][LDK];
+  alignas(16) E Qs[kChunk][LDK];
+  alignas(16) float Af[kChunk][LDF];  // A, then T in place
+  alignas(16) E Ps[kChunk][LDP];
+  alignas(16) float Ms[2][16][20];    // doubling-step intermediates of waves 0 and 1
+  alignas(16) float M2[32][36];       // A[2:4, 0:2] T[0:2, 0:2]
+  alignas(16) float sc[kScRows][kChunk];
+  float n[kChunk], eta[kChunk], la[kChunk], G[kChunk];
+};
+
+// A-operand or B-operand fragments of one 16-row tile over the contraction [0, K).
+template <typename E, int K>
+struct Frag {
+  static constexpr int STEP = is_bf16<E>() ? 32 : 4;
+  static constexpr int N = K / STEP;
+  typedef typename std::conditional<is_bf16<E>(), bf16x8, float>::type V;
+  V v[N];
+  __device__ __forceinline__ void load(const E* base, int ld, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (is_bf16<E>())
+        v[i] = *reinterpret_cast<const bf16x8*>(base + r * ld + i * 32 + 8 * kq);
+      else
+        v[i] = base[r * ld + i * 4 + kq];
+    }
+  }
+};
+
+template <typename E, int K>
+__device__ __forceinline__ void mma_frag(f32x4& acc, const Frag<E, K>& a, const Frag<E, K>& b) {
+#pragma unroll
+  for (int i = 0; i < Frag<E, K>::N; ++i) {
+    if constexpr (is_bf16<E>())
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b.v[i], acc, 0, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+  }
+}
+
+// Make this wave's LDS writes visible to its own later reads (other lanes).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
+  constexpr bool BF = is_bf16<E>();
+  constexpr int VN = Vec16<E>::N;
+  typedef typename Vec16<E>::type V16;
+  typedef PrepSmem<E, DK> Sm;
+  constexpr int LDK = Sm::LDK, LDF = Sm::LDF;
+  __shared__ Sm sm;
+
+  const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
+  const int64_t head = chunk_id / p.nchunks, c = chunk_id % p.nchunks;
+  const int64_t bb = head / p.H, hh = head % p.H;
+  const int64_t T = p.T, t0 = c * kChunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const E* __restrict__ gk = static_cast<const E*>(p.k);
+  const E* __restrict__ gq = static_cast<const E*>(p.q);
+  auto row_index = [&](int64_t t) { return (bb * T + t) * p.H + hh; };
+  Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
+
+  // ---- K and Q rows (zero past T), squared key norms, gates ----
+  {
+    constexpr int VPR = DK / VN, RPI = kThreads / VPR, IT = kChunk / RPI;
+    const int vc = tid % VPR;
+    V16 kv[IT], qv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = it * RPI + tid / VPR;
+      if (t0 + r < T) {
+        kv[it] = *reinterpret_cast<const V16*>(gk + row_index(t0 + r) * DK + vc * VN);
+        qv[it] = *reinterpret_cast<const V16*>(gq + row_index(t0 + r) * DK + vc * VN);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) kv[it][e] = qv[it][e] = from_f32<E>(0.f);
+      }
+    }
+    if (tid < kChunk) {
+      const bool valid = t0 + tid < T;
+      sm.eta[tid] = valid ? p.eta[row_index(t0 + tid)] : 0.f;
+      sm.la[tid] = valid ? p.log_alpha[row_index(t0 + tid)] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = it * RPI + tid / VPR;
+      *reinterpret_cast<V16*>(&sm.Ks[r][vc * VN]) = kv[it];
+      *reinterpret_cast<V16*>(&sm.Qs[r][vc * VN]) = qv[it];
+      float nn = 0.f;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const float x = to_f32(kv[it][e]);
+        nn += x * x;
+      }
+      nn = group_sum<VPR>(nn);
+      if (vc == 0) sm.n[r] = nn;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-token factors (wave 0) ----
+  if (wave == 0) {
+    const int r = lane;
+    const float G = wave_inclusive_scan(sm.la[r]);
+    const float GC = __shfl(G, kChunk - 1, kWave);  // padded rows add log 1 = 0
+    const float rs = (t0 + r < T) ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
+    sm.G[r] = G;
+    sm.sc[kScCoefR][r] = sm.eta[r] * rs;
+    sm.sc[kScEG][r] = __expf(G);
+    sm.sc[kScRs][r] = rs;
+    sm.sc[kScD2][r] = rs * __expf(GC - G);
+  }
+  __syncthreads();
+
+  // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): lower 16 x 16 tiles;
+  //      waves 0 and 2 take row tiles {0, 3}, waves 1 and 3 take {1, 2} (five tiles each) ----
+  {
+    const bool isP = wave >= 2;
+    const E* X = isP ? &sm.Qs[0][0] : &sm.Ks[0][0];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ti = (wave & 1) ? 1 + half : 3 * half;
+      Frag<E, DK> a;
+      a.load(X + ti * 16 * LDK, LDK, lane);
+      for (int tj = 0; tj <= ti; ++tj) {
+        Frag<E, DK> b;
+        b.load(&sm.Ks[tj * 16][0], LDK, lane);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma_frag(acc, a, b);
+        const int s = tj * 16 + lr;
+        const float Gs = sm.G[s], rss = sm.sc[kScRs][s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = ti * 16 + 4 * lq + e;
+          const float dec = __expf(sm.G[r] - Gs);
+          if (isP)
+            sm.Ps[r][s] = from_f32<E>(s <= r ? dec * acc[e] : 0.f);
+          else
+            sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * rss * dec * acc[e] : 0.f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- diagonal blocks of T by forward substitution (wave 0); waves 1-3 store P and the factors ----
+  if (wave == 0) {
+    const int base = (lane >> 4) * 16, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* arow = &sm.Af[base + i][base];
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
+      x[i] = (i == col) ? 1.f : -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
+  } else {
+    const int t = tid - kWave;  // 0 .. 191
+    constexpr int VPR = kChunk / VN;
+    E* gP = ws.P + chunk_id * kChunk * kChunk;
+    for (int i = t; i < kChunk * VPR; i += kThreads - kWave) {
+      const int r = i / VPR, c0 = (i % VPR) * VN;
+      V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
+      if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
+#pragma unroll
+        for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
+      }
+      *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
+    }
+    float* gS = ws.SC + chunk_id * kScRows * kChunk;
+    for (int i = t; i < kScRows * kChunk; i += kThreads - kWave) gS[i] = (&sm.sc[0][0])[i];
+  }
+  __syncthreads();
+
+  // ---- T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1) ----
+  if (wave < 2) {
+    const int i = 1 + 2 * wave, j = 2 * wave;
+    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(m, &sm.Af[16 * i][16 * j], LDF, 1, &sm.Af[16 * j][16 * j], LDF, 1, 0, 16, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Ms[wave][4 * lq + e][lr] = m[e];
+    wave_lds_sync();
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(t, &sm.Af[16 * i][16 * i], LDF, 1, &sm.Ms[wave][0][0], 20, 1, 0, 16, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Af[16 * i + 4 * lq + e][16 * j + lr] = -t[e];
+  }
+  __syncthreads();
+
+  // ---- M2 = A[2:4, 0:2] T[0:2, 0:2] (T lower: column block tj starts at row 16 tj) ----
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(m, &sm.Af[32 + 16 * ti][0], LDF, 1, &sm.Af[0][16 * tj], LDF, 1, 16 * tj, 32, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.M2[16 * ti + 4 * lq + e][16 * tj + lr] = m[e];
+  }
+  __syncthreads();
+  // ---- T[2:4, 0:2] = -T[2:4, 2:4] M2 (T[2:4, 2:4] lower: row block ti needs k < 16 (ti + 1)) ----
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(t, &sm.Af[32 + 16 * ti][32], LDF, 1, &sm.M2[0][16 * tj], 36, 1, 0, 16 * (ti + 1), lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Af[32 + 16 * ti + 4 * lq + e][16 * tj + lr] = -t[e];
+  }
+  __syncthreads();
+
+  // ---- T to the workspace (upper off-diagonal blocks are zero) ----
+  {
+    constexpr int VPR = kChunk / VN;
+    E* gT = ws.T + chunk_id * kChunk * kChunk;
+    for (int i = tid; i < kChunk * VPR; i += kThreads) {
+      const int r = i / VPR, c0 = (i % VPR) * VN;
+      V16 out;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const int s = c0 + e;
+        out[e] = from_f32<E>((s >> 4) > (r >> 4) ? 0.f : sm.Af[r][s]);
+      }
+      *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
+    }
+  }
+  (void)BF;
+}
+
+template <typename E>
+hipError_t launch_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
+  const int64_t grid = p.heads * p.nchunks;
+  if (d_k == 128)
+    hipLaunchKernelGGL((chunk_prep_kernel<E, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<E, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream) {
+  return bf16_io ? launch_e<bf16>(p, d_k, stream) : launch_e<float>(p, d_k, stream);
+}
+
+}  // namespace kla

@@ -103,6 +103,15 @@ def test_prepare_beta_rejects(kw, status):
     assert prep(**kw) == status
 
 
+def test_chunk_fwd_requires_its_workspace():
+    need = K.lib().kla_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    assert need > 0
+    assert chunk() == K.KLA_ERR_INVALID_VALUE
+    assert b"workspace" in L().kla_last_error()
+    assert chunk(ws=A16 * 64, ws_bytes=need - 1) == K.KLA_ERR_INVALID_VALUE
+    assert chunk(ws=A16 + 256, ws_bytes=need) == K.KLA_ERR_INVALID_VALUE  # overlaps q
+
+
 def test_workspace_size_is_host_only():
     assert K.lib().kla_chunk_fwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16) >= 0
     assert K.lib().kla_chunk_fwd_workspace_size(8, 4096, 8, 96, 128, 64, K.KLA_BF16) == 0

@@ -13,12 +13,16 @@
 //   S <- e^{G_C} S + K^T diag(e^{G_C - G}) D'
 // W S is never formed: W S = T diag(beta e^G) K S, folded into the single product T R.
 //
-// One workgroup (4 waves) owns one d_v slice (DVS columns) of one head and walks its chunks in
-// order. The slice of S stays in fp32 MFMA accumulators for the whole sequence; a bf16 copy
-// of S^T in LDS is the operand of the next chunk's K S and Q S. While chunk n is computed, the
-// inputs of chunk n+1 (K, Q, V slice, T, P, factors) are already in flight into registers.
-// The slices of one head get workgroup ids congruent mod 8, so they run on one XCD and share
-// its L2 for K, Q, T and P.
+// One workgroup of 8 waves owns one d_v slice (DVS columns) of one head and walks its chunks
+// in order. Waves 0-3 ("K waves") own token rows 16h of K, X and R, and S rows
+// [h DK/4, (h+1) DK/4); waves 4-7 ("Q waves") own token rows 16h of Q, Y and O. Every wave
+// computes one 16 x 16 tile of D. The slice of S stays in fp32 MFMA accumulators of the K
+// waves for the whole sequence; a bf16 copy of S^T in LDS is the B operand of K S and Q S.
+// A operands that belong to one wave's rows (K, Q, T, P) come from global memory straight
+// into MFMA fragment registers, one chunk ahead; K is also kept in LDS (double-buffered) so
+// that the K waves can read K^T fragments with the transposing LDS read of gfx950. The
+// slices of one head get workgroup ids congruent mod 8, so they run on one XCD and share its
+// L2 for K, Q, T and P. Three workgroup barriers per chunk.
 #include "chunk_common.h"
 
 namespace kla {
@@ -27,37 +31,102 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = kScanWaves * kWave;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <typename E, int DK, int DVS>
 struct ScanSmem {
-  static constexpr bool BF = is_bf16<E>();
   static constexpr int PAD = 16 / sizeof(E);
-  static constexpr int LDK = DK + PAD;      // Ks, Qs, STs rows
-  static constexpr int LDC = kChunk + PAD;  // KTs, Tb, Pb, RTs, DTs, DTs2 rows
-  static constexpr int LDO = DVS + PAD;     // Vs, Os rows
-  alignas(16) E Ks[kChunk][LDK];
-  alignas(16) E Qs[kChunk][LDK];
-  alignas(16) E KTs[BF ? DK : 1][LDC];      // K^T (bf16 path; fp32 reads Ks transposed)
-  alignas(16) E Vs[kChunk][LDO];
-  alignas(16) E Tb[kChunk][LDC];
-  alignas(16) E Pb[kChunk][LDC];
-  alignas(16) float sc[kScRows][kChunk];
-  alignas(16) E STs[DVS][LDK];
-  alignas(16) E RTs[DVS][LDC];
-  alignas(16) E DTs[DVS][LDC];
-  alignas(16) E DTs2[DVS][LDC];
-  alignas(16) E Os[kChunk][LDO];
+  static constexpr int LDK = DK + PAD;      // Ks, STs rows
+  static constexpr int LDC = kChunk + PAD;  // RTs, DTs, DTs2 rows
+  alignas(16) E Ks[2][kChunk][LDK];         // K of chunks n (buffer n & 1)
+  alignas(16) E STs[DVS][LDK];              // S^T slice (bf16 operand copy of the state)
+  alignas(16) E RTs[DVS][LDC];              // R^T
+  alignas(16) E DTs[DVS][LDC];              // D'^T
+  alignas(16) E DTs2[DVS][LDC];             // (diag(e^{G_C - G}) D')^T
 };
 
+// Per-lane MFMA fragments of 16 rows over a contraction of K elements.
+template <typename E, int K>
+struct Frag {
+  static constexpr int STEP = is_bf16<E>() ? 32 : 4;
+  static constexpr int N = K / STEP;
+  typedef typename std::conditional<is_bf16<E>(), bf16x8, float>::type V;
+  V v[N];
+  // rows base[r * ld + ...], r = lane % 16; valid = whether this lane's row exists
+  __device__ __forceinline__ void load(const E* base, int64_t ld, bool valid, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if constexpr (is_bf16<E>()) {
+        if (valid) {
+          v[i] = *reinterpret_cast<const bf16x8*>(base + r * ld + i * 32 + 8 * kq);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[i][e] = from_f32<bf16>(0.f);
+        }
+      } else {
+        v[i] = valid ? base[r * ld + i * 4 + kq] : 0.f;
+      }
+    }
+  }
+};
+
+template <typename E, int K>
+__device__ __forceinline__ void mma_frag(f32x4& acc, const Frag<E, K>& a, const E* B, int ldb, int nsteps,
+                                         int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < Frag<E, K>::N; ++i) {
+    if (i < nsteps) {
+      if constexpr (is_bf16<E>()) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(B + r * ldb + i * 32 + 8 * kq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], B[r * ldb + i * 4 + kq], acc, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// acc += K^T[m0 .. m0+16) [tokens 0..64) * B^T, with K row-major in LDS (Ks[token][d]) and B
+// stored [16 cols][ldb] token-contiguous. bf16: the A fragments come from two transposing
+// LDS reads (ds_read_b64_tr_b16) per 32-token step.
+template <typename E, int LDK>
+__device__ __forceinline__ void mma_kt(f32x4& acc, const E* Ks, int m0, const E* B, int ldb, int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+  if constexpr (is_bf16<E>()) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // lane (kq, r) supplies row 32s + 8kq + (r >> 2) (+4), columns m0 + 4 (r & 3) .. +3; it receives
+      // K[32s + 8kq + j][m0 + r] for j = 0..3 (and 4..7).
+      const E* p0 = Ks + (32 * s + 8 * kq + (r >> 2)) * LDK + m0 + 4 * (r & 3);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * LDK));
+      const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, both);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(B + r * ldb + 32 * s + 8 * kq);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < kChunk; k0 += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(k0 + kq) * LDK + m0 + r], B[r * ldb + k0 + kq], acc, 0, 0, 0);
+  }
+}
+
 template <typename E, int DK, int DV, int DVS>
-__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ChunkParams p) {
-  constexpr bool BF = is_bf16<E>();
-  constexpr int NS = DV / DVS;     // d_v slices per head
-  constexpr int TJ = DVS / 16;     // 16-column tiles per slice
-  constexpr int RT = DK / 64;      // 16-row tiles of S per wave
-  constexpr int VN = Vec16<E>::N;  // elements per 16-byte vector
-  typedef typename Vec16<E>::type V16;
+__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p) {
+  constexpr int NS = DV / DVS;   // d_v slices per head
+  constexpr int TJ = DVS / 16;   // 16-column tiles per slice
+  constexpr int RT = DK / 64;    // 16-row tiles of S per K wave
   typedef ScanSmem<E, DK, DVS> Sm;
   constexpr int LDK = Sm::LDK, LDC = Sm::LDC;
+  constexpr int STEP = is_bf16<E>() ? 32 : 4;
   __shared__ Sm sm;
 
   const int bid = blockIdx.x;
@@ -67,106 +136,75 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ChunkParams p) {
   const int slice = local % NS;
   if (head >= p.heads) return;
   const int64_t bb = head / p.H, hh = head % p.H;
-  const int64_t T = p.T, nchunks = p.nchunks;
+  const int64_t T = p.T, nchunks = p.nchunks, H = p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool kwave = wave < 4;
+  const int h = wave & 3;  // token-row tile of this wave
   const int lr = lane & 15, lq = lane >> 4;
   const int j0 = slice * DVS;
-  const E* __restrict__ gq = static_cast<const E*>(p.q);
-  const E* __restrict__ gk = static_cast<const E*>(p.k);
-  const E* __restrict__ gv = static_cast<const E*>(p.v);
-  E* __restrict__ go = static_cast<E*>(p.o);
-  auto row_index = [&](int64_t t) { return (bb * T + t) * p.H + hh; };
+  // Tile of D = T R this wave computes: row tile h, column tile dtj (all waves when TJ = 2).
+  const int dtj = wave >> 2;
+  const bool dwave = dtj < TJ;
+  const int kend = is_bf16<E>() ? (h < 2 ? 32 : 64) : 16 * (h + 1);  // T, P row block h: zero past 16(h+1)
+  const int tsteps = kend / STEP;
+
+  const E* gx = static_cast<const E*>(kwave ? p.k : p.q) + (bb * T * H + hh) * DK;  // token t at + t H DK
+  const E* gv = static_cast<const E*>(p.v) + (bb * T * H + hh) * DV + j0;
+  E* go = static_cast<E*>(p.o) + (bb * T * H + hh) * DV + j0;
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * nchunks);
   const int64_t chunk0 = head * nchunks;
 
-  // ---- register prefetch of one chunk's inputs ----
-  constexpr int KVPR = DK / VN;                                   // vectors per K/Q row
-  constexpr int NKV = kChunk * KVPR / kThreads;                   // K (and Q) vectors per thread
-  constexpr int VVPR = DVS / VN;                                  // vectors per V-slice row
-  constexpr int NVV = (kChunk * VVPR + kThreads - 1) / kThreads;  // V vectors per thread (ceil)
-  constexpr int TVPR = kChunk / VN;                               // vectors per T/P row
-  constexpr int NTV = kChunk * TVPR / kThreads;                   // T (and P) vectors per thread
-  static_assert(NKV * kThreads == kChunk * KVPR && NTV * kThreads == kChunk * TVPR, "tiling");
-  V16 pk[NKV], pq[NKV], pv[NVV], pt[NTV], pp[NTV];
-  float psc;
-
-  auto prefetch = [&](int64_t c) {
+  // ---- prefetched inputs of one chunk (per wave: its own rows) ----
+  struct In {
+    Frag<E, DK> x;      // K rows (K waves) or Q rows (Q waves) 16h .. 16h + 15
+    Frag<E, 64> t;      // T rows 16h (first tsteps steps)
+    Frag<E, 64> pm;     // P rows 16h (Q waves)
+    E v[TJ][4];         // V[16h + 4lq + e][16 tj + lr] (K waves)
+    f32x4 sc[kScRows];  // per-token factors of rows 16h + 4lq .. +3
+    float eGC;
+  };
+  auto fetch = [&](In& in, int64_t c) {
     const int64_t t0 = c * kChunk;
+    // Frag::load adds this lane's row (lane % 16) to the tile's first row t0 + 16h.
+    in.x.load(gx + (t0 + 16 * h) * H * DK, H * DK, t0 + 16 * h + lr < T, lane);
+    const E* gT = ws.T + (chunk0 + c) * kChunk * kChunk + 16 * h * kChunk;
+    const E* gP = ws.P + (chunk0 + c) * kChunk * kChunk + 16 * h * kChunk;
+    const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < NKV; ++i) {
-      const int idx = tid + i * kThreads, r = idx / KVPR, vc = idx % KVPR;
-      if (t0 + r < T) {
-        pk[i] = *reinterpret_cast<const V16*>(gk + row_index(t0 + r) * DK + vc * VN);
-        pq[i] = *reinterpret_cast<const V16*>(gq + row_index(t0 + r) * DK + vc * VN);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VN; ++e) pk[i][e] = pq[i][e] = from_f32<E>(0.f);
+    for (int i = 0; i < Frag<E, 64>::N; ++i) {
+      if (i < tsteps) {
+        if constexpr (is_bf16<E>()) {
+          in.t.v[i] = *reinterpret_cast<const bf16x8*>(gT + r * kChunk + i * 32 + 8 * kq);
+          if (!kwave) in.pm.v[i] = *reinterpret_cast<const bf16x8*>(gP + r * kChunk + i * 32 + 8 * kq);
+        } else {
+          in.t.v[i] = gT[r * kChunk + i * 4 + kq];
+          if (!kwave) in.pm.v[i] = gP[r * kChunk + i * 4 + kq];
+        }
       }
     }
+    if (kwave) {
 #pragma unroll
-    for (int i = 0; i < NVV; ++i) {
-      const int idx = tid + i * kThreads, r = idx / VVPR, vc = idx % VVPR;
-      if (idx < kChunk * VVPR && t0 + r < T) {
-        pv[i] = *reinterpret_cast<const V16*>(gv + row_index(t0 + r) * DV + j0 + vc * VN);
-      } else {
+      for (int e = 0; e < 4; ++e) {
+        const int64_t t = t0 + 16 * h + 4 * lq + e;
 #pragma unroll
-        for (int e = 0; e < VN; ++e) pv[i][e] = from_f32<E>(0.f);
+        for (int tj = 0; tj < TJ; ++tj) in.v[tj][e] = t < T ? gv[t * H * DV + 16 * tj + lr] : from_f32<E>(0.f);
       }
     }
-    const E* gT = ws.T + (chunk0 + c) * kChunk * kChunk;
-    const E* gP = ws.P + (chunk0 + c) * kChunk * kChunk;
+    const float* gs = ws.SC + (chunk0 + c) * kScRows * kChunk + 16 * h + 4 * lq;
 #pragma unroll
-    for (int i = 0; i < NTV; ++i) {
-      const int idx = tid + i * kThreads;
-      pt[i] = *reinterpret_cast<const V16*>(gT + idx * VN);
-      pp[i] = *reinterpret_cast<const V16*>(gP + idx * VN);
-    }
-    psc = ws.SC[(chunk0 + c) * kScRows * kChunk + tid];
+    for (int q = 0; q < kScRows; ++q) in.sc[q] = *reinterpret_cast<const f32x4*>(gs + q * kChunk);
+    in.eGC = ws.SC[(chunk0 + c) * kScRows * kChunk + kScEG * kChunk + kChunk - 1];
   };
 
-  auto commit = [&]() {
-#pragma unroll
-    for (int i = 0; i < NKV; ++i) {
-      const int idx = tid + i * kThreads, r = idx / KVPR, vc = idx % KVPR;
-      *reinterpret_cast<V16*>(&sm.Ks[r][vc * VN]) = pk[i];
-      *reinterpret_cast<V16*>(&sm.Qs[r][vc * VN]) = pq[i];
-      if constexpr (BF) {
-#pragma unroll
-        for (int e = 0; e < VN; ++e) sm.KTs[vc * VN + e][r] = pk[i][e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NVV; ++i) {
-      const int idx = tid + i * kThreads, r = idx / VVPR, vc = idx % VVPR;
-      if (idx < kChunk * VVPR) *reinterpret_cast<V16*>(&sm.Vs[r][vc * VN]) = pv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NTV; ++i) {
-      const int idx = tid + i * kThreads, r = idx / TVPR, vc = idx % TVPR;
-      *reinterpret_cast<V16*>(&sm.Tb[r][vc * VN]) = pt[i];
-      *reinterpret_cast<V16*>(&sm.Pb[r][vc * VN]) = pp[i];
-    }
-    (&sm.sc[0][0])[tid] = psc;
-  };
-
-  auto store_output = [&](int64_t t0) {
-    for (int i = tid; i < kChunk * VVPR; i += kThreads) {
-      const int r = i / VVPR, vc = i % VVPR;
-      if (t0 + r < T)
-        *reinterpret_cast<V16*>(go + row_index(t0 + r) * DV + j0 + vc * VN) =
-            *reinterpret_cast<const V16*>(&sm.Os[r][vc * VN]);
-    }
-  };
-
-  // ---- state slice -> accumulators; wave w owns S rows [w DK/4, (w+1) DK/4) ----
+  // ---- state slice -> accumulators of the K waves (rows h DK/4 + 16 rt + ...) ----
   f32x4 accS[RT][TJ];
-  {
+  if (kwave) {
     const float* Sin = p.state_in ? p.state_in + head * (int64_t)DK * DV : nullptr;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int tj = 0; tj < TJ; ++tj) {
-        const int row0 = wave * (DK / 4) + rt * 16 + 4 * lq;
+        const int row0 = h * (DK / 4) + rt * 16 + 4 * lq;
         const int col = j0 + tj * 16 + lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) accS[rt][tj][e] = Sin ? Sin[(int64_t)(row0 + e) * DV + col] : 0.f;
@@ -174,101 +212,98 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ChunkParams p) {
                   accS[rt][tj][3]);
       }
   }
+  __syncthreads();
 
-  if (nchunks > 0) prefetch(0);
-  // Row block w of T and P is zero past column 16 (w + 1).
-  const int kend = BF ? (wave < 2 ? 32 : 64) : 16 * (wave + 1);
+  In cur, nxt;
+  if (nchunks > 0) fetch(nxt, 0);
 
   for (int64_t c = 0; c < nchunks; ++c) {
-    if (c > 0) store_output((c - 1) * kChunk);
-    commit();
-    __syncthreads();
-    if (c + 1 < nchunks) prefetch(c + 1);
+    cur = nxt;
+    if (c + 1 < nchunks) fetch(nxt, c + 1);
+    const int buf = c & 1;
+    const int64_t t0 = c * kChunk;
 
-    // ---- X = K S -> R^T;  Y = e^G (Q S) stays in registers ----
-    f32x4 accY[TJ];
+    // ---- K waves: K rows -> LDS (for K^T later), X = K S -> R^T.  Q waves: Y = e^G (Q S) ----
+    f32x4 acc[TJ];
 #pragma unroll
     for (int tj = 0; tj < TJ; ++tj) {
-      f32x4 accX = {0.f, 0.f, 0.f, 0.f};
-      accY[tj] = accX;
+      acc[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      mma_frag(acc[tj], cur.x, &sm.STs[tj * 16][0], LDK, Frag<E, DK>::N, lane);
+    }
+    if (kwave) {
       const int r = lane & 15, kq = lane >> 4;
-      if constexpr (BF) {
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += 32) {
-          const bf16x8 s = *reinterpret_cast<const bf16x8*>(&sm.STs[tj * 16 + r][k0 + 8 * kq]);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.Ks[wave * 16 + r][k0 + 8 * kq]);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sm.Qs[wave * 16 + r][k0 + 8 * kq]);
-          accX = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s, accX, 0, 0, 0);
-          accY[tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, s, accY[tj], 0, 0, 0);
-        }
-      } else {
-        mma16<E>(accX, &sm.Ks[wave * 16][0], LDK, &sm.STs[tj * 16][0], LDK, DK, lane);
-        mma16<E>(accY[tj], &sm.Qs[wave * 16][0], LDK, &sm.STs[tj * 16][0], LDK, DK, lane);
+      for (int i = 0; i < Frag<E, DK>::N; ++i) {
+        if constexpr (is_bf16<E>())
+          *reinterpret_cast<bf16x8*>(&sm.Ks[buf][16 * h + r][i * 32 + 8 * kq]) = cur.x.v[i];
+        else
+          sm.Ks[buf][16 * h + r][i * 4 + kq] = cur.x.v[i];
       }
-      const int jj = tj * 16 + lr;
-      float R[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = wave * 16 + 4 * lq + e;
-        const float eg = sm.sc[kScEG][row];
-        R[e] = sm.sc[kScCoefR][row] * (to_f32(sm.Vs[row][jj]) - eg * accX[e]);
-        accY[tj][e] *= eg;
+      for (int tj = 0; tj < TJ; ++tj) {
+        float R[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          R[e] = cur.sc[kScCoefR][e] * (to_f32(cur.v[tj][e]) - cur.sc[kScEG][e] * acc[tj][e]);
+        store4<E>(&sm.RTs[tj * 16 + lr][16 * h + 4 * lq], R[0], R[1], R[2], R[3]);
       }
-      store4<E>(&sm.RTs[jj][wave * 16 + 4 * lq], R[0], R[1], R[2], R[3]);
+    } else {
+#pragma unroll
+      for (int tj = 0; tj < TJ; ++tj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tj][e] *= cur.sc[kScEG][e];
     }
     __syncthreads();
 
-    // ---- D = T R;  D' = rs D (-> DTs);  diag(e^{G_C - G}) D' (-> DTs2) ----
-#pragma unroll
-    for (int tj = 0; tj < TJ; ++tj) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma16<E>(acc, &sm.Tb[wave * 16][0], LDC, &sm.RTs[tj * 16][0], LDC, kend, lane);
-      const int jj = tj * 16 + lr;
+    // ---- D = T R, tile (h, dtj);  D' = rs D -> DTs;  e^{G_C - G} D' -> DTs2 ----
+    if (dwave) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      mma_frag(d, cur.t, &sm.RTs[dtj * 16][0], LDC, tsteps, lane);
       float d1[4], d2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = wave * 16 + 4 * lq + e;
-        d1[e] = sm.sc[kScRs][row] * acc[e];
-        d2[e] = sm.sc[kScD2][row] * acc[e];
+        d1[e] = cur.sc[kScRs][e] * d[e];
+        d2[e] = cur.sc[kScD2][e] * d[e];
       }
-      store4<E>(&sm.DTs[jj][wave * 16 + 4 * lq], d1[0], d1[1], d1[2], d1[3]);
-      store4<E>(&sm.DTs2[jj][wave * 16 + 4 * lq], d2[0], d2[1], d2[2], d2[3]);
+      store4<E>(&sm.DTs[dtj * 16 + lr][16 * h + 4 * lq], d1[0], d1[1], d1[2], d1[3]);
+      store4<E>(&sm.DTs2[dtj * 16 + lr][16 * h + 4 * lq], d2[0], d2[1], d2[2], d2[3]);
     }
     __syncthreads();
 
-    // ---- O = Y + P D';  S <- e^{G_C} S + K^T DTs2 ----
+    if (kwave) {
+      // ---- S <- e^{G_C} S + K^T DTs2 -> STs ----
 #pragma unroll
-    for (int tj = 0; tj < TJ; ++tj) {
-      mma16<E>(accY[tj], &sm.Pb[wave * 16][0], LDC, &sm.DTs[tj * 16][0], LDC, kend, lane);
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.Os[wave * 16 + 4 * lq + e][tj * 16 + lr] = from_f32<E>(accY[tj][e]);
-    }
-    const float eGC = sm.sc[kScEG][kChunk - 1];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int tj = 0; tj < TJ; ++tj) {
+          const int row0 = h * (DK / 4) + rt * 16;
+          accS[rt][tj] *= cur.eGC;
+          mma_kt<E, LDK>(accS[rt][tj], &sm.Ks[buf][0][0], row0, &sm.DTs2[tj * 16][0], LDC, lane);
+          store4<E>(&sm.STs[tj * 16 + lr][row0 + 4 * lq], accS[rt][tj][0], accS[rt][tj][1], accS[rt][tj][2],
+                    accS[rt][tj][3]);
+        }
+    } else {
+      // ---- O = Y + P D' -> global ----
 #pragma unroll
       for (int tj = 0; tj < TJ; ++tj) {
-        const int row0 = wave * (DK / 4) + rt * 16;
-        accS[rt][tj] *= eGC;
-        if constexpr (BF)
-          mma16<E>(accS[rt][tj], &sm.KTs[row0][0], LDC, &sm.DTs2[tj * 16][0], LDC, kChunk, lane);
-        else
-          mma16_f32s(accS[rt][tj], reinterpret_cast<const float*>(&sm.Ks[0][row0]), 1, LDK,
-                     reinterpret_cast<const float*>(&sm.DTs2[tj * 16][0]), 1, LDC, 0, kChunk, lane);
-        store4<E>(&sm.STs[tj * 16 + lr][row0 + 4 * lq], accS[rt][tj][0], accS[rt][tj][1], accS[rt][tj][2],
-                  accS[rt][tj][3]);
+        mma_frag(acc[tj], cur.pm, &sm.DTs[tj * 16][0], LDC, tsteps, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = t0 + 16 * h + 4 * lq + e;
+          if (t < T) go[t * H * DV + 16 * tj + lr] = from_f32<E>(acc[tj][e]);
+        }
       }
+    }
     __syncthreads();
   }
-  if (nchunks > 0) store_output((nchunks - 1) * kChunk);
 
-  if (p.state_out) {
+  if (p.state_out && kwave) {
     float* Sout = p.state_out + head * (int64_t)DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int tj = 0; tj < TJ; ++tj) {
-        const int row0 = wave * (DK / 4) + rt * 16 + 4 * lq;
+        const int row0 = h * (DK / 4) + rt * 16 + 4 * lq;
         const int col = j0 + tj * 16 + lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sout[(int64_t)(row0 + e) * DV + col] = accS[rt][tj][e];
@@ -278,11 +313,11 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ChunkParams p) {
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
-  constexpr int DVS = is_bf16<E>() ? 32 : 16;
+  constexpr int DVS = 32;
   constexpr int NS = DV / DVS;
   const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, DVS>), dim3((unsigned)(heads8 * NS)), dim3(kThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, DVS>), dim3((unsigned)(heads8 * NS)), dim3(kScanThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -29,8 +29,7 @@ struct PrepSmem {
   static constexpr int LDK = DK + PAD;
   static constexpr int LDP = kChunk + PAD;
   static constexpr int LDF = kChunk + 4;
-  alignas(16) E Ks[kChunk][LDK];
-  alignas(16) E Qs[kChunk][LDK];
+  alignas(16) E Ks[kChunk][LDK];      // K chunk (B operand of K K^T and Q K^T)
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
   alignas(16) float Ms[2][16][20];    // doubling-step intermediates of waves 0 and 1
@@ -46,14 +45,20 @@ struct Frag {
   static constexpr int N = K / STEP;
   typedef typename std::conditional<is_bf16<E>(), bf16x8, float>::type V;
   V v[N];
-  __device__ __forceinline__ void load(const E* base, int ld, int lane) {
+  __device__ __forceinline__ void load(const E* base, int64_t ld, int lane, bool valid = true) {
     const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if constexpr (is_bf16<E>())
-        v[i] = *reinterpret_cast<const bf16x8*>(base + r * ld + i * 32 + 8 * kq);
-      else
-        v[i] = base[r * ld + i * 4 + kq];
+      if constexpr (is_bf16<E>()) {
+        if (valid) {
+          v[i] = *reinterpret_cast<const bf16x8*>(base + r * ld + i * 32 + 8 * kq);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[i][e] = from_f32<bf16>(0.f);
+        }
+      } else {
+        v[i] = valid ? base[r * ld + i * 4 + kq] : 0.f;
+      }
     }
   }
 };
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;
   typedef PrepSmem<E, DK> Sm;
-  constexpr int LDK = Sm::LDK, LDF = Sm::LDF;
+  constexpr int LDF = Sm::LDF;
   __shared__ Sm sm;
 
   const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
@@ -96,40 +101,44 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   auto row_index = [&](int64_t t) { return (bb * T + t) * p.H + hh; };
   Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
 
-  // ---- K and Q rows (zero past T), squared key norms, gates ----
-  {
-    constexpr int VPR = DK / VN, RPI = kThreads / VPR, IT = kChunk / RPI;
-    const int vc = tid % VPR;
-    V16 kv[IT], qv[IT];
+  // ---- K rows (waves 0, 1) and Q rows (waves 2, 3) straight into MFMA A fragments: waves 0 and 2
+  //      take row tiles {0, 3}, waves 1 and 3 take {1, 2}. The K waves also put K into LDS (the
+  //      B operand of both products) and form the squared key norms. ----
+  const bool qwave = wave >= 2;
+  const int ti0 = (wave & 1) ? 1 : 0, ti1 = (wave & 1) ? 2 : 3;
+  const E* gx = (qwave ? gq : gk) + (bb * T * p.H + hh) * DK;  // token t at + t H DK
+  Frag<E, DK> a0, a1;
+  a0.load(gx + (t0 + 16 * ti0) * p.H * DK, p.H * DK, lane, t0 + 16 * ti0 + lr < T);
+  a1.load(gx + (t0 + 16 * ti1) * p.H * DK, p.H * DK, lane, t0 + 16 * ti1 + lr < T);
+  if (tid < kChunk) {
+    const bool valid = t0 + tid < T;
+    sm.eta[tid] = valid ? p.eta[row_index(t0 + tid)] : 0.f;
+    sm.la[tid] = valid ? p.log_alpha[row_index(t0 + tid)] : 0.f;
+  }
+  if (!qwave) {
+    const int kq = lane >> 4;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int r = it * RPI + tid / VPR;
-      if (t0 + r < T) {
-        kv[it] = *reinterpret_cast<const V16*>(gk + row_index(t0 + r) * DK + vc * VN);
-        qv[it] = *reinterpret_cast<const V16*>(gq + row_index(t0 + r) * DK + vc * VN);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VN; ++e) kv[it][e] = qv[it][e] = from_f32<E>(0.f);
-      }
-    }
-    if (tid < kChunk) {
-      const bool valid = t0 + tid < T;
-      sm.eta[tid] = valid ? p.eta[row_index(t0 + tid)] : 0.f;
-      sm.la[tid] = valid ? p.log_alpha[row_index(t0 + tid)] : 0.f;
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int r = it * RPI + tid / VPR;
-      *reinterpret_cast<V16*>(&sm.Ks[r][vc * VN]) = kv[it];
-      *reinterpret_cast<V16*>(&sm.Qs[r][vc * VN]) = qv[it];
+    for (int half = 0; half < 2; ++half) {
+      const Frag<E, DK>& a = half ? a1 : a0;
+      const int row = 16 * (half ? ti1 : ti0) + lr;
       float nn = 0.f;
 #pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        const float x = to_f32(kv[it][e]);
-        nn += x * x;
+      for (int i = 0; i < Frag<E, DK>::N; ++i) {
+        if constexpr (BF) {
+          *reinterpret_cast<bf16x8*>(&sm.Ks[row][i * 32 + 8 * kq]) = a.v[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = to_f32(a.v[i][e]);
+            nn += x * x;
+          }
+        } else {
+          sm.Ks[row][i * 4 + kq] = a.v[i];
+          nn += a.v[i] * a.v[i];
+        }
       }
-      nn = group_sum<VPR>(nn);
-      if (vc == 0) sm.n[r] = nn;
+      nn += __shfl_xor(nn, 16, kWave);
+      nn += __shfl_xor(nn, 32, kWave);
+      if (kq == 0) sm.n[row] = nn;
     }
   }
   __syncthreads();
@@ -148,28 +157,29 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   }
   __syncthreads();
 
-  // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): lower 16 x 16 tiles;
-  //      waves 0 and 2 take row tiles {0, 3}, waves 1 and 3 take {1, 2} (five tiles each) ----
+  // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): the lower 16 x 16 tiles of
+  //      this wave's two row tiles (five tiles per wave) ----
   {
-    const bool isP = wave >= 2;
-    const E* X = isP ? &sm.Qs[0][0] : &sm.Ks[0][0];
+    Frag<E, DK> bk[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj)
+      if (tj <= ti1) bk[tj].load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int ti = (wave & 1) ? 1 + half : 3 * half;
-      Frag<E, DK> a;
-      a.load(X + ti * 16 * LDK, LDK, lane);
-      for (int tj = 0; tj <= ti; ++tj) {
-        Frag<E, DK> b;
-        b.load(&sm.Ks[tj * 16][0], LDK, lane);
+      const int ti = half ? ti1 : ti0;
+      const Frag<E, DK>& a = half ? a1 : a0;
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        if (tj > ti) continue;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma_frag(acc, a, b);
+        mma_frag(acc, a, bk[tj]);
         const int s = tj * 16 + lr;
         const float Gs = sm.G[s], rss = sm.sc[kScRs][s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = ti * 16 + 4 * lq + e;
           const float dec = __expf(sm.G[r] - Gs);
-          if (isP)
+          if (qwave)
             sm.Ps[r][s] = from_f32<E>(s <= r ? dec * acc[e] : 0.f);
           else
             sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * rss * dec * acc[e] : 0.f;
@@ -252,10 +262,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
     for (int i = tid; i < kChunk * VPR; i += kThreads) {
       const int r = i / VPR, c0 = (i % VPR) * VN;
       V16 out;
+      const bool zero = (c0 >> 4) > (r >> 4);  // upper off-diagonal block
 #pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        const int s = c0 + e;
-        out[e] = from_f32<E>((s >> 4) > (r >> 4) ? 0.f : sm.Af[r][s]);
+      for (int e4 = 0; e4 < VN; e4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Af[r][c0 + e4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
       }
       *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
     }

@@ -19,7 +19,7 @@
 // computes one 16 x 16 tile of D. The slice of S stays in fp32 MFMA accumulators of the K
 // waves for the whole sequence; a bf16 copy of S^T in LDS is the B operand of K S and Q S.
 // A operands that belong to one wave's rows (K, Q, T, P) come from global memory straight
-// into MFMA fragment registers, one chunk ahead; K is also kept in LDS (double-buffered) so
+// into MFMA fragment registers, one to two chunks ahead; K is also kept in LDS (double-buffered) so
 // that the K waves can read K^T fragments with the transposing LDS read of gfx950. The
 // slices of one head get workgroup ids congruent mod 8, so they run on one XCD and share its
 // L2 for K, Q, T and P. Three workgroup barriers per chunk.
@@ -37,6 +37,40 @@ constexpr int kScanThreads = kScanWaves * kWave;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resources: a load whose byte offset is at or past `bytes` returns zeros and such a
+// store is dropped, so rows past T need no branches (and no branch breaks the compiler's
+// counting of outstanding loads).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Make this wave's LDS writes visible to its own later reads (other lanes).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename E>
+__device__ __forceinline__ typename Vec16<E>::type load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(typename Vec16<E>::type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <typename E>
+__device__ __forceinline__ E load1(rsrc_t r, uint32_t off) {
+  if constexpr (is_bf16<E>())
+    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <typename E>
+__device__ __forceinline__ void store1(E x, rsrc_t r, uint32_t off) {
+  if constexpr (is_bf16<E>())
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, off, 0, 0);
+}
 
 template <typename E, int DK, int DVS>
 struct ScanSmem {
@@ -48,6 +82,7 @@ struct ScanSmem {
   alignas(16) E RTs[DVS][LDC];              // R^T
   alignas(16) E DTs[DVS][LDC];              // D'^T
   alignas(16) E DTs2[DVS][LDC];             // (diag(e^{G_C - G}) D')^T
+  alignas(16) E Xs[8][16][DVS + PAD];       // per wave: its V tile (K waves) or O tile (Q waves)
 };
 
 // Per-lane MFMA fragments of 16 rows over a contraction of K elements.
@@ -57,21 +92,16 @@ struct Frag {
   static constexpr int N = K / STEP;
   typedef typename std::conditional<is_bf16<E>(), bf16x8, float>::type V;
   V v[N];
-  // rows base[r * ld + ...], r = lane % 16; valid = whether this lane's row exists
-  __device__ __forceinline__ void load(const E* base, int64_t ld, bool valid, int lane) {
+  // Row r = lane % 16 of the tile lies at byte offset off0 + r * ld_bytes of the resource.
+  __device__ __forceinline__ void load(rsrc_t rs, uint32_t off0, uint32_t ld_bytes, int lane) {
     const int r = lane & 15, kq = lane >> 4;
+    const uint32_t off = off0 + r * ld_bytes;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if constexpr (is_bf16<E>()) {
-        if (valid) {
-          v[i] = *reinterpret_cast<const bf16x8*>(base + r * ld + i * 32 + 8 * kq);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[i][e] = from_f32<bf16>(0.f);
-        }
-      } else {
-        v[i] = valid ? base[r * ld + i * 4 + kq] : 0.f;
-      }
+      if constexpr (is_bf16<E>())
+        v[i] = load16<E>(rs, off + (i * 32 + 8 * kq) * sizeof(E));
+      else
+        v[i] = load1<E>(rs, off + (i * 4 + kq) * sizeof(E));
     }
   }
 };
@@ -137,7 +167,8 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   if (head >= p.heads) return;
   const int64_t bb = head / p.H, hh = head % p.H;
   const int64_t T = p.T, nchunks = p.nchunks, H = p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool kwave = wave < 4;
   const int h = wave & 3;  // token-row tile of this wave
   const int lr = lane & 15, lq = lane >> 4;
@@ -147,53 +178,64 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   const bool dwave = dtj < TJ;
   const int kend = is_bf16<E>() ? (h < 2 ? 32 : 64) : 16 * (h + 1);  // T, P row block h: zero past 16(h+1)
   const int tsteps = kend / STEP;
+  // A wave's 16 x DVS tile of V or O moves as 16-byte pieces: LPR lanes per row, RPL rows per
+  // instruction, VPL instructions.
+  constexpr int VN = Vec16<E>::N, LPR = DVS / VN, RPL = kWave / LPR, VPL = 16 / RPL;
+  const int prow = lane / LPR, pcol = (lane % LPR) * VN;
 
-  const E* gx = static_cast<const E*>(kwave ? p.k : p.q) + (bb * T * H + hh) * DK;  // token t at + t H DK
-  const E* gv = static_cast<const E*>(p.v) + (bb * T * H + hh) * DV + j0;
-  E* go = static_cast<E*>(p.o) + (bb * T * H + hh) * DV + j0;
+  // Resources over this batch's rows of q/k, v and o, and over this head's workspace chunks.
+  // Byte offsets fit in 32 bits (checked on the host). The K waves store O through a resource
+  // of size 0, so both wave roles issue the same memory operations.
+  const int64_t brow = bb * T * H;  // first (token, head) row of this batch
+  const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);  // bytes per token
+  const rsrc_t rx = make_rsrc(static_cast<const E*>(kwave ? p.k : p.q) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, kwave ? (uint32_t)(T * vrow) : 0u);
+  const rsrc_t ro = make_rsrc(static_cast<const E*>(p.o) + brow * DV, kwave ? 0u : (uint32_t)(T * vrow));
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * nchunks);
   const int64_t chunk0 = head * nchunks;
+  constexpr uint32_t kMatBytes = kChunk * kChunk * sizeof(E), kScBytes = kScRows * kChunk * sizeof(float);
+  const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
+  const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
+  const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
+  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);  // head's column offset
 
-  // ---- prefetched inputs of one chunk (per wave: its own rows) ----
-  struct In {
+  // ---- prefetched inputs (per wave: its own rows) ----
+  // InX (K or Q fragments, V, per-token factors) is used up by the D phase of its chunk and is
+  // refilled with chunk c+2 right after; two sets alternate. InT (T, P, e^{G_C}) is refilled
+  // with chunk c+1 right after each part's last use. Loads thus stay in flight for one to two
+  // chunks.
+  struct InX {
     Frag<E, DK> x;      // K rows (K waves) or Q rows (Q waves) 16h .. 16h + 15
+    typename Vec16<E>::type vv[VPL];  // V rows 16h.. of the slice, row-major pieces (K waves)
+    f32x4 sc[kScRows];  // per-token factors of rows 16h + 4lq .. +3
+  };
+  struct InT {
     Frag<E, 64> t;      // T rows 16h (first tsteps steps)
     Frag<E, 64> pm;     // P rows 16h (Q waves)
-    E v[TJ][4];         // V[16h + 4lq + e][16 tj + lr] (K waves)
-    f32x4 sc[kScRows];  // per-token factors of rows 16h + 4lq .. +3
     float eGC;
   };
-  auto fetch = [&](In& in, int64_t c) {
-    const int64_t t0 = c * kChunk;
-    // Frag::load adds this lane's row (lane % 16) to the tile's first row t0 + 16h.
-    in.x.load(gx + (t0 + 16 * h) * H * DK, H * DK, t0 + 16 * h + lr < T, lane);
-    const E* gT = ws.T + (chunk0 + c) * kChunk * kChunk + 16 * h * kChunk;
-    const E* gP = ws.P + (chunk0 + c) * kChunk * kChunk + 16 * h * kChunk;
-    const int r = lane & 15, kq = lane >> 4;
+  // Fetches never branch: chunk indices past the end are clamped to the last chunk (the data
+  // is then unused) and rows past T read as zeros.
+  auto fetch_x = [&](InX& in, int64_t c) {
+    c = c < nchunks ? c : nchunks - 1;
+    const uint32_t t0 = (uint32_t)(c * kChunk);
+    in.x.load(rx, (t0 + 16 * h) * xrow + hcol_x, xrow, lane);
 #pragma unroll
-    for (int i = 0; i < Frag<E, 64>::N; ++i) {
-      if (i < tsteps) {
-        if constexpr (is_bf16<E>()) {
-          in.t.v[i] = *reinterpret_cast<const bf16x8*>(gT + r * kChunk + i * 32 + 8 * kq);
-          if (!kwave) in.pm.v[i] = *reinterpret_cast<const bf16x8*>(gP + r * kChunk + i * 32 + 8 * kq);
-        } else {
-          in.t.v[i] = gT[r * kChunk + i * 4 + kq];
-          if (!kwave) in.pm.v[i] = gP[r * kChunk + i * 4 + kq];
-        }
-      }
-    }
-    if (kwave) {
+    for (int i = 0; i < VPL; ++i)
+      in.vv[i] = load16<E>(rv, (t0 + 16 * h + i * RPL + prow) * vrow + hcol_v + pcol * sizeof(E));
+    const uint32_t so = (uint32_t)c * kScBytes + (16 * h + 4 * lq) * sizeof(float);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t t = t0 + 16 * h + 4 * lq + e;
-#pragma unroll
-        for (int tj = 0; tj < TJ; ++tj) in.v[tj][e] = t < T ? gv[t * H * DV + 16 * tj + lr] : from_f32<E>(0.f);
-      }
-    }
-    const float* gs = ws.SC + (chunk0 + c) * kScRows * kChunk + 16 * h + 4 * lq;
-#pragma unroll
-    for (int q = 0; q < kScRows; ++q) in.sc[q] = *reinterpret_cast<const f32x4*>(gs + q * kChunk);
-    in.eGC = ws.SC[(chunk0 + c) * kScRows * kChunk + kScEG * kChunk + kChunk - 1];
+    for (int q = 0; q < kScRows; ++q) in.sc[q] = load16<float>(rsc, so + q * kChunk * sizeof(float));
+  };
+  auto fetch_rows = [&](Frag<E, 64>& f, rsrc_t rs, int64_t c) {  // rows 16h of a [64][64] matrix
+    c = c < nchunks ? c : nchunks - 1;
+    f.load(rs, (uint32_t)c * kMatBytes + 16 * h * kChunk * sizeof(E), kChunk * sizeof(E), lane);
+  };
+  auto fetch_t = [&](InT& in, int64_t c) { fetch_rows(in.t, rt, c); };
+  auto fetch_p = [&](InT& in, int64_t c) {
+    fetch_rows(in.pm, rp, c);
+    const int64_t cc = c < nchunks ? c : nchunks - 1;
+    in.eGC = load1<float>(rsc, (uint32_t)cc * kScBytes + (kScEG * kChunk + kChunk - 1) * sizeof(float));
   };
 
   // ---- state slice -> accumulators of the K waves (rows h DK/4 + 16 rt + ...) ----
@@ -214,12 +256,16 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   }
   __syncthreads();
 
-  In cur, nxt;
-  if (nchunks > 0) fetch(nxt, 0);
+  InX x0, x1;
+  InT ct;
+  if (nchunks > 0) {
+    fetch_x(x0, 0);
+    fetch_t(ct, 0);
+    fetch_p(ct, 0);
+    fetch_x(x1, 1);
+  }
 
-  for (int64_t c = 0; c < nchunks; ++c) {
-    cur = nxt;
-    if (c + 1 < nchunks) fetch(nxt, c + 1);
+  auto step = [&](int64_t c, InX& cx) {
     const int buf = c & 1;
     const int64_t t0 = c * kChunk;
 
@@ -228,46 +274,52 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
 #pragma unroll
     for (int tj = 0; tj < TJ; ++tj) {
       acc[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      mma_frag(acc[tj], cur.x, &sm.STs[tj * 16][0], LDK, Frag<E, DK>::N, lane);
+      mma_frag(acc[tj], cx.x, &sm.STs[tj * 16][0], LDK, Frag<E, DK>::N, lane);
     }
     if (kwave) {
       const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
       for (int i = 0; i < Frag<E, DK>::N; ++i) {
         if constexpr (is_bf16<E>())
-          *reinterpret_cast<bf16x8*>(&sm.Ks[buf][16 * h + r][i * 32 + 8 * kq]) = cur.x.v[i];
+          *reinterpret_cast<bf16x8*>(&sm.Ks[buf][16 * h + r][i * 32 + 8 * kq]) = cx.x.v[i];
         else
-          sm.Ks[buf][16 * h + r][i * 4 + kq] = cur.x.v[i];
+          sm.Ks[buf][16 * h + r][i * 4 + kq] = cx.x.v[i];
       }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        *reinterpret_cast<typename Vec16<E>::type*>(&sm.Xs[wave][i * RPL + prow][pcol]) = cx.vv[i];
+      wave_lds_sync();
 #pragma unroll
       for (int tj = 0; tj < TJ; ++tj) {
         float R[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          R[e] = cur.sc[kScCoefR][e] * (to_f32(cur.v[tj][e]) - cur.sc[kScEG][e] * acc[tj][e]);
+          R[e] = cx.sc[kScCoefR][e] * (to_f32(sm.Xs[wave][4 * lq + e][16 * tj + lr]) - cx.sc[kScEG][e] * acc[tj][e]);
         store4<E>(&sm.RTs[tj * 16 + lr][16 * h + 4 * lq], R[0], R[1], R[2], R[3]);
       }
     } else {
 #pragma unroll
       for (int tj = 0; tj < TJ; ++tj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[tj][e] *= cur.sc[kScEG][e];
+        for (int e = 0; e < 4; ++e) acc[tj][e] *= cx.sc[kScEG][e];
     }
     __syncthreads();
 
     // ---- D = T R, tile (h, dtj);  D' = rs D -> DTs;  e^{G_C - G} D' -> DTs2 ----
     if (dwave) {
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      mma_frag(d, cur.t, &sm.RTs[dtj * 16][0], LDC, tsteps, lane);
+      mma_frag(d, ct.t, &sm.RTs[dtj * 16][0], LDC, tsteps, lane);
       float d1[4], d2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        d1[e] = cur.sc[kScRs][e] * d[e];
-        d2[e] = cur.sc[kScD2][e] * d[e];
+        d1[e] = cx.sc[kScRs][e] * d[e];
+        d2[e] = cx.sc[kScD2][e] * d[e];
       }
       store4<E>(&sm.DTs[dtj * 16 + lr][16 * h + 4 * lq], d1[0], d1[1], d1[2], d1[3]);
       store4<E>(&sm.DTs2[dtj * 16 + lr][16 * h + 4 * lq], d2[0], d2[1], d2[2], d2[3]);
     }
+    fetch_x(cx, c + 2);
+    fetch_t(ct, c + 1);
     __syncthreads();
 
     if (kwave) {
@@ -277,24 +329,34 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
 #pragma unroll
         for (int tj = 0; tj < TJ; ++tj) {
           const int row0 = h * (DK / 4) + rt * 16;
-          accS[rt][tj] *= cur.eGC;
+          accS[rt][tj] *= ct.eGC;
           mma_kt<E, LDK>(accS[rt][tj], &sm.Ks[buf][0][0], row0, &sm.DTs2[tj * 16][0], LDC, lane);
           store4<E>(&sm.STs[tj * 16 + lr][row0 + 4 * lq], accS[rt][tj][0], accS[rt][tj][1], accS[rt][tj][2],
                     accS[rt][tj][3]);
         }
     } else {
-      // ---- O = Y + P D' -> global ----
+      // ---- O = Y + P D' ----
 #pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) {
-        mma_frag(acc[tj], cur.pm, &sm.DTs[tj * 16][0], LDC, tsteps, lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t t = t0 + 16 * h + 4 * lq + e;
-          if (t < T) go[t * H * DV + 16 * tj + lr] = from_f32<E>(acc[tj][e]);
-        }
-      }
+      for (int tj = 0; tj < TJ; ++tj) mma_frag(acc[tj], ct.pm, &sm.DTs[tj * 16][0], LDC, tsteps, lane);
     }
+    // O -> global by both roles (the K waves' resource has size 0: their stores are dropped),
+    // transposed to row-major 16-byte pieces through this wave's LDS slot.
+#pragma unroll
+    for (int tj = 0; tj < TJ; ++tj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.Xs[wave][4 * lq + e][16 * tj + lr] = from_f32<E>(acc[tj][e]);
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(i32x4, *reinterpret_cast<const typename Vec16<E>::type*>(&sm.Xs[wave][i * RPL + prow][pcol])),
+          ro, (uint32_t)(t0 + 16 * h + i * RPL + prow) * vrow + hcol_v + pcol * sizeof(E), 0, 0);
+    fetch_p(ct, c + 1);
     __syncthreads();
+  };
+  for (int64_t c = 0; c < nchunks; c += 2) {
+    step(c, x0);
+    if (c + 1 < nchunks) step(c + 1, x1);
   }
 
   if (p.state_out && kwave) {

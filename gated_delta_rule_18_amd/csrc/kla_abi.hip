@@ -126,6 +126,10 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return KLA_OK;
   }
   if (B * H * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  // The kernels address one batch's rows of q/k/v/o, and one head's workspace, with 32-bit
+  // byte offsets (up to one chunk past T).
+  if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
   if (T > 0 && (!q || !k || !v || !eta || !log_alpha || !o))
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||

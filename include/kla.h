@@ -90,7 +90,9 @@ size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
  *              state_out may equal state_in (in-place update); any other overlap is an error.
  *   o          [B,T,H,d_v] of type dt; must not overlap any input.
  *   T          any length >= 0; a last partial chunk is handled. T = 0 writes
- *              state_out = S_0 and no output.
+ *              state_out = S_0 and no output. One batch entry's q/k/v/o rows must stay
+ *              below 2 GiB ((T + 64) * H * max(d_k, d_v) * element size < 2^31), else
+ *              KLA_ERR_NOT_SUPPORTED.
  *   workspace  device buffer of at least kla_chunk_fwd_workspace_size(...) bytes, or NULL
  *              when that size is 0.
  */

@@ -65,6 +65,7 @@ def prep(dk=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, k=A16, e
     (dict(o=A16 + 64), K.KLA_ERR_INVALID_VALUE),         # o overlaps q
     (dict(s_in=A16 * 32, s_out=A16 * 32 + 256), K.KLA_ERR_INVALID_VALUE),  # partial state overlap
     (dict(B=1 << 40, T=1 << 30), K.KLA_ERR_INVALID_VALUE),  # size overflow
+    (dict(T=1 << 20, H=16), K.KLA_ERR_NOT_SUPPORTED),        # one batch entry past 2 GiB
 ])
 def test_chunk_fwd_rejects(kw, status):
     assert chunk(**kw) == status

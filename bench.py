@@ -16,8 +16,8 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -56,6 +56,40 @@ def decode_bytes(w, es):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Source files of each timed part; the recorded HBM traffic of a part is only reported while
+# these files are byte-identical to the ones the counters were taken on.
+CSRC = os.path.join(ROOT, "gated_delta_rule_18_amd", "csrc")
+PART_SOURCES = {
+    "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "kla_device.h", "kla_launch.h"],
+    "decode": ["decode.hip", "kla_device.h", "kla_launch.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def sources_sha(part):
+    h = hashlib.sha256()
+    for f in PART_SOURCES[part]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, part):
+    """HBM bytes per launch of `part` on `workload`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs recorded in profiles/hbm_traffic.txt (each already scaled by the copy calibration),
+    or None if there is no record for the current sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = sources_sha(part)
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("traffic "):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split()[1:])
+        if kv.get("workload") == workload and kv.get("part") == part and kv.get("sources_sha") == want:
+            return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def cpu_baseline(w, head_tokens):
@@ -213,7 +247,7 @@ def main():
         flops = chunk_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
         nbytes = chunk_bytes(w, es)
         parts["chunk_fwd"] = {
-            "kernel": "chunk_fwd_kernel", "launches_per_step": 1, "ms_per_step": ms,
+            "kernel": "chunk_prep_kernel + chunk_scan_kernel", "launches_per_step": 1, "ms_per_step": ms,
             "kernel_avg_us": ms * 1e3, "tokens": fwd_tokens, "tokens_per_s": fwd_tokens / (ms * 1e-3),
             "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12,
@@ -229,17 +263,17 @@ def main():
             "algorithmic_bytes_per_launch": nbytes,
             "hbm_gbs": nbytes / (per * 1e-3) / 1e9, "hbm_frac": nbytes / (per * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
+    for name, part in parts.items():
+        part["sources_sha"] = sources_sha(name)
+        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, name)
     dom_name = max(parts, key=lambda p: parts[p]["ms_per_step"])
     dom = parts[dom_name]
+    roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": dom["hbm_traffic_bytes_per_launch"]}
     if dom_name == "chunk_fwd":
-        roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None,
-                "mfma_view": {"achieved": dom["mfma_tflops"],
-                              "peak": PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS,
-                              "unit": "TFLOP/s", "frac": dom["mfma_frac"]}}
-    else:
-        roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None}
+        roof["mfma_view"] = {"achieved": dom["mfma_tflops"],
+                             "peak": PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS,
+                             "unit": "TFLOP/s", "frac": dom["mfma_frac"]}
 
     tokens_per_step = fwd_tokens + dec_tokens
     ms_step = elapsed * 1e3 / args.steps

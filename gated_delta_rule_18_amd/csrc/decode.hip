@@ -6,148 +6,111 @@
 //            u = alpha S^T k,  p = alpha S^T q            (one pass over S)
 //            delta = beta (v - u),  o = p + kappa delta    (= S_new^T q)
 //            S <- alpha S + k delta^T                      (in place)
-// The kernel is HBM-bound: it reads and writes the fp32 state once. One workgroup owns
-// one d_v slice of one head and keeps that slice in registers between the read and the
-// write, so the state crosses HBM exactly twice per step.
+// The kernel is HBM-bound: it reads and writes the fp32 state once. One wave owns one d_v
+// slice (DVS columns) of one head: lane (rg, cg) holds rows rg, rg + RG, ... of columns
+// [4 cg, 4 cg + 4) in registers between the read and the write, and every reduction (over
+// d_k for S^T k and S^T q, and for ||k||^2 and k.q) is a wave shuffle. No LDS, no barrier:
+// the only latency is one round trip to memory.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 namespace {
 
-constexpr int kDecodeThreads = 256;
+constexpr int kXcdCount = 8;  // MI355X
 
-// DVS: width of the d_v slice one workgroup owns. Thread t owns columns
-// [4*(t % CG), +4) of the slice (one float4) and rows rg, rg + RG, rg + 2 RG, ...
 template <typename E, int DK, int DV, int DVS>
-__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
+__global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
     E* __restrict__ o, int64_t heads, float eps) {
-  constexpr int CG = DVS / 4;               // float4 column groups per slice
-  constexpr int RG = kDecodeThreads / CG;   // row groups
-  constexpr int RPT = DK / RG;              // rows per thread
-  constexpr int NSLICE = DV / DVS;
-  constexpr int WAVES = kDecodeThreads / kWave;
-  constexpr int RG_PER_WAVE = kWave / CG;   // row groups inside one wave
-  static_assert(RPT >= 1 && DK % RG == 0, "slice too narrow for this d_k");
+  constexpr int CG = DVS / 4;        // float4 column groups of the slice
+  constexpr int RG = kWave / CG;     // row groups
+  constexpr int RPT = DK / RG;       // rows per lane
+  constexpr int NS = DV / DVS;       // slices per head
+  constexpr int KPL = DK / kWave;    // elements of k (and q) per lane for the norms
+  static_assert(RG * CG == kWave && RPT * RG == DK && KPL * kWave == DK, "shape");
 
-  const int64_t head = blockIdx.x / NSLICE;
-  const int slice = blockIdx.x % NSLICE;
+  // Workgroups are dealt round-robin to the 8 XCDs: give the NS slices of one head ids that are
+  // congruent mod 8, so they share one XCD's L2 (slices narrower than a 128-byte line share lines).
+  const int xcd = blockIdx.x % kXcdCount;
+  const int local = blockIdx.x / kXcdCount;
+  const int64_t head = (int64_t)(local / NS) * kXcdCount + xcd;
+  const int slice = local % NS;
   if (head >= heads) return;
-  const int tid = threadIdx.x;
-  const int cg = tid % CG;
-  const int rg = tid / CG;
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x;
+  const int cg = lane % CG, rg = lane / CG;
   const int col0 = slice * DVS + 4 * cg;
 
-  __shared__ float s_k[DK];
-  __shared__ float s_q[DK];
-  __shared__ float s_red[WAVES][2][DVS];
-  __shared__ float s_delta[DVS];
-  __shared__ float s_scalar[2];
-
-  // Issue the state loads first: they are the bulk of the traffic.
+  // State first: it is the bulk of the traffic.
   float* S = state + head * (int64_t)DK * DV;
   f32x4 s[RPT];
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int row = rg + RG * m;
-    s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)row * DV + col0);
-  }
+  for (int m = 0; m < RPT; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0);
 
-  // q and k of this head, as fp32, plus the two reductions ||k||^2 and k.q (wave 0).
-  if (tid < DK) {
-    s_k[tid] = to_f32(k[head * DK + tid]);
-    s_q[tid] = to_f32(q[head * DK + tid]);
+  float kk[KPL], qq[KPL];
+  float nk = 0.f, kq = 0.f;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    kk[j] = to_f32(k[head * DK + lane + kWave * j]);
+    qq[j] = to_f32(q[head * DK + lane + kWave * j]);
+    nk += kk[j] * kk[j];
+    kq += kk[j] * qq[j];
   }
-  __syncthreads();
-  if (wave == 0) {
-    float nk = 0.f, kq = 0.f;
-    for (int i = tid; i < DK; i += kWave) {
-      nk += s_k[i] * s_k[i];
-      kq += s_k[i] * s_q[i];
-    }
-    nk = wave_sum(nk);
-    kq = wave_sum(kq);
-    if (tid == 0) {
-      s_scalar[0] = nk;
-      s_scalar[1] = kq;
-    }
-  }
+  nk = wave_sum(nk);
+  kq = wave_sum(kq);
+  const float alpha = __expf(log_alpha[head]);
+  const float beta = eta[head] / (nk + eps);
+  f32x4 vv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[head * DV + col0 + e]);
 
-  // Partial S^T k and S^T q over this thread's rows.
-  f32x4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+  // Partial S^T k and S^T q over this lane's rows; row r's k and q come from lane r % 64.
+  f32x4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
+  float krow[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
-    const int row = rg + RG * m;
-    const float kr = s_k[row], qr = s_q[row];
-    u += s[m] * kr;
-    p += s[m] * qr;
+    const int r = rg + RG * m;            // (RG * m) / 64 is this row's slot: RG divides 64
+    const int slot = (RG * m) / kWave;
+    krow[m] = __shfl(kk[slot], r % kWave, kWave);
+    const float qr = __shfl(qq[slot], r % kWave, kWave);
+    u += s[m] * krow[m];
+    pq += s[m] * qr;
   }
-  // Reduce over the row groups of this wave (lanes that share cg), then across waves.
 #pragma unroll
   for (int off = CG; off < kWave; off <<= 1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       u[e] += __shfl_xor(u[e], off, kWave);
-      p[e] += __shfl_xor(p[e], off, kWave);
+      pq[e] += __shfl_xor(pq[e], off, kWave);
     }
   }
-  if ((tid % kWave) < CG) {
+  const f32x4 delta = beta * (vv - alpha * u);
+  if (rg == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s_red[wave][0][4 * cg + e] = u[e];
-      s_red[wave][1][4 * cg + e] = p[e];
-    }
+    for (int e = 0; e < 4; ++e) o[head * DV + col0 + e] = from_f32<E>(alpha * pq[e] + kq * delta[e]);
   }
-  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * alpha + delta * krow[m];
+}
 
-  const float alpha = __expf(log_alpha[head]);
-  const float beta = eta[head] / (s_scalar[0] + eps);
-  const float kappa = s_scalar[1];
-  if (tid < DVS) {
-    float uu = 0.f, pp = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      uu += s_red[w][0][tid];
-      pp += s_red[w][1][tid];
-    }
-    const int j = slice * DVS + tid;
-    const float delta = beta * (to_f32(v[head * DV + j]) - alpha * uu);
-    s_delta[tid] = delta;
-    o[head * DV + j] = from_f32<E>(alpha * pp + kappa * delta);
-  }
-  __syncthreads();
-
-  const f32x4 d = *reinterpret_cast<const f32x4*>(&s_delta[4 * cg]);
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int row = rg + RG * m;
-    const f32x4 snew = s[m] * alpha + d * s_k[row];
-    *reinterpret_cast<f32x4*>(S + (int64_t)row * DV + col0) = snew;
-  }
-  (void)RG_PER_WAVE;
+template <typename E, int DK, int DV, int DVS>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t heads = a.B * a.H;
+  const int64_t grid = (heads + kXcdCount - 1) / kXcdCount * kXcdCount * (DV / DVS);
+  hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
+                     a.eps);
+  return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t stream) {
-  // Narrow slices when there are few heads, so that the grid still fills 256 CUs.
-  const int64_t heads = a.B * a.H;
-  if (heads >= 1024 || DV == 64) {
-    constexpr int DVS = DV;
-    const int64_t grid = heads * (DV / DVS);
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS>), dim3((unsigned)grid), dim3(kDecodeThreads), 0,
-                       stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state,
-                       (E*)a.o, heads, a.eps);
-  } else {
-    constexpr int DVS = 32;
-    const int64_t grid = heads * (DV / DVS);
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS>), dim3((unsigned)grid), dim3(kDecodeThreads), 0,
-                       stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state,
-                       (E*)a.o, heads, a.eps);
-  }
-  return hipGetLastError();
+  // Many heads: 32-column slices (16 rows of float4 per lane). Few heads: 16-column slices, so
+  // that the grid still puts a couple of waves on every CU.
+  if (a.B * a.H >= 512) return launch<E, DK, DV, 32>(a, stream);
+  return launch<E, DK, DV, 16>(a, stream);
 }
 
 template <typename E>

@@ -182,7 +182,7 @@ kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const 
     g_last_error[0] = '\0';
     return KLA_OK;
   }
-  if (B * H * 4 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  if ((B * H + 8) * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
   if (!q || !k || !v || !eta || !log_alpha || !state || !o) return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
       !aligned(eta, 4) || !aligned(log_alpha, 4))

@@ -132,7 +132,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-head-tokens", type=int, default=131072,
+    ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
                     help="size of the oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counter scaling)")

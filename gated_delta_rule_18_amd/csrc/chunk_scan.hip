@@ -75,7 +75,9 @@ __device__ __forceinline__ void store1(E x, rsrc_t r, uint32_t off) {
 template <typename E, int DK, int DVS>
 struct ScanSmem {
   static constexpr int PAD = 16 / sizeof(E);
-  static constexpr int LDK = DK + PAD;      // Ks, STs rows
+  // Ks/STs rows: a 32-byte row skew, so the four rows a 16-lane group reads with the
+  // transposing LDS read fall in disjoint bank ranges.
+  static constexpr int LDK = DK + 2 * PAD;
   static constexpr int LDC = kChunk + PAD;  // RTs, DTs, DTs2 rows
   alignas(16) E Ks[2][kChunk][LDK];         // K of chunks n (buffer n & 1)
   alignas(16) E STs[DVS][LDK];              // S^T slice (bf16 operand copy of the state)
@@ -184,8 +186,9 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   const int prow = lane / LPR, pcol = (lane % LPR) * VN;
 
   // Resources over this batch's rows of q/k, v and o, and over this head's workspace chunks.
-  // Byte offsets fit in 32 bits (checked on the host). The K waves store O through a resource
-  // of size 0, so both wave roles issue the same memory operations.
+  // Byte offsets fit in 32 bits (checked on the host). The K waves store O, and load P, through
+  // resources of size 0 (and the Q waves load V so), so both wave roles issue the same memory
+  // operations while only the role that needs the data moves it.
   const int64_t brow = bb * T * H;  // first (token, head) row of this batch
   const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);  // bytes per token
   const rsrc_t rx = make_rsrc(static_cast<const E*>(kwave ? p.k : p.q) + brow * DK, (uint32_t)(T * xrow));
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   const int64_t chunk0 = head * nchunks;
   constexpr uint32_t kMatBytes = kChunk * kChunk * sizeof(E), kScBytes = kScRows * kChunk * sizeof(float);
   const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
-  const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
+  const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, kwave ? 0u : (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
   const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);  // head's column offset
 

@@ -24,6 +24,9 @@ FLAGS = [
     "-I", str(ROOT / "include"), "-I", str(CSRC),
     "-Wno-unused-command-line-argument",
 ]
+# Per-source extra flags. The scan kernel keeps its MFMA accumulators in ordinary VGPRs (the
+# default places them in AGPRs and copies every value the VALU touches).
+EXTRA = {"chunk_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> pathlib.Path:
@@ -32,7 +35,7 @@ def build(verbose: bool = False) -> pathlib.Path:
     procs = []
     for src in SOURCES:
         obj = objdir / (src.rsplit(".", 1)[0] + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", str(CSRC / src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

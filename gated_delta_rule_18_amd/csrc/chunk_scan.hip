@@ -13,16 +13,32 @@
 //   S <- e^{G_C} S + K^T diag(e^{G_C - G}) D'
 // W S is never formed: W S = T diag(beta e^G) K S, folded into the single product T R.
 //
-// One workgroup of 8 waves owns one d_v slice (DVS columns) of one head and walks its chunks
-// in order. Waves 0-3 ("K waves") own token rows 16h of K, X and R, and S rows
-// [h DK/4, (h+1) DK/4); waves 4-7 ("Q waves") own token rows 16h of Q, Y and O. Every wave
-// computes one 16 x 16 tile of D. The slice of S stays in fp32 MFMA accumulators of the K
-// waves for the whole sequence; a bf16 copy of S^T in LDS is the B operand of K S and Q S.
-// A operands that belong to one wave's rows (K, Q, T, P) come from global memory straight
-// into MFMA fragment registers, one to two chunks ahead; K is also kept in LDS (double-buffered) so
-// that the K waves can read K^T fragments with the transposing LDS read of gfx950. The
-// slices of one head get workgroup ids congruent mod 8, so they run on one XCD and share its
-// L2 for K, Q, T and P. Three workgroup barriers per chunk.
+// Work split. A workgroup of W waves owns DVS = 16 W NT columns of one head's state and walks
+// the chunks in order; each wave owns 16 NT of those columns for every d_k row and every token,
+// so the chain S -> X -> R -> D -> (O, S) of its columns never leaves the wave and needs no
+// barrier. The slice of S lives in fp32 MFMA accumulators for the whole sequence. The
+// workgroups of one head get ids congruent mod 8, so they run on one XCD and share its L2.
+//
+// Chaining without data movement. The contraction index of every product is enumerated in
+// the order in which an MFMA accumulator holds its rows, so that the accumulators of one
+// product are, register for register, an operand of the next. In a 16 x 16 accumulator tile,
+// lane (g, c) (g = lane / 16, c = lane % 16) holds rows 4g .. 4g + 3 of column c. A "group" of
+// the contraction is 32 indices for v_mfma_f32_16x16x32_bf16 (one instruction: lane group g
+// feeds indices 32s + 4g + 0..3 from tile 2s and 32s + 16 + 4g + 0..3 from tile 2s + 1) and 16
+// indices for v_mfma_f32_16x16x4_f32 (four instructions: instruction i feeds index
+// 16s + 4g + i from tile s). A and B fragments of these MFMAs have the same lane layout, so an
+// accumulator block serves as B (contracting its rows) or, for a transposed product, as A. The
+// outputs are computed transposed (O^T = S^T Q^T + D'^T P^T), which leaves each lane four
+// consecutive columns of one token row: they go to global memory without a transpose.
+//
+// Operands in LDS. K, Q, T and P are read as A fragments along their rows (two 8-byte reads
+// per bf16 fragment), K also transposed for K^T with the transposing read of gfx950, and V as
+// four consecutive rows of one column (transposing read). All are row-major without padding,
+// their 16-byte chunks XOR-swizzled by row so that these reads are free of bank conflicts.
+// They arrive by direct-to-LDS buffer loads (no registers), a chunk ahead, into a ring of LDS
+// buffers: one workgroup barrier per chunk. Every global access goes through a buffer resource
+// (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
+// around memory operations.
 #include "chunk_common.h"
 
 namespace kla {
@@ -31,135 +47,168 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
-constexpr int kScanWaves = 8;
-constexpr int kScanThreads = kScanWaves * kWave;
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// Raw buffer resources: a load whose byte offset is at or past `bytes` returns zeros and such a
-// store is dropped, so rows past T need no branches (and no branch breaks the compiler's
-// counting of outstanding loads).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-// Make this wave's LDS writes visible to its own later reads (other lanes).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
 }
 
-template <typename E>
-__device__ __forceinline__ typename Vec16<E>::type load16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(typename Vec16<E>::type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-template <typename E>
-__device__ __forceinline__ E load1(rsrc_t r, uint32_t off) {
-  if constexpr (is_bf16<E>())
-    return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-  else
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-template <typename E>
-__device__ __forceinline__ void store1(E x, rsrc_t r, uint32_t off) {
-  if constexpr (is_bf16<E>())
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, off, 0, 0);
-  else
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, off, 0, 0);
+// Wait until at most M of the vector memory operations this wave issued are outstanding, the
+// direct-to-LDS loads included (s_waitcnt vmcnt(M); expcnt and lgkmcnt left at their maxima;
+// these operations complete in issue order). Placed before each barrier that publishes such
+// loads: the compiler's own wait placement does not cover LDS written by them on every path.
+template <int M>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(M >= 0 && M < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((M & 15) | ((M >> 4) << 14) | 0x0F70);
 }
 
-template <typename E, int DK, int DVS>
-struct ScanSmem {
-  static constexpr int PAD = 16 / sizeof(E);
-  // Ks/STs rows: a 32-byte row skew, so the four rows a 16-lane group reads with the
-  // transposing LDS read fall in disjoint bank ranges.
-  static constexpr int LDK = DK + 2 * PAD;
-  static constexpr int LDC = kChunk + PAD;  // RTs, DTs, DTs2 rows
-  alignas(16) E Ks[2][kChunk][LDK];         // K of chunks n (buffer n & 1)
-  alignas(16) E STs[DVS][LDK];              // S^T slice (bf16 operand copy of the state)
-  alignas(16) E RTs[DVS][LDC];              // R^T
-  alignas(16) E DTs[DVS][LDC];              // D'^T
-  alignas(16) E DTs2[DVS][LDC];             // (diag(e^{G_C - G}) D')^T
-  alignas(16) E Xs[8][16][DVS + PAD];       // per wave: its V tile (K waves) or O tile (Q waves)
+// ---- contraction groups ----------------------------------------------------------------------
+template <typename E>
+struct Grp {
+  static constexpr int K = is_bf16<E>() ? 32 : 16;  // contraction indices per group
+  typedef typename std::conditional<is_bf16<E>(), bf16x8, f32x4>::type V;
 };
 
-// Per-lane MFMA fragments of 16 rows over a contraction of K elements.
-template <typename E, int K>
-struct Frag {
-  static constexpr int STEP = is_bf16<E>() ? 32 : 4;
-  static constexpr int N = K / STEP;
-  typedef typename std::conditional<is_bf16<E>(), bf16x8, float>::type V;
-  V v[N];
-  // Row r = lane % 16 of the tile lies at byte offset off0 + r * ld_bytes of the resource.
-  __device__ __forceinline__ void load(rsrc_t rs, uint32_t off0, uint32_t ld_bytes, int lane) {
-    const int r = lane & 15, kq = lane >> 4;
-    const uint32_t off = off0 + r * ld_bytes;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if constexpr (is_bf16<E>())
-        v[i] = load16<E>(rs, off + (i * 32 + 8 * kq) * sizeof(E));
-      else
-        v[i] = load1<E>(rs, off + (i * 4 + kq) * sizeof(E));
-    }
-  }
-};
-
-template <typename E, int K>
-__device__ __forceinline__ void mma_frag(f32x4& acc, const Frag<E, K>& a, const E* B, int ldb, int nsteps,
-                                         int lane) {
-  const int r = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < Frag<E, K>::N; ++i) {
-    if (i < nsteps) {
-      if constexpr (is_bf16<E>()) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(B + r * ldb + i * 32 + 8 * kq);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b, acc, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], B[r * ldb + i * 4 + kq], acc, 0, 0, 0);
-      }
-    }
-  }
-}
-
-// acc += K^T[m0 .. m0+16) [tokens 0..64) * B^T, with K row-major in LDS (Ks[token][d]) and B
-// stored [16 cols][ldb] token-contiguous. bf16: the A fragments come from two transposing
-// LDS reads (ds_read_b64_tr_b16) per 32-token step.
-template <typename E, int LDK>
-__device__ __forceinline__ void mma_kt(f32x4& acc, const E* Ks, int m0, const E* B, int ldb, int lane) {
-  const int r = lane & 15, kq = lane >> 4;
+template <typename E>
+__device__ __forceinline__ f32x4 mma(typename Grp<E>::V a, typename Grp<E>::V b, f32x4 c) {
   if constexpr (is_bf16<E>()) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      // lane (kq, r) supplies row 32s + 8kq + (r >> 2) (+4), columns m0 + 4 (r & 3) .. +3; it receives
-      // K[32s + 8kq + j][m0 + r] for j = 0..3 (and 4..7).
-      const E* p0 = Ks + (32 * s + 8 * kq + (r >> 2)) * LDK + m0 + 4 * (r & 3);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * LDK));
-      const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, both);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(B + r * ldb + 32 * s + 8 * kq);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-    }
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   } else {
 #pragma unroll
-    for (int k0 = 0; k0 < kChunk; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(k0 + kq) * LDK + m0 + r], B[r * ldb + k0 + kq], acc, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+    return c;
   }
 }
 
-template <typename E, int DK, int DV, int DVS>
-__global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p) {
-  constexpr int NS = DV / DVS;   // d_v slices per head
-  constexpr int TJ = DVS / 16;   // 16-column tiles per slice
-  constexpr int RT = DK / 64;    // 16-row tiles of S per K wave
-  typedef ScanSmem<E, DK, DVS> Sm;
-  constexpr int LDK = Sm::LDK, LDC = Sm::LDC;
-  constexpr int STEP = is_bf16<E>() ? 32 : 4;
-  __shared__ Sm sm;
+template <typename E>
+__device__ __forceinline__ typename Grp<E>::V acc_grp(const f32x4* tiles, int s) {
+  if constexpr (is_bf16<E>()) {
+    const f32x4 a = tiles[2 * s], b = tiles[2 * s + 1];
+    bf16x8 v = {from_f32<bf16>(a[0]), from_f32<bf16>(a[1]), from_f32<bf16>(a[2]), from_f32<bf16>(a[3]),
+                from_f32<bf16>(b[0]), from_f32<bf16>(b[1]), from_f32<bf16>(b[2]), from_f32<bf16>(b[3])};
+    return v;
+  } else {
+    return tiles[s];
+  }
+}
+
+// Physical 16-byte chunk of logical chunk cc in row r of a matrix with CPR chunks per row.
+template <typename E, int CPR>
+__device__ __forceinline__ int swz(int r, int cc) {
+  if constexpr (is_bf16<E>()) {
+    static_assert(CPR == 16 || CPR == 8 || CPR == 4, "bf16 row width");
+    if constexpr (CPR == 16) return cc ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    if constexpr (CPR == 8) return cc ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    return cc ^ (((r >> 2) & 1) << 1);
+  } else {
+    static_assert(CPR >= 16, "fp32 row width");
+    return cc ^ (r & 15);
+  }
+}
+
+// Element offset of (r, col) in a swizzled row-major matrix of NCOL columns.
+template <typename E, int NCOL>
+__device__ __forceinline__ int at(int r, int col) {
+  constexpr int PER = 16 / sizeof(E), CPR = NCOL / PER;
+  return r * NCOL + PER * swz<E, CPR>(r, col / PER) + col % PER;
+}
+
+// A operand of group s along row `row` (k = column index).
+template <typename E, int NCOL>
+__device__ __forceinline__ typename Grp<E>::V row_grp(const E* M, int row, int s, int g) {
+  if constexpr (is_bf16<E>()) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(M + at<E, NCOL>(row, 32 * s + 4 * g));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(M + at<E, NCOL>(row, 32 * s + 16 + 4 * g));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return *reinterpret_cast<const f32x4*>(M + at<E, NCOL>(row, 16 * s + 4 * g));
+  }
+}
+
+// A operand of group s of K^T for state row tile rt: A(m, k) = K[k][16 rt + m], k = token.
+template <typename E, int DK>
+__device__ __forceinline__ typename Grp<E>::V kt_grp(const E* Ks, int rt, int s, int g, int c) {
+  if constexpr (is_bf16<E>()) {
+    const int r0 = 32 * s + 4 * g + (c >> 2), col = 16 * rt + 4 * (c & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<E, DK>(r0, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<E, DK>(r0 + 16, col)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = Ks[at<E, DK>(16 * s + 4 * g + i, 16 * rt + c)];
+    return v;
+  }
+}
+
+// Rows r0 + 4g + 0..3 of column col0 + c, as fp32.
+template <typename E, int NCOL>
+__device__ __forceinline__ f32x4 col4(const E* M, int r0, int col0, int g, int c) {
+  f32x4 out;
+  if constexpr (is_bf16<E>()) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(M + at<E, NCOL>(r0 + 4 * g + (c >> 2), col0 + 4 * (c & 3))));
+    const bf16x4 b = __builtin_bit_cast(bf16x4, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = to_f32(b[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = M[at<E, NCOL>(r0 + 4 * g + j, col0 + c)];
+  }
+  return out;
+}
+
+// One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz).
+template <typename E, int DK, int DVS>
+struct ScanBuf {
+  alignas(16) E K[kChunk * DK];
+  alignas(16) E Q[kChunk * DK];
+  alignas(16) E T[kChunk * kChunk];
+  alignas(16) E P[kChunk * kChunk];
+  alignas(16) E V[kChunk * DVS];
+  alignas(16) float sc[kScRows * kChunk];
+};
+
+// Buffers in the ring: two where they fit in 160 KiB of LDS, else one. (A third buffer, for a
+// prefetch distance of two chunks, measured slower: the loads are not the bottleneck once they
+// are a chunk ahead, and the three-way unrolled loop costs registers.)
+template <typename E, int DK, int DVS>
+constexpr int scan_ring() {
+  return 2 * sizeof(ScanBuf<E, DK, DVS>) <= 160 * 1024 ? 2 : 1;
+}
+
+template <typename E, int DK, int DV, int W, int NT>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
+  constexpr bool BF = is_bf16<E>();
+  constexpr int GK = Grp<E>::K;
+  typedef typename Grp<E>::V GV;
+  constexpr int NC = 16 * NT;        // state columns per wave
+  constexpr int DVS = W * NC;        // state columns per workgroup
+  constexpr int NS = DV / DVS;       // workgroups per head
+  constexpr int RTK = DK / 16;       // 16-row tiles of S
+  constexpr int NGD = DK / GK;       // groups over d_k
+  constexpr int NGT = kChunk / GK;   // groups over the chunk's tokens
+  constexpr int PER = 16 / sizeof(E);
+  typedef ScanBuf<E, DK, DVS> Buf;
+  constexpr int NB = scan_ring<E, DK, DVS>();  // LDS buffers: chunks c .. c + NB - 1 in flight
+  constexpr int DIST = NB > 1 ? NB - 1 : 1;     // prefetch distance
+  static_assert(DV % DVS == 0, "shape");
+  // Distinct LDS objects (not an array indexed by chunk), so that the compiler can tell the
+  // buffer being read from the ones later chunks are loaded into.
+  __shared__ Buf buf0;
+  __shared__ typename std::conditional<(NB >= 2), Buf, int>::type buf1;
+  __shared__ typename std::conditional<(NB >= 3), Buf, int>::type buf2;
 
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
@@ -171,219 +220,286 @@ __global__ __launch_bounds__(kScanThreads) void chunk_scan_kernel(ChunkParams p)
   const int64_t T = p.T, nchunks = p.nchunks, H = p.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool kwave = wave < 4;
-  const int h = wave & 3;  // token-row tile of this wave
-  const int lr = lane & 15, lq = lane >> 4;
-  const int j0 = slice * DVS;
-  // Tile of D = T R this wave computes: row tile h, column tile dtj (all waves when TJ = 2).
-  const int dtj = wave >> 2;
-  const bool dwave = dtj < TJ;
-  const int kend = is_bf16<E>() ? (h < 2 ? 32 : 64) : 16 * (h + 1);  // T, P row block h: zero past 16(h+1)
-  const int tsteps = kend / STEP;
-  // A wave's 16 x DVS tile of V or O moves as 16-byte pieces: LPR lanes per row, RPL rows per
-  // instruction, VPL instructions.
-  constexpr int VN = Vec16<E>::N, LPR = DVS / VN, RPL = kWave / LPR, VPL = 16 / RPL;
-  const int prow = lane / LPR, pcol = (lane % LPR) * VN;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int j0 = slice * DVS;  // first state column of this workgroup
+  const int cw = wave * NC;    // first column of this wave within the slice
 
-  // Resources over this batch's rows of q/k, v and o, and over this head's workspace chunks.
-  // Byte offsets fit in 32 bits (checked on the host). The K waves store O, and load P, through
-  // resources of size 0 (and the Q waves load V so), so both wave roles issue the same memory
-  // operations while only the role that needs the data moves it.
-  const int64_t brow = bb * T * H;  // first (token, head) row of this batch
+  // ---- resources: this batch's rows of q/k/v/o, this head's workspace chunks ----
+  const int64_t brow = bb * T * H;
   const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);  // bytes per token
-  const rsrc_t rx = make_rsrc(static_cast<const E*>(kwave ? p.k : p.q) + brow * DK, (uint32_t)(T * xrow));
-  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, kwave ? (uint32_t)(T * vrow) : 0u);
-  const rsrc_t ro = make_rsrc(static_cast<const E*>(p.o) + brow * DV, kwave ? 0u : (uint32_t)(T * vrow));
+  const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, (uint32_t)(T * vrow));
+  const rsrc_t ro = make_rsrc(static_cast<const E*>(p.o) + brow * DV, (uint32_t)(T * vrow));
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * nchunks);
   const int64_t chunk0 = head * nchunks;
   constexpr uint32_t kMatBytes = kChunk * kChunk * sizeof(E), kScBytes = kScRows * kChunk * sizeof(float);
   const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
-  const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, kwave ? 0u : (uint32_t)(nchunks * kMatBytes));
+  const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
-  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);  // head's column offset
+  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
 
-  // ---- prefetched inputs (per wave: its own rows) ----
-  // InX (K or Q fragments, V, per-token factors) is used up by the D phase of its chunk and is
-  // refilled with chunk c+2 right after; two sets alternate. InT (T, P, e^{G_C}) is refilled
-  // with chunk c+1 right after each part's last use. Loads thus stay in flight for one to two
-  // chunks.
-  struct InX {
-    Frag<E, DK> x;      // K rows (K waves) or Q rows (Q waves) 16h .. 16h + 15
-    typename Vec16<E>::type vv[VPL];  // V rows 16h.. of the slice, row-major pieces (K waves)
-    f32x4 sc[kScRows];  // per-token factors of rows 16h + 4lq .. +3
-  };
-  struct InT {
-    Frag<E, 64> t;      // T rows 16h (first tsteps steps)
-    Frag<E, 64> pm;     // P rows 16h (Q waves)
-    float eGC;
-  };
-  // Fetches never branch: chunk indices past the end are clamped to the last chunk (the data
-  // is then unused) and rows past T read as zeros.
-  auto fetch_x = [&](InX& in, int64_t c) {
+  // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the waves. Lane l of
+  // block b fills physical chunk 64 b + l; its source is the logical chunk stored there. ----
+  constexpr int CK = DK / PER, CT = kChunk / PER, CV = DVS / PER;  // 16-byte chunks per row
+  constexpr int BK = kChunk * CK / 64, BT = kChunk * CT / 64, BV = kChunk * CV / 64;  // blocks
+  static_assert(BK % W == 0 && BT % W == 0 && BV % W == 0, "block split");
+  constexpr int NBK = BK / W, NBT = BT / W, NBV = BV / W;
+  // Per-lane byte offsets within a row-block, excluding the chunk's base (fixed for the kernel).
+  uint32_t offk[NBK], offt[NBT], offv[NBV];
+#pragma unroll
+  for (int i = 0; i < NBK; ++i) {
+    const int ph = 64 * (wave + W * i) + lane, r = ph / CK;
+    offk[i] = r * xrow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
+  }
+#pragma unroll
+  for (int i = 0; i < NBT; ++i) {
+    const int ph = 64 * (wave + W * i) + lane, r = ph / CT;
+    offt[i] = (r * CT + swz<E, CT>(r, ph % CT)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < NBV; ++i) {
+    const int ph = 64 * (wave + W * i) + lane, r = ph / CV;
+    offv[i] = r * vrow + hcol_v + 16 * swz<E, CV>(r, ph % CV);
+  }
+  // Every wave issues the same NDMA loads per chunk (the factor block is loaded by all of them,
+  // identical bytes), so that the wait counts below are compile-time constants. A chunk past
+  // the end is clamped to the last one (loaded again, never read).
+  constexpr int NDMA = 2 * NBK + 2 * NBT + NBV + 1;
+  constexpr int NST = 4 * NT;  // output stores per chunk and wave
+  auto fetch = [&](Buf& B, int64_t c) {
     c = c < nchunks ? c : nchunks - 1;
     const uint32_t t0 = (uint32_t)(c * kChunk);
-    in.x.load(rx, (t0 + 16 * h) * xrow + hcol_x, xrow, lane);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      in.vv[i] = load16<E>(rv, (t0 + 16 * h + i * RPL + prow) * vrow + hcol_v + pcol * sizeof(E));
-    const uint32_t so = (uint32_t)c * kScBytes + (16 * h + 4 * lq) * sizeof(float);
-#pragma unroll
-    for (int q = 0; q < kScRows; ++q) in.sc[q] = load16<float>(rsc, so + q * kChunk * sizeof(float));
-  };
-  auto fetch_rows = [&](Frag<E, 64>& f, rsrc_t rs, int64_t c) {  // rows 16h of a [64][64] matrix
-    c = c < nchunks ? c : nchunks - 1;
-    f.load(rs, (uint32_t)c * kMatBytes + 16 * h * kChunk * sizeof(E), kChunk * sizeof(E), lane);
-  };
-  auto fetch_t = [&](InT& in, int64_t c) { fetch_rows(in.t, rt, c); };
-  auto fetch_p = [&](InT& in, int64_t c) {
-    fetch_rows(in.pm, rp, c);
-    const int64_t cc = c < nchunks ? c : nchunks - 1;
-    in.eGC = load1<float>(rsc, (uint32_t)cc * kScBytes + (kScEG * kChunk + kChunk - 1) * sizeof(float));
-  };
-
-  // ---- state slice -> accumulators of the K waves (rows h DK/4 + 16 rt + ...) ----
-  f32x4 accS[RT][TJ];
-  if (kwave) {
-    const float* Sin = p.state_in ? p.state_in + head * (int64_t)DK * DV : nullptr;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) {
-        const int row0 = h * (DK / 4) + rt * 16 + 4 * lq;
-        const int col = j0 + tj * 16 + lr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) accS[rt][tj][e] = Sin ? Sin[(int64_t)(row0 + e) * DV + col] : 0.f;
-        store4<E>(&sm.STs[tj * 16 + lr][row0], accS[rt][tj][0], accS[rt][tj][1], accS[rt][tj][2],
-                  accS[rt][tj][3]);
-      }
-  }
-  __syncthreads();
-
-  InX x0, x1;
-  InT ct;
-  if (nchunks > 0) {
-    fetch_x(x0, 0);
-    fetch_t(ct, 0);
-    fetch_p(ct, 0);
-    fetch_x(x1, 1);
-  }
-
-  auto step = [&](int64_t c, InX& cx) {
-    const int buf = c & 1;
-    const int64_t t0 = c * kChunk;
-
-    // ---- K waves: K rows -> LDS (for K^T later), X = K S -> R^T.  Q waves: Y = e^G (Q S) ----
-    f32x4 acc[TJ];
-#pragma unroll
-    for (int tj = 0; tj < TJ; ++tj) {
-      acc[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      mma_frag(acc[tj], cx.x, &sm.STs[tj * 16][0], LDK, Frag<E, DK>::N, lane);
+    for (int i = 0; i < NBK; ++i) {
+      const int blk = wave + W * i;
+      dma16(rk, B.K + blk * 64 * PER, t0 * xrow + offk[i]);
+      dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
     }
-    if (kwave) {
-      const int r = lane & 15, kq = lane >> 4;
 #pragma unroll
-      for (int i = 0; i < Frag<E, DK>::N; ++i) {
-        if constexpr (is_bf16<E>())
-          *reinterpret_cast<bf16x8*>(&sm.Ks[buf][16 * h + r][i * 32 + 8 * kq]) = cx.x.v[i];
-        else
-          sm.Ks[buf][16 * h + r][i * 4 + kq] = cx.x.v[i];
-      }
+    for (int i = 0; i < NBT; ++i) {
+      const int blk = wave + W * i;
+      dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
+      dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
+    }
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        *reinterpret_cast<typename Vec16<E>::type*>(&sm.Xs[wave][i * RPL + prow][pcol]) = cx.vv[i];
-      wave_lds_sync();
+    for (int i = 0; i < NBV; ++i) {
+      const int blk = wave + W * i;
+      dma16(rv, B.V + blk * 64 * PER, t0 * vrow + offv[i]);
+    }
+    dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
+  };
+
+  // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[16 rt + 4g + e][j0 + cw + 16 ct + c] ----
+  f32x4 S[RTK][NT];
+  if (p.state_in) {
+    const float* Sin = p.state_in + head * (int64_t)DK * DV;
 #pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) {
-        float R[4];
+    for (int r = 0; r < RTK; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          R[e] = cx.sc[kScCoefR][e] * (to_f32(sm.Xs[wave][4 * lq + e][16 * tj + lr]) - cx.sc[kScEG][e] * acc[tj][e]);
-        store4<E>(&sm.RTs[tj * 16 + lr][16 * h + 4 * lq], R[0], R[1], R[2], R[3]);
-      }
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[r][ct][e] = Sin[(int64_t)(16 * r + 4 * g + e) * DV + j0 + cw + 16 * ct + c16];
+  } else {
+#pragma unroll
+    for (int r = 0; r < RTK; ++r)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) S[r][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One chunk: B holds its operands; chunk c + DIST is loaded into Bn meanwhile (Bn held chunk
+  // c - 1). Issue order per wave: the loads of chunks 0 .. DIST - 1, then per chunk k the loads
+  // of chunk k + DIST and the k's output stores. Before chunk c's barrier the loads of chunk c
+  // must be complete: younger are (DIST - 1) chunks of loads and, from c >= DIST on, the stores
+  // of DIST chunks (fewer stores before that: waiting for more is still correct).
+  auto step = [&](Buf& B, Buf& Bn, int64_t c) __attribute__((always_inline)) {
+    if constexpr (NB == 1) {
+      wait_vmem<0>();
     } else {
-#pragma unroll
-      for (int tj = 0; tj < TJ; ++tj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[tj][e] *= cx.sc[kScEG][e];
+      if (c < DIST)
+        wait_vmem<(DIST - 1) * NDMA>();
+      else
+        wait_vmem<(DIST - 1) * NDMA + DIST * NST>();
     }
-    __syncthreads();
+    __syncthreads();  // chunk c's operands are in LDS; every wave is done with chunk c - 1
+    if constexpr (NB > 1) fetch(Bn, c + DIST);
+    const uint32_t t0 = (uint32_t)(c * kChunk);
 
-    // ---- D = T R, tile (h, dtj);  D' = rs D -> DTs;  e^{G_C - G} D' -> DTs2 ----
-    if (dwave) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      mma_frag(d, ct.t, &sm.RTs[dtj * 16][0], LDC, tsteps, lane);
-      float d1[4], d2[4];
+    // ---- X = K S (token rows x this wave's columns) and Y^T = S^T Q^T ----
+    GV sb[NGD][NT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        d1[e] = cx.sc[kScRs][e] * d[e];
-        d2[e] = cx.sc[kScD2][e] * d[e];
-      }
-      store4<E>(&sm.DTs[dtj * 16 + lr][16 * h + 4 * lq], d1[0], d1[1], d1[2], d1[3]);
-      store4<E>(&sm.DTs2[dtj * 16 + lr][16 * h + 4 * lq], d2[0], d2[1], d2[2], d2[3]);
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 tiles[RTK];
+#pragma unroll
+      for (int r = 0; r < RTK; ++r) tiles[r] = S[r][ct];
+#pragma unroll
+      for (int s = 0; s < NGD; ++s) sb[s][ct] = acc_grp<E>(tiles, s);
     }
-    fetch_x(cx, c + 2);
-    fetch_t(ct, c + 1);
-    __syncthreads();
-
-    if (kwave) {
-      // ---- S <- e^{G_C} S + K^T DTs2 -> STs ----
+    f32x4 X[4][NT], Y[NT][4];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int tj = 0; tj < TJ; ++tj) {
-          const int row0 = h * (DK / 4) + rt * 16;
-          accS[rt][tj] *= ct.eGC;
-          mma_kt<E, LDK>(accS[rt][tj], &sm.Ks[buf][0][0], row0, &sm.DTs2[tj * 16][0], LDC, lane);
-          store4<E>(&sm.STs[tj * 16 + lr][row0 + 4 * lq], accS[rt][tj][0], accS[rt][tj][1], accS[rt][tj][2],
-                    accS[rt][tj][3]);
+      for (int ct = 0; ct < NT; ++ct) X[r][ct] = Y[ct][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NGD; ++s) {
+        const GV ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
+        const GV aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
+          Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
         }
-    } else {
-      // ---- O = Y + P D' ----
-#pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) mma_frag(acc[tj], ct.pm, &sm.DTs[tj * 16][0], LDC, tsteps, lane);
+      }
     }
-    // O -> global by both roles (the K waves' resource has size 0: their stores are dropped),
-    // transposed to row-major 16-byte pieces through this wave's LDS slot.
+
+    // ---- R = eta rs (V - e^G X), in place of X ----
 #pragma unroll
-    for (int tj = 0; tj < TJ; ++tj)
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 coefR = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + 16 * r + 4 * g]);
+      const f32x4 eG = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + 16 * r + 4 * g]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.Xs[wave][4 * lq + e][16 * tj + lr] = from_f32<E>(acc[tj][e]);
-    wave_lds_sync();
+      for (int ct = 0; ct < NT; ++ct) {
+        const f32x4 v = col4<E, DVS>(B.V, 16 * r, cw + 16 * ct, g, c16);
+        X[r][ct] = coefR * (v - eG * X[r][ct]);
+      }
+    }
+
+    // ---- D = T R (T lower triangular: row tile r needs tokens below 16 (r + 1)) ----
+    GV rb[NT][NGT];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(i32x4, *reinterpret_cast<const typename Vec16<E>::type*>(&sm.Xs[wave][i * RPL + prow][pcol])),
-          ro, (uint32_t)(t0 + 16 * h + i * RPL + prow) * vrow + hcol_v + pcol * sizeof(E), 0, 0);
-    fetch_p(ct, c + 1);
-    __syncthreads();
+    for (int ct = 0; ct < NT; ++ct) {
+      const f32x4 tiles[4] = {X[0][ct], X[1][ct], X[2][ct], X[3][ct]};
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) rb[ct][s] = acc_grp<E>(tiles, s);
+    }
+    f32x4 D1[NT][4], D2[NT][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      f32x4 d[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) d[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) {
+        if (GK * s < 16 * (r + 1)) {
+          const GV at_ = row_grp<E, kChunk>(B.T, 16 * r + c16, s, g);
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) d[ct] = mma<E>(at_, rb[ct][s], d[ct]);
+        }
+      }
+      const f32x4 rs = *reinterpret_cast<const f32x4*>(&B.sc[kScRs * kChunk + 16 * r + 4 * g]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&B.sc[kScD2 * kChunk + 16 * r + 4 * g]);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        D1[ct][r] = rs * d[ct];
+        D2[ct][r] = dd * d[ct];
+      }
+    }
+    GV b1[NT][NGT], b2[NT][NGT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) {
+        b1[ct][s] = acc_grp<E>(D1[ct], s);
+        b2[ct][s] = acc_grp<E>(D2[ct], s);
+      }
+
+    // ---- O^T = (Y^T scaled by e^G per token) + D'^T P^T ----
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float eGt = B.sc[kScEG * kChunk + 16 * r + c16];
+      f32x4 o[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) o[ct] = eGt * Y[ct][r];
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) {
+        if (GK * s < 16 * (r + 1)) {
+          const GV ap = row_grp<E, kChunk>(B.P, 16 * r + c16, s, g);
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) o[ct] = mma<E>(b1[ct][s], ap, o[ct]);
+        }
+      }
+      const uint32_t off = (t0 + 16 * r + c16) * vrow + hcol_v + (cw + 4 * g) * sizeof(E);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        if constexpr (BF) {
+          const bf16x4 ob = {from_f32<bf16>(o[ct][0]), from_f32<bf16>(o[ct][1]), from_f32<bf16>(o[ct][2]),
+                             from_f32<bf16>(o[ct][3])};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, off + 16 * ct * sizeof(E), 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[ct]), ro, off + 16 * ct * sizeof(E), 0, 0);
+        }
+      }
+    }
+
+    // ---- S <- e^{G_C} S + K^T diag(e^{G_C - G}) D' ----
+    const float eGC = B.sc[kScEG * kChunk + kChunk - 1];
+#pragma unroll
+    for (int r = 0; r < RTK; ++r) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) S[r][ct] *= eGC;
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) {
+        const GV ak = kt_grp<E, DK>(B.K, r, s, g, c16);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) S[r][ct] = mma<E>(ak, b2[ct][s], S[r][ct]);
+      }
+    }
+    if constexpr (NB == 1) {
+      __syncthreads();
+      if (c + 1 < nchunks) fetch(B, c + 1);
+    }
   };
-  for (int64_t c = 0; c < nchunks; c += 2) {
-    step(c, x0);
-    if (c + 1 < nchunks) step(c + 1, x1);
+
+  if (nchunks > 0) {  // chunks 0 .. DIST - 1
+    fetch(buf0, 0);
+    if constexpr (NB == 3) fetch(buf1, 1);
+  }
+  if constexpr (NB == 3) {
+    for (int64_t c = 0; c < nchunks; c += 3) {
+      step(buf0, buf2, c);
+      if (c + 1 < nchunks) step(buf1, buf0, c + 1);
+      if (c + 2 < nchunks) step(buf2, buf1, c + 2);
+    }
+  } else if constexpr (NB == 2) {
+    for (int64_t c = 0; c < nchunks; c += 2) {
+      step(buf0, buf1, c);
+      if (c + 1 < nchunks) step(buf1, buf0, c + 1);
+    }
+  } else {
+    for (int64_t c = 0; c < nchunks; ++c) step(buf0, buf0, c);
   }
 
-  if (p.state_out && kwave) {
+  wait_vmem<0>();  // no load into LDS outlives the workgroup
+  if (p.state_out) {
     float* Sout = p.state_out + head * (int64_t)DK * DV;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int r = 0; r < RTK; ++r)
 #pragma unroll
-      for (int tj = 0; tj < TJ; ++tj) {
-        const int row0 = h * (DK / 4) + rt * 16 + 4 * lq;
-        const int col = j0 + tj * 16 + lr;
+      for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sout[(int64_t)(row0 + e) * DV + col] = accS[rt][tj][e];
-      }
+        for (int e = 0; e < 4; ++e) Sout[(int64_t)(16 * r + 4 * g + e) * DV + j0 + cw + 16 * ct + c16] = S[r][ct][e];
   }
+}
+
+template <typename E, int DK, int DV, int W, int NT>
+hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
+  constexpr int NS = DV / (W * 16 * NT);
+  const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3(W * kWave), 0,
+                     stream, p);
+  return hipGetLastError();
 }
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
-  constexpr int DVS = 32;
-  constexpr int NS = DV / DVS;
-  const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, DVS>), dim3((unsigned)(heads8 * NS)), dim3(kScanThreads), 0,
-                     stream, p);
-  return hipGetLastError();
+  // bf16: two waves of 16 columns per workgroup (32 columns; four workgroups per 128-column
+  // head). This split measured fastest: a wave's time per chunk is set by latency, not by
+  // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
+  // need a single LDS buffer, whose load is not overlapped, so more columns share it).
+  if constexpr (is_bf16<E>())
+    return launch_wnt<E, DK, DV, 2, 1>(p, stream);
+  else
+    return launch_wnt<E, DK, DV, 4, 1>(p, stream);
 }
 
 template <typename E>

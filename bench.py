@@ -10,7 +10,9 @@ output and the decode step. Other workloads (--workload) time one part alone.
 
 Inputs are generated (seeded) and copied to HBM before the timed region. Kernels
 are launched through the C ABI with pre-marshalled pointers on torch's current
-stream; HIP events on that stream time each part. Prints one JSON line.
+stream; the decode steps of a bench step are replayed from a HIP graph captured
+once before timing (--decode-launch eager issues them one call at a time). HIP
+events on that stream time each part. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -132,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-launch", default="graph", choices=("graph", "eager"),
+                    help="decode steps replayed from a HIP graph (default) or launched one call at a time")
     ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
                     help="size of the oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -205,6 +209,27 @@ def main():
     if pre is None:  # decode-only workloads start from their S0 and keep decoding step after step
         state.copy_(dec["S0"])
 
+    def run_decode(launch_stream):
+        for a in dec_args:
+            st = dec_fn(*a[:-1], launch_stream)
+            if st:
+                K.check(st)
+
+    # The decode steps of one bench step are replayed from a HIP graph (as a serving loop
+    # would issue them): one kernel per token either way, but the host's per-call cost
+    # (several microseconds through ctypes) no longer paces a kernel that runs in about as long.
+    dec_graph = None
+    if dec_args and args.decode_launch == "graph":
+        saved = state.clone()
+        run_decode(sp)  # first launches outside capture (module load)
+        torch.cuda.synchronize()
+        dec_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dec_graph):
+            run_decode(ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
+        torch.cuda.synchronize()
+        state.copy_(saved)
+        del saved
+
     def one_step(ev):
         if fwd_args is not None:
             ev["fwd"][0].record(stream)
@@ -214,10 +239,10 @@ def main():
                 K.check(st)
         if dec_args:
             ev["dec"][0].record(stream)
-            for a in dec_args:
-                st = dec_fn(*a)
-                if st:
-                    K.check(st)
+            if dec_graph is not None:
+                dec_graph.replay()
+            else:
+                run_decode(sp)
             ev["dec"][1].record(stream)
 
     def new_events():
@@ -258,7 +283,8 @@ def main():
         per = ms / w.steps
         nbytes = decode_bytes(w, es)
         parts["decode"] = {
-            "kernel": "decode_step_kernel", "launches_per_step": w.steps, "ms_per_step": ms,
+            "kernel": "decode_step_kernel", "launches_per_step": w.steps, "launch": args.decode_launch,
+            "ms_per_step": ms,
             "kernel_avg_us": per * 1e3, "tokens": dec_tokens, "tokens_per_s": dec_tokens / (ms * 1e-3),
             "algorithmic_bytes_per_launch": nbytes,
             "hbm_gbs": nbytes / (per * 1e-3) / 1e9, "hbm_frac": nbytes / (per * 1e-3) / 1e9 / PEAK_HBM_GBS}

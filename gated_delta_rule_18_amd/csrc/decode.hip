@@ -8,9 +8,10 @@
 //            S <- alpha S + k delta^T                      (in place)
 // The kernel is HBM-bound: it reads and writes the fp32 state once. One wave owns one d_v
 // slice (DVS columns) of one head: lane (rg, cg) holds rows rg, rg + RG, ... of columns
-// [4 cg, 4 cg + 4) in registers between the read and the write, and every reduction (over
-// d_k for S^T k and S^T q, and for ||k||^2 and k.q) is a wave shuffle. No LDS, no barrier:
-// the only latency is one round trip to memory.
+// [4 cg, 4 cg + 4) in registers between the read and the write, with the k and q entries of
+// those rows. ||k||^2, k.q, S^T k and S^T q are summed over the lane's rows and then reduced in
+// one pass over the row groups (DPP rotations within 16-lane rows, two exchanges across rows).
+// No LDS, no barrier: the only latency is one round trip to memory.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -18,6 +19,20 @@ namespace kla {
 namespace {
 
 constexpr int kXcdCount = 8;  // MI355X
+
+// Sum of x over the lanes of the wave whose index is congruent to this lane's mod CG (CG a power
+// of two, 4 <= CG <= 16): DPP row rotations inside each 16-lane row, then exchanges across rows.
+template <int CG>
+__device__ __forceinline__ float class_sum(float x) {
+  static_assert(CG == 4 || CG == 8 || CG == 16, "class width");
+  if constexpr (CG == 4)  // row_ror:4
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  if constexpr (CG <= 8)  // row_ror:8
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __shfl_xor(x, 16, kWave);
+  x += __shfl_xor(x, 32, kWave);
+  return x;
+}
 
 template <typename E, int DK, int DV, int DVS>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
@@ -28,8 +43,7 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   constexpr int RG = kWave / CG;     // row groups
   constexpr int RPT = DK / RG;       // rows per lane
   constexpr int NS = DV / DVS;       // slices per head
-  constexpr int KPL = DK / kWave;    // elements of k (and q) per lane for the norms
-  static_assert(RG * CG == kWave && RPT * RG == DK && KPL * kWave == DK, "shape");
+  static_assert(RG * CG == kWave && RPT * RG == DK, "shape");
 
   // Workgroups are dealt round-robin to the 8 XCDs: give the NS slices of one head ids that are
   // congruent mod 8, so they share one XCD's L2 (slices narrower than a 128-byte line share lines).
@@ -42,49 +56,62 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   const int cg = lane % CG, rg = lane / CG;
   const int col0 = slice * DVS + 4 * cg;
 
-  // State first: it is the bulk of the traffic.
+  // Everything is loaded up front: the state rows rg + RG m of this lane's four columns (the bulk
+  // of the traffic), and the k and q entries of those same rows (read directly when a lane has
+  // few rows, which keeps them off the critical path).
   float* S = state + head * (int64_t)DK * DV;
   f32x4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0);
-
-  float kk[KPL], qq[KPL];
-  float nk = 0.f, kq = 0.f;
+  float kr[RPT], qr[RPT];
+  if constexpr (RPT <= 8) {
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    kk[j] = to_f32(k[head * DK + lane + kWave * j]);
-    qq[j] = to_f32(q[head * DK + lane + kWave * j]);
-    nk += kk[j] * kk[j];
-    kq += kk[j] * qq[j];
+    for (int m = 0; m < RPT; ++m) {
+      kr[m] = to_f32(k[head * DK + rg + RG * m]);
+      qr[m] = to_f32(q[head * DK + rg + RG * m]);
+    }
+  } else {
+    // Many rows per lane: load k and q once across the wave and pass row r's values from lane
+    // r % 64 (fewer memory instructions for a kernel that is bound by memory).
+    constexpr int KPL = DK / kWave;
+    float kk[KPL], qq[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      kk[j] = to_f32(k[head * DK + lane + kWave * j]);
+      qq[j] = to_f32(q[head * DK + lane + kWave * j]);
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + RG * m, slot = (RG * m) / kWave;  // RG divides 64
+      kr[m] = __shfl(kk[slot], r % kWave, kWave);
+      qr[m] = __shfl(qq[slot], r % kWave, kWave);
+    }
   }
-  nk = wave_sum(nk);
-  kq = wave_sum(kq);
-  const float alpha = __expf(log_alpha[head]);
-  const float beta = eta[head] / (nk + eps);
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[head * DV + col0 + e]);
+  const float alpha = __expf(log_alpha[head]);
+  const float et = eta[head];
 
-  // Partial S^T k and S^T q over this lane's rows; row r's k and q come from lane r % 64.
+  // Partial sums over this lane's rows, then one joint reduction over the row groups (the lanes
+  // congruent mod CG): ||k||^2, k.q, (S^T k) and (S^T q) for the four columns.
+  float nk = 0.f, kq = 0.f;
   f32x4 u = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-  float krow[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
-    const int r = rg + RG * m;            // (RG * m) / 64 is this row's slot: RG divides 64
-    const int slot = (RG * m) / kWave;
-    krow[m] = __shfl(kk[slot], r % kWave, kWave);
-    const float qr = __shfl(qq[slot], r % kWave, kWave);
-    u += s[m] * krow[m];
-    pq += s[m] * qr;
+    nk += kr[m] * kr[m];
+    kq += kr[m] * qr[m];
+    u += s[m] * kr[m];
+    pq += s[m] * qr[m];
   }
+  nk = class_sum<CG>(nk);
+  kq = class_sum<CG>(kq);
 #pragma unroll
-  for (int off = CG; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u[e] += __shfl_xor(u[e], off, kWave);
-      pq[e] += __shfl_xor(pq[e], off, kWave);
-    }
+  for (int e = 0; e < 4; ++e) {
+    u[e] = class_sum<CG>(u[e]);
+    pq[e] = class_sum<CG>(pq[e]);
   }
+  const float beta = et / (nk + eps);
   const f32x4 delta = beta * (vv - alpha * u);
   if (rg == 0) {
 #pragma unroll
@@ -92,7 +119,7 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   }
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
-    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * alpha + delta * krow[m];
+    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * alpha + delta * kr[m];
 }
 
 template <typename E, int DK, int DV, int DVS>

@@ -271,3 +271,40 @@ def test_decode_continues_chunk_fwd():
     report("decode vs chunk_fwd f32", o=e_o, S=e_S)
     assert e_o <= 1e-4 and e_S <= 1e-4
     assert math.isfinite(e_o)
+
+
+def test_decode_steps_replayed_from_a_hip_graph():
+    """Decode steps captured in a HIP graph (as the benchmark and a serving loop issue them)
+    replay to the eager result, bit for bit, on every replay, with eager work in between."""
+    w = wl.custom("graph", 243, B=4, H=16, dk=128, dv=128, steps=16, dtype="bf16", s0_std=0.02)
+    inp = wl.decode_inputs(w)
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    eta, la, S0 = dev(inp["eta"]), dev(inp["log_alpha"]), dev(inp["S0"])
+    S = S0.clone()
+    o = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda:0")
+
+    def run():
+        for s in range(w.steps):
+            kla.kla_decode_step(q[s], k[s], v[s], eta[s], la[s], S, eps=w.eps, o=o[s])
+
+    run()
+    torch.cuda.synchronize()
+    o_ref, S_ref = o.clone(), S.clone()
+    g = torch.cuda.CUDAGraph()
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    x = dev(wl.prefill_inputs(wl.custom("graph_eager", 244, B=1, H=2, dk=128, dv=128, T=100))["q"], "bf16")
+    for rep in range(3):
+        S.copy_(S0)
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {rep}: outputs differ"
+        assert torch.equal(S, S_ref), f"replay {rep}: state differs"
+        kla.kla_chunk_fwd(x, x, x, torch.full(x.shape[:3], 0.5, device="cuda:0"),
+                          torch.zeros(x.shape[:3], device="cuda:0"))  # eager work between replays
+        torch.cuda.synchronize()

@@ -94,7 +94,14 @@ def recorded_traffic(workload, part):
     return None
 
 
-def cpu_baseline(w, head_tokens):
+def unit_keys(k):
+    """Keys scaled to unit norm: input preparation for the beta-given modes, which are used with
+    normalised keys (the plain delta rule diverges when beta ||k||^2 exceeds 2)."""
+    n = np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+    return (k / np.maximum(n, 1e-3)).astype(np.float32)
+
+
+def cpu_baseline(w, head_tokens, mode="kla"):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: every head
     of the batch over the first head_tokens / (B H) prefill tokens (or decode steps). Single
     threaded; the recurrence costs the same per token at any position."""
@@ -104,7 +111,15 @@ def cpu_baseline(w, head_tokens):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     n = max(1, min(head_tokens // w.heads, w.T if w.T else w.steps))
-    if w.T:
+    if w.T and mode != "kla":
+        x = wl.prefill_inputs(w.with_(T=n))
+        heads = lambda a: np.moveaxis(a, 2, 1).reshape(w.heads, n, *a.shape[3:])  # [B, T, H, ...] -> [BH, T, ...]
+        la = x["log_alpha"] if mode == "gdn" else np.zeros_like(x["log_alpha"])
+        args = (heads(x["q"]), heads(unit_keys(x["k"])), heads(x["v"]), heads(x["eta"]), heads(la))
+        run = lambda: oracle.gated_delta_recurrent(*args)
+        what = (f"oracle gated_delta_recurrent ({mode}) on all {w.heads} heads (B={w.B}, H={w.H}) of the first "
+                f"{n} prefill tokens")
+    elif w.T:
         x = wl.prefill_inputs(w.with_(T=n))
         args = (x["q"], x["k"], x["v"], x["eta"], x["log_alpha"], w.eps)
         run = lambda: oracle.kla_forward(*args)
@@ -134,6 +149,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="kla", choices=("kla", "gdn", "deltanet"),
+                    help="kla: Kaczmarz step from eta (the headline); gdn: beta given (kla_gdn_* entry points, "
+                         "beta drawn like eta, unit-norm keys); deltanet: gdn without the gate")
     ap.add_argument("--decode-launch", default="graph", choices=("graph", "eager"),
                     help="decode steps replayed from a HIP graph (default) or launched one call at a time")
     ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
@@ -174,14 +192,19 @@ def main():
     t_gen = time.perf_counter()
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
     pre = dec = None
+    gdn = args.mode != "kla"
     if w.T:
         x = wl.prefill_inputs(w)
+        if gdn:
+            x["k"] = unit_keys(x["k"])
         pre = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         pre["o"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
     state = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=device)
     if w.steps:
         x = wl.decode_inputs(w)
+        if gdn:
+            x["k"] = unit_keys(x["k"])
         dec = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         dec["o"] = torch.empty((w.steps, w.B, w.H, w.dv), dtype=tdt, device=device)
@@ -195,16 +218,22 @@ def main():
     if pre is not None:
         ws_bytes = int(L.kla_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
-        fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), P(pre["log_alpha"]), None, P(state),
-                    P(pre["o"]), w.B, w.T, w.H, w.dk, w.dv, 64, ctypes.c_float(w.eps), code, P(workspace),
-                    ws_bytes, sp)
+        la = None if args.mode == "deltanet" else P(pre["log_alpha"])
+        if gdn:  # beta drawn like eta
+            fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), la, None, P(state), P(pre["o"]),
+                        w.B, w.T, w.H, w.dk, w.dv, 64, code, P(workspace), ws_bytes, sp)
+        else:
+            fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), la, None, P(state), P(pre["o"]),
+                        w.B, w.T, w.H, w.dk, w.dv, 64, ctypes.c_float(w.eps), code, P(workspace), ws_bytes, sp)
     dec_args = []
     if dec is not None:
         for s in range(w.steps):
-            dec_args.append((P(dec["q"][s]), P(dec["k"][s]), P(dec["v"][s]), P(dec["eta"][s]),
-                             P(dec["log_alpha"][s]), P(state), P(dec["o"][s]), w.B, w.H, w.dk, w.dv,
-                             ctypes.c_float(w.eps), code, sp))
-    fwd_fn, dec_fn = L.kla_chunk_fwd, L.kla_decode_step
+            la = None if args.mode == "deltanet" else P(dec["log_alpha"][s])
+            tail = (code, sp) if gdn else (ctypes.c_float(w.eps), code, sp)
+            dec_args.append((P(dec["q"][s]), P(dec["k"][s]), P(dec["v"][s]), P(dec["eta"][s]), la, P(state),
+                             P(dec["o"][s]), w.B, w.H, w.dk, w.dv) + tail)
+    fwd_fn, dec_fn = ((L.kla_gdn_chunk_fwd, L.kla_gdn_decode_step) if gdn else
+                      (L.kla_chunk_fwd, L.kla_decode_step))
 
     if pre is None:  # decode-only workloads start from their S0 and keep decoding step after step
         state.copy_(dec["S0"])
@@ -291,7 +320,7 @@ def main():
 
     for name, part in parts.items():
         part["sources_sha"] = sources_sha(name)
-        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, name)
+        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, name) if args.mode == "kla" else None
     dom_name = max(parts, key=lambda p: parts[p]["ms_per_step"])
     dom = parts[dom_name]
     roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,
@@ -316,14 +345,14 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded; distributions of the workload description)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "decode_steps": w.steps, "d_k": w.dk,
-                   "d_v": w.dv, "chunk": 64, "parallelism": "single GPU"},
+        "config": {"workload": w.name, "mode": args.mode, "B": w.B, "H": w.H, "T": w.T, "decode_steps": w.steps,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": 64, "parallelism": "single GPU"},
         "parts": parts,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on a bounded sample ({args.cpu_head_tokens} head-tokens)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_head_tokens)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_head_tokens, args.mode)
     print(json.dumps(result), flush=True)
 
 

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     kla_chunk_fwd,
     kla_chunk_fwd_workspace_size,
     kla_decode_step,
+    kla_gdn_chunk_fwd,
+    kla_gdn_decode_step,
     kla_prepare_beta,
     lib,
 )

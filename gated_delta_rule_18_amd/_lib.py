@@ -27,6 +27,8 @@ _SIGNATURES = {
     "kla_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _c_void_p]),
+    "kla_gdn_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_gdn_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_int, _c_void_p]),
     "kla_status_string": (ctypes.c_char_p, [_int]),
     "kla_last_error": (ctypes.c_char_p, []),
 }
@@ -188,4 +190,71 @@ def kla_decode_step(q, k, v, eta, log_alpha, state, eps=1e-6, o=None, stream=Non
     _need(o, "o", (B, H, dv), dt, dev)
     check(lib().kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state), _ptr(o),
                                 B, H, dk, dv, float(eps), _dtype_code(q), _stream(dev, stream)))
+    return o
+
+
+def _fwd_tensors(q, k, v, gate_name, gate, log_alpha, log_alpha_optional, state_in, return_state, o, state_out):
+    torch = _torch()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(gate, gate_name, (B, T, H), torch.float32, dev)
+    if log_alpha is not None or not log_alpha_optional:
+        _need(log_alpha, "log_alpha", (B, T, H), torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(o, "o", (B, T, H, dv), dt, dev)
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", (B, H, dk, dv), torch.float32, dev)
+    return B, T, H, dk, dv, dev, o, state_out
+
+
+def kla_gdn_chunk_fwd(q, k, v, beta, log_alpha=None, state_in=None, return_state=True, o=None, state_out=None,
+                      chunk=CHUNK, workspace=None, stream=None):
+    """Chunkwise gated DeltaNet forward with beta given: as kla_chunk_fwd with beta [B, T, H] fp32
+    in place of eta (no key normalisation, no eps); log_alpha None means alpha = 1 (DeltaNet)."""
+    torch = _torch()
+    B, T, H, dk, dv, dev, o, state_out = _fwd_tensors(q, k, v, "beta", beta, log_alpha, True, state_in,
+                                                      return_state, o, state_out)
+    code = _dtype_code(q)
+    need = kla_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().kla_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(state_in),
+                                  _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, code, _ptr(workspace), ws_bytes,
+                                  _stream(dev, stream)))
+    return o, state_out
+
+
+def kla_gdn_decode_step(q, k, v, beta, log_alpha, state, o=None, stream=None):
+    """One gated DeltaNet decode step with beta [B, H] fp32 given, in place on ``state``;
+    log_alpha [B, H] fp32 or None (alpha = 1). Returns o [B, H, d_v]."""
+    torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, H, dk), dt, dev)
+    _need(k, "k", (B, H, dk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(beta, "beta", (B, H), torch.float32, dev)
+    if log_alpha is not None:
+        _need(log_alpha, "log_alpha", (B, H), torch.float32, dev)
+    _need(state, "state", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(o, "o", (B, H, dv), dt, dev)
+    check(lib().kla_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(state), _ptr(o),
+                                    B, H, dk, dv, _dtype_code(q), _stream(dev, stream)))
     return o

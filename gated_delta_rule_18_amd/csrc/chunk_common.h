@@ -94,6 +94,7 @@ struct ChunkParams {
   void* ws;
   int64_t heads, H, T, nchunks;
   float eps;
+  bool beta_given;  // eta holds beta itself (gated DeltaNet); log_alpha may then be null (alpha = 1)
 };
 
 }  // namespace kla

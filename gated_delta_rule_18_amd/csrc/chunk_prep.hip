@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   a1.load(gx + (t0 + 16 * ti1) * p.H * DK, p.H * DK, lane, t0 + 16 * ti1 + lr < T);
   if (tid < kChunk) {
     const bool valid = t0 + tid < T;
-    sm.eta[tid] = valid ? p.eta[row_index(t0 + tid)] : 0.f;
-    sm.la[tid] = valid ? p.log_alpha[row_index(t0 + tid)] : 0.f;
+    sm.eta[tid] = valid ? p.eta[row_index(t0 + tid)] : 0.f;  // eta, or beta when beta_given
+    sm.la[tid] = valid && p.log_alpha ? p.log_alpha[row_index(t0 + tid)] : 0.f;
   }
   if (!qwave) {
     const int kq = lane >> 4;
@@ -148,9 +148,22 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
     const int r = lane;
     const float G = wave_inclusive_scan(sm.la[r]);
     const float GC = __shfl(G, kChunk - 1, kWave);  // padded rows add log 1 = 0
-    const float rs = (t0 + r < T) ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
+    // Balanced factors: A[r][s] = eta_r rs_r rs_s e^{G_r - G_s} k_r.k_s is a diagonal similarity of
+    // beta_r e^{G_r - G_s} k_r.k_s when beta_r = eta_r rs_r^2. Kaczmarz step: rs = 1/sqrt(|k|^2 + eps).
+    // Given beta (gated DeltaNet): rs = sqrt(|beta|), eta = sign(beta).
+    const bool valid = t0 + r < T;
+    float rs, et;
+    if (p.beta_given) {
+      const float b = sm.eta[r];
+      rs = valid ? sqrtf(fabsf(b)) : 0.f;
+      et = b < 0.f ? -1.f : 1.f;
+      sm.eta[r] = et;
+    } else {
+      rs = valid ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
+      et = sm.eta[r];
+    }
     sm.G[r] = G;
-    sm.sc[kScCoefR][r] = sm.eta[r] * rs;
+    sm.sc[kScCoefR][r] = et * rs;
     sm.sc[kScEG][r] = __expf(G);
     sm.sc[kScRs][r] = rs;
     sm.sc[kScD2][r] = rs * __expf(GC - G);

@@ -519,7 +519,7 @@ size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t, int64
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
   ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
-                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps};
+                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given};
   if (p.nchunks > 0) {
     const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;

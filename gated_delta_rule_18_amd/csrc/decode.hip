@@ -38,7 +38,7 @@ template <typename E, int DK, int DV, int DVS>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
-    E* __restrict__ o, int64_t heads, float eps) {
+    E* __restrict__ o, int64_t heads, float eps, bool beta_given) {
   constexpr int CG = DVS / 4;        // float4 column groups of the slice
   constexpr int RG = kWave / CG;     // row groups
   constexpr int RPT = DK / RG;       // rows per lane
@@ -90,8 +90,8 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[head * DV + col0 + e]);
-  const float alpha = __expf(log_alpha[head]);
-  const float et = eta[head];
+  const float alpha = log_alpha ? __expf(log_alpha[head]) : 1.f;
+  const float et = eta[head];  // eta, or beta itself when beta_given
 
   // Partial sums over this lane's rows, then one joint reduction over the row groups (the lanes
   // congruent mod CG): ||k||^2, k.q, (S^T k) and (S^T q) for the four columns.
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
     u[e] = class_sum<CG>(u[e]);
     pq[e] = class_sum<CG>(pq[e]);
   }
-  const float beta = et / (nk + eps);
+  const float beta = beta_given ? et : et / (nk + eps);
   const f32x4 delta = beta * (vv - alpha * u);
   if (rg == 0) {
 #pragma unroll
@@ -128,7 +128,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = (heads + kXcdCount - 1) / kXcdCount * kXcdCount * (DV / DVS);
   hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS>), dim3((unsigned)grid), dim3(kWave), 0, stream,
                      (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
-                     a.eps);
+                     a.eps, a.beta_given);
   return hipGetLastError();
 }
 

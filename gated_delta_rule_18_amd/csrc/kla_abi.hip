@@ -16,6 +16,11 @@ kla_status_t fail(kla_status_t st, const char* fmt, const char* what) {
   return st;
 }
 
+kla_status_t fail(kla_status_t st, const char* fmt, const char* what, const char* detail) {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, what, detail);
+  return st;
+}
+
 kla_status_t launched(hipError_t e, const char* what) {
   if (e == hipSuccess) {
     g_last_error[0] = '\0';
@@ -107,11 +112,16 @@ size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
   return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
 }
 
-kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
-                           const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
-                           int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  const char* fn = "kla_chunk_fwd";
+}  // extern "C"
+
+namespace {
+
+// kla_chunk_fwd and kla_gdn_chunk_fwd: eta is eta (Kaczmarz step) or beta itself (beta_given,
+// where log_alpha may be null for alpha = 1).
+kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+                            const float* eta, const float* log_alpha, const float* state_in, float* state_out,
+                            void* o, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                            float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (!supported_head(d_k) || !supported_head(d_v))
@@ -130,7 +140,7 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
   // byte offsets (up to one chunk past T).
   if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
-  if (T > 0 && (!q || !k || !v || !eta || !log_alpha || !o))
+  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !o))
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||
       !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4))
@@ -148,10 +158,9 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
               rw = range("workspace", workspace, (int64_t)(need > 0 ? workspace_bytes : 0));
   const Range* ins[6] = {&rq, &rk, &rv, &re, &rl, &rsi};
   for (const Range* i : ins) {
-    if (overlap(ro, *i)) return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: o overlaps %s", i->name);
-    if (i != &rsi && overlap(rso, *i))
-      return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: state_out overlaps %s", i->name);
-    if (overlap(rw, *i)) return fail(KLA_ERR_INVALID_VALUE, "kla_chunk_fwd: workspace overlaps %s", i->name);
+    if (overlap(ro, *i)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps %s", fn, i->name);
+    if (i != &rsi && overlap(rso, *i)) return fail(KLA_ERR_INVALID_VALUE, "%s: state_out overlaps %s", fn, i->name);
+    if (overlap(rw, *i)) return fail(KLA_ERR_INVALID_VALUE, "%s: workspace overlaps %s", fn, i->name);
   }
   if (overlap(ro, rso) || overlap(rw, ro) || overlap(rw, rso))
     return fail(KLA_ERR_INVALID_VALUE, "%s: outputs overlap", fn);
@@ -162,14 +171,14 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return KLA_OK;
   }
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
-                   workspace, workspace_bytes};
+                   workspace, workspace_bytes, beta_given};
   return launched(kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
-                             float* state, void* o, int64_t B, int64_t H, int64_t d_k, int64_t d_v, float eps,
-                             kla_dtype_t dt, void* stream) {
-  const char* fn = "kla_decode_step";
+// kla_decode_step and kla_gdn_decode_step (as chunk_fwd_impl).
+kla_status_t decode_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+                         const float* eta, const float* log_alpha, float* state, void* o, int64_t B, int64_t H,
+                         int64_t d_k, int64_t d_v, float eps, kla_dtype_t dt, void* stream) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (!supported_head(d_k) || !supported_head(d_v))
@@ -183,7 +192,8 @@ kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const 
     return KLA_OK;
   }
   if ((B * H + 8) * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
-  if (!q || !k || !v || !eta || !log_alpha || !state || !o) return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
+  if (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !state || !o)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
       !aligned(eta, 4) || !aligned(log_alpha, 4))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
@@ -194,11 +204,44 @@ kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const 
                         range("log_alpha", log_alpha, B * H * 4)};
   if (overlap(ro, rs)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps state", fn);
   for (const Range& i : ins) {
-    if (overlap(ro, i)) return fail(KLA_ERR_INVALID_VALUE, "kla_decode_step: o overlaps %s", i.name);
-    if (overlap(rs, i)) return fail(KLA_ERR_INVALID_VALUE, "kla_decode_step: state overlaps %s", i.name);
+    if (overlap(ro, i)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps %s", fn, i.name);
+    if (overlap(rs, i)) return fail(KLA_ERR_INVALID_VALUE, "%s: state overlaps %s", fn, i.name);
   }
-  kla::DecodeArgs a{q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt == KLA_BF16};
+  kla::DecodeArgs a{q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt == KLA_BF16, beta_given};
   return launched(kla::launch_decode_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                           const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
+                           int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_chunk_fwd", false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v,
+                        chunk, eps, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,
+                               const float* log_alpha, const float* state_in, float* state_out, void* o, int64_t B,
+                               int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, kla_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_gdn_chunk_fwd", true, q, k, v, beta, log_alpha, state_in, state_out, o, B, T, H, d_k,
+                        d_v, chunk, 0.f, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                             float* state, void* o, int64_t B, int64_t H, int64_t d_k, int64_t d_v, float eps,
+                             kla_dtype_t dt, void* stream) {
+  return decode_impl("kla_decode_step", false, q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt, stream);
+}
+
+kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v, const float* beta,
+                                 const float* log_alpha, float* state, void* o, int64_t B, int64_t H, int64_t d_k,
+                                 int64_t d_v, kla_dtype_t dt, void* stream) {
+  return decode_impl("kla_gdn_decode_step", true, q, k, v, beta, log_alpha, state, o, B, H, d_k, d_v, 0.f, dt,
+                     stream);
 }
 
 }  // extern "C"

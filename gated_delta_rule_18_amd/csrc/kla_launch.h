@@ -21,6 +21,7 @@ struct DecodeArgs {
   int64_t B, H, d_k, d_v;
   float eps;
   bool bf16;
+  bool beta_given;  // eta holds beta itself; log_alpha may be null (alpha = 1)
 };
 
 struct PrepareArgs {
@@ -48,6 +49,7 @@ struct ChunkArgs {
   bool bf16;
   void* workspace;
   size_t workspace_bytes;
+  bool beta_given;  // eta holds beta itself; log_alpha may be null (alpha = 1)
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);

@@ -120,6 +120,38 @@ kla_status_t kla_decode_step(const void* q, const void* k, const void* v,
                              int64_t B, int64_t H, int64_t d_k, int64_t d_v,
                              float eps, kla_dtype_t dt, void* stream);
 
+/*
+ * kla_gdn_chunk_fwd — kla_chunk_fwd with the step size supplied by the caller: the gated
+ * DeltaNet recurrence this method modifies, and DeltaNet itself.
+ * Source: "Deep Dive into KDA", section 2.2 (Gated DeltaNet,
+ * S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t v_t k_t^T, with the same state layout
+ * as above) and section 2.1 (DeltaNet: the same without the gate); "Kaczmarz Linear
+ * Attention", Abstract (KLA changes only how beta_t is obtained, not the recurrence or its
+ * chunkwise algorithm).
+ *   beta       [B,T,H] fp32, beta_t used as given (any finite value; no eps, no key norm).
+ *   log_alpha  [B,T,H] fp32, or NULL for alpha_t = 1 (DeltaNet).
+ * Everything else (layouts, T, state_in/state_out, workspace, kla_chunk_fwd_workspace_size,
+ * errors) is as for kla_chunk_fwd.
+ */
+kla_status_t kla_gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                               const float* beta, const float* log_alpha,
+                               const float* state_in, float* state_out, void* o,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                               kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kla_gdn_decode_step — kla_decode_step with beta supplied by the caller (gated DeltaNet;
+ * DeltaNet when log_alpha is NULL). Source: "Deep Dive into KDA", sections 2.1 and 2.2.
+ *   beta [B,H] fp32 as given; log_alpha [B,H] fp32 or NULL (alpha = 1). Otherwise as
+ *   kla_decode_step: u = alpha S^T k, p = alpha S^T q, delta = beta (v - u),
+ *   o = p + (k.q) delta, S <- alpha S + k delta^T (in place).
+ */
+kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v,
+                                 const float* beta, const float* log_alpha,
+                                 float* state, void* o,
+                                 int64_t B, int64_t H, int64_t d_k, int64_t d_v,
+                                 kla_dtype_t dt, void* stream);
+
 /* Static text for a status code. */
 const char* kla_status_string(kla_status_t status);
 

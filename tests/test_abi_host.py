@@ -16,7 +16,8 @@ def L():
 def test_exports_every_declared_symbol():
     names = K.declared_functions()
     assert set(names) == {"kla_prepare_beta", "kla_chunk_fwd_workspace_size", "kla_chunk_fwd",
-                          "kla_decode_step", "kla_status_string", "kla_last_error"}
+                          "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
+                          "kla_last_error"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -123,3 +124,44 @@ def test_python_wrapper_rejects_without_gpu_work():
     q = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         K.kla_chunk_fwd(q, q, q[..., :32].contiguous(), torch.zeros(1, 4, 2), torch.zeros(1, 4, 1))
+
+
+def gdn_chunk(dk=128, dv=128, chunk_len=64, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16, k=A16 * 2, v=A16 * 3,
+              beta=A16 * 4, la=A16 * 5, o=A16 * 6):
+    return L().kla_gdn_chunk_fwd(p(q), p(k), p(v), p(beta) if beta else None, p(la) if la else None, None, None,
+                                 p(o), B, T, H, dk, dv, chunk_len, dt, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(chunk_len=16), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(beta=0), K.KLA_ERR_INVALID_VALUE),                      # beta is required
+    (dict(beta=A16 * 4 + 2), K.KLA_ERR_INVALID_VALUE),            # misaligned
+    (dict(o=A16 * 2 + 64), K.KLA_ERR_INVALID_VALUE),              # o overlaps k
+    (dict(la=0, o=A16 * 2 + 64), K.KLA_ERR_INVALID_VALUE),        # log_alpha may be null; o still overlaps k
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),                        # ... and the workspace is still required
+])
+def test_gdn_chunk_fwd_rejects(kw, status):
+    assert gdn_chunk(**kw) == status
+    assert L().kla_last_error().startswith(b"kla_gdn_chunk_fwd")
+
+
+def gdn_decode(dk=128, dv=128, dt=K.KLA_BF16, B=1, H=1, beta=A16 * 4, la=A16 * 5, state=A16 * 8, o=A16 * 16):
+    return L().kla_gdn_decode_step(p(A16), p(A16 * 2), p(A16 * 3), p(beta) if beta else None,
+                                   p(la) if la else None, p(state) if state else None, p(o), B, H, dk, dv, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(beta=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(state=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(la=0, o=A16 * 8 + 16), K.KLA_ERR_INVALID_VALUE),        # null log_alpha accepted; o inside the state
+    (dict(dt=5), K.KLA_ERR_INVALID_VALUE),
+])
+def test_gdn_decode_step_rejects(kw, status):
+    assert gdn_decode(**kw) == status
+
+
+def test_gdn_empty_is_a_no_op():
+    assert gdn_decode(B=0) == K.KLA_OK
+    assert gdn_chunk(B=0) == K.KLA_OK

@@ -308,3 +308,102 @@ def test_decode_steps_replayed_from_a_hip_graph():
         kla.kla_chunk_fwd(x, x, x, torch.full(x.shape[:3], 0.5, device="cuda:0"),
                           torch.zeros(x.shape[:3], device="cuda:0"))  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- gated DeltaNet / DeltaNet (beta given)
+
+def _unit_keys(k):
+    """Keys scaled to unit norm (input preparation for the beta-given modes, which are used with
+    normalised keys: with ||k|| up to 4 and beta up to 1 the delta rule itself diverges)."""
+    n = np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+    return (k / np.maximum(n, 1e-3)).astype(np.float32)
+
+
+def _gdn_case(w, with_gate=True, beta_sign=1.0):
+    inp = wl.prefill_inputs(w)
+    inp["k"] = wl.round_to_bf16(_unit_keys(inp["k"])) if w.dtype == "bf16" else _unit_keys(inp["k"])
+    beta = (inp["eta"] * beta_sign).astype(np.float32)  # drawn like eta: sigmoid(N(0, 1))
+    la = inp["log_alpha"] if with_gate else np.zeros_like(inp["log_alpha"])
+    return inp, beta, la
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gated", [True, False], ids=["gdn", "deltanet"])
+@pytest.mark.parametrize("dk,dv,T", [(128, 128, 250), (64, 64, 131), (128, 64, 64)])
+def test_gdn_chunk_fwd(dtype, gated, dk, dv, T):
+    w = wl.custom("gdn", 250, B=2, H=3, dk=dk, dv=dv, T=T, dtype=dtype)
+    inp, beta, la = _gdn_case(w, gated)
+    o, S = kla.kla_gdn_chunk_fwd(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype), dev(beta),
+                                 dev(la) if gated else None)
+    torch.cuda.synchronize()
+    heads = all_heads(w)
+    ro, rS = oracle.gated_delta_recurrent(_sel(inp["q"], heads), _sel(inp["k"], heads), _sel(inp["v"], heads),
+                                          _sel(beta, heads), _sel(la, heads))
+    eo = rel_l2(_sel(host(o), heads), ro)
+    eS = rel_l2(np.stack([host(S)[b, h] for b, h in heads]), rS)
+    report(f"gdn chunk {dtype} {'gated' if gated else 'deltanet'} dk={dk} dv={dv} T={T}", o=eo, S_T=eS)
+    assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gdn_chunk_fwd_signed_and_zero_beta(dtype):
+    """beta of either sign (the balanced factors use |beta| and its sign), zero beta on a
+    stretch of tokens, and an initial state."""
+    w = wl.custom("gdn_sign", 251, B=1, H=4, dk=128, dv=128, T=200, dtype=dtype, s0_std=0.05)
+    inp, beta, la = _gdn_case(w)
+    beta = beta * np.where(np.arange(w.T) % 3 == 0, -0.5, 1.0)[None, :, None].astype(np.float32)
+    beta[:, 40:90] = 0.0
+    S0 = np.random.default_rng(7).normal(0, 0.05, (1, 4, 128, 128)).astype(np.float32)
+    o, S = kla.kla_gdn_chunk_fwd(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype), dev(beta),
+                                 dev(la), state_in=dev(S0))
+    torch.cuda.synchronize()
+    heads = all_heads(w)
+    ro, rS = oracle.gated_delta_recurrent(_sel(inp["q"], heads), _sel(inp["k"], heads), _sel(inp["v"], heads),
+                                          _sel(beta, heads), _sel(la, heads), np.stack([S0[b, h] for b, h in heads]))
+    eo = rel_l2(_sel(host(o), heads), ro)
+    eS = rel_l2(np.stack([host(S)[b, h] for b, h in heads]), rS)
+    report(f"gdn chunk signed/zero beta {dtype}", o=eo, S_T=eS)
+    assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
+
+
+def test_gdn_with_the_kaczmarz_step_equals_kla():
+    """Feeding kla_gdn_chunk_fwd the library's own Kaczmarz step (kla_prepare_beta) reproduces
+    kla_chunk_fwd: the two balanced factorisations of the same recurrence agree."""
+    w = wl.custom("gdn_vs_kla", 252, B=2, H=2, dk=128, dv=128, T=300)
+    inp = wl.prefill_inputs(w)
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    eta, la = dev(inp["eta"]), dev(inp["log_alpha"])
+    beta, _ = kla.kla_prepare_beta(k, eta, la, eps=w.eps, with_gcum=False)
+    o1, S1 = kla.kla_chunk_fwd(q, k, v, eta, la, eps=w.eps)
+    o2, S2 = kla.kla_gdn_chunk_fwd(q, k, v, beta, la)
+    torch.cuda.synchronize()
+    eo, eS = rel_l2(host(o2), host(o1)), rel_l2(host(S2), host(S1))
+    report("gdn(kaczmarz beta) vs kla", o=eo, S_T=eS)
+    assert eo <= 1e-2 and eS <= 1e-2, (eo, eS)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gated", [True, False], ids=["gdn", "deltanet"])
+def test_gdn_decode_steps(dtype, gated):
+    w = wl.custom("gdn_dec", 253, B=3, H=5, dk=128, dv=128, steps=20, dtype=dtype, s0_std=0.05)
+    inp = wl.decode_inputs(w)
+    kk = _unit_keys(inp["k"])
+    kk = wl.round_to_bf16(kk) if dtype == "bf16" else kk
+    beta = inp["eta"]
+    la = inp["log_alpha"] if gated else np.zeros_like(inp["log_alpha"])
+    S = dev(inp["S0"])
+    outs = []
+    for s in range(w.steps):
+        o = kla.kla_gdn_decode_step(dev(inp["q"][s], dtype), dev(kk[s], dtype), dev(inp["v"][s], dtype),
+                                    dev(beta[s]), dev(la[s]) if gated else None, S)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    # oracle: the recurrence over the steps, heads flattened
+    N = w.B * w.H
+    flat = lambda x: np.moveaxis(x, 0, 2).reshape(N, w.steps, *x.shape[3:])  # [steps, B, H, ...] -> [N, steps, ...]
+    ro, rS = oracle.gated_delta_recurrent(flat(inp["q"]), flat(kk), flat(inp["v"]), flat(beta), flat(la),
+                                          inp["S0"].reshape(N, w.dk, w.dv))
+    eo = rel_l2(flat(np.stack(outs)), ro)
+    eS = rel_l2(host(S).reshape(N, w.dk, w.dv), rS)
+    report(f"gdn decode {dtype} {'gated' if gated else 'deltanet'}", o=eo, S=eS)
+    assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)

@@ -8,9 +8,12 @@ from ._lib import (  # noqa: F401
     KLA_BF16,
     KLA_F32,
     KLAError,
+    kla_chunk_bwd,
+    kla_chunk_bwd_workspace_size,
     kla_chunk_fwd,
     kla_chunk_fwd_workspace_size,
     kla_decode_step,
+    kla_gdn_chunk_bwd,
     kla_gdn_chunk_fwd,
     kla_gdn_decode_step,
     kla_prepare_beta,

@@ -29,6 +29,9 @@ _SIGNATURES = {
     "kla_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _c_void_p]),
     "kla_gdn_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_gdn_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_int, _c_void_p]),
+    "kla_chunk_bwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
+    "kla_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_gdn_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_status_string": (ctypes.c_char_p, [_int]),
     "kla_last_error": (ctypes.c_char_p, []),
 }
@@ -258,3 +261,74 @@ def kla_gdn_decode_step(q, k, v, beta, log_alpha, state, o=None, stream=None):
     check(lib().kla_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(state), _ptr(o),
                                     B, H, dk, dv, _dtype_code(q), _stream(dev, stream)))
     return o
+
+
+def kla_chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16) -> int:
+    return int(lib().kla_chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+
+
+def _bwd(fn_name, gate_name, q, k, v, gate, log_alpha, log_alpha_optional, do, state_in, dstate_out, eps,
+         want_dstate_in, chunk, workspace, stream, out):
+    torch = _torch()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(do, "do", (B, T, H, dv), dt, dev)
+    _need(gate, gate_name, (B, T, H), torch.float32, dev)
+    if log_alpha is not None or not log_alpha_optional:
+        _need(log_alpha, "log_alpha", (B, T, H), torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", (B, H, dk, dv), torch.float32, dev)
+    if dstate_out is not None:
+        _need(dstate_out, "dstate_out", (B, H, dk, dv), torch.float32, dev)
+    out = dict(out or {})
+    shapes = {"dq": ((B, T, H, dk), dt), "dk": ((B, T, H, dk), dt), "dv": ((B, T, H, dv), dt),
+              "d" + gate_name: ((B, T, H), torch.float32), "dlog_alpha": ((B, T, H), torch.float32),
+              "dstate_in": ((B, H, dk, dv), torch.float32)}
+    for name, (shape, dtype) in shapes.items():
+        if name == "dlog_alpha" and log_alpha is None:
+            out[name] = None
+            continue
+        if name == "dstate_in" and not want_dstate_in:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+        _need(out[name], name, shape, dtype, dev)
+    code = _dtype_code(q)
+    need = kla_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(log_alpha), _ptr(state_in), _ptr(do), _ptr(dstate_out),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["d" + gate_name]), _ptr(out["dlog_alpha"]),
+            _ptr(out["dstate_in"]), B, T, H, dk, dv, chunk]
+    args += [float(eps)] if eps is not None else []
+    args += [code, _ptr(workspace), ws_bytes, _stream(dev, stream)]
+    check(getattr(lib(), fn_name)(*args))
+    return out
+
+
+def kla_chunk_bwd(q, k, v, eta, log_alpha, do, eps=1e-6, state_in=None, dstate_out=None, want_dstate_in=True,
+                  chunk=CHUNK, workspace=None, stream=None, out=None):
+    """Gradients of L = sum(do * o) + sum(dstate_out * S_T) through kla_chunk_fwd on the same inputs.
+    q, k [B, T, H, d_k], v, do [B, T, H, d_v] (bf16 or fp32, one dtype); eta, log_alpha [B, T, H] fp32;
+    state_in, dstate_out [B, H, d_k, d_v] fp32 or None (zeros). Returns a dict with dq, dk, dv (input
+    dtype), deta, dlog_alpha (fp32) and dstate_in (fp32, or None when not wanted); tensors given in
+    ``out`` under those names are written in place."""
+    return _bwd("kla_chunk_bwd", "eta", q, k, v, eta, log_alpha, False, do, state_in, dstate_out, eps,
+                want_dstate_in, chunk, workspace, stream, out)
+
+
+def kla_gdn_chunk_bwd(q, k, v, beta, log_alpha, do, state_in=None, dstate_out=None, want_dstate_in=True,
+                      chunk=CHUNK, workspace=None, stream=None, out=None):
+    """kla_chunk_bwd for the gated DeltaNet form (beta given, log_alpha None for alpha = 1).
+    Returns dq, dk, dv, dbeta, dlog_alpha (None when log_alpha is) and dstate_in."""
+    return _bwd("kla_gdn_chunk_bwd", "beta", q, k, v, beta, log_alpha, True, do, state_in, dstate_out, None,
+                want_dstate_in, chunk, workspace, stream, out)
+

@@ -16,7 +16,8 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkla.so"
-SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip"]
+SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip",
+           "chunk_bwd_scan.hip", "chunk_bwd_grad.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -24,9 +25,10 @@ FLAGS = [
     "-I", str(ROOT / "include"), "-I", str(CSRC),
     "-Wno-unused-command-line-argument",
 ]
-# Per-source extra flags. The scan kernel keeps its MFMA accumulators in ordinary VGPRs (the
+# Per-source extra flags. The scan kernels keep their MFMA accumulators in ordinary VGPRs (the
 # default places them in AGPRs and copies every value the VALU touches).
-EXTRA = {"chunk_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"chunk_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "chunk_bwd_scan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> pathlib.Path:

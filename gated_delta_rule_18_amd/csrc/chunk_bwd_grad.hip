@@ -1,0 +1,449 @@
+// Chunkwise backward, the chunk-parallel part: dq, dk, dv, deta (or dbeta) and dlog(alpha)
+// of every chunk, all chunks at once (one workgroup per chunk of one head), from the states
+// and gradients the two scans left in the workspace.
+//
+// Sources: "Deep Dive into KDA", section 3 (the chunkwise forward differentiated here: the
+// WY/UT solve, the triangular-masked intra-chunk scores and the log-domain decay ratios,
+// never a division by a decayed quantity); "Kaczmarz Linear Attention", Abstract (the step
+// size beta = eta / (||k||^2 + eps)).
+//
+// For a chunk with entering state S, leaving-state gradient dS', Delta and Zb (chunk_common.h),
+// the forward's factors (eta rs, e^G, rs) and L[r][s] = e^{G_r - G_s} (s <= r):
+//   Na = -(Zb Delta^T) o L (s < r);  Ma = diag(eta rs) Na;  Mp = (dO Delta^T) o L (s <= r)
+//   dq = Mp K + diag(e^G) dO S^T
+//   dk = Ma K + Ma^T K + Mp^T Q - diag(eta rs e^G) Zb S^T + diag(e^{G_C - G}) Delta dS'^T
+//        - 2 eta rs^2 deta k                                    (the last term: KLA only)
+//   dv = diag(eta rs) Zb
+//   deta_r = rs_r (Zb_r.v_r - e^{G_r} k_r.(Zb S^T)_r + sum_s (Na o K K^T)[r][s])
+//   dG_r   = -eta_r rs_r e^{G_r} k_r.(Zb S^T)_r + e^{G_r} q_r.(dO S^T)_r
+//            + rowsum_r(E) - colsum_r(E) - e^{G_C - G_r} k_r.(Delta dS'^T)_r,
+//            E = diag(eta rs) (Na o K K^T) + Mp o Q K^T,
+//   plus, on the last row (G_C), e^{G_C} <S, dS'> + sum_r e^{G_C - G_r} k_r.(Delta dS'^T)_r;
+//   dlog(alpha)_j = sum over r >= j of dG_r within the chunk (G is the chunk-local prefix).
+// With beta given (gated DeltaNet; factors eta = beta, rs = 1) deta is d(beta) and dk has no
+// step-size term.
+//
+// Products. The C x C products (K K^T, Q K^T, Zb Delta^T, dO Delta^T) are spread over the
+// waves by lower-triangular 16 x 16 tile; the d_k x C outputs are computed transposed
+// (dk^T = K^T Ma^T + ..., one d_k row block per wave) so that each lane holds four consecutive
+// d_k entries of one token and stores them in one 8-byte (bf16) or 16-byte (fp32) store. The
+// workspace's tile-ordered Delta, Zb, S and dS' are transposed into LDS on the way in (one
+// 8- or 16-byte LDS write per lane piece) and read back with the transposing LDS read.
+#include "tile_ops.h"
+
+namespace kla {
+
+namespace {
+
+template <typename E, int DK, int DV>
+struct GradSmem {
+  alignas(16) E Ks[kChunk * DK];
+  alignas(16) E Qs[kChunk * DK];
+  alignas(16) E dOs[kChunk * DV];
+  alignas(16) E Dt[DV * kChunk];  // Delta^T
+  alignas(16) E Zt[DV * kChunk];  // Zb^T
+  alignas(16) E St[DV * DK];      // V ([64][DV]) while the C x C tiles are formed, then S^T, then dS'^T
+  alignas(16) E Ma[kChunk * kChunk];
+  alignas(16) E Mp[kChunk * kChunk];
+  float G[kChunk], eG[kChunk], cr[kChunk], rs[kChunk], zv[kChunk], kcoef[kChunk];
+  // Partial sums, one slot per producer, added in a fixed order (bitwise reproducible):
+  // per lower-triangular C x C tile (row sums of its 16 rows, column sums of its 16 columns) ...
+  float rowA[10][16], rowE[10][16], colE[10][16];
+  // ... and per wave (token-row dot products over that wave's d_k rows; <S, dS'>).
+  float kzs[4][kChunk], qos[4][kChunk], kds[4][kChunk], sds[4];
+};
+
+template <typename E, int DK, int DV>
+constexpr bool grad_fits() {
+  return sizeof(GradSmem<E, DK, DV>) <= 160 * 1024;
+}
+
+// Elements 4h .. 4h + 3 of eight bf16.
+__device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
+  return h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
+}
+
+// lower-triangular tile k (0..9) -> (ti, tj), ti >= tj
+__device__ __forceinline__ void tri_tile(int k, int& ti, int& tj) {
+  ti = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+  tj = k - ti * (ti + 1) / 2;
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) {
+  constexpr bool BF = is_bf16<E>();
+  constexpr int GK = Grp<E>::K;
+  typedef typename Grp<E>::V GV;
+  constexpr int PER = 16 / sizeof(E);
+  typedef typename Vec16<E>::type V16;
+  constexpr int NGD = DK / GK, NGV = DV / GK, NGT = kChunk / GK;
+  constexpr int NI = DK / 64;  // 16-row tiles of d_k per wave
+  typedef GradSmem<E, DK, DV> Sm;
+  __shared__ Sm sm;
+
+  const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
+  const int64_t head = chunk_id / p.nchunks, c = chunk_id % p.nchunks;
+  const int64_t bb = head / p.H, hh = head % p.H;
+  const int64_t T = p.T, H = p.H;
+  const int64_t t0 = c * kChunk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+
+  const int64_t brow = bb * T * H;
+  const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);
+  const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, (uint32_t)(T * vrow));
+  const rsrc_t rdo = make_rsrc(static_cast<const E*>(p.dout) + brow * DV, (uint32_t)(T * vrow));
+  const rsrc_t rdq = make_rsrc(static_cast<E*>(p.dq) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rdk = make_rsrc(static_cast<E*>(p.dk) + brow * DK, (uint32_t)(T * xrow));
+  const rsrc_t rdv = make_rsrc(static_cast<E*>(p.dv) + brow * DV, (uint32_t)(T * vrow));
+  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = hh * DV * sizeof(E);
+  const uint32_t x0 = (uint32_t)t0 * xrow, v0 = (uint32_t)t0 * vrow;
+  const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * p.nchunks, DK, DV);
+
+  // ---- row-major operands straight into LDS (direct-to-LDS loads; rows past T read zeros) ----
+  auto dma_rows = [&](rsrc_t r, E* dst, uint32_t base, uint32_t rowb, uint32_t hcol, auto ncol_tag) {
+    constexpr int NCOL = decltype(ncol_tag)::value;
+    constexpr int CPR = NCOL / PER, NBLK = kChunk * CPR / 64;
+    static_assert(NBLK % 4 == 0, "block split");
+#pragma unroll
+    for (int i = 0; i < NBLK / 4; ++i) {
+      const int blk = wave + 4 * i, ph = 64 * blk + lane, row = ph / CPR;
+      dma16(r, dst + blk * 64 * PER, base + row * rowb + hcol + 16 * swz<E, CPR>(row, ph % CPR));
+    }
+  };
+  dma_rows(rk, sm.Ks, x0, xrow, hcol_x, std::integral_constant<int, DK>());
+  dma_rows(rq, sm.Qs, x0, xrow, hcol_x, std::integral_constant<int, DK>());
+  dma_rows(rdo, sm.dOs, v0, vrow, hcol_v, std::integral_constant<int, DV>());
+  dma_rows(rv, sm.St, v0, vrow, hcol_v, std::integral_constant<int, DV>());
+
+  // ---- tile-ordered [64 x DV] blocks, transposed into LDS: lane piece (rows 4g..4g+3 of
+  //      column c of tile (rt, ct)) -> row 16 ct + c, columns 16 rt + 4g .. + 3 ----
+  auto load_t64 = [&](const E* src, E* dst) {
+    constexpr int NCH = kChunk * DV / PER / kThreads;  // 16-byte chunks per thread
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + kThreads * i;
+      const V16 x = *reinterpret_cast<const V16*>(src + ci * PER);
+#pragma unroll
+      for (int h = 0; h < PER / 4; ++h) {
+        const int pi = ci * (PER / 4) + h, ti = pi >> 6, l = pi & 63;
+        const int rt = ti / (DV / 16), ct = ti % (DV / 16);
+        E* d = dst + at<E, kChunk>(16 * ct + (l & 15), 16 * rt + 4 * (l >> 4));
+        if constexpr (BF) {
+          *reinterpret_cast<bf16x4*>(d) = half4(x, h);
+        } else {
+          *reinterpret_cast<f32x4*>(d) = x;
+        }
+      }
+    }
+  };
+  load_t64(bw.Dl + chunk_id * kChunk * DV, sm.Dt);
+  load_t64(bw.Zb + chunk_id * kChunk * DV, sm.Zt);
+
+  // ---- per-token factors; the chunk-local decay prefix G as the forward forms it ----
+  if (wave == 0) {
+    const bool valid = t0 + lane < T;
+    const float la = valid && p.log_alpha ? p.log_alpha[(bb * T + t0 + lane) * H + hh] : 0.f;
+    sm.G[lane] = wave_inclusive_scan(la);
+    const float* sc = ws.SC + chunk_id * kScRows * kChunk;
+    sm.cr[lane] = sc[kScCoefR * kChunk + lane];
+    sm.eG[lane] = sc[kScEG * kChunk + lane];
+    sm.rs[lane] = sc[kScRs * kChunk + lane];
+  }
+  wait_vmem<0>();
+  __syncthreads();
+
+  // ---- S and dS' (tile-ordered [DK x DV]) into registers while the C x C tiles are formed ----
+  constexpr int NSR = DK * DV / PER / kThreads;
+  const E* gS = bw.Sn + chunk_id * DK * DV;
+  const E* gdS = bw.dSn + chunk_id * DK * DV;
+  V16 sreg[NSR], dsreg[NSR];
+#pragma unroll
+  for (int i = 0; i < NSR; ++i) {
+    sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + kThreads * i) * PER);
+    dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + kThreads * i) * PER);
+  }
+
+  // ---- C x C tiles: K K^T, Q K^T, Zb Delta^T, dO Delta^T -> Ma, Mp and the decay sums ----
+  for (int k = wave; k < 10; k += 4) {
+    int ti, tj;
+    tri_tile(k, ti, tj);
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, F = kk, dp = kk;
+#pragma unroll
+    for (int s = 0; s < NGD; ++s) {
+      const GV bk = row_grp<E, DK>(sm.Ks, 16 * tj + c16, s, g);
+      kk = mma<E>(row_grp<E, DK>(sm.Ks, 16 * ti + c16, s, g), bk, kk);
+      qk = mma<E>(row_grp<E, DK>(sm.Qs, 16 * ti + c16, s, g), bk, qk);
+    }
+#pragma unroll
+    for (int s = 0; s < NGV; ++s) {
+      const GV bd = kt_grp<E, kChunk>(sm.Dt, tj, s, g, c16);
+      F = mma<E>(kt_grp<E, kChunk>(sm.Zt, ti, s, g, c16), bd, F);
+      dp = mma<E>(row_grp<E, DV>(sm.dOs, 16 * ti + c16, s, g), bd, dp);
+    }
+    const int s = 16 * tj + c16;
+    const float Gs = sm.G[s];
+    float csum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ti + 4 * g + e;
+      const float L = s <= r ? __expf(sm.G[r] - Gs) : 0.f;
+      const float na = s < r ? -F[e] * L : 0.f;
+      const float naKK = na * kk[e];
+      const float crr = sm.cr[r];
+      const float mp = dp[e] * L;
+      const float ee = crr * naKK + mp * qk[e];
+      sm.Ma[at<E, kChunk>(r, s)] = from_f32<E>(crr * na);
+      sm.Mp[at<E, kChunk>(r, s)] = from_f32<E>(mp);
+      csum += ee;
+      const float ra = group_sum<16>(naKK), re = group_sum<16>(ee);
+      if (c16 == 0) {
+        sm.rowA[k][4 * g + e] = ra;
+        sm.rowE[k][4 * g + e] = re;
+      }
+    }
+    csum += __shfl_xor(csum, 16, kWave);
+    csum += __shfl_xor(csum, 32, kWave);
+    if (g == 0) sm.colE[k][c16] = csum;
+  }
+  // upper off-diagonal tiles of Ma and Mp are zero
+  for (int i = tid; i < 6 * 256; i += kThreads) {
+    const int k = i >> 8, e = i & 255;
+    const int ti = k < 3 ? 0 : k < 5 ? 1 : 2, tj = k < 3 ? k + 1 : k < 5 ? k - 1 : 3;
+    const int r = 16 * ti + (e >> 4), s = 16 * tj + (e & 15);
+    sm.Ma[at<E, kChunk>(r, s)] = from_f32<E>(0.f);
+    sm.Mp[at<E, kChunk>(r, s)] = from_f32<E>(0.f);
+  }
+  // Zb_r . v_r (V sits in St for now): four threads per token
+  {
+    const int r = tid >> 2, q = tid & 3;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = q * (DV / 4); j < (q + 1) * (DV / 4); ++j)
+      acc += to_f32(sm.St[at<E, DV>(r, j)]) * to_f32(sm.Zt[at<E, kChunk>(j, r)]);
+    acc += __shfl_xor(acc, 1, kWave);
+    acc += __shfl_xor(acc, 2, kWave);
+    if (q == 0) sm.zv[r] = acc;
+  }
+  // <S, dS'> over this thread's pieces (same positions in both)
+  {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSR; ++i)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc += to_f32(sreg[i][e]) * to_f32(dsreg[i][e]);
+    acc = wave_sum(acc);
+    if (lane == 0) sm.sds[wave] = acc;
+  }
+  __syncthreads();
+
+  // tile-ordered [DK x DV] registers -> transposed LDS [DV][DK]
+  auto put_state = [&](const V16* regs) {
+#pragma unroll
+    for (int i = 0; i < NSR; ++i) {
+      const int ci = tid + kThreads * i;
+#pragma unroll
+      for (int h = 0; h < PER / 4; ++h) {
+        const int pi = ci * (PER / 4) + h, ti = pi >> 6, l = pi & 63;
+        const int rt = ti / (DV / 16), ct = ti % (DV / 16);
+        E* d = sm.St + at<E, DK>(16 * ct + (l & 15), 16 * rt + 4 * (l >> 4));
+        if constexpr (BF) {
+          *reinterpret_cast<bf16x4*>(d) = half4(regs[i], h);
+        } else {
+          *reinterpret_cast<f32x4*>(d) = regs[i];
+        }
+      }
+    }
+  };
+  put_state(sreg);
+  __syncthreads();
+
+  // ---- d_k x C products, transposed outputs: this wave's d_k tiles it = NI wave .. ----
+  f32x4 accK[NI][4], accQ[NI][4], accZS[NI][4], accOS[NI][4], accDS[NI][4];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int it = NI * wave + ii;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 k_ = {0.f, 0.f, 0.f, 0.f}, q_ = k_, zs = k_, os = k_;
+#pragma unroll
+      for (int s = 0; s < NGT; ++s) {
+        const GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
+        if (GK * s < 16 * (rt + 1)) {  // Ma[r][s], Mp[r][s] vanish for s > r
+          k_ = mma<E>(ak, row_grp<E, kChunk>(sm.Ma, 16 * rt + c16, s, g), k_);
+          q_ = mma<E>(ak, row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g), q_);
+        }
+        if (GK * (s + 1) > 16 * rt) {  // Ma[r][s], Mp[r][s] over r >= s
+          const GV aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16);
+          k_ = mma<E>(ak, kt_grp<E, kChunk>(sm.Ma, rt, s, g, c16), k_);
+          k_ = mma<E>(aq, kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16), k_);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NGV; ++s) {
+        const GV as = kt_grp<E, DK>(sm.St, it, s, g, c16);
+        zs = mma<E>(as, kt_grp<E, kChunk>(sm.Zt, rt, s, g, c16), zs);
+        os = mma<E>(as, row_grp<E, DV>(sm.dOs, 16 * rt + c16, s, g), os);
+      }
+      accK[ii][rt] = k_;
+      accQ[ii][rt] = q_;
+      accZS[ii][rt] = zs;
+      accOS[ii][rt] = os;
+    }
+  }
+  __syncthreads();
+  put_state(dsreg);
+  __syncthreads();
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int it = NI * wave + ii;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4 ds = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NGV; ++s)
+        ds = mma<E>(kt_grp<E, DK>(sm.St, it, s, g, c16), kt_grp<E, kChunk>(sm.Dt, rt, s, g, c16), ds);
+      accDS[ii][rt] = ds;
+    }
+  }
+
+  // ---- token-row dot products over d_k: k.(Zb S^T), q.(dO S^T), k.(Delta dS'^T) ----
+  f32x4 kv[NI][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = 16 * rt + c16;
+    float a = 0.f, b = 0.f, d = 0.f;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int i0 = 16 * (NI * wave + ii) + 4 * g;
+      f32x4 kx, qx;
+      if constexpr (BF) {
+        const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&sm.Ks[at<E, DK>(r, i0)]);
+        const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&sm.Qs[at<E, DK>(r, i0)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kx[e] = to_f32(kb[e]);
+          qx[e] = to_f32(qb[e]);
+        }
+      } else {
+        kx = *reinterpret_cast<const f32x4*>(&sm.Ks[at<E, DK>(r, i0)]);
+        qx = *reinterpret_cast<const f32x4*>(&sm.Qs[at<E, DK>(r, i0)]);
+      }
+      kv[ii][rt] = kx;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a += kx[e] * accZS[ii][rt][e];
+        b += qx[e] * accOS[ii][rt][e];
+        d += kx[e] * accDS[ii][rt][e];
+      }
+    }
+    a += __shfl_xor(a, 16, kWave);
+    a += __shfl_xor(a, 32, kWave);
+    b += __shfl_xor(b, 16, kWave);
+    b += __shfl_xor(b, 32, kWave);
+    d += __shfl_xor(d, 16, kWave);
+    d += __shfl_xor(d, 32, kWave);
+    if (g == 0) {
+      sm.kzs[wave][r] = a;
+      sm.qos[wave][r] = b;
+      sm.kds[wave][r] = d;
+    }
+  }
+  __syncthreads();
+
+  // ---- per token: deta, dG, and dlog(alpha) as the within-chunk suffix sum of dG ----
+  if (wave == 0) {
+    const int r = lane, ti = r >> 4, rr = r & 15;
+    float rowA = 0.f, rowE = 0.f, colE = 0.f;
+    for (int tj = 0; tj <= ti; ++tj) {  // tiles (ti, tj): row r
+      rowA += sm.rowA[ti * (ti + 1) / 2 + tj][rr];
+      rowE += sm.rowE[ti * (ti + 1) / 2 + tj][rr];
+    }
+    for (int tk = ti; tk < 4; ++tk) colE += sm.colE[tk * (tk + 1) / 2 + ti][rr];  // tiles (tk, ti): column r
+    const float kzs = (sm.kzs[0][r] + sm.kzs[1][r]) + (sm.kzs[2][r] + sm.kzs[3][r]);
+    const float qos = (sm.qos[0][r] + sm.qos[1][r]) + (sm.qos[2][r] + sm.qos[3][r]);
+    const float kds = (sm.kds[0][r] + sm.kds[1][r]) + (sm.kds[2][r] + sm.kds[3][r]);
+    const float sds = (sm.sds[0] + sm.sds[1]) + (sm.sds[2] + sm.sds[3]);
+    const float crr = sm.cr[r], eGr = sm.eG[r], GC = sm.G[kChunk - 1];
+    const float de = sm.rs[r] * (sm.zv[r] - eGr * kzs + rowA);
+    const float wsr = __expf(GC - sm.G[r]) * kds;
+    float dG = -crr * eGr * kzs + rowE - colE + eGr * qos - wsr;
+    const float wtot = wave_sum(wsr);
+    if (r == kChunk - 1) dG += __expf(GC) * sds + wtot;
+    const float incl = wave_inclusive_scan(dG);
+    const float tot = __shfl(incl, kChunk - 1, kWave);
+    const int64_t row = (bb * T + t0 + r) * H + hh;
+    if (t0 + r < T) {
+      p.deta[row] = de;
+      if (p.dlog_alpha) p.dlog_alpha[row] = tot - incl + dG;
+    }
+    sm.kcoef[r] = p.beta_given ? 0.f : -2.f * crr * sm.rs[r] * de;
+  }
+  __syncthreads();
+
+  // ---- dk, dq: four consecutive d_k entries of one token per lane ----
+  const float GC = sm.G[kChunk - 1];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = 16 * rt + c16;
+    const float crr = sm.cr[r], eGr = sm.eG[r], dec = __expf(GC - sm.G[r]), kc = sm.kcoef[r];
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int i0 = 16 * (NI * wave + ii) + 4 * g;
+      const f32x4 dk = accK[ii][rt] - (crr * eGr) * accZS[ii][rt] + dec * accDS[ii][rt] + kc * kv[ii][rt];
+      const f32x4 dq = accQ[ii][rt] + eGr * accOS[ii][rt];
+      const uint32_t off = x0 + r * xrow + hcol_x + i0 * sizeof(E);
+      store4_rsrc<E>(rdk, off, dk);
+      store4_rsrc<E>(rdq, off, dq);
+    }
+  }
+  // ---- dv = diag(eta rs) Zb: four threads per token, 16-byte stores ----
+  {
+    const int r = tid >> 2, q = tid & 3;
+    const float crr = sm.cr[r];
+#pragma unroll
+    for (int j0 = q * (DV / 4); j0 < (q + 1) * (DV / 4); j0 += PER) {
+      V16 out;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) out[e] = from_f32<E>(crr * to_f32(sm.Zt[at<E, kChunk>(j0 + e, r)]));
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, out), rdv,
+                                             v0 + r * vrow + hcol_v + j0 * sizeof(E), 0, 0);
+    }
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_dk_dv(const ChunkBwdParams& p, hipStream_t stream) {
+  if constexpr (grad_fits<E, DK, DV>()) {
+    hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)(p.heads * p.nchunks)), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidConfiguration;
+  }
+}
+
+template <typename E>
+hipError_t launch_e(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, hipStream_t stream) {
+  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128>(p, stream);
+  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64>(p, stream);
+  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64>(p, stream);
+  return launch_dk_dv<E, 64, 128>(p, stream);
+}
+
+}  // namespace
+
+bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16_io) {
+  if (bf16_io) return true;
+  return d_k == 64 && d_v == 64;  // fp32 operands of 128-wide heads exceed 160 KiB of LDS
+}
+
+hipError_t launch_chunk_grad(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
+  return bf16_io ? launch_e<bf16>(p, d_k, d_v, stream) : launch_e<float>(p, d_k, d_v, stream);
+}
+
+}  // namespace kla

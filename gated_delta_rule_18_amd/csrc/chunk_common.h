@@ -69,7 +69,7 @@ struct Workspace {
   E* T;
   E* P;
   float* SC;
-  static size_t bytes(int64_t nchunks_total) {
+  __host__ __device__ static size_t bytes(int64_t nchunks_total) {
     return (size_t)nchunks_total * (2 * kChunk * kChunk * sizeof(E) + kScRows * kChunk * sizeof(float));
   }
   __host__ __device__ static Workspace at(void* base, int64_t nchunks_total) {
@@ -95,6 +95,62 @@ struct ChunkParams {
   int64_t heads, H, T, nchunks;
   float eps;
   bool beta_given;  // eta holds beta itself (gated DeltaNet); log_alpha may then be null (alpha = 1)
+  // With beta_given: factor beta as eta_r = beta_r, rs_r = 1 (no balancing) instead of
+  // eta_r = sign(beta_r), rs_r = sqrt(|beta_r|). The backward needs the unbalanced factors to
+  // form d(beta) on tokens whose beta is zero.
+  bool unit_rs;
+};
+
+// Backward workspace: the forward workspace above, then per chunk (same chunk ids)
+//   Sn  [DK x DV] of E : the state entering the chunk
+//   dSn [DK x DV] of E : the gradient of the state leaving the chunk
+//   Dl  [64 x DV] of E : Delta = U - W S of the chunk (the page's new-value term)
+//   Zb  [64 x DV] of E : diag(rs) (I + A)^-T dDelta, the gradient of the solve's right side
+// each in MFMA accumulator order: 16 x 16 tiles (row tile major, then column tile), 64 lanes
+// per tile, four consecutive rows of one column per lane (lane = 16 g + c holds rows
+// 4g .. 4g + 3 of column c). Producers store whole tiles with one coalesced store per lane.
+template <typename E>
+struct BwdSpace {
+  E* Sn;
+  E* dSn;
+  E* Dl;
+  E* Zb;
+  __host__ __device__ static size_t bytes(int64_t n, int dk, int dv) {
+    return Workspace<E>::bytes(n) + (size_t)n * (2 * dk * dv + 2 * kChunk * dv) * sizeof(E);
+  }
+  __host__ __device__ static BwdSpace at(void* base, int64_t n, int dk, int dv) {
+    E* p = reinterpret_cast<E*>(static_cast<char*>(base) + Workspace<E>::bytes(n));
+    BwdSpace w;
+    w.Sn = p;
+    w.dSn = w.Sn + (size_t)n * dk * dv;
+    w.Dl = w.dSn + (size_t)n * dk * dv;
+    w.Zb = w.Dl + (size_t)n * kChunk * dv;
+    return w;
+  }
+};
+
+// Offset (elements) of tile (rt, ct) lane `lane` in a tile-ordered block with NCT column tiles.
+__host__ __device__ constexpr int tile_off(int rt, int ct, int nct, int lane) { return ((rt * nct + ct) * 64 + lane) * 4; }
+
+struct ChunkBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* log_alpha;
+  const float* state_in;    // may be null
+  const void* dout;         // dL/do
+  const float* dstate_out;  // dL/dS_T, may be null
+  void* dq;
+  void* dk;
+  void* dv;
+  float* deta;        // dL/deta, or dL/dbeta when beta_given
+  float* dlog_alpha;  // may be null when log_alpha is
+  float* dstate_in;   // dL/dS_0, may be null
+  void* ws;
+  int64_t heads, H, T, nchunks;
+  float eps;
+  bool beta_given;
 };
 
 }  // namespace kla

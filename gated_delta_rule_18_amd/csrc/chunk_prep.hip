@@ -150,10 +150,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
     const float GC = __shfl(G, kChunk - 1, kWave);  // padded rows add log 1 = 0
     // Balanced factors: A[r][s] = eta_r rs_r rs_s e^{G_r - G_s} k_r.k_s is a diagonal similarity of
     // beta_r e^{G_r - G_s} k_r.k_s when beta_r = eta_r rs_r^2. Kaczmarz step: rs = 1/sqrt(|k|^2 + eps).
-    // Given beta (gated DeltaNet): rs = sqrt(|beta|), eta = sign(beta).
+    // Given beta (gated DeltaNet): rs = sqrt(|beta|), eta = sign(beta); or, for the backward,
+    // rs = 1, eta = beta.
     const bool valid = t0 + r < T;
     float rs, et;
-    if (p.beta_given) {
+    if (p.beta_given && p.unit_rs) {
+      rs = valid ? 1.f : 0.f;
+      et = sm.eta[r];
+    } else if (p.beta_given) {
       const float b = sm.eta[r];
       rs = valid ? sqrtf(fabsf(b)) : 0.f;
       et = b < 0.f ? -1.f : 1.f;

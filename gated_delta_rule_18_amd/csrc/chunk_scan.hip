@@ -39,7 +39,7 @@
 // buffers: one workgroup barrier per chunk. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
-#include "chunk_common.h"
+#include "tile_ops.h"
 
 namespace kla {
 
@@ -47,148 +47,9 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at dst + 16 l.
-__device__ __forceinline__ void dma16(rsrc_t r, void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
-}
-
-// Wait until at most M of the vector memory operations this wave issued are outstanding, the
-// direct-to-LDS loads included (s_waitcnt vmcnt(M); expcnt and lgkmcnt left at their maxima;
-// these operations complete in issue order). Placed before each barrier that publishes such
-// loads: the compiler's own wait placement does not cover LDS written by them on every path.
-template <int M>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(M >= 0 && M < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((M & 15) | ((M >> 4) << 14) | 0x0F70);
-}
-
-// ---- contraction groups ----------------------------------------------------------------------
-template <typename E>
-struct Grp {
-  static constexpr int K = is_bf16<E>() ? 32 : 16;  // contraction indices per group
-  typedef typename std::conditional<is_bf16<E>(), bf16x8, f32x4>::type V;
-};
-
-template <typename E>
-__device__ __forceinline__ f32x4 mma(typename Grp<E>::V a, typename Grp<E>::V b, f32x4 c) {
-  if constexpr (is_bf16<E>()) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
-    return c;
-  }
-}
-
-template <typename E>
-__device__ __forceinline__ typename Grp<E>::V acc_grp(const f32x4* tiles, int s) {
-  if constexpr (is_bf16<E>()) {
-    const f32x4 a = tiles[2 * s], b = tiles[2 * s + 1];
-    bf16x8 v = {from_f32<bf16>(a[0]), from_f32<bf16>(a[1]), from_f32<bf16>(a[2]), from_f32<bf16>(a[3]),
-                from_f32<bf16>(b[0]), from_f32<bf16>(b[1]), from_f32<bf16>(b[2]), from_f32<bf16>(b[3])};
-    return v;
-  } else {
-    return tiles[s];
-  }
-}
-
-// Physical 16-byte chunk of logical chunk cc in row r of a matrix with CPR chunks per row.
-template <typename E, int CPR>
-__device__ __forceinline__ int swz(int r, int cc) {
-  if constexpr (is_bf16<E>()) {
-    static_assert(CPR == 16 || CPR == 8 || CPR == 4, "bf16 row width");
-    if constexpr (CPR == 16) return cc ^ (((r & 7) << 1) | ((r >> 3) & 1));
-    if constexpr (CPR == 8) return cc ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-    return cc ^ (((r >> 2) & 1) << 1);
-  } else {
-    static_assert(CPR >= 16, "fp32 row width");
-    return cc ^ (r & 15);
-  }
-}
-
-// Element offset of (r, col) in a swizzled row-major matrix of NCOL columns.
-template <typename E, int NCOL>
-__device__ __forceinline__ int at(int r, int col) {
-  constexpr int PER = 16 / sizeof(E), CPR = NCOL / PER;
-  return r * NCOL + PER * swz<E, CPR>(r, col / PER) + col % PER;
-}
-
-// A operand of group s along row `row` (k = column index).
-template <typename E, int NCOL>
-__device__ __forceinline__ typename Grp<E>::V row_grp(const E* M, int row, int s, int g) {
-  if constexpr (is_bf16<E>()) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(M + at<E, NCOL>(row, 32 * s + 4 * g));
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(M + at<E, NCOL>(row, 32 * s + 16 + 4 * g));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  } else {
-    return *reinterpret_cast<const f32x4*>(M + at<E, NCOL>(row, 16 * s + 4 * g));
-  }
-}
-
-// A operand of group s of K^T for state row tile rt: A(m, k) = K[k][16 rt + m], k = token.
-template <typename E, int DK>
-__device__ __forceinline__ typename Grp<E>::V kt_grp(const E* Ks, int rt, int s, int g, int c) {
-  if constexpr (is_bf16<E>()) {
-    const int r0 = 32 * s + 4 * g + (c >> 2), col = 16 * rt + 4 * (c & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<E, DK>(r0, col)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<E, DK>(r0 + 16, col)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  } else {
-    f32x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = Ks[at<E, DK>(16 * s + 4 * g + i, 16 * rt + c)];
-    return v;
-  }
-}
-
-// Rows r0 + 4g + 0..3 of column col0 + c, as fp32.
-template <typename E, int NCOL>
-__device__ __forceinline__ f32x4 col4(const E* M, int r0, int col0, int g, int c) {
-  f32x4 out;
-  if constexpr (is_bf16<E>()) {
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(M + at<E, NCOL>(r0 + 4 * g + (c >> 2), col0 + 4 * (c & 3))));
-    const bf16x4 b = __builtin_bit_cast(bf16x4, v);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = to_f32(b[j]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = M[at<E, NCOL>(r0 + 4 * g + j, col0 + c)];
-  }
-  return out;
-}
-
-// One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz).
-template <typename E, int DK, int DVS>
-struct ScanBuf {
-  alignas(16) E K[kChunk * DK];
-  alignas(16) E Q[kChunk * DK];
-  alignas(16) E T[kChunk * kChunk];
-  alignas(16) E P[kChunk * kChunk];
-  alignas(16) E V[kChunk * DVS];
-  alignas(16) float sc[kScRows * kChunk];
-};
-
-// Buffers in the ring: two where they fit in 160 KiB of LDS, else one. (A third buffer, for a
-// prefetch distance of two chunks, measured slower: the loads are not the bottleneck once they
-// are a chunk ahead, and the three-way unrolled loop costs registers.)
-template <typename E, int DK, int DVS>
-constexpr int scan_ring() {
-  return 2 * sizeof(ScanBuf<E, DK, DVS>) <= 160 * 1024 ? 2 : 1;
-}
-
-template <typename E, int DK, int DV, int W, int NT>
+// REC (backward recompute): no outputs; instead every chunk's entering state S and its Delta
+// (rs D) are stored to the backward workspace, and Q and P are not loaded.
+template <typename E, int DK, int DV, int W, int NT, bool REC>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
   constexpr bool BF = is_bf16<E>();
   constexpr int GK = Grp<E>::K;
@@ -238,6 +99,12 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
   const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
+  // Backward recompute: this head's state and Delta blocks, tile-ordered (chunk_common.h).
+  constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * nchunks, DK, DV);
+  const rsrc_t rsn = make_rsrc(bw.Sn + chunk0 * DK * DV, REC ? (uint32_t)(nchunks * kSBytes) : 0u);
+  const rsrc_t rdl = make_rsrc(bw.Dl + chunk0 * kChunk * DV, REC ? (uint32_t)(nchunks * kDBytes) : 0u);
+  const int ct0 = (j0 + cw) / 16;  // first global 16-column tile of this wave
 
   // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the waves. Lane l of
   // block b fills physical chunk 64 b + l; its source is the logical chunk stored there. ----
@@ -265,8 +132,8 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   // Every wave issues the same NDMA loads per chunk (the factor block is loaded by all of them,
   // identical bytes), so that the wait counts below are compile-time constants. A chunk past
   // the end is clamped to the last one (loaded again, never read).
-  constexpr int NDMA = 2 * NBK + 2 * NBT + NBV + 1;
-  constexpr int NST = 4 * NT;  // output stores per chunk and wave
+  constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : 2 * NBK + 2 * NBT + NBV + 1;
+  constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < nchunks ? c : nchunks - 1;
     const uint32_t t0 = (uint32_t)(c * kChunk);
@@ -274,13 +141,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave + W * i;
       dma16(rk, B.K + blk * 64 * PER, t0 * xrow + offk[i]);
-      dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
+      if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
       const int blk = wave + W * i;
       dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
-      dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
+      if constexpr (!REC) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
@@ -324,6 +191,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     __syncthreads();  // chunk c's operands are in LDS; every wave is done with chunk c - 1
     if constexpr (NB > 1) fetch(Bn, c + DIST);
     const uint32_t t0 = (uint32_t)(c * kChunk);
+    if constexpr (REC) {  // the state entering chunk c
+#pragma unroll
+      for (int r = 0; r < RTK; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          store4_rsrc<E>(rsn, (uint32_t)c * kSBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), S[r][ct]);
+    }
 
     // ---- X = K S (token rows x this wave's columns) and Y^T = S^T Q^T ----
     GV sb[NGD][NT];
@@ -343,11 +217,12 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int s = 0; s < NGD; ++s) {
         const GV ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
-        const GV aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
-          Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
+        for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
+        if constexpr (!REC) {
+          const GV aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
         }
       }
     }
@@ -403,9 +278,16 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
         b2[ct][s] = acc_grp<E>(D2[ct], s);
       }
 
-    // ---- O^T = (Y^T scaled by e^G per token) + D'^T P^T ----
+    // ---- O^T = (Y^T scaled by e^G per token) + D'^T P^T; or, recomputing, Delta = D' ----
+    if constexpr (REC) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+          store4_rsrc<E>(rdl, (uint32_t)c * kDBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), D1[ct][r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4 && !REC; ++r) {
       const float eGt = B.sc[kScEG * kChunk + 16 * r + c16];
       f32x4 o[NT];
 #pragma unroll
@@ -481,36 +363,40 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   }
 }
 
-template <typename E, int DK, int DV, int W, int NT>
+template <typename E, int DK, int DV, int W, int NT, bool REC>
 hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   constexpr int NS = DV / (W * 16 * NT);
   const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3(W * kWave), 0,
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, REC>), dim3((unsigned)(heads8 * NS)), dim3(W * kWave), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool REC>
 hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
   // bf16: two waves of 16 columns per workgroup (32 columns; four workgroups per 128-column
   // head). This split measured fastest: a wave's time per chunk is set by latency, not by
   // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
   // need a single LDS buffer, whose load is not overlapped, so more columns share it).
   if constexpr (is_bf16<E>())
-    return launch_wnt<E, DK, DV, 2, 1>(p, stream);
+    return launch_wnt<E, DK, DV, 2, 1, REC>(p, stream);
   else
-    return launch_wnt<E, DK, DV, 4, 1>(p, stream);
+    return launch_wnt<E, DK, DV, 4, 1, REC>(p, stream);
 }
 
-template <typename E>
+template <typename E, bool REC = false>
 hipError_t launch_scan(const ChunkParams& p, int64_t d_k, int64_t d_v, hipStream_t stream) {
-  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128>(p, stream);
-  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64>(p, stream);
-  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64>(p, stream);
-  return launch_dk_dv<E, 64, 128>(p, stream);
+  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128, REC>(p, stream);
+  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64, REC>(p, stream);
+  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64, REC>(p, stream);
+  return launch_dk_dv<E, 64, 128, REC>(p, stream);
 }
 
 }  // namespace
+
+hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
+  return bf16_io ? launch_scan<bf16, true>(p, d_k, d_v, stream) : launch_scan<float, true>(p, d_k, d_v, stream);
+}
 
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t, int64_t, bool bf16_io) {
   const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
@@ -519,7 +405,7 @@ size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t, int64
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
   ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
-                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given};
+                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
   if (p.nchunks > 0) {
     const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;

@@ -112,6 +112,13 @@ size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
   return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
 }
 
+size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                    kla_dtype_t dt) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
+    return 0;
+  return kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+}
+
 }  // extern "C"
 
 namespace {
@@ -173,6 +180,77 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, cons
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
                    workspace, workspace_bytes, beta_given};
   return launched(kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// kla_chunk_bwd and kla_gdn_chunk_bwd (as chunk_fwd_impl; deta receives dL/dbeta when beta_given).
+kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+                            const float* eta, const float* log_alpha, const float* state_in, const void* dout,
+                            const float* dstate_out, void* dq, void* dk, void* dv, float* deta, float* dlog_alpha,
+                            float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                            int64_t chunk, float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
+  if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
+  if (!supported_head(d_k) || !supported_head(d_v))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k and d_v must be 64 or 128", fn);
+  if (!kla::chunk_grad_supported(d_k, d_v, dt == KLA_BF16))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: fp32 gradients need d_k = d_v = 64", fn);
+  if (chunk != kla::kChunk) return fail(KLA_ERR_NOT_SUPPORTED, "%s: chunk must be 64", fn);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(KLA_ERR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+  int64_t n = 1;
+  if (!mul_ok(n, B) || !mul_ok(n, T) || !mul_ok(n, H) || !mul_ok(n, d_k > d_v ? d_k : d_v))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: size overflow", fn);
+  if (B == 0 || H == 0) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  const int64_t es = dt == KLA_BF16 ? 2 : 4;
+  const int64_t nchunks = (T + kla::kChunk - 1) / kla::kChunk;
+  if (B * H * 8 > 0x7fffffffLL || B * H * nchunks > 0x7fffffffLL)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  // 32-bit byte offsets within one batch entry's rows and within one head's workspace blocks.
+  if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * es >= (int64_t(1) << 31) ||
+      (nchunks + 1) * d_k * d_v * es >= (int64_t(1) << 31))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
+  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !dout || !dq || !dk || !dv || !deta ||
+                (log_alpha && !dlog_alpha)))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+      !aligned(dk, 16) || !aligned(dv, 16) || !aligned(state_in, 16) || !aligned(dstate_out, 16) ||
+      !aligned(dstate_in, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4) || !aligned(deta, 4) ||
+      !aligned(dlog_alpha, 4) || !aligned(workspace, 16))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
+  const size_t need = kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+  if (T > 0 && (!workspace || workspace_bytes < need))
+    return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
+  const int64_t tok = B * T * H;
+  const int64_t sbytes = B * H * d_k * d_v * 4;
+  const Range ins[8] = {range("q", q, tok * d_k * es),          range("k", k, tok * d_k * es),
+                        range("v", v, tok * d_v * es),          range("eta", eta, tok * 4),
+                        range("log_alpha", log_alpha, tok * 4), range("state_in", state_in, sbytes),
+                        range("do", dout, tok * d_v * es),      range("dstate_out", dstate_out, sbytes)};
+  const Range outs[7] = {range("dq", dq, T > 0 ? tok * d_k * es : 0),
+                         range("dk", dk, T > 0 ? tok * d_k * es : 0),
+                         range("dv", dv, T > 0 ? tok * d_v * es : 0),
+                         range("deta", deta, T > 0 ? tok * 4 : 0),
+                         range("dlog_alpha", dlog_alpha, T > 0 ? tok * 4 : 0),
+                         range("dstate_in", dstate_in, sbytes),
+                         range("workspace", workspace, T > 0 ? (int64_t)workspace_bytes : 0)};
+  for (int i = 0; i < 7; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(KLA_ERR_INVALID_VALUE, "%s: %s overlaps an input", fn, outs[i].name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j])) return fail(KLA_ERR_INVALID_VALUE, "%s: %s overlaps another output", fn,
+                                                 outs[i].name);
+  }
+  if (T == 0 && !dstate_in) {
+    g_last_error[0] = '\0';
+    return KLA_OK;
+  }
+  kla::ChunkBwdArgs a{q,  k,  v,    eta,        log_alpha, state_in, dout, dstate_out, dq,  dk,
+                      dv, deta, dlog_alpha, dstate_in, B,  T,        H,    d_k,        d_v, eps,
+                      dt == KLA_BF16, workspace, workspace_bytes, beta_given};
+  return launched(kla::launch_chunk_bwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 // kla_decode_step and kla_gdn_decode_step (as chunk_fwd_impl).
@@ -242,6 +320,27 @@ kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v, co
                                  int64_t d_v, kla_dtype_t dt, void* stream) {
   return decode_impl("kla_gdn_decode_step", true, q, k, v, beta, log_alpha, state, o, B, H, d_k, d_v, 0.f, dt,
                      stream);
+}
+
+kla_status_t kla_chunk_bwd(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                           const float* state_in, const void* dout, const float* dstate_out, void* dq, void* dk,
+                           void* dv, float* deta, float* dlog_alpha, float* dstate_in, int64_t B, int64_t T,
+                           int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kla_chunk_bwd", false, q, k, v, eta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
+                        deta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, eps, dt, workspace, workspace_bytes,
+                        stream);
+}
+
+kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* beta,
+                               const float* log_alpha, const float* state_in, const void* dout,
+                               const float* dstate_out, void* dq, void* dk, void* dv, float* dbeta,
+                               float* dlog_alpha, float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                               int64_t d_v, int64_t chunk, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return chunk_bwd_impl("kla_gdn_chunk_bwd", true, q, k, v, beta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
+                        dbeta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, 0.f, dt, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"

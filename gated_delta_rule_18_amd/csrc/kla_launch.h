@@ -52,9 +52,35 @@ struct ChunkArgs {
   bool beta_given;  // eta holds beta itself; log_alpha may be null (alpha = 1)
 };
 
+struct ChunkBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* log_alpha;   // may be null when beta_given (alpha = 1)
+  const float* state_in;    // may be null: S_0 = 0
+  const void* dout;         // dL/do
+  const float* dstate_out;  // dL/dS_T, may be null (zero)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* deta;        // dL/deta, or dL/dbeta when beta_given
+  float* dlog_alpha;  // may be null only when log_alpha is
+  float* dstate_in;   // dL/dS_0, may be null
+  int64_t B, T, H, d_k, d_v;
+  float eps;
+  bool bf16;
+  void* workspace;
+  size_t workspace_bytes;
+  bool beta_given;
+};
+
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prepare_beta(const PrepareArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
+size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16);
 
 }  // namespace kla

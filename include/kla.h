@@ -152,6 +152,64 @@ kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v,
                                  int64_t B, int64_t H, int64_t d_k, int64_t d_v,
                                  kla_dtype_t dt, void* stream);
 
+/*
+ * kla_chunk_bwd_workspace_size — bytes of device workspace kla_chunk_bwd and
+ * kla_gdn_chunk_bwd need for these sizes (0 when T = 0 or the sizes are not supported).
+ * Host-only; never fails. For bf16 and d_k = d_v = 128 it is about 113 KiB per chunk of
+ * 64 tokens per head: the forward's per-chunk factors plus every chunk's entering state,
+ * state gradient, Delta and solve gradient.
+ */
+size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                    int64_t chunk, kla_dtype_t dt);
+
+/*
+ * kla_chunk_bwd — gradients of the chunkwise forward (training).
+ * Source: "Kaczmarz Linear Attention", Abstract (the chunkwise form serves training, with the
+ * step size beta_t = eta_t / (||k_t||^2 + eps)); "Deep Dive into KDA", section 3 (the
+ * chunkwise forward that is differentiated). The pages give no backward formulas: the result
+ * is the exact gradient of the token recurrence, up to rounding.
+ * For the scalar loss L = sum(do * o) + sum(dstate_out * S_T), with o and S_T the outputs of
+ * kla_chunk_fwd on the same inputs, computes
+ *   dq, dk     [B,T,H,d_k] of type dt   dL/dq, dL/dk (dk includes the path through beta)
+ *   dv         [B,T,H,d_v] of type dt   dL/dv
+ *   deta       [B,T,H] fp32             dL/deta
+ *   dlog_alpha [B,T,H] fp32             dL/dlog(alpha)
+ *   dstate_in  [B,H,d_k,d_v] fp32       dL/dS_0, or NULL if not wanted
+ * Inputs: q, k, v, eta, log_alpha, state_in (NULL for S_0 = 0) exactly as given to
+ * kla_chunk_fwd; do [B,T,H,d_v] of type dt; dstate_out [B,H,d_k,d_v] fp32 or NULL (zero).
+ * The forward is recomputed inside; o is not needed.
+ *   Supported: bf16 with d_k, d_v in {64, 128}; fp32 with d_k = d_v = 64 (else
+ *   KLA_ERR_NOT_SUPPORTED). chunk must be 64. Any T >= 0 (a last partial chunk is handled);
+ *   T = 0 writes dstate_in = dstate_out (or zeros) and nothing else.
+ *   No output may overlap an input or another output (KLA_ERR_INVALID_VALUE).
+ *   workspace  device buffer of at least kla_chunk_bwd_workspace_size(...) bytes (NULL when
+ *              T = 0); its contents on entry do not matter.
+ * Stream-ordered and asynchronous; the library allocates nothing and keeps no pointer.
+ */
+kla_status_t kla_chunk_bwd(const void* q, const void* k, const void* v,
+                           const float* eta, const float* log_alpha, const float* state_in,
+                           const void* dout, const float* dstate_out,
+                           void* dq, void* dk, void* dv, float* deta, float* dlog_alpha,
+                           float* dstate_in,
+                           int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                           float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * kla_gdn_chunk_bwd — kla_chunk_bwd with beta supplied by the caller (gated DeltaNet;
+ * DeltaNet when log_alpha is NULL). Source: "Deep Dive into KDA", sections 2.1-3.
+ *   beta [B,T,H] fp32 as given; dbeta [B,T,H] fp32 receives dL/dbeta (the key norm does not
+ *   enter beta, so dk has no step-size path). log_alpha may be NULL (alpha = 1), and then
+ *   dlog_alpha may be NULL too. Otherwise as kla_chunk_bwd.
+ */
+kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v,
+                               const float* beta, const float* log_alpha, const float* state_in,
+                               const void* dout, const float* dstate_out,
+                               void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                               float* dstate_in,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                               kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* kla_status_string(kla_status_t status);
 

@@ -17,7 +17,7 @@ def test_exports_every_declared_symbol():
     names = K.declared_functions()
     assert set(names) == {"kla_prepare_beta", "kla_chunk_fwd_workspace_size", "kla_chunk_fwd",
                           "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
-                          "kla_last_error"}
+                          "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -165,3 +165,69 @@ def test_gdn_decode_step_rejects(kw, status):
 def test_gdn_empty_is_a_no_op():
     assert gdn_decode(B=0) == K.KLA_OK
     assert gdn_chunk(B=0) == K.KLA_OK
+
+
+WS = A16 * 256  # fake workspace address, far from the tensors below
+
+
+def bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16, k=A16 * 2, v=A16 * 3,
+        eta=A16 * 4, la=A16 * 5, s_in=0, do=A16 * 6, ds_out=0, dq=A16 * 7, dk_=A16 * 8, dv_=A16 * 9,
+        deta=A16 * 10, dla=A16 * 11, ds_in=0, ws=WS, ws_bytes=None, gdn=False):
+    if ws_bytes is None:
+        ws_bytes = max(K.lib().kla_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk_len, dt), 0)
+    opt = lambda x: p(x) if x else None
+    head = [p(q), p(k), p(v), opt(eta), opt(la), opt(s_in), opt(do), opt(ds_out), opt(dq), opt(dk_), opt(dv_),
+            opt(deta), opt(dla), opt(ds_in), B, T, H, dk, dv, chunk_len]
+    tail = [dt, opt(ws), ws_bytes, None]
+    if gdn:
+        return L().kla_gdn_chunk_bwd(*head, *tail)
+    return L().kla_chunk_bwd(*head, eps, *tail)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(chunk_len=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(dt=K.KLA_F32), K.KLA_ERR_NOT_SUPPORTED),             # fp32 gradients need d = 64
+    (dict(dt=K.KLA_F32, dk=64, dv=128), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(eps=-1.0), K.KLA_ERR_INVALID_VALUE),
+    (dict(T=-3), K.KLA_ERR_INVALID_VALUE),
+    (dict(do=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(dla=0), K.KLA_ERR_INVALID_VALUE),                    # log_alpha given: dlog_alpha required
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),                     # KLA needs log_alpha
+    (dict(deta=A16 * 10 + 2), K.KLA_ERR_INVALID_VALUE),        # misaligned
+    (dict(dq=A16 * 2 + 64), K.KLA_ERR_INVALID_VALUE),          # dq overlaps k
+    (dict(dv_=A16 * 7), K.KLA_ERR_INVALID_VALUE),              # dv overlaps dq
+    (dict(ws=0), K.KLA_ERR_INVALID_VALUE),                     # workspace required
+    (dict(ws_bytes=1024), K.KLA_ERR_INVALID_VALUE),            # ... and big enough
+    (dict(ws=A16 * 6 + 512), K.KLA_ERR_INVALID_VALUE),         # workspace overlaps do
+    (dict(T=1 << 20, H=16), K.KLA_ERR_NOT_SUPPORTED),          # one batch entry past 2 GiB
+])
+def test_chunk_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+    assert L().kla_last_error().startswith(b"kla_chunk_bwd")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(la=0, dla=0, dk=100), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(eta=0), K.KLA_ERR_INVALID_VALUE),                    # beta required
+    (dict(la=0, deta=0), K.KLA_ERR_INVALID_VALUE),             # dbeta required
+    (dict(la=0, dla=0, dk_=A16 * 6), K.KLA_ERR_INVALID_VALUE),  # dk overlaps do
+])
+def test_gdn_chunk_bwd_rejects(kw, status):
+    assert bwd(gdn=True, **kw) == status
+    assert L().kla_last_error().startswith(b"kla_gdn_chunk_bwd")
+
+
+def test_chunk_bwd_empty_is_a_no_op():
+    assert bwd(B=0) == K.KLA_OK
+    assert bwd(H=0, q=0) == K.KLA_OK
+    assert bwd(T=0, ws=0) == K.KLA_OK  # nothing to write without dstate_in
+
+
+def test_bwd_workspace_size():
+    need = K.lib().kla_chunk_bwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16)
+    fwd = K.lib().kla_chunk_fwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16)
+    # the forward's per-chunk factors, then per chunk two bf16 states and two 64 x 128 blocks
+    assert need == fwd + 8 * 8 * 64 * (2 * 128 * 128 + 2 * 64 * 128) * 2
+    assert K.lib().kla_chunk_bwd_workspace_size(8, 0, 8, 128, 128, 64, K.KLA_BF16) == 0
+

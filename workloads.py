@@ -11,6 +11,8 @@ Distributions (per element i.i.d.; scalars are per (b, t, h)):
   eta   = sigmoid(N(0, eta_std))                                   (already activated)
   log_alpha = -U(a_lo, a_hi)                                       (alpha = exp(log_alpha))
   S0    = N(0, s0_std) fp32, or zeros
+  do    = N(0, 1) (the cotangent of o for gradient checks; bf16-rounded for bf16 workloads)
+  dS_T  = N(0, dst_std) fp32 (the cotangent of the final state), or absent
 bf16 workloads round q, k, v from fp32 to bf16 (round to nearest even); the
 arrays returned here hold those rounded values as fp32, so that an fp64 upcast
 is exact and both sides see the very same numbers.
@@ -33,6 +35,7 @@ SEED = 20260509
 _TID = {
     "q": 1, "k": 2, "v": 3, "eta": 4, "log_alpha": 5, "scale": 6, "S0": 7,
     "dec_q": 11, "dec_k": 12, "dec_v": 13, "dec_eta": 14, "dec_log_alpha": 15, "dec_scale": 16,
+    "do": 21, "dST": 22, "S0_prefill": 23,
 }
 
 
@@ -174,3 +177,22 @@ def decode_inputs(w: Workload) -> dict:
 def custom(name: str, wid: int, **kw) -> Workload:
     """A test workload with its own stream key (wid >= 100 keeps it apart from the named ones)."""
     return Workload(name=name, wid=wid, **kw)
+
+
+def grad_inputs(w: Workload, s0_std: float = 0.0, dst_std: float = 0.0) -> dict:
+    """Cotangents for gradient checks, all heads: do [B, T, H, dv] (bf16-rounded for bf16
+    workloads), and, when the std is positive, an initial state S0 and a final-state cotangent
+    dST [B, H, dk, dv] fp32 (else None)."""
+    do = np.empty((w.B, w.T, w.H, w.dv), np.float32)
+    S0 = np.empty((w.B, w.H, w.dk, w.dv), np.float32) if s0_std > 0 else None
+    dST = np.empty((w.B, w.H, w.dk, w.dv), np.float32) if dst_std > 0 else None
+    for b in range(w.B):
+        for h in range(w.H):
+            x = _rng(w, "do", b, h).standard_normal((w.T, w.dv), dtype=np.float32)
+            do[b, :, h] = round_to_bf16(x) if w.dtype == "bf16" else x
+            if S0 is not None:
+                S0[b, h] = _rng(w, "S0_prefill", b, h).normal(0.0, s0_std, (w.dk, w.dv))
+            if dST is not None:
+                dST[b, h] = _rng(w, "dST", b, h).normal(0.0, dst_std, (w.dk, w.dv))
+    return {"do": do, "S0": S0, "dST": dST}
+

@@ -7,6 +7,9 @@ d_k=d_v=128 (bf16 q/k/v/o, fp32 state and gates) followed by 512 recurrent decod
 steps that continue from the prefill's final states, so every stage runs: the
 beta/decay prologue, the chunk products, the triangular solve, the state scan, the
 output and the decode step. Other workloads (--workload) time one part alone.
+--pass bwd times the chunkwise backward (kla_chunk_bwd: the gradients of a loss on the
+prefill outputs with respect to every input) on a prefill workload instead, as its own
+JSON line.
 
 Inputs are generated (seeded) and copied to HBM before the timed region. Kernels
 are launched through the C ABI with pre-marshalled pointers on torch's current
@@ -32,6 +35,7 @@ sys.path.insert(0, ROOT)
 import workloads as wl  # noqa: E402
 
 METRIC = "chunked-fwd tokens/s + decode tokens/s at 1 GPU; % MFMA / HBM roofline"
+METRIC_BWD = "chunked-bwd tokens/s at 1 GPU; % MFMA / HBM roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
@@ -50,6 +54,20 @@ def chunk_bytes(w, es):
     return w.heads * w.T * per_tok + w.heads * w.dk * w.dv * 4
 
 
+def bwd_flops_per_head_token(dk, dv, C=64):
+    """Dense chunk-product count of the backward: the per-chunk factors again (K K^T, Q K^T),
+    the recompute scan (K S, T R, K^T Delta), the reverse scan (K dS', P^T dO, T^T R',
+    Q^T dO, K^T Zb) and the gradient kernel (K K^T, Q K^T, Zb Delta^T, dO Delta^T, four
+    C x C x d_k products, three C x d_k x d_v products)."""
+    return C * (16 * dk + 10 * dv) + 16 * dk * dv
+
+
+def bwd_bytes(w, es):
+    """Algorithmic HBM bytes of one backward launch: q, k, v, do, eta, log_alpha read once;
+    dq, dk, dv, deta, dlog_alpha written once (no initial state, no state cotangent)."""
+    return w.heads * w.T * ((3 * w.dk + 3 * w.dv) * es + 16)
+
+
 def decode_bytes(w, es):
     """Algorithmic HBM bytes of one decode launch: the fp32 state read and written once,
     q, k, v, o, eta, log_alpha."""
@@ -64,8 +82,11 @@ def log(*a):
 # these files are byte-identical to the ones the counters were taken on.
 CSRC = os.path.join(ROOT, "gated_delta_rule_18_amd", "csrc")
 PART_SOURCES = {
-    "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "kla_device.h", "kla_launch.h"],
+    "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "tile_ops.h", "kla_device.h",
+                  "kla_launch.h"],
     "decode": ["decode.hip", "kla_device.h", "kla_launch.h"],
+    "chunk_bwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "chunk_bwd_scan.hip", "chunk_bwd_grad.hip",
+                  "tile_ops.h", "kla_device.h", "kla_launch.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -142,6 +163,110 @@ def cpu_baseline(w, head_tokens, mode="kla"):
             "sample": f"{what}: {tokens} tokens in {dt:.2f} s (fp64 numpy, one thread)"}
 
 
+def cpu_baseline_bwd(w, head_tokens):
+    """The fp64 gradient oracle (autodiff of the token loop), as it stands, on a bounded sample:
+    the first 8 heads (or all, if fewer) over the first head_tokens / 8 prefill tokens."""
+    import oracle
+    import torch
+    torch.set_num_threads(1)
+    nh = min(8, w.heads)
+    n = max(1, min(head_tokens // nh, w.T))
+    sub = w.with_(T=n)
+    x = wl.prefill_inputs(sub)
+    g = wl.grad_inputs(sub)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:nh]
+    sel = lambda a: np.stack([a[b, :, h] for b, h in heads])
+    args = (sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["eta"]), sel(x["log_alpha"]), w.eps, None, sel(g["do"]))
+    t0 = time.perf_counter()
+    oracle.kla_vjp(*args)
+    dt = time.perf_counter() - t0
+    return {"value": nh * n / dt / w.H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle kla_vjp (fp64 autodiff of the token loop, one thread) on {nh} heads x the first {n} "
+                      f"prefill tokens: {nh * n} head-tokens in {dt:.2f} s, reported per token of all {w.H} heads"}
+
+
+def run_bwd(args, w):
+    """--pass bwd: time kla_chunk_bwd (or kla_gdn_chunk_bwd) over the workload's prefill."""
+    import torch
+    from gated_delta_rule_18_amd import _lib as K
+    device = torch.device("cuda:0")
+    es = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
+    L = K.lib()
+    gdn = args.mode != "kla"
+    log(f"[bench] generating {w.name} ({w.note}) and its output cotangent ...")
+    on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
+    x = wl.prefill_inputs(w)
+    if gdn:
+        x["k"] = unit_keys(x["k"])
+    x["do"] = wl.grad_inputs(w)["do"]
+    t = {n: on(x[n], tdt if n in ("q", "k", "v", "do") else torch.float32) for n in x}
+    del x
+    out = {"dq": torch.empty_like(t["q"]), "dk": torch.empty_like(t["k"]), "dv": torch.empty_like(t["v"]),
+           "deta": torch.empty_like(t["eta"]), "dla": torch.empty_like(t["log_alpha"])}
+    ws_bytes = int(L.kla_chunk_bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(device)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda a: ctypes.c_void_p(a.data_ptr())
+    la = None if args.mode == "deltanet" else P(t["log_alpha"])
+    dla = None if args.mode == "deltanet" else P(out["dla"])
+    head = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), la, None, P(t["do"]), None, P(out["dq"]), P(out["dk"]),
+            P(out["dv"]), P(out["deta"]), dla, None, w.B, w.T, w.H, w.dk, w.dv, 64)
+    if gdn:
+        call = lambda: L.kla_gdn_chunk_bwd(*head, code, P(workspace), ws_bytes, sp)
+    else:
+        call = lambda: L.kla_chunk_bwd(*head, ctypes.c_float(w.eps), code, P(workspace), ws_bytes, sp)
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    log(f"[bench] warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        K.check(call())
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} step(s)")
+    evs = [ev() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        st = call()
+        e[1].record(stream)
+        if st:
+            K.check(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed region {elapsed * 1e3:.2f} ms")
+    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    tokens = w.B * w.T
+    flops = bwd_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
+    nbytes = bwd_bytes(w, es)
+    peak_mfma = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
+    part = {"kernel": "chunk_prep_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + chunk_grad_kernel",
+            "launches_per_step": 1, "ms_per_step": ms, "kernel_avg_us": ms * 1e3, "tokens": tokens,
+            "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
+            "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
+            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "workspace_bytes": ws_bytes, "sources_sha": sources_sha("chunk_bwd")}
+    part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, "chunk_bwd") if args.mode == "kla" else None
+    roof = {"bound": "mfma", "kernel": part["kernel"], "achieved": part["mfma_tflops"], "peak": peak_mfma,
+            "unit": "TFLOP/s", "frac": part["mfma_frac"], "traffic": part["hbm_traffic_bytes_per_launch"],
+            "hbm_view": {"achieved": part["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": part["hbm_frac"]}}
+    result = {
+        "metric": METRIC_BWD, "value": tokens * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; distributions of the workload description; do ~ N(0, 1))",
+        "config": {"workload": w.name, "pass": "bwd", "mode": args.mode, "B": w.B, "H": w.H, "T": w.T,
+                   "d_k": w.dk, "d_v": w.dv, "chunk": 64, "parallelism": "single GPU"},
+        "parts": {"chunk_bwd": part}, "roofline": roof}
+    if not args.no_cpu_baseline and not gdn:
+        log("[bench] cpu baseline: gradient oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_bwd_head_tokens)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +281,10 @@ def main():
                     help="decode steps replayed from a HIP graph (default) or launched one call at a time")
     ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
                     help="size of the oracle's bounded sample, in head-tokens")
+    ap.add_argument("--pass", dest="pass_", default="fwd", choices=("fwd", "bwd"),
+                    help="fwd: the hot path (default); bwd: the chunkwise backward over a prefill workload")
+    ap.add_argument("--cpu-bwd-head-tokens", type=int, default=8192,
+                    help="size of the gradient oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -181,6 +310,13 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
         return
+
+    if args.pass_ == "bwd":
+        w = wl.WORKLOADS["fwd_b8h8_t4096" if args.workload == "mixed_b4h16" else args.workload]
+        if not w.T:
+            print("--pass bwd needs a prefill workload", file=sys.stderr)
+            sys.exit(2)
+        return run_bwd(args, w.with_(steps=0))
 
     w = wl.WORKLOADS[args.workload]
     es = 2 if w.dtype == "bf16" else 4

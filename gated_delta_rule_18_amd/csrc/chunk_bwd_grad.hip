@@ -35,6 +35,9 @@ namespace kla {
 
 namespace {
 
+constexpr int kGradWaves = 8;
+constexpr int kGradThreads = kGradWaves * kWave;
+
 template <typename E, int DK, int DV>
 struct GradSmem {
   alignas(16) E Ks[kChunk * DK];
@@ -49,8 +52,8 @@ struct GradSmem {
   // Partial sums, one slot per producer, added in a fixed order (bitwise reproducible):
   // per lower-triangular C x C tile (row sums of its 16 rows, column sums of its 16 columns) ...
   float rowA[10][16], rowE[10][16], colE[10][16];
-  // ... and per wave (token-row dot products over that wave's d_k rows; <S, dS'>).
-  float kzs[4][kChunk], qos[4][kChunk], kds[4][kChunk], sds[4];
+  // ... per 16-row d_k tile (token-row dot products), and per wave (<S, dS'>).
+  float kzs[DK / 16][kChunk], qos[DK / 16][kChunk], kds[DK / 16][kChunk], sds[kGradWaves];
 };
 
 template <typename E, int DK, int DV>
@@ -63,6 +66,21 @@ __device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
   return h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
 }
 
+// Sum over the 16 lanes of a DPP row (lanes with equal lane / 16), in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+// Sum over the four lanes c, c + 16, c + 32, c + 48.
+__device__ __forceinline__ float col4_sum(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  return x + __shfl_xor(x, 32, kWave);
+}
+
 // lower-triangular tile k (0..9) -> (ti, tj), ti >= tj
 __device__ __forceinline__ void tri_tile(int k, int& ti, int& tj) {
   ti = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
@@ -70,14 +88,17 @@ __device__ __forceinline__ void tri_tile(int k, int& ti, int& tj) {
 }
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) {
+__global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams p) {
   constexpr bool BF = is_bf16<E>();
   constexpr int GK = Grp<E>::K;
   typedef typename Grp<E>::V GV;
   constexpr int PER = 16 / sizeof(E);
   typedef typename Vec16<E>::type V16;
   constexpr int NGD = DK / GK, NGV = DV / GK, NGT = kChunk / GK;
-  constexpr int NI = DK / 64;  // 16-row tiles of d_k per wave
+  constexpr int NW = kGradWaves, NT_ = kGradThreads;
+  constexpr int NIT = DK / 16;           // 16-row tiles of d_k
+  constexpr int TPW = NIT * 4 / NW;      // (d_k tile, token tile) output tiles per wave
+  static_assert(TPW * NW == NIT * 4, "tile split");
   typedef GradSmem<E, DK, DV> Sm;
   __shared__ Sm sm;
 
@@ -104,14 +125,25 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
   const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * p.nchunks, DK, DV);
 
-  // ---- row-major operands straight into LDS (direct-to-LDS loads; rows past T read zeros) ----
+  // ---- every load of the chunk is issued up front: S and dS' into registers (they are
+  //      needed last), the row-major operands straight into LDS, Delta and Zb through
+  //      registers (transposed on the way into LDS) ----
+  constexpr int NSR = DK * DV / PER / NT_;
+  const E* gS = bw.Sn + chunk_id * DK * DV;
+  const E* gdS = bw.dSn + chunk_id * DK * DV;
+  V16 sreg[NSR], dsreg[NSR];
+#pragma unroll
+  for (int i = 0; i < NSR; ++i) {
+    sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + NT_ * i) * PER);
+    dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + NT_ * i) * PER);
+  }
   auto dma_rows = [&](rsrc_t r, E* dst, uint32_t base, uint32_t rowb, uint32_t hcol, auto ncol_tag) {
     constexpr int NCOL = decltype(ncol_tag)::value;
     constexpr int CPR = NCOL / PER, NBLK = kChunk * CPR / 64;
-    static_assert(NBLK % 4 == 0, "block split");
+    static_assert(NBLK % NW == 0, "block split");
 #pragma unroll
-    for (int i = 0; i < NBLK / 4; ++i) {
-      const int blk = wave + 4 * i, ph = 64 * blk + lane, row = ph / CPR;
+    for (int i = 0; i < NBLK / NW; ++i) {
+      const int blk = wave + NW * i, ph = 64 * blk + lane, row = ph / CPR;
       dma16(r, dst + blk * 64 * PER, base + row * rowb + hcol + 16 * swz<E, CPR>(row, ph % CPR));
     }
   };
@@ -120,23 +152,25 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   dma_rows(rdo, sm.dOs, v0, vrow, hcol_v, std::integral_constant<int, DV>());
   dma_rows(rv, sm.St, v0, vrow, hcol_v, std::integral_constant<int, DV>());
 
-  // ---- tile-ordered [64 x DV] blocks, transposed into LDS: lane piece (rows 4g..4g+3 of
-  //      column c of tile (rt, ct)) -> row 16 ct + c, columns 16 rt + 4g .. + 3 ----
+  // tile-ordered [64 x DV] blocks, transposed into LDS: lane piece (rows 4g..4g+3 of column c of
+  // tile (rt, ct)) -> row 16 ct + c, columns 16 rt + 4g .. + 3
   auto load_t64 = [&](const E* src, E* dst) {
-    constexpr int NCH = kChunk * DV / PER / kThreads;  // 16-byte chunks per thread
+    constexpr int NCH = kChunk * DV / PER / NT_;  // 16-byte chunks per thread
+    V16 x[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) x[i] = *reinterpret_cast<const V16*>(src + (tid + NT_ * i) * PER);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + kThreads * i;
-      const V16 x = *reinterpret_cast<const V16*>(src + ci * PER);
+      const int ci = tid + NT_ * i;
 #pragma unroll
       for (int h = 0; h < PER / 4; ++h) {
         const int pi = ci * (PER / 4) + h, ti = pi >> 6, l = pi & 63;
         const int rt = ti / (DV / 16), ct = ti % (DV / 16);
         E* d = dst + at<E, kChunk>(16 * ct + (l & 15), 16 * rt + 4 * (l >> 4));
         if constexpr (BF) {
-          *reinterpret_cast<bf16x4*>(d) = half4(x, h);
+          *reinterpret_cast<bf16x4*>(d) = half4(x[i], h);
         } else {
-          *reinterpret_cast<f32x4*>(d) = x;
+          *reinterpret_cast<f32x4*>(d) = x[i];
         }
       }
     }
@@ -144,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   load_t64(bw.Dl + chunk_id * kChunk * DV, sm.Dt);
   load_t64(bw.Zb + chunk_id * kChunk * DV, sm.Zt);
 
-  // ---- per-token factors; the chunk-local decay prefix G as the forward forms it ----
+  // per-token factors; the chunk-local decay prefix G as the forward forms it
   if (wave == 0) {
     const bool valid = t0 + lane < T;
     const float la = valid && p.log_alpha ? p.log_alpha[(bb * T + t0 + lane) * H + hh] : 0.f;
@@ -154,25 +188,29 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
     sm.eG[lane] = sc[kScEG * kChunk + lane];
     sm.rs[lane] = sc[kScRs * kChunk + lane];
   }
+  // Upper off-diagonal tiles of Ma and Mp that the 32-token contraction groups below reach,
+  // (0, 1) and (2, 3), are zero (fp32 groups are 16 tokens wide and reach none).
+  {
+    constexpr int CPT = 16 / PER;  // 16-byte chunks per tile row
+    const int i = tid;
+    if (i < 2 * 2 * 16 * CPT) {
+      const int cc = i % CPT, rr = (i / CPT) % 16, tile = (i / (16 * CPT)) % 2, arr = i / (32 * CPT);
+      const int r = 16 * (2 * tile) + rr, col = 16 * (2 * tile + 1) + PER * cc;
+      V16 z;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) z[e] = from_f32<E>(0.f);
+      *reinterpret_cast<V16*>((arr ? sm.Mp : sm.Ma) + at<E, kChunk>(r, col)) = z;
+    }
+  }
   wait_vmem<0>();
   __syncthreads();
 
-  // ---- S and dS' (tile-ordered [DK x DV]) into registers while the C x C tiles are formed ----
-  constexpr int NSR = DK * DV / PER / kThreads;
-  const E* gS = bw.Sn + chunk_id * DK * DV;
-  const E* gdS = bw.dSn + chunk_id * DK * DV;
-  V16 sreg[NSR], dsreg[NSR];
-#pragma unroll
-  for (int i = 0; i < NSR; ++i) {
-    sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + kThreads * i) * PER);
-    dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + kThreads * i) * PER);
-  }
-
-  // ---- C x C tiles: K K^T, Q K^T, Zb Delta^T, dO Delta^T -> Ma, Mp and the decay sums ----
-  for (int k = wave; k < 10; k += 4) {
+  // ---- C x C tiles: K K^T, Q K^T, Zb Delta^T, dO Delta^T -> Ma, Mp and the decay sums;
+  //      on diagonal tiles also Zb V^T, whose diagonal is Zb_r . v_r ----
+  for (int k = wave; k < 10; k += NW) {
     int ti, tj;
     tri_tile(k, ti, tj);
-    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, F = kk, dp = kk;
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, F = kk, dp = kk, zvv = kk;
 #pragma unroll
     for (int s = 0; s < NGD; ++s) {
       const GV bk = row_grp<E, DK>(sm.Ks, 16 * tj + c16, s, g);
@@ -182,8 +220,14 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
 #pragma unroll
     for (int s = 0; s < NGV; ++s) {
       const GV bd = kt_grp<E, kChunk>(sm.Dt, tj, s, g, c16);
-      F = mma<E>(kt_grp<E, kChunk>(sm.Zt, ti, s, g, c16), bd, F);
+      const GV az = kt_grp<E, kChunk>(sm.Zt, ti, s, g, c16);
+      F = mma<E>(az, bd, F);
       dp = mma<E>(row_grp<E, DV>(sm.dOs, 16 * ti + c16, s, g), bd, dp);
+      if (ti == tj) zvv = mma<E>(az, row_grp<E, DV>(sm.St, 16 * tj + c16, s, g), zvv);
+    }
+    if (ti == tj && (c16 >> 2) == g) {
+      const int e = c16 & 3;
+      sm.zv[16 * ti + c16] = e == 0 ? zvv[0] : e == 1 ? zvv[1] : e == 2 ? zvv[2] : zvv[3];
     }
     const int s = 16 * tj + c16;
     const float Gs = sm.G[s];
@@ -200,34 +244,14 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
       sm.Ma[at<E, kChunk>(r, s)] = from_f32<E>(crr * na);
       sm.Mp[at<E, kChunk>(r, s)] = from_f32<E>(mp);
       csum += ee;
-      const float ra = group_sum<16>(naKK), re = group_sum<16>(ee);
+      const float ra = row16_sum(naKK), re = row16_sum(ee);
       if (c16 == 0) {
         sm.rowA[k][4 * g + e] = ra;
         sm.rowE[k][4 * g + e] = re;
       }
     }
-    csum += __shfl_xor(csum, 16, kWave);
-    csum += __shfl_xor(csum, 32, kWave);
+    csum = col4_sum(csum);
     if (g == 0) sm.colE[k][c16] = csum;
-  }
-  // upper off-diagonal tiles of Ma and Mp are zero
-  for (int i = tid; i < 6 * 256; i += kThreads) {
-    const int k = i >> 8, e = i & 255;
-    const int ti = k < 3 ? 0 : k < 5 ? 1 : 2, tj = k < 3 ? k + 1 : k < 5 ? k - 1 : 3;
-    const int r = 16 * ti + (e >> 4), s = 16 * tj + (e & 15);
-    sm.Ma[at<E, kChunk>(r, s)] = from_f32<E>(0.f);
-    sm.Mp[at<E, kChunk>(r, s)] = from_f32<E>(0.f);
-  }
-  // Zb_r . v_r (V sits in St for now): four threads per token
-  {
-    const int r = tid >> 2, q = tid & 3;
-    float acc = 0.f;
-#pragma unroll
-    for (int j = q * (DV / 4); j < (q + 1) * (DV / 4); ++j)
-      acc += to_f32(sm.St[at<E, DV>(r, j)]) * to_f32(sm.Zt[at<E, kChunk>(j, r)]);
-    acc += __shfl_xor(acc, 1, kWave);
-    acc += __shfl_xor(acc, 2, kWave);
-    if (q == 0) sm.zv[r] = acc;
   }
   // <S, dS'> over this thread's pieces (same positions in both)
   {
@@ -245,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   auto put_state = [&](const V16* regs) {
 #pragma unroll
     for (int i = 0; i < NSR; ++i) {
-      const int ci = tid + kThreads * i;
+      const int ci = tid + NT_ * i;
 #pragma unroll
       for (int h = 0; h < PER / 4; ++h) {
         const int pi = ci * (PER / 4) + h, ti = pi >> 6, l = pi & 63;
@@ -262,95 +286,83 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   put_state(sreg);
   __syncthreads();
 
-  // ---- d_k x C products, transposed outputs: this wave's d_k tiles it = NI wave .. ----
-  f32x4 accK[NI][4], accQ[NI][4], accZS[NI][4], accOS[NI][4], accDS[NI][4];
+  // ---- d_k x C products, transposed outputs; this wave's tiles (it, rt) ----
+  f32x4 accK[TPW], accQ[TPW], accZS[TPW], accOS[TPW], accDS[TPW];
 #pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int it = NI * wave + ii;
+  for (int t = 0; t < TPW; ++t) {
+    const int it = (wave * TPW + t) / 4, rt = (wave * TPW + t) % 4;
+    f32x4 k_ = {0.f, 0.f, 0.f, 0.f}, q_ = k_, zs = k_, os = k_;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 k_ = {0.f, 0.f, 0.f, 0.f}, q_ = k_, zs = k_, os = k_;
-#pragma unroll
-      for (int s = 0; s < NGT; ++s) {
-        const GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
-        if (GK * s < 16 * (rt + 1)) {  // Ma[r][s], Mp[r][s] vanish for s > r
-          k_ = mma<E>(ak, row_grp<E, kChunk>(sm.Ma, 16 * rt + c16, s, g), k_);
-          q_ = mma<E>(ak, row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g), q_);
-        }
-        if (GK * (s + 1) > 16 * rt) {  // Ma[r][s], Mp[r][s] over r >= s
-          const GV aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16);
-          k_ = mma<E>(ak, kt_grp<E, kChunk>(sm.Ma, rt, s, g, c16), k_);
-          k_ = mma<E>(aq, kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16), k_);
-        }
+    for (int s = 0; s < NGT; ++s) {
+      const GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
+      if (GK * s < 16 * (rt + 1)) {  // Ma[r][s], Mp[r][s] vanish for s > r
+        k_ = mma<E>(ak, row_grp<E, kChunk>(sm.Ma, 16 * rt + c16, s, g), k_);
+        q_ = mma<E>(ak, row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g), q_);
       }
-#pragma unroll
-      for (int s = 0; s < NGV; ++s) {
-        const GV as = kt_grp<E, DK>(sm.St, it, s, g, c16);
-        zs = mma<E>(as, kt_grp<E, kChunk>(sm.Zt, rt, s, g, c16), zs);
-        os = mma<E>(as, row_grp<E, DV>(sm.dOs, 16 * rt + c16, s, g), os);
+      if (GK * (s + 1) > 16 * rt) {  // Ma[r][s], Mp[r][s] over r >= s
+        const GV aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16);
+        k_ = mma<E>(ak, kt_grp<E, kChunk>(sm.Ma, rt, s, g, c16), k_);
+        k_ = mma<E>(aq, kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16), k_);
       }
-      accK[ii][rt] = k_;
-      accQ[ii][rt] = q_;
-      accZS[ii][rt] = zs;
-      accOS[ii][rt] = os;
     }
+#pragma unroll
+    for (int s = 0; s < NGV; ++s) {
+      const GV as = kt_grp<E, DK>(sm.St, it, s, g, c16);
+      zs = mma<E>(as, kt_grp<E, kChunk>(sm.Zt, rt, s, g, c16), zs);
+      os = mma<E>(as, row_grp<E, DV>(sm.dOs, 16 * rt + c16, s, g), os);
+    }
+    accK[t] = k_;
+    accQ[t] = q_;
+    accZS[t] = zs;
+    accOS[t] = os;
   }
   __syncthreads();
   put_state(dsreg);
   __syncthreads();
 #pragma unroll
-  for (int ii = 0; ii < NI; ++ii) {
-    const int it = NI * wave + ii;
+  for (int t = 0; t < TPW; ++t) {
+    const int it = (wave * TPW + t) / 4, rt = (wave * TPW + t) % 4;
+    f32x4 ds = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4 ds = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NGV; ++s)
-        ds = mma<E>(kt_grp<E, DK>(sm.St, it, s, g, c16), kt_grp<E, kChunk>(sm.Dt, rt, s, g, c16), ds);
-      accDS[ii][rt] = ds;
-    }
+    for (int s = 0; s < NGV; ++s)
+      ds = mma<E>(kt_grp<E, DK>(sm.St, it, s, g, c16), kt_grp<E, kChunk>(sm.Dt, rt, s, g, c16), ds);
+    accDS[t] = ds;
   }
 
-  // ---- token-row dot products over d_k: k.(Zb S^T), q.(dO S^T), k.(Delta dS'^T) ----
-  f32x4 kv[NI][4];
+  // ---- token-row dot products over each d_k tile: k.(Zb S^T), q.(dO S^T), k.(Delta dS'^T) ----
+  f32x4 kv[TPW];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int r = 16 * rt + c16;
-    float a = 0.f, b = 0.f, d = 0.f;
-#pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int i0 = 16 * (NI * wave + ii) + 4 * g;
-      f32x4 kx, qx;
-      if constexpr (BF) {
-        const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&sm.Ks[at<E, DK>(r, i0)]);
-        const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&sm.Qs[at<E, DK>(r, i0)]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kx[e] = to_f32(kb[e]);
-          qx[e] = to_f32(qb[e]);
-        }
-      } else {
-        kx = *reinterpret_cast<const f32x4*>(&sm.Ks[at<E, DK>(r, i0)]);
-        qx = *reinterpret_cast<const f32x4*>(&sm.Qs[at<E, DK>(r, i0)]);
-      }
-      kv[ii][rt] = kx;
+  for (int t = 0; t < TPW; ++t) {
+    const int it = (wave * TPW + t) / 4, rt = (wave * TPW + t) % 4;
+    const int r = 16 * rt + c16, i0 = 16 * it + 4 * g;
+    f32x4 kx, qx;
+    if constexpr (BF) {
+      const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&sm.Ks[at<E, DK>(r, i0)]);
+      const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&sm.Qs[at<E, DK>(r, i0)]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        a += kx[e] * accZS[ii][rt][e];
-        b += qx[e] * accOS[ii][rt][e];
-        d += kx[e] * accDS[ii][rt][e];
+        kx[e] = to_f32(kb[e]);
+        qx[e] = to_f32(qb[e]);
       }
+    } else {
+      kx = *reinterpret_cast<const f32x4*>(&sm.Ks[at<E, DK>(r, i0)]);
+      qx = *reinterpret_cast<const f32x4*>(&sm.Qs[at<E, DK>(r, i0)]);
     }
-    a += __shfl_xor(a, 16, kWave);
-    a += __shfl_xor(a, 32, kWave);
-    b += __shfl_xor(b, 16, kWave);
-    b += __shfl_xor(b, 32, kWave);
-    d += __shfl_xor(d, 16, kWave);
-    d += __shfl_xor(d, 32, kWave);
+    kv[t] = kx;
+    float a = 0.f, b = 0.f, d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a += kx[e] * accZS[t][e];
+      b += qx[e] * accOS[t][e];
+      d += kx[e] * accDS[t][e];
+    }
+    a = col4_sum(a);
+    b = col4_sum(b);
+    d = col4_sum(d);
     if (g == 0) {
-      sm.kzs[wave][r] = a;
-      sm.qos[wave][r] = b;
-      sm.kds[wave][r] = d;
+      sm.kzs[it][r] = a;
+      sm.qos[it][r] = b;
+      sm.kds[it][r] = d;
     }
   }
   __syncthreads();
@@ -364,10 +376,15 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
       rowE += sm.rowE[ti * (ti + 1) / 2 + tj][rr];
     }
     for (int tk = ti; tk < 4; ++tk) colE += sm.colE[tk * (tk + 1) / 2 + ti][rr];  // tiles (tk, ti): column r
-    const float kzs = (sm.kzs[0][r] + sm.kzs[1][r]) + (sm.kzs[2][r] + sm.kzs[3][r]);
-    const float qos = (sm.qos[0][r] + sm.qos[1][r]) + (sm.qos[2][r] + sm.qos[3][r]);
-    const float kds = (sm.kds[0][r] + sm.kds[1][r]) + (sm.kds[2][r] + sm.kds[3][r]);
-    const float sds = (sm.sds[0] + sm.sds[1]) + (sm.sds[2] + sm.sds[3]);
+    float kzs = 0.f, qos = 0.f, kds = 0.f, sds = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      kzs += sm.kzs[it][r];
+      qos += sm.qos[it][r];
+      kds += sm.kds[it][r];
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sds += sm.sds[w];
     const float crr = sm.cr[r], eGr = sm.eG[r], GC = sm.G[kChunk - 1];
     const float de = sm.rs[r] * (sm.zv[r] - eGr * kzs + rowA);
     const float wsr = __expf(GC - sm.G[r]) * kds;
@@ -388,39 +405,33 @@ __global__ __launch_bounds__(kThreads) void chunk_grad_kernel(ChunkBwdParams p) 
   // ---- dk, dq: four consecutive d_k entries of one token per lane ----
   const float GC = sm.G[kChunk - 1];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int r = 16 * rt + c16;
+  for (int t = 0; t < TPW; ++t) {
+    const int it = (wave * TPW + t) / 4, rt = (wave * TPW + t) % 4;
+    const int r = 16 * rt + c16, i0 = 16 * it + 4 * g;
     const float crr = sm.cr[r], eGr = sm.eG[r], dec = __expf(GC - sm.G[r]), kc = sm.kcoef[r];
-#pragma unroll
-    for (int ii = 0; ii < NI; ++ii) {
-      const int i0 = 16 * (NI * wave + ii) + 4 * g;
-      const f32x4 dk = accK[ii][rt] - (crr * eGr) * accZS[ii][rt] + dec * accDS[ii][rt] + kc * kv[ii][rt];
-      const f32x4 dq = accQ[ii][rt] + eGr * accOS[ii][rt];
-      const uint32_t off = x0 + r * xrow + hcol_x + i0 * sizeof(E);
-      store4_rsrc<E>(rdk, off, dk);
-      store4_rsrc<E>(rdq, off, dq);
-    }
+    const f32x4 dk = accK[t] - (crr * eGr) * accZS[t] + dec * accDS[t] + kc * kv[t];
+    const f32x4 dq = accQ[t] + eGr * accOS[t];
+    const uint32_t off = x0 + r * xrow + hcol_x + i0 * sizeof(E);
+    store4_rsrc<E>(rdk, off, dk);
+    store4_rsrc<E>(rdq, off, dq);
   }
-  // ---- dv = diag(eta rs) Zb: four threads per token, 16-byte stores ----
-  {
-    const int r = tid >> 2, q = tid & 3;
-    const float crr = sm.cr[r];
+  // ---- dv = diag(eta rs) Zb: the transposing read of Zb^T gives four consecutive d_v
+  //      entries of one token per lane ----
+  constexpr int NJT = DV / 16;
 #pragma unroll
-    for (int j0 = q * (DV / 4); j0 < (q + 1) * (DV / 4); j0 += PER) {
-      V16 out;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) out[e] = from_f32<E>(crr * to_f32(sm.Zt[at<E, kChunk>(j0 + e, r)]));
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, out), rdv,
-                                             v0 + r * vrow + hcol_v + j0 * sizeof(E), 0, 0);
-    }
+  for (int t = 0; t < 4 * NJT / NW; ++t) {
+    const int q = wave * (4 * NJT / NW) + t, rt = q % 4, jt = q / 4;
+    const int r = 16 * rt + c16;
+    const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
+    store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
   }
 }
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkBwdParams& p, hipStream_t stream) {
   if constexpr (grad_fits<E, DK, DV>()) {
-    hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)(p.heads * p.nchunks)), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)(p.heads * p.nchunks)), dim3(kGradThreads),
+                       0, stream, p);
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;

@@ -17,7 +17,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkla.so"
 SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip",
-           "chunk_bwd_scan.hip", "chunk_bwd_grad.hip"]
+           "chunk_seg.hip", "chunk_bwd_scan.hip", "chunk_bwd_grad.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -82,6 +82,51 @@ struct Workspace {
   }
 };
 
+// Modes of the scan kernel: the forward; the backward's recompute (entering states and Delta
+// to the backward workspace, no outputs); the first pass of the segment scan (below).
+enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2 };
+
+// State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four).
+__host__ __device__ constexpr int scan_cols(bool bf16) { return bf16 ? 32 : 64; }
+
+// Segment scan of the forward, for few heads and long sequences (where one workgroup per head
+// and column slice leaves most compute units idle). The chunks of a head are cut into nseg
+// segments of seg_len chunks that are scanned at the same time:
+//   pass 1  every segment from a zero entering state (the first from S_0), giving its outputs
+//           O0 (written to o) and end state; after the first segment also the d_k "identity"
+//           columns (state I, no values), giving the segment's state transition M and, per
+//           chunk, Y = (e^G o Q) M_n - P W M_n, the response of the chunk's output to the
+//           entering state;
+//   pass 2  S_1 = end state of segment 0, S_{j+1} = M_j S_j + (end state of segment j);
+//   pass 3  o += Y S_j on every chunk after the first segment.
+// Every step is the same linear algebra as the one-pass scan (the state recursion is linear
+// in the entering state).
+struct SegPlan {
+  int64_t nseg, seg_len;
+};
+
+template <typename E>
+struct SegSpace {
+  E* Y;         // [n][64][DK]: outputs of the identity columns
+  float* Send;  // [heads * nseg][DK][DV]: end state of each segment from its own entering state
+  float* Mseg;  // [heads * nseg][DK][DK]: state transition of each segment
+  E* SinT;      // [heads * nseg][DV][DK]: entering state of each segment, transposed (pass 2)
+  __host__ __device__ static size_t bytes(int64_t n, int64_t nsegs, int dk, int dv) {
+    return Workspace<E>::bytes(n) + (size_t)n * kChunk * dk * sizeof(E) +
+           (size_t)nsegs * ((dk * dv + dk * dk) * sizeof(float) + dk * dv * sizeof(E));
+  }
+  __host__ __device__ static SegSpace at(void* base, int64_t n, int64_t nsegs, int dk, int dv) {
+    char* p = static_cast<char*>(base) + Workspace<E>::bytes(n);
+    SegSpace w;
+    w.Y = reinterpret_cast<E*>(p);
+    p += (size_t)n * kChunk * dk * sizeof(E);
+    w.Send = reinterpret_cast<float*>(p);
+    w.Mseg = w.Send + (size_t)nsegs * dk * dv;
+    w.SinT = reinterpret_cast<E*>(w.Mseg + (size_t)nsegs * dk * dk);
+    return w;
+  }
+};
+
 struct ChunkParams {
   const void* q;
   const void* k;
@@ -99,6 +144,7 @@ struct ChunkParams {
   // eta_r = sign(beta_r), rs_r = sqrt(|beta_r|). The backward needs the unbalanced factors to
   // form d(beta) on tokens whose beta is zero.
   bool unit_rs;
+  int64_t nseg = 1, seg_len = 0;  // segment scan (kScanSeg): segments per head, chunks per segment
 };
 
 // Backward workspace: the forward workspace above, then per chunk (same chunk ids)

@@ -39,6 +39,8 @@
 // buffers: one workgroup barrier per chunk. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
+#include <cstdlib>
+
 #include "tile_ops.h"
 
 namespace kla {
@@ -47,10 +49,13 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
-// REC (backward recompute): no outputs; instead every chunk's entering state S and its Delta
-// (rs D) are stored to the backward workspace, and Q and P are not loaded.
-template <typename E, int DK, int DV, int W, int NT, bool REC>
+// MODE kScanRec (backward recompute): no outputs; instead every chunk's entering state S and its
+// Delta (rs D) are stored to the backward workspace, and Q and P are not loaded.
+// MODE kScanSeg (segment scan, pass 1): workgroups cover (head, segment) pairs and, besides the
+// DV / DVS slices of the state, DK / DVS slices of identity columns (chunk_common.h).
+template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
+  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg;
   constexpr bool BF = is_bf16<E>();
   constexpr int GK = Grp<E>::K;
   typedef typename Grp<E>::V GV;
@@ -71,19 +76,30 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   __shared__ typename std::conditional<(NB >= 2), Buf, int>::type buf1;
   __shared__ typename std::conditional<(NB >= 3), Buf, int>::type buf2;
 
+  // Workgroup -> (head, segment) and slice. The workgroups of one (head, segment) get ids
+  // congruent mod 8, so they run on one XCD and share its L2.
+  constexpr int NSK = SEG ? DK / DVS : 0;  // identity-column slices (segment scan)
+  constexpr int NSA = NS + NSK;
+  static_assert(!SEG || DK % DVS == 0, "shape");
+  const int64_t nseg = SEG ? p.nseg : 1;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int local = bid / kXcds;
-  const int64_t head = (int64_t)(local / NS) * kXcds + xcd;
-  const int slice = local % NS;
-  if (head >= p.heads) return;
+  const int64_t vh = (int64_t)(local / NSA) * kXcds + xcd;  // head * nseg + segment
+  const int slice = local % NSA;
+  if (vh >= p.heads * nseg) return;
+  const int64_t head = vh / nseg, seg = vh % nseg;
+  const bool mpart = slice >= NS;  // identity columns: segments after the first only
+  if (mpart && seg == 0) return;
   const int64_t bb = head / p.H, hh = head % p.H;
   const int64_t T = p.T, nchunks = p.nchunks, H = p.H;
+  const int64_t cb = SEG ? seg * p.seg_len : 0;                                     // first chunk
+  const int64_t ce = SEG ? (cb + p.seg_len < nchunks ? cb + p.seg_len : nchunks) : nchunks;  // end
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  const int j0 = slice * DVS;  // first state column of this workgroup
-  const int cw = wave * NC;    // first column of this wave within the slice
+  const int j0 = (mpart ? slice - NS : slice) * DVS;  // first state (or identity) column of this workgroup
+  const int cw = wave * NC;                          // first column of this wave within the slice
 
   // ---- resources: this batch's rows of q/k/v/o, this head's workspace chunks ----
   const int64_t brow = bb * T * H;
@@ -98,13 +114,20 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
-  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
+  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + (mpart ? 0 : j0)) * sizeof(E);
   // Backward recompute: this head's state and Delta blocks, tile-ordered (chunk_common.h).
   constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
   const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * nchunks, DK, DV);
   const rsrc_t rsn = make_rsrc(bw.Sn + chunk0 * DK * DV, REC ? (uint32_t)(nchunks * kSBytes) : 0u);
   const rsrc_t rdl = make_rsrc(bw.Dl + chunk0 * kChunk * DV, REC ? (uint32_t)(nchunks * kDBytes) : 0u);
   const int ct0 = (j0 + cw) / 16;  // first global 16-column tile of this wave
+  // Output rows: o (the state columns; after the first segment of a segment scan these are
+  // outputs from a zero entering state, corrected in place later), or, for identity columns, Y
+  // in the segment workspace ([chunk][64][DK] per head). One store form for both.
+  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.heads * nchunks, p.heads * nseg, DK, DV);
+  const rsrc_t rout = mpart ? make_rsrc(sg.Y + chunk0 * kChunk * DK, (uint32_t)(nchunks * kChunk * DK * sizeof(E))) : ro;
+  const uint32_t orow = mpart ? DK * sizeof(E) : vrow;                       // bytes per output row
+  const uint32_t ocol = mpart ? (j0 + cw) * sizeof(E) : hcol_v + cw * sizeof(E);  // this wave's first column
 
   // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the waves. Lane l of
   // block b fills physical chunk 64 b + l; its source is the logical chunk stored there. ----
@@ -135,7 +158,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : 2 * NBK + 2 * NBT + NBV + 1;
   constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
-    c = c < nchunks ? c : nchunks - 1;
+    c = c < ce ? c : ce - 1;
     const uint32_t t0 = (uint32_t)(c * kChunk);
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
@@ -159,7 +182,14 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 
   // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[16 rt + 4g + e][j0 + cw + 16 ct + c] ----
   f32x4 S[RTK][NT];
-  if (p.state_in) {
+  if (mpart) {  // identity columns
+#pragma unroll
+    for (int r = 0; r < RTK; ++r)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[r][ct][e] = 16 * r + 4 * g + e == j0 + cw + 16 * ct + c16 ? 1.f : 0.f;
+  } else if (p.state_in && seg == 0) {
     const float* Sin = p.state_in + head * (int64_t)DK * DV;
 #pragma unroll
     for (int r = 0; r < RTK; ++r)
@@ -183,7 +213,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     if constexpr (NB == 1) {
       wait_vmem<0>();
     } else {
-      if (c < DIST)
+      if (c - cb < DIST)
         wait_vmem<(DIST - 1) * NDMA>();
       else
         wait_vmem<(DIST - 1) * NDMA + DIST * NST>();
@@ -227,14 +257,15 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       }
     }
 
-    // ---- R = eta rs (V - e^G X), in place of X ----
+    // ---- R = eta rs (V - e^G X), in place of X (identity columns carry no values) ----
+    const float vscale = mpart ? 0.f : 1.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const f32x4 coefR = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + 16 * r + 4 * g]);
       const f32x4 eG = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + 16 * r + 4 * g]);
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        const f32x4 v = col4<E, DVS>(B.V, 16 * r, cw + 16 * ct, g, c16);
+        const f32x4 v = vscale * col4<E, DVS>(B.V, 16 * r, cw + 16 * ct, g, c16);
         X[r][ct] = coefR * (v - eG * X[r][ct]);
       }
     }
@@ -300,17 +331,9 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
           for (int ct = 0; ct < NT; ++ct) o[ct] = mma<E>(b1[ct][s], ap, o[ct]);
         }
       }
-      const uint32_t off = (t0 + 16 * r + c16) * vrow + hcol_v + (cw + 4 * g) * sizeof(E);
+      const uint32_t off = (t0 + 16 * r + c16) * orow + ocol + 4 * g * sizeof(E);
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) {
-        if constexpr (BF) {
-          const bf16x4 ob = {from_f32<bf16>(o[ct][0]), from_f32<bf16>(o[ct][1]), from_f32<bf16>(o[ct][2]),
-                             from_f32<bf16>(o[ct][3])};
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, off + 16 * ct * sizeof(E), 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[ct]), ro, off + 16 * ct * sizeof(E), 0, 0);
-        }
-      }
+      for (int ct = 0; ct < NT; ++ct) store4_rsrc<E>(rout, off + 16 * ct * sizeof(E), o[ct]);
     }
 
     // ---- S <- e^{G_C} S + K^T diag(e^{G_C - G}) D' ----
@@ -328,31 +351,40 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
     if constexpr (NB == 1) {
       __syncthreads();
-      if (c + 1 < nchunks) fetch(B, c + 1);
+      if (c + 1 < ce) fetch(B, c + 1);
     }
   };
 
-  if (nchunks > 0) {  // chunks 0 .. DIST - 1
-    fetch(buf0, 0);
-    if constexpr (NB == 3) fetch(buf1, 1);
+  if (ce > cb) {  // chunks cb .. cb + DIST - 1
+    fetch(buf0, cb);
+    if constexpr (NB == 3) fetch(buf1, cb + 1);
   }
   if constexpr (NB == 3) {
-    for (int64_t c = 0; c < nchunks; c += 3) {
+    for (int64_t c = cb; c < ce; c += 3) {
       step(buf0, buf2, c);
-      if (c + 1 < nchunks) step(buf1, buf0, c + 1);
-      if (c + 2 < nchunks) step(buf2, buf1, c + 2);
+      if (c + 1 < ce) step(buf1, buf0, c + 1);
+      if (c + 2 < ce) step(buf2, buf1, c + 2);
     }
   } else if constexpr (NB == 2) {
-    for (int64_t c = 0; c < nchunks; c += 2) {
+    for (int64_t c = cb; c < ce; c += 2) {
       step(buf0, buf1, c);
-      if (c + 1 < nchunks) step(buf1, buf0, c + 1);
+      if (c + 1 < ce) step(buf1, buf0, c + 1);
     }
   } else {
-    for (int64_t c = 0; c < nchunks; ++c) step(buf0, buf0, c);
+    for (int64_t c = cb; c < ce; ++c) step(buf0, buf0, c);
   }
 
   wait_vmem<0>();  // no load into LDS outlives the workgroup
-  if (p.state_out) {
+  if (SEG) {  // end state of the segment, or its transition (identity columns)
+    float* dst = mpart ? sg.Mseg + vh * DK * DK : sg.Send + vh * DK * DV;
+    const int ld = mpart ? DK : DV;
+#pragma unroll
+    for (int r = 0; r < RTK; ++r)
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(int64_t)(16 * r + 4 * g + e) * ld + j0 + cw + 16 * ct + c16] = S[r][ct][e];
+  } else if (p.state_out) {
     float* Sout = p.state_out + head * (int64_t)DK * DV;
 #pragma unroll
     for (int r = 0; r < RTK; ++r)
@@ -363,43 +395,78 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   }
 }
 
-template <typename E, int DK, int DV, int W, int NT, bool REC>
+template <typename E, int DK, int DV, int W, int NT, int MODE>
 hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
-  constexpr int NS = DV / (W * 16 * NT);
-  const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, REC>), dim3((unsigned)(heads8 * NS)), dim3(W * kWave), 0,
+  constexpr int DVS = W * 16 * NT;
+  static_assert(DVS == scan_cols(is_bf16<E>()), "column split as planned");
+  constexpr int NSA = DV / DVS + (MODE == kScanSeg ? DK / DVS : 0);
+  const int64_t units = p.heads * (MODE == kScanSeg ? p.nseg : 1);  // (head, segment) pairs
+  const int64_t units8 = (units + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3(W * kWave), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-template <typename E, int DK, int DV, bool REC>
+template <typename E, int DK, int DV, int MODE>
 hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
   // bf16: two waves of 16 columns per workgroup (32 columns; four workgroups per 128-column
   // head). This split measured fastest: a wave's time per chunk is set by latency, not by
   // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
   // need a single LDS buffer, whose load is not overlapped, so more columns share it).
   if constexpr (is_bf16<E>())
-    return launch_wnt<E, DK, DV, 2, 1, REC>(p, stream);
+    return launch_wnt<E, DK, DV, 2, 1, MODE>(p, stream);
   else
-    return launch_wnt<E, DK, DV, 4, 1, REC>(p, stream);
+    return launch_wnt<E, DK, DV, 4, 1, MODE>(p, stream);
 }
 
-template <typename E, bool REC = false>
+template <typename E, int MODE = kScanFwd>
 hipError_t launch_scan(const ChunkParams& p, int64_t d_k, int64_t d_v, hipStream_t stream) {
-  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128, REC>(p, stream);
-  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64, REC>(p, stream);
-  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64, REC>(p, stream);
-  return launch_dk_dv<E, 64, 128, REC>(p, stream);
+  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128, MODE>(p, stream);
+  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64, MODE>(p, stream);
+  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64, MODE>(p, stream);
+  return launch_dk_dv<E, 64, 128, MODE>(p, stream);
 }
 
 }  // namespace
 
+hipError_t launch_seg_combine(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream);
+hipError_t launch_seg_fix(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream);
+
 hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
-  return bf16_io ? launch_scan<bf16, true>(p, d_k, d_v, stream) : launch_scan<float, true>(p, d_k, d_v, stream);
+  return bf16_io ? launch_scan<bf16, kScanRec>(p, d_k, d_v, stream) : launch_scan<float, kScanRec>(p, d_k, d_v, stream);
 }
 
-size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t, int64_t, bool bf16_io) {
-  const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
+// Segments for a forward of `heads` heads and `nchunks` chunks. One segment while the one-pass
+// scan's workgroups (heads x column slices) fill the 256 compute units; else enough segments
+// for one workgroup per compute unit over both column kinds, at least eight chunks each. (One
+// scan workgroup fills a compute unit's LDS, and the output correction grows with the number
+// of segments: on B1 H16 T65536, 2 segments measured 1.29 ms, 4 1.32 ms, 8 1.37 ms, against
+// 1.90 ms unsegmented.) KLA_FWD_SEGMENTS, when set, fixes the number of segments (a tuning
+// and testing override).
+SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool bf16_io) {
+  if (nchunks < 2) return SegPlan{1, nchunks};
+  const int64_t cols = scan_cols(bf16_io);
+  const int64_t units8 = (heads + kXcds - 1) / kXcds * kXcds;
+  int64_t nseg = 1;
+  if (const char* env = std::getenv("KLA_FWD_SEGMENTS")) {
+    nseg = std::atoll(env);
+  } else if (units8 * (d_v / cols) < 256 && nchunks >= 32) {
+    const int64_t per = heads * ((d_v + d_k) / cols);  // workgroups per segment
+    nseg = (256 + per - 1) / per;
+    if (nseg > nchunks / 8) nseg = nchunks / 8;
+  }
+  if (nseg < 1) nseg = 1;
+  if (nseg > nchunks) nseg = nchunks;
+  const int64_t len = (nchunks + nseg - 1) / nseg;
+  return SegPlan{(nchunks + len - 1) / len, len};
+}
+
+size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io) {
+  const int64_t nch = (T + kChunk - 1) / kChunk, n = B * H * nch;
+  const SegPlan sp = seg_plan(B * H, nch, d_k, d_v, bf16_io);
+  if (sp.nseg > 1)
+    return bf16_io ? SegSpace<bf16>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v)
+                   : SegSpace<float>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v);
   return bf16_io ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n);
 }
 
@@ -410,7 +477,16 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;
   }
-  return a.bf16 ? launch_scan<bf16>(p, a.d_k, a.d_v, stream) : launch_scan<float>(p, a.d_k, a.d_v, stream);
+  const SegPlan sp = seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16);
+  if (sp.nseg <= 1)
+    return a.bf16 ? launch_scan<bf16>(p, a.d_k, a.d_v, stream) : launch_scan<float>(p, a.d_k, a.d_v, stream);
+  p.nseg = sp.nseg;
+  p.seg_len = sp.seg_len;
+  hipError_t e = a.bf16 ? launch_scan<bf16, kScanSeg>(p, a.d_k, a.d_v, stream)
+                        : launch_scan<float, kScanSeg>(p, a.d_k, a.d_v, stream);
+  if (e == hipSuccess) e = launch_seg_combine(p, a.d_k, a.d_v, a.bf16, stream);
+  if (e == hipSuccess) e = launch_seg_fix(p, a.d_k, a.d_v, a.bf16, stream);
+  return e;
 }
 
 }  // namespace kla

@@ -76,6 +76,33 @@ def test_chunk_fwd_rejects(kw, status):
 def test_chunk_fwd_empty_batch_is_a_no_op():
     assert chunk(B=0) == K.KLA_OK
     assert chunk(H=0, q=0, k=0) == K.KLA_OK
+    assert chunk(T=0) == K.KLA_OK  # no state requested: nothing to write, nothing launched
+
+
+@pytest.mark.parametrize("segments", [None, "3", "0", "-2", "100000"])
+def test_chunk_fwd_plan_is_host_only_and_total(segments, monkeypatch):
+    """The workspace size (which depends on the segment plan) is defined for every length,
+    and KLA_FWD_SEGMENTS only changes it, never breaks it."""
+    if segments is None:
+        monkeypatch.delenv("KLA_FWD_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("KLA_FWD_SEGMENTS", segments)
+    for T in (1, 2, 63, 64, 65, 129, 4096, 65536):
+        for H in (1, 16, 64):
+            assert K.lib().kla_chunk_fwd_workspace_size(1, T, H, 128, 128, 64, K.KLA_BF16) > 0
+    assert chunk(T=0) == K.KLA_OK
+
+
+def test_long_few_head_forward_plans_segments(monkeypatch):
+    """B1 H16 T65536: the one-pass scan would occupy 64 of 256 compute units, so the plan
+    segments the sequence and the workspace grows by the segment buffers; B8 H8 T4096 does not."""
+    monkeypatch.delenv("KLA_FWD_SEGMENTS", raising=False)
+    ws = lambda B, T, H: K.lib().kla_chunk_fwd_workspace_size(B, T, H, 128, 128, 64, K.KLA_BF16)
+    monkeypatch.setenv("KLA_FWD_SEGMENTS", "1")
+    one_long, one_b8 = ws(1, 65536, 16), ws(8, 4096, 8)
+    monkeypatch.delenv("KLA_FWD_SEGMENTS")
+    assert ws(1, 65536, 16) > one_long
+    assert ws(8, 4096, 8) == one_b8
 
 
 @pytest.mark.parametrize("kw,status", [

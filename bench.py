@@ -82,8 +82,8 @@ def log(*a):
 # these files are byte-identical to the ones the counters were taken on.
 CSRC = os.path.join(ROOT, "gated_delta_rule_18_amd", "csrc")
 PART_SOURCES = {
-    "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "tile_ops.h", "kla_device.h",
-                  "kla_launch.h"],
+    "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "chunk_seg.hip", "tile_ops.h",
+                  "kla_device.h", "kla_launch.h"],
     "decode": ["decode.hip", "kla_device.h", "kla_launch.h"],
     "chunk_bwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "chunk_bwd_scan.hip", "chunk_bwd_grad.hip",
                   "tile_ops.h", "kla_device.h", "kla_launch.h"],
@@ -436,8 +436,11 @@ def main():
         ms = sum(e["fwd"][0].elapsed_time(e["fwd"][1]) for e in evs) / args.steps
         flops = chunk_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
         nbytes = chunk_bytes(w, es)
+        segs = 1 if w.heads * (w.dv // (32 if es == 2 else 64)) >= 256 or w.T < 32 * 64 else None
         parts["chunk_fwd"] = {
-            "kernel": "chunk_prep_kernel + chunk_scan_kernel", "launches_per_step": 1, "ms_per_step": ms,
+            "kernel": "chunk_prep_kernel + chunk_scan_kernel" + (
+                "" if segs == 1 else " (+ seg_combine_kernel + seg_fix_kernel when the plan segments)"),
+            "launches_per_step": 1, "ms_per_step": ms,
             "kernel_avg_us": ms * 1e3, "tokens": fwd_tokens, "tokens_per_s": fwd_tokens / (ms * 1e-3),
             "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12,

@@ -13,6 +13,8 @@ Sources (titles as the pages give them):
     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t v_t k_t^T, output o_t = S_t q_t;
     section 3: the chunkwise inter-chunk state update and intra-chunk output,
     with log-domain decay prefixes.
+  * "Deep Dive into KDA", section 2.3: the per-channel (diagonal) decay of KDA,
+    kda_recurrent / kda_forward / kda_chunked.
   * kla_grad: gradients of the same token loop (reverse-mode autodiff in fp64 on
     the CPU), for the chunkwise backward; the pages give no backward formulas.
 
@@ -31,5 +33,8 @@ from .kla_oracle import (  # noqa: F401
     kla_decode_steps,
     kla_chunked,
     kla_prepare_beta,
+    kda_recurrent,
+    kda_forward,
+    kda_chunked,
 )
 from .kla_grad import gated_delta_vjp, kla_vjp, kla_backward  # noqa: F401,E402

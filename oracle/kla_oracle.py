@@ -193,3 +193,75 @@ def kla_chunked(q, k, v, eta, log_alpha, eps, S0=None, chunk=64):
         Kt = np.exp(G[:, -1:] - G)[:, :, None] * K
         S = np.exp(G[:, -1])[:, None, None] * S + Kt.transpose(0, 2, 1) @ Delta
     return o, S
+
+
+def kda_recurrent(q, k, v, beta, log_a, S0=None):
+    """The delta rule with a per-channel (diagonal) decay ("Deep Dive into KDA", section 2.3),
+    in the [d_k, d_v] state orientation of this module: Diag(a_t) scales the state's d_k rows,
+    the dimension the keys index ("each memory dimension" forgets at its own rate):
+
+        S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T,    o_t = S_t^T q_t.
+
+    Head-major: q, k [N, T, d_k]; v [N, T, d_v]; beta [N, T]; log_a [N, T, d_k]; S0 [N, d_k, d_v]
+    or None. Per token: decay S' = Diag(a_t) S; recall u = S'^T k_t; write S_t = S' + beta_t k_t
+    (v_t - u)^T; read o_t = S_t^T q_t. Returns o [N, T, d_v] and S_T, fp64."""
+    q, k, v, beta, log_a = map(_f64, (q, k, v, beta, log_a))
+    N, T, dk = k.shape
+    dv = v.shape[-1]
+    S = np.zeros((N, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.empty((N, T, dv))
+    a = np.exp(log_a)
+    for t in range(T):
+        kt = k[:, t]
+        S *= a[:, t, :, None]
+        u = np.einsum("nij,ni->nj", S, kt)
+        S += beta[:, t, None, None] * (kt[:, :, None] * (v[:, t] - u)[:, None, :])
+        o[:, t] = np.einsum("nij,ni->nj", S, q[:, t])
+    return o, S
+
+
+def kda_forward(q, k, v, eta, log_a, eps, S0=None, beta_given=False):
+    """Library layout: q, k [B, T, H, d_k]; v [B, T, H, d_v]; eta (or beta when beta_given)
+    [B, T, H]; log_a [B, T, H, d_k]; S0 [B, H, d_k, d_v] or None. The step is the Kaczmarz
+    beta = eta / (||k||^2 + eps) unless beta is given. Returns o [B, T, H, d_v], S_T."""
+    B, T, H, dk = np.shape(k)
+    dv = np.shape(v)[-1]
+    kh = _to_heads(k)
+    b = _to_heads(eta) if beta_given else kaczmarz_step_size(kh, _to_heads(eta), eps)
+    s0 = None if S0 is None else _f64(S0).reshape(B * H, dk, dv)
+    o, S = kda_recurrent(_to_heads(q), kh, _to_heads(v), b, _to_heads(log_a), s0)
+    return _from_heads(o, B, H), S.reshape(B, H, dk, dv)
+
+
+def kda_chunked(q, k, v, beta, log_a, S0=None, chunk=64):
+    """Chunkwise form of kda_recurrent ("Deep Dive into KDA", section 3, with the diagonal
+    decay: Gamma holds per-channel cumulative decays). Per chunk, with G [C, d_k] the chunk-local
+    inclusive prefix of log a and S the entering state:
+      A[r, s] = beta_r sum_i k_r[i] k_s[i] exp(G_r[i] - G_s[i])   (s < r)
+      P[r, s] = sum_i q_r[i] k_s[i] exp(G_r[i] - G_s[i])          (s <= r)
+      Delta   = (I + A)^-1 diag(beta) (V - (K o e^G) S)
+      O       = (Q o e^G) S + P Delta
+      S      <- Diag(e^{G_C}) S + (K o e^{G_C - G})^T Delta
+    The page's K / Gamma is replaced by the ratios exp(G_r - G_s) with s <= r, never above 1.
+    Head-major as kda_recurrent; the last chunk may be shorter."""
+    q, k, v, beta, log_a = map(_f64, (q, k, v, beta, log_a))
+    N, T, dk = k.shape
+    dv = v.shape[-1]
+    S = np.zeros((N, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.empty((N, T, dv))
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, min(c0 + chunk, T))
+        K, Q, V, b = k[:, sl], q[:, sl], v[:, sl], beta[:, sl]
+        C = K.shape[1]
+        G = np.cumsum(log_a[:, sl], axis=1)                        # [N, C, dk]
+        incl = np.tril(np.ones((C, C), dtype=bool))
+        D = np.where(incl[None, :, :, None], G[:, :, None, :] - G[:, None, :, :], -np.inf)
+        R = np.exp(D)                                               # [N, C, C, dk], ratios <= 1
+        KK = np.einsum("nri,nsi,nrsi->nrs", K, K, R)
+        QK = np.einsum("nri,nsi,nrsi->nrs", Q, K, R)
+        A = b[:, :, None] * KK * np.tril(np.ones((C, C)), -1)
+        Tinv = np.linalg.solve(np.eye(C) + A, np.broadcast_to(np.eye(C), A.shape))
+        Delta = Tinv @ (b[:, :, None] * (V - (K * np.exp(G)) @ S))
+        o[:, sl] = (Q * np.exp(G)) @ S + QK @ Delta
+        S = np.exp(G[:, -1])[:, :, None] * S + (K * np.exp(G[:, -1:] - G)).transpose(0, 2, 1) @ Delta
+    return o, S

@@ -16,6 +16,9 @@ from ._lib import (  # noqa: F401
     kla_gdn_chunk_bwd,
     kla_gdn_chunk_fwd,
     kla_gdn_decode_step,
+    kla_kda_chunk_fwd,
+    kla_kda_chunk_fwd_workspace_size,
+    kla_kda_decode_step,
     kla_prepare_beta,
     lib,
 )

@@ -32,6 +32,10 @@ _SIGNATURES = {
     "kla_chunk_bwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_gdn_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_kda_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
+    "kla_kda_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
+                                                               _c_void_p]),
+    "kla_kda_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
     "kla_status_string": (ctypes.c_char_p, [_int]),
     "kla_last_error": (ctypes.c_char_p, []),
 }
@@ -331,4 +335,52 @@ def kla_gdn_chunk_bwd(q, k, v, beta, log_alpha, do, state_in=None, dstate_out=No
     Returns dq, dk, dv, dbeta, dlog_alpha (None when log_alpha is) and dstate_in."""
     return _bwd("kla_gdn_chunk_bwd", "beta", q, k, v, beta, log_alpha, True, do, state_in, dstate_out, None,
                 want_dstate_in, chunk, workspace, stream, out)
+
+
+def kla_kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16) -> int:
+    return int(lib().kla_kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+
+
+def kla_kda_chunk_fwd(q, k, v, eta, log_a, eps=1e-6, beta_given=False, state_in=None, return_state=True, o=None,
+                      state_out=None, chunk=CHUNK, workspace=None, stream=None):
+    """Chunkwise forward with a per-channel decay (KDA's gate): log_a [B, T, H, d_k] fp32; eta
+    [B, T, H] fp32 is eta of the Kaczmarz step, or beta itself when beta_given. Otherwise as
+    kla_chunk_fwd. Returns (o, final state or None)."""
+    torch = _torch()
+    B, T, H, dk, dv, dev, o, state_out = _fwd_tensors(q, k, v, "eta", eta, None, True, state_in, return_state, o,
+                                                      state_out)
+    _need(log_a, "log_a", (B, T, H, dk), torch.float32, dev)
+    code = _dtype_code(q)
+    need = kla_kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().kla_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in),
+                                  _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, float(eps), int(bool(beta_given)),
+                                  code, _ptr(workspace), ws_bytes, _stream(dev, stream)))
+    return o, state_out
+
+
+def kla_kda_decode_step(q, k, v, eta, log_a, state, eps=1e-6, beta_given=False, o=None, stream=None):
+    """One decode step with a per-channel decay, in place on ``state``: log_a [B, H, d_k] fp32;
+    eta [B, H] (eta of the Kaczmarz step, or beta when beta_given). Returns o [B, H, d_v]."""
+    torch = _torch()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, H, dk), dt, dev)
+    _need(k, "k", (B, H, dk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(eta, "eta", (B, H), torch.float32, dev)
+    _need(log_a, "log_a", (B, H, dk), torch.float32, dev)
+    _need(state, "state", (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(o, "o", (B, H, dv), dt, dev)
+    check(lib().kla_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state), _ptr(o),
+                                    B, H, dk, dv, float(eps), int(bool(beta_given)), _dtype_code(q),
+                                    _stream(dev, stream)))
+    return o
 

@@ -84,7 +84,7 @@ struct Workspace {
 
 // Modes of the scan kernel: the forward; the backward's recompute (entering states and Delta
 // to the backward workspace, no outputs); the first pass of the segment scan (below).
-enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2 };
+enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3 };
 
 // State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four).
 __host__ __device__ constexpr int scan_cols(bool bf16) { return bf16 ? 32 : 64; }
@@ -123,6 +123,31 @@ struct SegSpace {
     w.Send = reinterpret_cast<float*>(p);
     w.Mseg = w.Send + (size_t)nsegs * dk * dv;
     w.SinT = reinterpret_cast<E*>(w.Mseg + (size_t)nsegs * dk * dk);
+    return w;
+  }
+};
+
+// KDA (per-channel decay) workspace: the forward workspace above, then per chunk the decayed
+// operands of the scan, in the input dtype, rows of d_k:
+//   K1 [64][DK] = K o e^G,  Q1 [64][DK] = Q o e^G,  K2 [64][DK] = K o e^{G_C - G}
+// and the chunk's state decay gamma [DK] = e^{G_C} (fp32), where G [64][DK] is the chunk-local
+// inclusive prefix of log a per channel. Every exponent is <= 0.
+template <typename E>
+struct KdaSpace {
+  E* K1;
+  E* Q1;
+  E* K2;
+  float* gamma;
+  __host__ __device__ static size_t bytes(int64_t n, int dk) {
+    return Workspace<E>::bytes(n) + (size_t)n * dk * (3 * kChunk * sizeof(E) + sizeof(float));
+  }
+  __host__ __device__ static KdaSpace at(void* base, int64_t n, int dk) {
+    E* p = reinterpret_cast<E*>(static_cast<char*>(base) + Workspace<E>::bytes(n));
+    KdaSpace w;
+    w.K1 = p;
+    w.Q1 = w.K1 + (size_t)n * kChunk * dk;
+    w.K2 = w.Q1 + (size_t)n * kChunk * dk;
+    w.gamma = reinterpret_cast<float*>(w.K2 + (size_t)n * kChunk * dk);
     return w;
   }
 };

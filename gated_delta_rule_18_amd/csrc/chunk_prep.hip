@@ -81,6 +81,101 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// T = (I + A)^-1 in place of A in sm.Af, and the chunk's P, T and factor rows to the workspace.
+// Called by all threads of the workgroup once A (sm.Af, fp32, zero on and above the diagonal),
+// P (sm.Ps) and the factor rows (sm.sc) are in LDS and published by a barrier.
+template <typename E, typename Sm>
+__device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
+  constexpr int VN = Vec16<E>::N;
+  typedef typename Vec16<E>::type V16;
+  constexpr int LDF = Sm::LDF;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  // ---- diagonal blocks of T by forward substitution (wave 0); waves 1-3 store P and the factors ----
+  if (wave == 0) {
+    const int base = (lane >> 4) * 16, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* arow = &sm.Af[base + i][base];
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
+      x[i] = (i == col) ? 1.f : -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
+  } else {
+    const int t = tid - kWave;  // 0 .. 191
+    constexpr int VPR = kChunk / VN;
+    E* gP = ws.P + chunk_id * kChunk * kChunk;
+    for (int i = t; i < kChunk * VPR; i += kThreads - kWave) {
+      const int r = i / VPR, c0 = (i % VPR) * VN;
+      V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
+      if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
+#pragma unroll
+        for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
+      }
+      *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
+    }
+    float* gS = ws.SC + chunk_id * kScRows * kChunk;
+    for (int i = t; i < kScRows * kChunk; i += kThreads - kWave) gS[i] = (&sm.sc[0][0])[i];
+  }
+  __syncthreads();
+
+  // ---- T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1) ----
+  if (wave < 2) {
+    const int i = 1 + 2 * wave, j = 2 * wave;
+    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(m, &sm.Af[16 * i][16 * j], LDF, 1, &sm.Af[16 * j][16 * j], LDF, 1, 0, 16, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Ms[wave][4 * lq + e][lr] = m[e];
+    wave_lds_sync();
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(t, &sm.Af[16 * i][16 * i], LDF, 1, &sm.Ms[wave][0][0], 20, 1, 0, 16, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Af[16 * i + 4 * lq + e][16 * j + lr] = -t[e];
+  }
+  __syncthreads();
+
+  // ---- M2 = A[2:4, 0:2] T[0:2, 0:2] (T lower: column block tj starts at row 16 tj) ----
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x4 m = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(m, &sm.Af[32 + 16 * ti][0], LDF, 1, &sm.Af[0][16 * tj], LDF, 1, 16 * tj, 32, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.M2[16 * ti + 4 * lq + e][16 * tj + lr] = m[e];
+  }
+  __syncthreads();
+  // ---- T[2:4, 0:2] = -T[2:4, 2:4] M2 (T[2:4, 2:4] lower: row block ti needs k < 16 (ti + 1)) ----
+  {
+    const int ti = wave >> 1, tj = wave & 1;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(t, &sm.Af[32 + 16 * ti][32], LDF, 1, &sm.M2[0][16 * tj], 36, 1, 0, 16 * (ti + 1), lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Af[32 + 16 * ti + 4 * lq + e][16 * tj + lr] = -t[e];
+  }
+  __syncthreads();
+
+  // ---- T to the workspace (upper off-diagonal blocks are zero) ----
+  {
+    constexpr int VPR = kChunk / VN;
+    E* gT = ws.T + chunk_id * kChunk * kChunk;
+    for (int i = tid; i < kChunk * VPR; i += kThreads) {
+      const int r = i / VPR, c0 = (i % VPR) * VN;
+      V16 out;
+      const bool zero = (c0 >> 4) > (r >> 4);  // upper off-diagonal block
+#pragma unroll
+      for (int e4 = 0; e4 < VN; e4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Af[r][c0 + e4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
+      }
+      *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
+    }
+  }
+}
+
 template <typename E, int DK>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   constexpr bool BF = is_bf16<E>();
@@ -206,90 +301,228 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   }
   __syncthreads();
 
-  // ---- diagonal blocks of T by forward substitution (wave 0); waves 1-3 store P and the factors ----
-  if (wave == 0) {
-    const int base = (lane >> 4) * 16, col = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float* arow = &sm.Af[base + i][base];
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
-      x[i] = (i == col) ? 1.f : -s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
-  } else {
-    const int t = tid - kWave;  // 0 .. 191
-    constexpr int VPR = kChunk / VN;
-    E* gP = ws.P + chunk_id * kChunk * kChunk;
-    for (int i = t; i < kChunk * VPR; i += kThreads - kWave) {
-      const int r = i / VPR, c0 = (i % VPR) * VN;
-      V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
-      if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
-#pragma unroll
-        for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
-      }
-      *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
-    }
-    float* gS = ws.SC + chunk_id * kScRows * kChunk;
-    for (int i = t; i < kScRows * kChunk; i += kThreads - kWave) gS[i] = (&sm.sc[0][0])[i];
-  }
-  __syncthreads();
-
-  // ---- T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1) ----
-  if (wave < 2) {
-    const int i = 1 + 2 * wave, j = 2 * wave;
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(m, &sm.Af[16 * i][16 * j], LDF, 1, &sm.Af[16 * j][16 * j], LDF, 1, 0, 16, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Ms[wave][4 * lq + e][lr] = m[e];
-    wave_lds_sync();
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(t, &sm.Af[16 * i][16 * i], LDF, 1, &sm.Ms[wave][0][0], 20, 1, 0, 16, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Af[16 * i + 4 * lq + e][16 * j + lr] = -t[e];
-  }
-  __syncthreads();
-
-  // ---- M2 = A[2:4, 0:2] T[0:2, 0:2] (T lower: column block tj starts at row 16 tj) ----
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(m, &sm.Af[32 + 16 * ti][0], LDF, 1, &sm.Af[0][16 * tj], LDF, 1, 16 * tj, 32, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.M2[16 * ti + 4 * lq + e][16 * tj + lr] = m[e];
-  }
-  __syncthreads();
-  // ---- T[2:4, 0:2] = -T[2:4, 2:4] M2 (T[2:4, 2:4] lower: row block ti needs k < 16 (ti + 1)) ----
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(t, &sm.Af[32 + 16 * ti][32], LDF, 1, &sm.M2[0][16 * tj], 36, 1, 0, 16 * (ti + 1), lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Af[32 + 16 * ti + 4 * lq + e][16 * tj + lr] = -t[e];
-  }
-  __syncthreads();
-
-  // ---- T to the workspace (upper off-diagonal blocks are zero) ----
-  {
-    constexpr int VPR = kChunk / VN;
-    E* gT = ws.T + chunk_id * kChunk * kChunk;
-    for (int i = tid; i < kChunk * VPR; i += kThreads) {
-      const int r = i / VPR, c0 = (i % VPR) * VN;
-      V16 out;
-      const bool zero = (c0 >> 4) > (r >> 4);  // upper off-diagonal block
-#pragma unroll
-      for (int e4 = 0; e4 < VN; e4 += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Af[r][c0 + e4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
-      }
-      *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
-    }
-  }
+  solve_and_store<E>(sm, ws, chunk_id);
   (void)BF;
+}
+
+// ---- KDA: per-channel decay ("Deep Dive into KDA", sections 2.3 and 3) ----
+// With G [64][d_k] the chunk-local prefix of log a per channel:
+//   A[r][s] = eta_r rs_r rs_s sum_i k_r[i] k_s[i] e^{G_r[i] - G_s[i]}   (s < r)
+//   P[r][s] = sum_i q_r[i] k_s[i] e^{G_r[i] - G_s[i]}                   (s <= r)
+// Off the diagonal 16 x 16 blocks the sum is one MFMA product of decayed operands referenced to
+// the row block's first token b: (k_r o e^{G_r - G_b}) . (k_s o e^{G_b - G_s}), both exponents
+// <= 0 since s < b <= r. Inside a diagonal block it is summed per element, each ratio formed as
+// one exponential of a non-positive difference (no prefix product is ever divided by). The scan's
+// operands K o e^G, Q o e^G, K o e^{G_C - G} and gamma = e^{G_C} go to the workspace, and the
+// factor rows carry e^G = 1 and rs e^{G_C - G} = rs (the decay lives in the operands).
+template <typename E, int DK>
+struct PrepKdaSmem {
+  static constexpr int PAD = 16 / sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDG = DK + 4;
+  static constexpr int LDP = kChunk + PAD;
+  static constexpr int LDF = kChunk + 4;
+  alignas(16) E Ks[kChunk][LDK];
+  alignas(16) E Qs[kChunk][LDK];
+  alignas(16) float Gm[kChunk][LDG];  // log a, then its chunk-local prefix per channel
+  alignas(16) float Af[kChunk][LDF];  // A, then T in place
+  alignas(16) E Ps[kChunk][LDP];
+  alignas(16) float Ms[2][16][20];
+  alignas(16) float M2[32][36];
+  alignas(16) float sc[kScRows][kChunk];
+  float n[kChunk], eta[kChunk];
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p) {
+  constexpr bool BF = is_bf16<E>();
+  constexpr int VN = Vec16<E>::N;
+  typedef typename Vec16<E>::type V16;
+  typedef PrepKdaSmem<E, DK> Sm;
+  __shared__ Sm sm;
+
+  const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
+  const int64_t head = chunk_id / p.nchunks, c = chunk_id % p.nchunks;
+  const int64_t bb = head / p.H, hh = head % p.H;
+  const int64_t T = p.T, t0 = c * kChunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  auto row_index = [&](int64_t t) { return (bb * T + t) * p.H + hh; };
+  const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
+  const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, p.heads * p.nchunks, DK);
+
+  // ---- K, Q rows, log a and eta of the chunk into LDS (rows past T are zero) ----
+  {
+    constexpr int CPR = DK / VN;
+    const E* gk = static_cast<const E*>(p.k);
+    const E* gq = static_cast<const E*>(p.q);
+    for (int i = tid; i < kChunk * CPR; i += kThreads) {
+      const int r = i / CPR, c0 = (i % CPR) * VN;
+      const bool valid = t0 + r < T;
+      V16 kx, qx;
+      if (valid) {
+        kx = *reinterpret_cast<const V16*>(gk + row_index(t0 + r) * DK + c0);
+        qx = *reinterpret_cast<const V16*>(gq + row_index(t0 + r) * DK + c0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) kx[e] = qx[e] = from_f32<E>(0.f);
+      }
+      *reinterpret_cast<V16*>(&sm.Ks[r][c0]) = kx;
+      *reinterpret_cast<V16*>(&sm.Qs[r][c0]) = qx;
+    }
+    for (int i = tid; i < kChunk * DK / 4; i += kThreads) {
+      const int r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (t0 + r < T) x = *reinterpret_cast<const f32x4*>(p.log_alpha + row_index(t0 + r) * DK + c4);
+      *reinterpret_cast<f32x4*>(&sm.Gm[r][c4]) = x;
+    }
+    if (tid < kChunk) sm.eta[tid] = t0 + tid < T ? p.eta[row_index(t0 + tid)] : 0.f;
+  }
+  __syncthreads();
+
+  // ---- per-channel prefix of log a over the chunk's tokens; squared key norms ----
+  static_assert(DK <= kThreads - kChunk, "one thread per channel, one per row");
+  if (tid < DK) {
+    float acc = 0.f;
+    for (int r = 0; r < kChunk; ++r) {
+      acc += sm.Gm[r][tid];
+      sm.Gm[r][tid] = acc;
+    }
+  } else if (tid >= kThreads - kChunk) {
+    const int r = tid - (kThreads - kChunk);
+    float nn = 0.f;
+    for (int i = 0; i < DK; ++i) {
+      const float x = to_f32(sm.Ks[r][i]);
+      nn += x * x;
+    }
+    sm.n[r] = nn;
+  }
+  __syncthreads();
+
+  // ---- factors (wave 0): as for the scalar gate, with e^G = 1 and rs e^{G_C - G} = rs ----
+  if (wave == 0) {
+    const int r = lane;
+    const bool valid = t0 + r < T;
+    float rs, et;
+    if (p.beta_given && p.unit_rs) {
+      rs = valid ? 1.f : 0.f;
+      et = sm.eta[r];
+    } else if (p.beta_given) {
+      const float b = sm.eta[r];
+      rs = valid ? sqrtf(fabsf(b)) : 0.f;
+      et = b < 0.f ? -1.f : 1.f;
+      sm.eta[r] = et;
+    } else {
+      rs = valid ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
+      et = sm.eta[r];
+    }
+    sm.sc[kScCoefR][r] = et * rs;
+    sm.sc[kScEG][r] = 1.f;
+    sm.sc[kScRs][r] = rs;
+    sm.sc[kScD2][r] = rs;
+  }
+  // ---- decayed scan operands and gamma to the workspace ----
+  {
+    constexpr int CPR = DK / VN;
+    E* k1 = kw.K1 + chunk_id * kChunk * DK;
+    E* q1 = kw.Q1 + chunk_id * kChunk * DK;
+    E* k2 = kw.K2 + chunk_id * kChunk * DK;
+    for (int i = tid; i < kChunk * CPR; i += kThreads) {
+      const int r = i / CPR, c0 = (i % CPR) * VN;
+      const V16 kx = *reinterpret_cast<const V16*>(&sm.Ks[r][c0]);
+      const V16 qx = *reinterpret_cast<const V16*>(&sm.Qs[r][c0]);
+      V16 a, b, d;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const float G = sm.Gm[r][c0 + e], eg = __expf(G), ed = __expf(sm.Gm[kChunk - 1][c0 + e] - G);
+        a[e] = from_f32<E>(to_f32(kx[e]) * eg);
+        b[e] = from_f32<E>(to_f32(qx[e]) * eg);
+        d[e] = from_f32<E>(to_f32(kx[e]) * ed);
+      }
+      *reinterpret_cast<V16*>(k1 + r * DK + c0) = a;
+      *reinterpret_cast<V16*>(q1 + r * DK + c0) = b;
+      *reinterpret_cast<V16*>(k2 + r * DK + c0) = d;
+    }
+    if (tid < DK) kw.gamma[chunk_id * DK + tid] = __expf(sm.Gm[kChunk - 1][tid]);
+  }
+  __syncthreads();
+
+  // ---- off-diagonal 16 x 16 blocks (I, J), J < I: MFMA on operands decayed to b = 16 I ----
+  for (int t = wave; t < 6; t += 4) {
+    const int I = t >= 3 ? 3 : t >= 1 ? 2 : 1, J = t - (I * (I - 1)) / 2, b = 16 * I;
+    const int ra = 16 * I + lr, rb = 16 * J + lr;  // this lane's A row and B row
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+    if constexpr (BF) {
+#pragma unroll
+      for (int i = 0; i < DK / 32; ++i) {
+        bf16x8 ak, aq, bk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = 32 * i + 8 * lq + e;
+          const float Gb = sm.Gm[b][ch];
+          const float fa = __expf(sm.Gm[ra][ch] - Gb), fb = __expf(Gb - sm.Gm[rb][ch]);
+          ak[e] = from_f32<bf16>(to_f32(sm.Ks[ra][ch]) * fa);
+          aq[e] = from_f32<bf16>(to_f32(sm.Qs[ra][ch]) * fa);
+          bk[e] = from_f32<bf16>(to_f32(sm.Ks[rb][ch]) * fb);
+        }
+        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, kk, 0, 0, 0);
+        qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, qk, 0, 0, 0);
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < DK / 4; ++i) {
+        const int ch = 4 * i + lq;
+        const float Gb = sm.Gm[b][ch];
+        const float fa = __expf(sm.Gm[ra][ch] - Gb), fb = __expf(Gb - sm.Gm[rb][ch]);
+        const float bk = sm.Ks[rb][ch] * fb;
+        kk = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.Ks[ra][ch] * fa, bk, kk, 0, 0, 0);
+        qk = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.Qs[ra][ch] * fa, bk, qk, 0, 0, 0);
+      }
+    }
+    const int s = 16 * J + lr;
+    const float rss = sm.sc[kScRs][s];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * lq + e;
+      sm.Af[r][s] = sm.eta[r] * sm.sc[kScRs][r] * rss * kk[e];
+      sm.Ps[r][s] = from_f32<E>(qk[e]);
+    }
+  }
+  // ---- diagonal 16 x 16 blocks: one thread per (r, s), summed per channel ----
+  {
+    const int rr = tid >> 4, ss = tid & 15;
+    for (int I = 0; I < 4; ++I) {
+      const int r = 16 * I + rr, s = 16 * I + ss;
+      float a = 0.f, pq = 0.f;
+      if (s <= r) {
+        for (int i = 0; i < DK; i += 4) {
+          const f32x4 Gr = *reinterpret_cast<const f32x4*>(&sm.Gm[r][i]);
+          const f32x4 Gs = *reinterpret_cast<const f32x4*>(&sm.Gm[s][i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = __expf(Gr[e] - Gs[e]) * to_f32(sm.Ks[s][i + e]);
+            a += to_f32(sm.Ks[r][i + e]) * w;
+            pq += to_f32(sm.Qs[r][i + e]) * w;
+          }
+        }
+      }
+      sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * sm.sc[kScRs][s] * a : 0.f;
+      sm.Ps[r][s] = from_f32<E>(s <= r ? pq : 0.f);
+    }
+  }
+  __syncthreads();
+
+  solve_and_store<E>(sm, ws, chunk_id);
+}
+
+template <typename E>
+hipError_t launch_kda_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
+  const int64_t grid = p.heads * p.nchunks;
+  if (d_k == 128)
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <typename E>
@@ -306,6 +539,10 @@ hipError_t launch_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
 
 hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream) {
   return bf16_io ? launch_e<bf16>(p, d_k, stream) : launch_e<float>(p, d_k, stream);
+}
+
+hipError_t launch_chunk_prep_kda(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream) {
+  return bf16_io ? launch_kda_e<bf16>(p, d_k, stream) : launch_kda_e<float>(p, d_k, stream);
 }
 
 }  // namespace kla

@@ -53,9 +53,11 @@ namespace {
 // Delta (rs D) are stored to the backward workspace, and Q and P are not loaded.
 // MODE kScanSeg (segment scan, pass 1): workgroups cover (head, segment) pairs and, besides the
 // DV / DVS slices of the state, DK / DVS slices of identity columns (chunk_common.h).
+// MODE kScanKda (per-channel decay): K, Q and the update's K2 are the decayed operands of the
+// KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
-  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg;
+  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg, KDA = MODE == kScanKda;
   constexpr bool BF = is_bf16<E>();
   constexpr int GK = Grp<E>::K;
   typedef typename Grp<E>::V GV;
@@ -66,8 +68,8 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   constexpr int NGD = DK / GK;       // groups over d_k
   constexpr int NGT = kChunk / GK;   // groups over the chunk's tokens
   constexpr int PER = 16 / sizeof(E);
-  typedef ScanBuf<E, DK, DVS> Buf;
-  constexpr int NB = scan_ring<E, DK, DVS>();  // LDS buffers: chunks c .. c + NB - 1 in flight
+  typedef ScanBuf<E, DK, DVS, KDA> Buf;
+  constexpr int NB = scan_ring<E, DK, DVS, KDA>();  // LDS buffers: chunks c .. c + NB - 1 in flight
   constexpr int DIST = NB > 1 ? NB - 1 : 1;     // prefetch distance
   static_assert(DV % DVS == 0, "shape");
   // Distinct LDS objects (not an array indexed by chunk), so that the compiler can tell the
@@ -104,17 +106,24 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   // ---- resources: this batch's rows of q/k/v/o, this head's workspace chunks ----
   const int64_t brow = bb * T * H;
   const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);  // bytes per token
-  const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
-  const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
-  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, (uint32_t)(T * vrow));
-  const rsrc_t ro = make_rsrc(static_cast<const E*>(p.o) + brow * DV, (uint32_t)(T * vrow));
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * nchunks);
   const int64_t chunk0 = head * nchunks;
+  // K and Q rows: the q/k tensors (token stride H DK), or with KDA the decayed operands of the
+  // workspace (chunk-contiguous rows of DK).
+  const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, p.heads * nchunks, DK);
+  const uint32_t krow = KDA ? DK * sizeof(E) : xrow;
+  const uint32_t kspan = KDA ? (uint32_t)(nchunks * kChunk * DK * sizeof(E)) : (uint32_t)(T * xrow);
+  const rsrc_t rk = make_rsrc(KDA ? (const void*)(kw.K1 + chunk0 * kChunk * DK) : (const void*)(static_cast<const E*>(p.k) + brow * DK), kspan);
+  const rsrc_t rq = make_rsrc(KDA ? (const void*)(kw.Q1 + chunk0 * kChunk * DK) : (const void*)(static_cast<const E*>(p.q) + brow * DK), kspan);
+  const rsrc_t rk2 = make_rsrc(kw.K2 + chunk0 * kChunk * DK, KDA ? kspan : 0u);
+  const rsrc_t rgam = make_rsrc(kw.gamma + chunk0 * DK, KDA ? (uint32_t)(nchunks * DK * 4) : 0u);
+  const rsrc_t rv = make_rsrc(static_cast<const E*>(p.v) + brow * DV, (uint32_t)(T * vrow));
+  const rsrc_t ro = make_rsrc(static_cast<const E*>(p.o) + brow * DV, (uint32_t)(T * vrow));
   constexpr uint32_t kMatBytes = kChunk * kChunk * sizeof(E), kScBytes = kScRows * kChunk * sizeof(float);
   const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rp = make_rsrc(ws.P + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
-  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + (mpart ? 0 : j0)) * sizeof(E);
+  const uint32_t hcol_x = KDA ? 0u : hh * DK * sizeof(E), hcol_v = (hh * DV + (mpart ? 0 : j0)) * sizeof(E);
   // Backward recompute: this head's state and Delta blocks, tile-ordered (chunk_common.h).
   constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
   const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * nchunks, DK, DV);
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
   for (int i = 0; i < NBK; ++i) {
     const int ph = 64 * (wave + W * i) + lane, r = ph / CK;
-    offk[i] = r * xrow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
+    offk[i] = r * krow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
   }
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   // Every wave issues the same NDMA loads per chunk (the factor block is loaded by all of them,
   // identical bytes), so that the wait counts below are compile-time constants. A chunk past
   // the end is clamped to the last one (loaded again, never read).
-  constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : 2 * NBK + 2 * NBT + NBV + 1;
+  constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : KDA ? 3 * NBK + 2 * NBT + NBV + 2 : 2 * NBK + 2 * NBT + NBV + 1;
   constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < ce ? c : ce - 1;
@@ -163,8 +172,9 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave + W * i;
-      dma16(rk, B.K + blk * 64 * PER, t0 * xrow + offk[i]);
-      if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
+      dma16(rk, B.K + blk * 64 * PER, t0 * krow + offk[i]);
+      if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * krow + offk[i]);
+      if constexpr (KDA) dma16(rk2, B.K2 + blk * 64 * PER, t0 * krow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
@@ -178,6 +188,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       dma16(rv, B.V + blk * 64 * PER, t0 * vrow + offv[i]);
     }
     dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
+    if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
 
   // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[16 rt + 4g + e][j0 + cw + 16 ct + c] ----
@@ -336,15 +347,21 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       for (int ct = 0; ct < NT; ++ct) store4_rsrc<E>(rout, off + 16 * ct * sizeof(E), o[ct]);
     }
 
-    // ---- S <- e^{G_C} S + K^T diag(e^{G_C - G}) D' ----
+    // ---- S <- e^{G_C} S + K^T diag(e^{G_C - G}) D' (KDA: Diag(gamma) S + K2^T D') ----
     const float eGC = B.sc[kScEG * kChunk + kChunk - 1];
 #pragma unroll
     for (int r = 0; r < RTK; ++r) {
+      if constexpr (KDA) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * r + 4 * g]);
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) S[r][ct] *= eGC;
+        for (int ct = 0; ct < NT; ++ct) S[r][ct] *= gm;
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) S[r][ct] *= eGC;
+      }
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
-        const GV ak = kt_grp<E, DK>(B.K, r, s, g, c16);
+        const GV ak = kt_grp<E, DK>(KDA ? B.K2 : B.K, r, s, g, c16);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) S[r][ct] = mma<E>(ak, b2[ct][s], S[r][ct]);
       }
@@ -459,6 +476,25 @@ SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool 
   if (nseg > nchunks) nseg = nchunks;
   const int64_t len = (nchunks + nseg - 1) / nseg;
   return SegPlan{(nchunks + len - 1) / len, len};
+}
+
+hipError_t launch_chunk_prep_kda(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream);
+
+size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t, bool bf16_io) {
+  const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
+  return bf16_io ? KdaSpace<bf16>::bytes(n, (int)d_k) : KdaSpace<float>::bytes(n, (int)d_k);
+}
+
+// KDA forward: the per-channel prep, then the scan in its KDA mode (one pass; no segments).
+hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
+  ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
+                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
+  if (p.nchunks > 0) {
+    const hipError_t e = launch_chunk_prep_kda(p, a.d_k, a.bf16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return a.bf16 ? launch_scan<bf16, kScanKda>(p, a.d_k, a.d_v, stream)
+                : launch_scan<float, kScanKda>(p, a.d_k, a.d_v, stream);
 }
 
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io) {

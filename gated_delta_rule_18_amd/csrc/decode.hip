@@ -34,7 +34,10 @@ __device__ __forceinline__ float class_sum(float x) {
   return x;
 }
 
-template <typename E, int DK, int DV, int DVS>
+// KDA: log_alpha holds log a [heads][DK], a per-channel decay of the state's rows
+// ("Deep Dive into KDA", section 2.3): u = (Diag(a) S)^T k, p = (Diag(a) S)^T q,
+// delta = beta (v - u), o = p + (k.q) delta, S <- Diag(a) S + k delta^T.
+template <typename E, int DK, int DV, int DVS, bool KDA>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
@@ -63,34 +66,40 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   f32x4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0);
-  float kr[RPT], qr[RPT];
+  float kr[RPT], qr[RPT], lr_[RPT];
   if constexpr (RPT <= 8) {
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       kr[m] = to_f32(k[head * DK + rg + RG * m]);
       qr[m] = to_f32(q[head * DK + rg + RG * m]);
+      if constexpr (KDA) lr_[m] = log_alpha[head * DK + rg + RG * m];
     }
   } else {
     // Many rows per lane: load k and q once across the wave and pass row r's values from lane
     // r % 64 (fewer memory instructions for a kernel that is bound by memory).
     constexpr int KPL = DK / kWave;
-    float kk[KPL], qq[KPL];
+    float kk[KPL], qq[KPL], ll[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       kk[j] = to_f32(k[head * DK + lane + kWave * j]);
       qq[j] = to_f32(q[head * DK + lane + kWave * j]);
+      if constexpr (KDA) ll[j] = log_alpha[head * DK + lane + kWave * j];
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int r = rg + RG * m, slot = (RG * m) / kWave;  // RG divides 64
       kr[m] = __shfl(kk[slot], r % kWave, kWave);
       qr[m] = __shfl(qq[slot], r % kWave, kWave);
+      if constexpr (KDA) lr_[m] = __shfl(ll[slot], r % kWave, kWave);
     }
   }
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[head * DV + col0 + e]);
-  const float alpha = log_alpha ? __expf(log_alpha[head]) : 1.f;
+  const float alpha = KDA ? 1.f : log_alpha ? __expf(log_alpha[head]) : 1.f;
+  float ar[RPT];  // per-row decay (KDA)
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) ar[m] = KDA ? __expf(lr_[m]) : 1.f;
   const float et = eta[head];  // eta, or beta itself when beta_given
 
   // Partial sums over this lane's rows, then one joint reduction over the row groups (the lanes
@@ -101,8 +110,13 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   for (int m = 0; m < RPT; ++m) {
     nk += kr[m] * kr[m];
     kq += kr[m] * qr[m];
-    u += s[m] * kr[m];
-    pq += s[m] * qr[m];
+    if constexpr (KDA) {
+      u += s[m] * (ar[m] * kr[m]);
+      pq += s[m] * (ar[m] * qr[m]);
+    } else {
+      u += s[m] * kr[m];
+      pq += s[m] * qr[m];
+    }
   }
   nk = class_sum<CG>(nk);
   kq = class_sum<CG>(kq);
@@ -119,16 +133,21 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   }
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
-    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * alpha + delta * kr[m];
+    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * (alpha * ar[m]) + delta * kr[m];
 }
 
 template <typename E, int DK, int DV, int DVS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   const int64_t heads = a.B * a.H;
   const int64_t grid = (heads + kXcdCount - 1) / kXcdCount * kXcdCount * (DV / DVS);
-  hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
-                     a.eps, a.beta_given);
+  if (a.kda)
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, true>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
+                       a.eps, a.beta_given);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, false>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
+                       a.eps, a.beta_given);
   return hipGetLastError();
 }
 

@@ -112,6 +112,13 @@ size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
   return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
 }
 
+size_t kla_kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                        kla_dtype_t dt) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
+    return 0;
+  return kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+}
+
 size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                                     kla_dtype_t dt) {
   if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
@@ -123,9 +130,10 @@ size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
 
 namespace {
 
-// kla_chunk_fwd and kla_gdn_chunk_fwd: eta is eta (Kaczmarz step) or beta itself (beta_given,
-// where log_alpha may be null for alpha = 1).
-kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+// kla_chunk_fwd, kla_gdn_chunk_fwd and kla_kda_chunk_fwd: eta is eta (Kaczmarz step) or beta itself
+// (beta_given, where a scalar log_alpha may be null for alpha = 1); with kda, log_alpha is the
+// per-channel log a [B, T, H, d_k] and required.
+kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                             const float* eta, const float* log_alpha, const float* state_in, float* state_out,
                             void* o, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                             float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream) {
@@ -147,12 +155,13 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, cons
   // byte offsets (up to one chunk past T).
   if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
-  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !o))
+  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && (!beta_given || kda)) || !o))
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||
-      !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4))
+      !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, kda ? 16 : 4))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
-  const size_t need = kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+  const size_t need = kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+                          : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
   if (T > 0 && need > 0 && (!workspace || workspace_bytes < need))
     return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
   const int64_t es = dt == KLA_BF16 ? 2 : 4;
@@ -160,7 +169,7 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, cons
   const int64_t sbytes = B * H * d_k * d_v * 4;
   const Range rq = range("q", q, tok * d_k * es), rk = range("k", k, tok * d_k * es),
               rv = range("v", v, tok * d_v * es), re = range("eta", eta, tok * 4),
-              rl = range("log_alpha", log_alpha, tok * 4), rsi = range("state_in", state_in, sbytes),
+              rl = range("log_alpha", log_alpha, tok * 4 * (kda ? d_k : 1)), rsi = range("state_in", state_in, sbytes),
               rso = range("state_out", state_out, sbytes), ro = range("o", o, tok * d_v * es),
               rw = range("workspace", workspace, (int64_t)(need > 0 ? workspace_bytes : 0));
   const Range* ins[6] = {&rq, &rk, &rv, &re, &rl, &rsi};
@@ -179,7 +188,9 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, const void* q, cons
   }
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
                    workspace, workspace_bytes, beta_given};
-  return launched(kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)), fn);
+  return launched(kda ? kla::launch_chunk_kda_fwd(a, static_cast<hipStream_t>(stream))
+                      : kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)),
+                  fn);
 }
 
 // kla_chunk_bwd and kla_gdn_chunk_bwd (as chunk_fwd_impl; deta receives dL/dbeta when beta_given).
@@ -253,8 +264,8 @@ kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, cons
   return launched(kla::launch_chunk_bwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
-// kla_decode_step and kla_gdn_decode_step (as chunk_fwd_impl).
-kla_status_t decode_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+// kla_decode_step, kla_gdn_decode_step and kla_kda_decode_step (as chunk_fwd_impl).
+kla_status_t decode_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                          const float* eta, const float* log_alpha, float* state, void* o, int64_t B, int64_t H,
                          int64_t d_k, int64_t d_v, float eps, kla_dtype_t dt, void* stream) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
@@ -270,7 +281,7 @@ kla_status_t decode_impl(const char* fn, bool beta_given, const void* q, const v
     return KLA_OK;
   }
   if ((B * H + 8) * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
-  if (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !state || !o)
+  if (!q || !k || !v || !eta || (!log_alpha && (!beta_given || kda)) || !state || !o)
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
       !aligned(eta, 4) || !aligned(log_alpha, 4))
@@ -279,13 +290,13 @@ kla_status_t decode_impl(const char* fn, bool beta_given, const void* q, const v
   const Range rs = range("state", state, B * H * d_k * d_v * 4), ro = range("o", o, B * H * d_v * es);
   const Range ins[5] = {range("q", q, B * H * d_k * es), range("k", k, B * H * d_k * es),
                         range("v", v, B * H * d_v * es), range("eta", eta, B * H * 4),
-                        range("log_alpha", log_alpha, B * H * 4)};
+                        range("log_alpha", log_alpha, B * H * 4 * (kda ? d_k : 1))};
   if (overlap(ro, rs)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps state", fn);
   for (const Range& i : ins) {
     if (overlap(ro, i)) return fail(KLA_ERR_INVALID_VALUE, "%s: o overlaps %s", fn, i.name);
     if (overlap(rs, i)) return fail(KLA_ERR_INVALID_VALUE, "%s: state overlaps %s", fn, i.name);
   }
-  kla::DecodeArgs a{q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt == KLA_BF16, beta_given};
+  kla::DecodeArgs a{q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt == KLA_BF16, beta_given, kda};
   return launched(kla::launch_decode_step(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -297,7 +308,7 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
                            int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return chunk_fwd_impl("kla_chunk_fwd", false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v,
+  return chunk_fwd_impl("kla_chunk_fwd", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v,
                         chunk, eps, dt, workspace, workspace_bytes, stream);
 }
 
@@ -305,20 +316,20 @@ kla_status_t kla_gdn_chunk_fwd(const void* q, const void* k, const void* v, cons
                                const float* log_alpha, const float* state_in, float* state_out, void* o, int64_t B,
                                int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, kla_dtype_t dt,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_fwd_impl("kla_gdn_chunk_fwd", true, q, k, v, beta, log_alpha, state_in, state_out, o, B, T, H, d_k,
+  return chunk_fwd_impl("kla_gdn_chunk_fwd", true, false, q, k, v, beta, log_alpha, state_in, state_out, o, B, T, H, d_k,
                         d_v, chunk, 0.f, dt, workspace, workspace_bytes, stream);
 }
 
 kla_status_t kla_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
                              float* state, void* o, int64_t B, int64_t H, int64_t d_k, int64_t d_v, float eps,
                              kla_dtype_t dt, void* stream) {
-  return decode_impl("kla_decode_step", false, q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt, stream);
+  return decode_impl("kla_decode_step", false, false, q, k, v, eta, log_alpha, state, o, B, H, d_k, d_v, eps, dt, stream);
 }
 
 kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v, const float* beta,
                                  const float* log_alpha, float* state, void* o, int64_t B, int64_t H, int64_t d_k,
                                  int64_t d_v, kla_dtype_t dt, void* stream) {
-  return decode_impl("kla_gdn_decode_step", true, q, k, v, beta, log_alpha, state, o, B, H, d_k, d_v, 0.f, dt,
+  return decode_impl("kla_gdn_decode_step", true, false, q, k, v, beta, log_alpha, state, o, B, H, d_k, d_v, 0.f, dt,
                      stream);
 }
 
@@ -341,6 +352,21 @@ kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v, cons
   return chunk_bwd_impl("kla_gdn_chunk_bwd", true, q, k, v, beta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
                         dbeta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, 0.f, dt, workspace, workspace_bytes,
                         stream);
+}
+
+kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* eta, const float* log_a,
+                               const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
+                               int64_t d_k, int64_t d_v, int64_t chunk, float eps, int beta_given, kla_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_kda_chunk_fwd", beta_given != 0, true, q, k, v, eta, log_a, state_in, state_out, o, B,
+                        T, H, d_k, d_v, chunk, beta_given ? 0.f : eps, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_kda_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_a,
+                                 float* state, void* o, int64_t B, int64_t H, int64_t d_k, int64_t d_v, float eps,
+                                 int beta_given, kla_dtype_t dt, void* stream) {
+  return decode_impl("kla_kda_decode_step", beta_given != 0, true, q, k, v, eta, log_a, state, o, B, H, d_k, d_v,
+                     beta_given ? 0.f : eps, dt, stream);
 }
 
 }  // extern "C"

@@ -22,6 +22,7 @@ struct DecodeArgs {
   float eps;
   bool bf16;
   bool beta_given;  // eta holds beta itself; log_alpha may be null (alpha = 1)
+  bool kda = false;  // log_alpha holds log a [B, H, d_k] (per-channel decay)
 };
 
 struct PrepareArgs {
@@ -80,6 +81,9 @@ hipError_t launch_prepare_beta(const PrepareArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
+// Per-channel decay (KDA): ChunkArgs.log_alpha / DecodeArgs.log_alpha hold log a [.., d_k].
+hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);
+size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
 size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
 bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16);
 

@@ -154,8 +154,10 @@ __device__ __forceinline__ void store4_rsrc(rsrc_t r, uint32_t off, f32x4 v) {
   }
 }
 
-// One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz).
-template <typename E, int DK, int DVS>
+// One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz). With the
+// per-channel decay (KDA) the buffer also holds the state-update operand K2 and the chunk's
+// state decay gamma (a 1 KiB block, of which the first DK entries are this chunk's).
+template <typename E, int DK, int DVS, bool KDA = false>
 struct ScanBuf {
   alignas(16) E K[kChunk * DK];
   alignas(16) E Q[kChunk * DK];
@@ -163,14 +165,16 @@ struct ScanBuf {
   alignas(16) E P[kChunk * kChunk];
   alignas(16) E V[kChunk * DVS];
   alignas(16) float sc[kScRows * kChunk];
+  alignas(16) E K2[KDA ? kChunk * DK : 8];
+  alignas(16) float gam[KDA ? 256 : 4];
 };
 
 // Buffers in the ring: two where they fit in 160 KiB of LDS, else one. (A third buffer, for a
 // prefetch distance of two chunks, measured slower: the loads are not the bottleneck once they
 // are a chunk ahead, and the three-way unrolled loop costs registers.)
-template <typename E, int DK, int DVS>
+template <typename E, int DK, int DVS, bool KDA = false>
 constexpr int scan_ring() {
-  return 2 * sizeof(ScanBuf<E, DK, DVS>) <= 160 * 1024 ? 2 : 1;
+  return 2 * sizeof(ScanBuf<E, DK, DVS, KDA>) <= 160 * 1024 ? 2 : 1;
 }
 
 }  // namespace kla

@@ -153,6 +153,50 @@ kla_status_t kla_gdn_decode_step(const void* q, const void* k, const void* v,
                                  kla_dtype_t dt, void* stream);
 
 /*
+ * kla_kda_chunk_fwd_workspace_size — bytes of device workspace kla_kda_chunk_fwd needs (0 when
+ * T = 0 or the sizes are not supported). Host-only; never fails. About 65 KiB per chunk of 64
+ * tokens per head for bf16 and d_k = 128: the forward's per-chunk factors plus the decayed
+ * operands K o e^G, Q o e^G, K o e^{G_C - G} and the chunk's decay e^{G_C}.
+ */
+size_t kla_kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                        int64_t chunk, kla_dtype_t dt);
+
+/*
+ * kla_kda_chunk_fwd — chunkwise forward with a per-channel (diagonal) decay, KDA's gate.
+ * Source: "Deep Dive into KDA", section 2.3 (S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1}
+ * + beta_t v_t k_t^T) and section 3 (the chunkwise form with per-channel Gamma; decay prefixes in
+ * the log domain, section 5). In this library's [d_k, d_v] state orientation Diag(a_t) scales
+ * the state's d_k rows: S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1} + beta_t k_t v_t^T,
+ * o_t = S_t^T q_t.
+ *   log_a      [B,T,H,d_k] fp32, log of the per-channel decay (<= 0 in use; any finite value is
+ *              accepted), 16-byte aligned.
+ *   eta        [B,T,H] fp32: eta of the Kaczmarz step beta = eta / (||k||^2 + eps)
+ *              ("Kaczmarz Linear Attention", Abstract) when beta_given = 0, else beta itself
+ *              (eps is then ignored).
+ *   Everything else (layouts, T, state_in/state_out aliasing, workspace, errors) as for
+ *   kla_chunk_fwd. One pass over the chunks (no segment plan).
+ */
+kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v,
+                               const float* eta, const float* log_a,
+                               const float* state_in, float* state_out, void* o,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                               float eps, int beta_given, kla_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kla_kda_decode_step — one recurrent decode step with the per-channel decay (section 2.3):
+ * u = (Diag(a) S)^T k, p = (Diag(a) S)^T q, delta = beta (v - u), o = p + (k.q) delta,
+ * S <- Diag(a) S + k delta^T (in place).
+ *   log_a [B,H,d_k] fp32; eta / beta_given / eps as for kla_kda_chunk_fwd; the rest as for
+ *   kla_decode_step.
+ */
+kla_status_t kla_kda_decode_step(const void* q, const void* k, const void* v,
+                                 const float* eta, const float* log_a,
+                                 float* state, void* o,
+                                 int64_t B, int64_t H, int64_t d_k, int64_t d_v,
+                                 float eps, int beta_given, kla_dtype_t dt, void* stream);
+
+/*
  * kla_chunk_bwd_workspace_size — bytes of device workspace kla_chunk_bwd and
  * kla_gdn_chunk_bwd need for these sizes (0 when T = 0 or the sizes are not supported).
  * Host-only; never fails. For bf16 and d_k = d_v = 128 it is about 113 KiB per chunk of

@@ -17,7 +17,8 @@ def test_exports_every_declared_symbol():
     names = K.declared_functions()
     assert set(names) == {"kla_prepare_beta", "kla_chunk_fwd_workspace_size", "kla_chunk_fwd",
                           "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
-                          "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd"}
+                          "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd",
+                          "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -257,4 +258,50 @@ def test_bwd_workspace_size():
     # the forward's per-chunk factors, then per chunk two bf16 states and two 64 x 128 blocks
     assert need == fwd + 8 * 8 * 64 * (2 * 128 * 128 + 2 * 64 * 128) * 2
     assert K.lib().kla_chunk_bwd_workspace_size(8, 0, 8, 128, 128, 64, K.KLA_BF16) == 0
+
+
+def kda_chunk(dk=128, dv=128, chunk_len=64, eps=1e-6, beta_given=0, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16,
+              k=A16 * 2, v=A16 * 3, eta=A16 * 4, la=A16 * 5, o=A16 * 6, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = max(K.lib().kla_kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk_len, dt), 0)
+    opt = lambda x: p(x) if x else None
+    return L().kla_kda_chunk_fwd(opt(q), opt(k), opt(v), opt(eta), opt(la), None, None, opt(o), B, T, H, dk, dv,
+                                 chunk_len, eps, beta_given, dt, opt(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(chunk_len=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),                     # the per-channel decay is required
+    (dict(la=0, beta_given=1), K.KLA_ERR_INVALID_VALUE),       # ... also with beta given
+    (dict(la=A16 * 5 + 4), K.KLA_ERR_INVALID_VALUE),           # log a rows are read 16 bytes at a time
+    (dict(o=A16 * 5 + 4096), K.KLA_ERR_INVALID_VALUE),         # o inside log a ([B,T,H,d_k] fp32 = 32 KiB)
+    (dict(ws=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(ws_bytes=4096), K.KLA_ERR_INVALID_VALUE),
+    (dict(eps=-1.0), K.KLA_ERR_INVALID_VALUE),
+])
+def test_kda_chunk_fwd_rejects(kw, status):
+    assert kda_chunk(**kw) == status
+    assert L().kla_last_error().startswith(b"kla_kda_chunk_fwd")
+
+
+def test_kda_workspace_and_empty():
+    need = K.lib().kla_kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    base = K.lib().kla_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    assert need == base + 128 * (3 * 64 * 2 + 4)  # K o e^G, Q o e^G, K o e^{G_C - G} (bf16), gamma (fp32)
+    assert kda_chunk(B=0) == K.KLA_OK
+    assert kda_chunk(T=0, ws=0) == K.KLA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(dk=32), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(o=A16 * 5 + 64), K.KLA_ERR_INVALID_VALUE),           # o inside log a ([B,H,d_k])
+])
+def test_kda_decode_step_rejects(kw, status):
+    d = dict(dk=128, dv=128, la=A16 * 5, o=A16 * 16)
+    d.update(kw)
+    st = L().kla_kda_decode_step(p(A16), p(A16 * 2), p(A16 * 3), p(A16 * 4), p(d["la"]) if d["la"] else None,
+                                 p(A16 * 8), p(d["o"]), 1, 1, d["dk"], d["dv"], 1e-6, 0, K.KLA_BF16, None)
+    assert st == status
 

@@ -13,6 +13,7 @@ Distributions (per element i.i.d.; scalars are per (b, t, h)):
   S0    = N(0, s0_std) fp32, or zeros
   do    = N(0, 1) (the cotangent of o for gradient checks; bf16-rounded for bf16 workloads)
   dS_T  = N(0, dst_std) fp32 (the cotangent of the final state), or absent
+  log a = -U(a_lo, a_hi) per channel (per-channel decay, [.., d_k]), the scalar gate's range
 bf16 workloads round q, k, v from fp32 to bf16 (round to nearest even); the
 arrays returned here hold those rounded values as fp32, so that an fp64 upcast
 is exact and both sides see the very same numbers.
@@ -35,7 +36,7 @@ SEED = 20260509
 _TID = {
     "q": 1, "k": 2, "v": 3, "eta": 4, "log_alpha": 5, "scale": 6, "S0": 7,
     "dec_q": 11, "dec_k": 12, "dec_v": 13, "dec_eta": 14, "dec_log_alpha": 15, "dec_scale": 16,
-    "do": 21, "dST": 22, "S0_prefill": 23,
+    "do": 21, "dST": 22, "S0_prefill": 23, "log_a": 24, "dec_log_a": 25,
 }
 
 
@@ -195,4 +196,20 @@ def grad_inputs(w: Workload, s0_std: float = 0.0, dst_std: float = 0.0) -> dict:
             if dST is not None:
                 dST[b, h] = _rng(w, "dST", b, h).normal(0.0, dst_std, (w.dk, w.dv))
     return {"do": do, "S0": S0, "dST": dST}
+
+
+def channel_log_decay(w: Workload, decode: bool = False) -> np.ndarray:
+    """Per-channel log decays for all heads: [B, T, H, dk] (prefill) or [steps, B, H, dk]
+    (decode), each element -U(a_lo, a_hi) with the workload's scalar-gate range."""
+    a_lo, a_hi = w.log_alpha_range
+    n = w.steps if decode else w.T
+    out = np.empty((n, w.B, w.H, w.dk) if decode else (w.B, n, w.H, w.dk), np.float32)
+    for b in range(w.B):
+        for h in range(w.H):
+            x = -_rng(w, "dec_log_a" if decode else "log_a", b, h).uniform(a_lo, a_hi, (n, w.dk))
+            if decode:
+                out[:, b, h] = x
+            else:
+                out[b, :, h] = x
+    return out
 

@@ -132,7 +132,13 @@ def cpu_baseline(w, head_tokens, mode="kla"):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     n = max(1, min(head_tokens // w.heads, w.T if w.T else w.steps))
-    if w.T and mode != "kla":
+    if w.T and mode == "kda":
+        x = wl.prefill_inputs(w.with_(T=n))
+        la = wl.channel_log_decay(w.with_(T=n))
+        args = (x["q"], x["k"], x["v"], x["eta"], la, w.eps)
+        run = lambda: oracle.kda_forward(*args)
+        what = f"oracle kda_forward on all {w.heads} heads (B={w.B}, H={w.H}) of the first {n} prefill tokens"
+    elif w.T and mode != "kla":
         x = wl.prefill_inputs(w.with_(T=n))
         heads = lambda a: np.moveaxis(a, 2, 1).reshape(w.heads, n, *a.shape[3:])  # [B, T, H, ...] -> [BH, T, ...]
         la = x["log_alpha"] if mode == "gdn" else np.zeros_like(x["log_alpha"])
@@ -274,9 +280,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="kla", choices=("kla", "gdn", "deltanet"),
+    ap.add_argument("--mode", default="kla", choices=("kla", "gdn", "deltanet", "kda"),
                     help="kla: Kaczmarz step from eta (the headline); gdn: beta given (kla_gdn_* entry points, "
-                         "beta drawn like eta, unit-norm keys); deltanet: gdn without the gate")
+                         "beta drawn like eta, unit-norm keys); deltanet: gdn without the gate; kda: the Kaczmarz "
+                         "step with a per-channel decay (kla_kda_* entry points, log a per channel drawn like "
+                         "log alpha)")
     ap.add_argument("--decode-launch", default="graph", choices=("graph", "eager"),
                     help="decode steps replayed from a HIP graph (default) or launched one call at a time")
     ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
@@ -328,11 +336,14 @@ def main():
     t_gen = time.perf_counter()
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
     pre = dec = None
-    gdn = args.mode != "kla"
+    gdn = args.mode in ("gdn", "deltanet")
+    kda = args.mode == "kda"
     if w.T:
         x = wl.prefill_inputs(w)
         if gdn:
             x["k"] = unit_keys(x["k"])
+        if kda:
+            x["log_a"] = wl.channel_log_decay(w)
         pre = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         pre["o"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
@@ -341,6 +352,8 @@ def main():
         x = wl.decode_inputs(w)
         if gdn:
             x["k"] = unit_keys(x["k"])
+        if kda:
+            x["log_a"] = wl.channel_log_decay(w, decode=True)
         dec = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         dec["o"] = torch.empty((w.steps, w.B, w.H, w.dv), dtype=tdt, device=device)
@@ -352,10 +365,14 @@ def main():
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     fwd_args = None
     if pre is not None:
-        ws_bytes = int(L.kla_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
+        ws_fn = L.kla_kda_chunk_fwd_workspace_size if kda else L.kla_chunk_fwd_workspace_size
+        ws_bytes = int(ws_fn(w.B, w.T, w.H, w.dk, w.dv, 64, code))
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
-        la = None if args.mode == "deltanet" else P(pre["log_alpha"])
-        if gdn:  # beta drawn like eta
+        la = None if args.mode == "deltanet" else P(pre["log_a" if kda else "log_alpha"])
+        if kda:
+            fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), la, None, P(state), P(pre["o"]),
+                        w.B, w.T, w.H, w.dk, w.dv, 64, ctypes.c_float(w.eps), 0, code, P(workspace), ws_bytes, sp)
+        elif gdn:  # beta drawn like eta
             fwd_args = (P(pre["q"]), P(pre["k"]), P(pre["v"]), P(pre["eta"]), la, None, P(state), P(pre["o"]),
                         w.B, w.T, w.H, w.dk, w.dv, 64, code, P(workspace), ws_bytes, sp)
         else:
@@ -364,11 +381,12 @@ def main():
     dec_args = []
     if dec is not None:
         for s in range(w.steps):
-            la = None if args.mode == "deltanet" else P(dec["log_alpha"][s])
-            tail = (code, sp) if gdn else (ctypes.c_float(w.eps), code, sp)
+            la = None if args.mode == "deltanet" else P(dec["log_a" if kda else "log_alpha"][s])
+            tail = (code, sp) if gdn else (ctypes.c_float(w.eps), 0, code, sp) if kda else (ctypes.c_float(w.eps), code, sp)
             dec_args.append((P(dec["q"][s]), P(dec["k"][s]), P(dec["v"][s]), P(dec["eta"][s]), la, P(state),
                              P(dec["o"][s]), w.B, w.H, w.dk, w.dv) + tail)
     fwd_fn, dec_fn = ((L.kla_gdn_chunk_fwd, L.kla_gdn_decode_step) if gdn else
+                      (L.kla_kda_chunk_fwd, L.kla_kda_decode_step) if kda else
                       (L.kla_chunk_fwd, L.kla_decode_step))
 
     if pre is None:  # decode-only workloads start from their S0 and keep decoding step after step
@@ -438,8 +456,9 @@ def main():
         nbytes = chunk_bytes(w, es)
         segs = 1 if w.heads * (w.dv // (32 if es == 2 else 64)) >= 256 or w.T < 32 * 64 else None
         parts["chunk_fwd"] = {
-            "kernel": "chunk_prep_kernel + chunk_scan_kernel" + (
-                "" if segs == 1 else " (+ seg_combine_kernel + seg_fix_kernel when the plan segments)"),
+            "kernel": "chunk_prep_kda_kernel + chunk_scan_kernel (KDA mode)" if args.mode == "kda" else
+                      "chunk_prep_kernel + chunk_scan_kernel" + (
+                          "" if segs == 1 else " (+ seg_combine_kernel + seg_fix_kernel when the plan segments)"),
             "launches_per_step": 1, "ms_per_step": ms,
             "kernel_avg_us": ms * 1e3, "tokens": fwd_tokens, "tokens_per_s": fwd_tokens / (ms * 1e-3),
             "algorithmic_flop": flops, "algorithmic_bytes": nbytes,

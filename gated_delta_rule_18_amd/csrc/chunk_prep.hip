@@ -18,7 +18,7 @@
 // registers (one wave, a lane per column), then the off-diagonal blocks by two doubling steps
 // on fp32 MFMA: T10 = -T11 A10 T00 and T32 = -T33 A32 T22, then
 // T[2:4, 0:2] = -T[2:4, 2:4] (A[2:4, 0:2] T[0:2, 0:2]). T overwrites A in place.
-#include "chunk_common.h"
+#include "tile_ops.h"
 
 namespace kla {
 namespace {
@@ -312,9 +312,19 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
 // Off the diagonal 16 x 16 blocks the sum is one MFMA product of decayed operands referenced to
 // the row block's first token b: (k_r o e^{G_r - G_b}) . (k_s o e^{G_b - G_s}), both exponents
 // <= 0 since s < b <= r. Inside a diagonal block it is summed per element, each ratio formed as
-// one exponential of a non-positive difference (no prefix product is ever divided by). The scan's
+// one exponential of a non-positive difference, or (bf16) as a running product of the per-token
+// decays a_j = e^{G_j - G_{j-1}} <= 1 (no prefix product is ever divided by). The scan's
 // operands K o e^G, Q o e^G, K o e^{G_C - G} and gamma = e^{G_C} go to the workspace, and the
 // factor rows carry e^G = 1 and rs e^{G_C - G} = rs (the decay lives in the operands).
+// Sum over the 16 lanes of a DPP row (lanes with equal lane / 16), in every lane of the row.
+__device__ __forceinline__ float dpp_row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
 template <typename E, int DK>
 struct PrepKdaSmem {
   static constexpr int PAD = 16 / sizeof(E);
@@ -325,6 +335,9 @@ struct PrepKdaSmem {
   alignas(16) E Ks[kChunk][LDK];
   alignas(16) E Qs[kChunk][LDK];
   alignas(16) float Gm[kChunk][LDG];  // log a, then its chunk-local prefix per channel
+  // per-token decays a = e^{log a} (bf16 diagonal blocks; fp32 forms the ratios directly)
+  alignas(16) float Ad[is_bf16<E>() ? kChunk : 1][LDG];
+  float part[kThreads / DK][DK];      // prefix-scan partial totals
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
   alignas(16) float Ms[2][16][20];
@@ -351,51 +364,73 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
   const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, p.heads * p.nchunks, DK);
 
-  // ---- K, Q rows, log a and eta of the chunk into LDS (rows past T are zero) ----
+  // ---- K, Q rows, log a and eta of the chunk into LDS: every load issued first, through
+  //      buffer resources over this batch entry's rows (rows past T read as zero) ----
   {
-    constexpr int CPR = DK / VN;
-    const E* gk = static_cast<const E*>(p.k);
-    const E* gq = static_cast<const E*>(p.q);
-    for (int i = tid; i < kChunk * CPR; i += kThreads) {
-      const int r = i / CPR, c0 = (i % CPR) * VN;
-      const bool valid = t0 + r < T;
-      V16 kx, qx;
-      if (valid) {
-        kx = *reinterpret_cast<const V16*>(gk + row_index(t0 + r) * DK + c0);
-        qx = *reinterpret_cast<const V16*>(gq + row_index(t0 + r) * DK + c0);
-      } else {
+    constexpr int CPR = DK / VN, NKQ = kChunk * CPR / kThreads, NL = kChunk * DK / 4 / kThreads;
+    const int64_t brow = bb * T * p.H;
+    const uint32_t xrow = p.H * DK * sizeof(E), lrow = p.H * DK * 4;  // bytes per token
+    const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
+    const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
+    const rsrc_t rl = make_rsrc(p.log_alpha + brow * DK, (uint32_t)(T * lrow));
+    i32x4 kx[NKQ], qx[NKQ], lx[NL];
 #pragma unroll
-        for (int e = 0; e < VN; ++e) kx[e] = qx[e] = from_f32<E>(0.f);
-      }
-      *reinterpret_cast<V16*>(&sm.Ks[r][c0]) = kx;
-      *reinterpret_cast<V16*>(&sm.Qs[r][c0]) = qx;
+    for (int j = 0; j < NKQ; ++j) {
+      const int i = tid + kThreads * j, r = i / CPR, c0 = (i % CPR) * VN;
+      const uint32_t off = (uint32_t)((t0 + r) * xrow + (hh * DK + c0) * sizeof(E));
+      kx[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      qx[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
-    for (int i = tid; i < kChunk * DK / 4; i += kThreads) {
-      const int r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (t0 + r < T) x = *reinterpret_cast<const f32x4*>(p.log_alpha + row_index(t0 + r) * DK + c4);
-      *reinterpret_cast<f32x4*>(&sm.Gm[r][c4]) = x;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int i = tid + kThreads * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      lx[j] = __builtin_amdgcn_raw_buffer_load_b128(rl, (uint32_t)((t0 + r) * lrow + (hh * DK + c4) * 4), 0, 0);
     }
-    if (tid < kChunk) sm.eta[tid] = t0 + tid < T ? p.eta[row_index(t0 + tid)] : 0.f;
+    const float et = tid < kChunk && t0 + tid < T ? p.eta[row_index(t0 + tid)] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NKQ; ++j) {
+      const int i = tid + kThreads * j, r = i / CPR, c0 = (i % CPR) * VN;
+      *reinterpret_cast<i32x4*>(&sm.Ks[r][c0]) = kx[j];
+      *reinterpret_cast<i32x4*>(&sm.Qs[r][c0]) = qx[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int i = tid + kThreads * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      *reinterpret_cast<i32x4*>(&sm.Gm[r][c4]) = lx[j];
+    }
+    if (tid < kChunk) sm.eta[tid] = et;
   }
   __syncthreads();
 
-  // ---- per-channel prefix of log a over the chunk's tokens; squared key norms ----
-  static_assert(DK <= kThreads - kChunk, "one thread per channel, one per row");
-  if (tid < DK) {
-    float acc = 0.f;
-    for (int r = 0; r < kChunk; ++r) {
-      acc += sm.Gm[r][tid];
-      sm.Gm[r][tid] = acc;
-    }
-  } else if (tid >= kThreads - kChunk) {
-    const int r = tid - (kThreads - kChunk);
+  // ---- per-channel prefix of log a over the chunk's tokens: NPART threads per channel, each a
+  //      run of tokens in registers, then the runs' totals; the per-token decays e^{log a} ----
+  constexpr int NPART = kThreads / DK, RUN = kChunk / NPART;
+  const int ch = tid % DK, part = tid / DK;
+  float run[RUN];
+#pragma unroll
+  for (int j = 0; j < RUN; ++j) run[j] = sm.Gm[part * RUN + j][ch];
+  if constexpr (BF) {
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) sm.Ad[part * RUN + j][ch] = __expf(run[j]);
+  }
+#pragma unroll
+  for (int j = 1; j < RUN; ++j) run[j] += run[j - 1];
+  sm.part[part][ch] = run[RUN - 1];
+  if (tid < kChunk) {  // squared key norms
     float nn = 0.f;
-    for (int i = 0; i < DK; ++i) {
-      const float x = to_f32(sm.Ks[r][i]);
-      nn += x * x;
+    for (int i = 0; i < DK; i += VN) {
+      const V16 x = *reinterpret_cast<const V16*>(&sm.Ks[tid][i]);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) nn += to_f32(x[e]) * to_f32(x[e]);
     }
-    sm.n[r] = nn;
+    sm.n[tid] = nn;
+  }
+  __syncthreads();
+  {
+    float off = 0.f;
+    for (int j = 0; j < part; ++j) off += sm.part[j][ch];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) sm.Gm[part * RUN + j][ch] = run[j] + off;
   }
   __syncthreads();
 
@@ -488,8 +523,52 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
       sm.Ps[r][s] = from_f32<E>(qk[e]);
     }
   }
-  // ---- diagonal 16 x 16 blocks: one thread per (r, s), summed per channel ----
-  {
+  // ---- diagonal 16 x 16 blocks ----
+  if constexpr (BF) {
+    // thread (s, channel slice): for r = s .. 15 the ratio w = prod_{j = s+1..r} a_j is updated
+    // by one multiply per channel; the 16 channel slices of an s share a DPP row and are summed
+    // there. Every lane runs all 16 r (w = 0 before s), so the DPP sums stay uniform.
+    constexpr int CS = DK / 16;  // channels per slice: 8 or 4
+    typedef typename std::conditional<CS == 8, bf16x8, bf16x4>::type KV;
+    const int ss = tid >> 4 & 15, sl = tid & 15, c0 = CS * sl;
+    for (int I = 0; I < 4; ++I) {
+      const int b = 16 * I, s = b + ss;
+      const KV ks = *reinterpret_cast<const KV*>(&sm.Ks[s][c0]);
+      float w[CS];
+#pragma unroll
+      for (int c = 0; c < CS; ++c) w[c] = 0.f;
+      float ra = 0.f, rp = 0.f;  // this lane keeps the sums of row r = b + sl
+#pragma unroll 4
+      for (int rr = 0; rr < 16; ++rr) {
+        const int r = b + rr;
+        float ad[CS];  // read unconditionally (a select below, not a branch per channel)
+#pragma unroll
+        for (int c = 0; c < CS; c += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[r][c0 + c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ad[c + e] = x[e];
+        }
+        const KV kr = *reinterpret_cast<const KV*>(&sm.Ks[r][c0]);
+        const KV qr = *reinterpret_cast<const KV*>(&sm.Qs[r][c0]);
+        const bool first = rr == ss;
+        float a = 0.f, pq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CS; ++c) {
+          w[c] = first ? 1.f : w[c] * ad[c];
+          const float x = to_f32(ks[c]) * w[c];
+          a += to_f32(kr[c]) * x;
+          pq += to_f32(qr[c]) * x;
+        }
+        a = dpp_row16_sum(a);
+        pq = dpp_row16_sum(pq);
+        ra = rr == sl ? a : ra;
+        rp = rr == sl ? pq : rp;
+      }
+      const int r = b + sl;
+      sm.Af[r][s] = sl > ss ? sm.eta[r] * sm.sc[kScRs][r] * sm.sc[kScRs][s] * ra : 0.f;
+      sm.Ps[r][s] = from_f32<E>(sl >= ss ? rp : 0.f);
+    }
+  } else {  // one thread per (r, s), summed per channel
     const int rr = tid >> 4, ss = tid & 15;
     for (int I = 0; I < 4; ++I) {
       const int r = 16 * I + rr, s = 16 * I + ss;

@@ -23,17 +23,24 @@
 namespace kla {
 namespace {
 
+// Ks is dead once every wave holds its B fragments in registers (a barrier follows their
+// loads), so P is staged in the same bytes; once P is stored, the solve's intermediates use
+// them. At 37 KiB (bf16, d_k = 128) four workgroups share a CU.
 template <typename E, int DK>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(E);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDP = kChunk + PAD;
   static constexpr int LDF = kChunk + 4;
-  alignas(16) E Ks[kChunk][LDK];      // K chunk (B operand of K K^T and Q K^T)
+  union {
+    alignas(16) E Ks[kChunk][LDK];  // K chunk (B operand of K K^T and Q K^T)
+    alignas(16) E Ps[kChunk][LDP];
+    struct {
+      alignas(16) float Ms[2][16][20];  // doubling-step intermediates of waves 0 and 1
+      alignas(16) float M2[32][36];     // A[2:4, 0:2] T[0:2, 0:2]
+    };
+  };
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
-  alignas(16) E Ps[kChunk][LDP];
-  alignas(16) float Ms[2][16][20];    // doubling-step intermediates of waves 0 and 1
-  alignas(16) float M2[32][36];       // A[2:4, 0:2] T[0:2, 0:2]
   alignas(16) float sc[kScRows][kChunk];
   float n[kChunk], eta[kChunk], la[kChunk], G[kChunk];
 };
@@ -272,29 +279,50 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): the lower 16 x 16 tiles of
   //      this wave's two row tiles (five tiles per wave) ----
   {
-    Frag<E, DK> bk[4];
+    // All products first (one B tile of K in registers at a time), then the scaled entries.
+    f32x4 acc[2][4];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj)
-      if (tj <= ti1) bk[tj].load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
+    for (int tj = 0; tj < 4; ++tj) {
+      acc[0][tj] = acc[1][tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (tj > ti1) continue;
+      Frag<E, DK> bk;
+      bk.load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
+      if (tj <= ti0) mma_frag(acc[0][tj], a0, bk);
+      mma_frag(acc[1][tj], a1, bk);
+    }
+    // Per-token values of the columns (all tiles) and of this lane's rows, read before any A or P
+    // entry is written.
+    float Gs[4], rss[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      Gs[tj] = sm.G[tj * 16 + lr];
+      rss[tj] = sm.sc[kScRs][tj * 16 + lr];
+    }
+    f32x4 Gr[2], cr[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * (half ? ti1 : ti0) + 4 * lq + e;
+        Gr[half][e] = sm.G[r];
+        cr[half][e] = sm.eta[r] * sm.sc[kScRs][r];
+      }
+    __syncthreads();  // K is no longer read: P may now overwrite it
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int ti = half ? ti1 : ti0;
-      const Frag<E, DK>& a = half ? a1 : a0;
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
         if (tj > ti) continue;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma_frag(acc, a, bk[tj]);
         const int s = tj * 16 + lr;
-        const float Gs = sm.G[s], rss = sm.sc[kScRs][s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = ti * 16 + 4 * lq + e;
-          const float dec = __expf(sm.G[r] - Gs);
+          const float dec = __expf(Gr[half][e] - Gs[tj]);
           if (qwave)
-            sm.Ps[r][s] = from_f32<E>(s <= r ? dec * acc[e] : 0.f);
+            sm.Ps[r][s] = from_f32<E>(s <= r ? dec * acc[half][tj][e] : 0.f);
           else
-            sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * rss * dec * acc[e] : 0.f;
+            sm.Af[r][s] = s < r ? cr[half][e] * rss[tj] * dec * acc[half][tj][e] : 0.f;
         }
       }
     }

@@ -245,37 +245,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   }
   __syncthreads();
 
-  // ---- per-token factors (wave 0) ----
-  if (wave == 0) {
-    const int r = lane;
-    const float G = wave_inclusive_scan(sm.la[r]);
-    const float GC = __shfl(G, kChunk - 1, kWave);  // padded rows add log 1 = 0
-    // Balanced factors: A[r][s] = eta_r rs_r rs_s e^{G_r - G_s} k_r.k_s is a diagonal similarity of
-    // beta_r e^{G_r - G_s} k_r.k_s when beta_r = eta_r rs_r^2. Kaczmarz step: rs = 1/sqrt(|k|^2 + eps).
-    // Given beta (gated DeltaNet): rs = sqrt(|beta|), eta = sign(beta); or, for the backward,
-    // rs = 1, eta = beta.
-    const bool valid = t0 + r < T;
-    float rs, et;
-    if (p.beta_given && p.unit_rs) {
-      rs = valid ? 1.f : 0.f;
-      et = sm.eta[r];
-    } else if (p.beta_given) {
-      const float b = sm.eta[r];
-      rs = valid ? sqrtf(fabsf(b)) : 0.f;
-      et = b < 0.f ? -1.f : 1.f;
-      sm.eta[r] = et;
-    } else {
-      rs = valid ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
-      et = sm.eta[r];
-    }
-    sm.G[r] = G;
-    sm.sc[kScCoefR][r] = et * rs;
-    sm.sc[kScEG][r] = __expf(G);
-    sm.sc[kScRs][r] = rs;
-    sm.sc[kScD2][r] = rs * __expf(GC - G);
-  }
-  __syncthreads();
-
   // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): the lower 16 x 16 tiles of
   //      this wave's two row tiles (five tiles per wave) ----
   {
@@ -290,8 +259,37 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
       if (tj <= ti0) mma_frag(acc[0][tj], a0, bk);
       mma_frag(acc[1][tj], a1, bk);
     }
-    // Per-token values of the columns (all tiles) and of this lane's rows, read before any A or P
-    // entry is written.
+    // ---- per-token factors (wave 0, after its products; the other waves' products overlap) ----
+    if (wave == 0) {
+      const int r = lane;
+      const float G = wave_inclusive_scan(sm.la[r]);
+      const float GC = __shfl(G, kChunk - 1, kWave);  // padded rows add log 1 = 0
+      // Balanced factors: A[r][s] = eta_r rs_r rs_s e^{G_r - G_s} k_r.k_s is a diagonal similarity of
+      // beta_r e^{G_r - G_s} k_r.k_s when beta_r = eta_r rs_r^2. Kaczmarz step: rs = 1/sqrt(|k|^2 + eps).
+      // Given beta (gated DeltaNet): rs = sqrt(|beta|), eta = sign(beta); or, for the backward,
+      // rs = 1, eta = beta.
+      const bool valid = t0 + r < T;
+      float rs, et;
+      if (p.beta_given && p.unit_rs) {
+        rs = valid ? 1.f : 0.f;
+        et = sm.eta[r];
+      } else if (p.beta_given) {
+        const float b = sm.eta[r];
+        rs = valid ? sqrtf(fabsf(b)) : 0.f;
+        et = b < 0.f ? -1.f : 1.f;
+        sm.eta[r] = et;
+      } else {
+        rs = valid ? 1.f / sqrtf(sm.n[r] + p.eps) : 0.f;
+        et = sm.eta[r];
+      }
+      sm.G[r] = G;
+      sm.sc[kScCoefR][r] = et * rs;
+      sm.sc[kScEG][r] = __expf(G);
+      sm.sc[kScRs][r] = rs;
+      sm.sc[kScD2][r] = rs * __expf(GC - G);
+    }
+    __syncthreads();  // factors in LDS; K no longer read: P may now overwrite it
+    // Per-token values of the columns (all tiles) and of this lane's rows.
     float Gs[4], rss[4];
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
@@ -307,7 +305,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
         Gr[half][e] = sm.G[r];
         cr[half][e] = sm.eta[r] * sm.sc[kScRs][r];
       }
-    __syncthreads();  // K is no longer read: P may now overwrite it
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int ti = half ? ti1 : ti0;

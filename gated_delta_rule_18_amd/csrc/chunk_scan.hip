@@ -31,10 +31,15 @@
 // outputs are computed transposed (O^T = S^T Q^T + D'^T P^T), which leaves each lane four
 // consecutive columns of one token row: they go to global memory without a transpose.
 //
-// Operands in LDS. K, Q, T and P are read as A fragments along their rows (two 8-byte reads
-// per bf16 fragment), K also transposed for K^T with the transposing read of gfx950, and V as
-// four consecutive rows of one column (transposing read). All are row-major without padding,
-// their 16-byte chunks XOR-swizzled by row so that these reads are free of bank conflicts.
+// For bf16 the forward modes enumerate the contraction differently (tile_ops.h, whole-chunk
+// layout): lane group g feeds the 8 consecutive indices 32s + 8g + 0..7, the token tiles and
+// state tiles holding their rows in the matching order, so that a fragment along a row is one
+// 16-byte LDS read and needs no register moves; the backward recompute keeps the order above.
+//
+// Operands in LDS. K, Q, T and P are read as A fragments along their rows, K also transposed
+// for K^T with the transposing read of gfx950, and V as four rows of one column (transposing
+// read). All are row-major without padding, their 16-byte chunks XOR-swizzled by row so that
+// these reads are free of bank conflicts.
 // They arrive by direct-to-LDS buffer loads (no registers), a chunk ahead, into a ring of LDS
 // buffers: one workgroup barrier per chunk. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
@@ -59,6 +64,11 @@ template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
   constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg, KDA = MODE == kScanKda;
   constexpr bool BF = is_bf16<E>();
+  // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
+  // fragment along a row is one 16-byte LDS read. The recompute keeps the row-split layout, in
+  // which the backward kernels read the states and Deltas it stores.
+  constexpr bool PERM = BF && !REC;
+  constexpr int LT = PERM ? kLayTok : kLaySplit, LL = PERM ? kLayLin : kLaySplit;  // K, T, V / Q, P
   constexpr int GK = Grp<E>::K;
   typedef typename Grp<E>::V GV;
   constexpr int NC = 16 * NT;        // state columns per wave
@@ -145,21 +155,23 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   static_assert(BK % W == 0 && BT % W == 0 && BV % W == 0, "block split");
   constexpr int NBK = BK / W, NBT = BT / W, NBV = BV / W;
   // Per-lane byte offsets within a row-block, excluding the chunk's base (fixed for the kernel).
-  uint32_t offk[NBK], offt[NBT], offv[NBV];
+  uint32_t offk[NBK], offq[NBK], offt[NBT], offp[NBT], offv[NBV];
 #pragma unroll
   for (int i = 0; i < NBK; ++i) {
     const int ph = 64 * (wave + W * i) + lane, r = ph / CK;
-    offk[i] = r * krow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
+    offk[i] = r * krow + hcol_x + 16 * swz<E, CK, LT>(r, ph % CK);
+    offq[i] = r * krow + hcol_x + 16 * swz<E, CK, LL>(r, ph % CK);
   }
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
     const int ph = 64 * (wave + W * i) + lane, r = ph / CT;
-    offt[i] = (r * CT + swz<E, CT>(r, ph % CT)) * 16;
+    offt[i] = (r * CT + swz<E, CT, LT>(r, ph % CT)) * 16;
+    offp[i] = (r * CT + swz<E, CT, LL>(r, ph % CT)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < NBV; ++i) {
     const int ph = 64 * (wave + W * i) + lane, r = ph / CV;
-    offv[i] = r * vrow + hcol_v + 16 * swz<E, CV>(r, ph % CV);
+    offv[i] = r * vrow + hcol_v + 16 * swz<E, CV, LT>(r, ph % CV);
   }
   // Every wave issues the same NDMA loads per chunk (the factor block is loaded by all of them,
   // identical bytes), so that the wait counts below are compile-time constants. A chunk past
@@ -173,14 +185,14 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     for (int i = 0; i < NBK; ++i) {
       const int blk = wave + W * i;
       dma16(rk, B.K + blk * 64 * PER, t0 * krow + offk[i]);
-      if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * krow + offk[i]);
+      if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * krow + offq[i]);
       if constexpr (KDA) dma16(rk2, B.K2 + blk * 64 * PER, t0 * krow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
       const int blk = wave + W * i;
       dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
-      if constexpr (!REC) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
+      if constexpr (!REC) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offp[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
@@ -191,7 +203,10 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
 
-  // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[16 rt + 4g + e][j0 + cw + 16 ct + c] ----
+  // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[srow(rt, e)][j0 + cw + 16 ct + c] ----
+  auto srow = [&](int rt, int e) { return PERM ? k_row(rt, g, e) : 16 * rt + 4 * g + e; };
+  // First token of the four (consecutive) tokens that lane group g holds in token tile r.
+  auto trow4 = [&](int r) { return PERM ? tok_row(r, 4 * g) : 16 * r + 4 * g; };
   f32x4 S[RTK][NT];
   if (mpart) {  // identity columns
 #pragma unroll
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[r][ct][e] = 16 * r + 4 * g + e == j0 + cw + 16 * ct + c16 ? 1.f : 0.f;
+        for (int e = 0; e < 4; ++e) S[r][ct][e] = srow(r, e) == j0 + cw + 16 * ct + c16 ? 1.f : 0.f;
   } else if (p.state_in && seg == 0) {
     const float* Sin = p.state_in + head * (int64_t)DK * DV;
 #pragma unroll
@@ -207,7 +222,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[r][ct][e] = Sin[(int64_t)(16 * r + 4 * g + e) * DV + j0 + cw + 16 * ct + c16];
+        for (int e = 0; e < 4; ++e) S[r][ct][e] = Sin[(int64_t)srow(r, e) * DV + j0 + cw + 16 * ct + c16];
   } else {
 #pragma unroll
     for (int r = 0; r < RTK; ++r)
@@ -248,7 +263,12 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int r = 0; r < RTK; ++r) tiles[r] = S[r][ct];
 #pragma unroll
-      for (int s = 0; s < NGD; ++s) sb[s][ct] = acc_grp<E>(tiles, s);
+      for (int s = 0; s < NGD; ++s) {
+        if constexpr (PERM)
+          sb[s][ct] = state_grp(tiles, s, g);
+        else
+          sb[s][ct] = acc_grp<E>(tiles, s);
+      }
     }
     f32x4 X[4][NT], Y[NT][4];
 #pragma unroll
@@ -257,26 +277,38 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       for (int ct = 0; ct < NT; ++ct) X[r][ct] = Y[ct][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NGD; ++s) {
-        const GV ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
+        GV ak;
+        if constexpr (PERM)
+          ak = row8_grp<DK, kLayTok>(B.K, tok_row(r, c16), s, g);
+        else
+          ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
         if constexpr (!REC) {
-          const GV aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
+          GV aq;
+          if constexpr (PERM)
+            aq = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+          else
+            aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
         }
       }
     }
 
+    // Scheduling fences around the middle of the step: without them the scheduler, working on
+    // the whole step at once, issues each LDS fragment read right before its MFMA and waits on it
+    // (measured 30 % slower); fenced, it keeps several reads in flight in every part.
+    __builtin_amdgcn_sched_barrier(0);
     // ---- R = eta rs (V - e^G X), in place of X (identity columns carry no values) ----
     const float vscale = mpart ? 0.f : 1.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f32x4 coefR = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + 16 * r + 4 * g]);
-      const f32x4 eG = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + 16 * r + 4 * g]);
+      const f32x4 coefR = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + trow4(r)]);
+      const f32x4 eG = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + trow4(r)]);
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        const f32x4 v = vscale * col4<E, DVS>(B.V, 16 * r, cw + 16 * ct, g, c16);
+        const f32x4 v = vscale * col4<E, DVS, LT>(B.V, PERM ? tok_row(r, 0) : 16 * r, cw + 16 * ct, g, c16);
         X[r][ct] = coefR * (v - eG * X[r][ct]);
       }
     }
@@ -298,13 +330,17 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
         if (GK * s < 16 * (r + 1)) {
-          const GV at_ = row_grp<E, kChunk>(B.T, 16 * r + c16, s, g);
+          GV at_;
+          if constexpr (PERM)
+            at_ = row8_grp<kChunk, kLayTok>(B.T, tok_row(r, c16), s, g);
+          else
+            at_ = row_grp<E, kChunk>(B.T, 16 * r + c16, s, g);
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) d[ct] = mma<E>(at_, rb[ct][s], d[ct]);
         }
       }
-      const f32x4 rs = *reinterpret_cast<const f32x4*>(&B.sc[kScRs * kChunk + 16 * r + 4 * g]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&B.sc[kScD2 * kChunk + 16 * r + 4 * g]);
+      const f32x4 rs = *reinterpret_cast<const f32x4*>(&B.sc[kScRs * kChunk + trow4(r)]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&B.sc[kScD2 * kChunk + trow4(r)]);
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
         D1[ct][r] = rs * d[ct];
@@ -337,7 +373,11 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
         if (GK * s < 16 * (r + 1)) {
-          const GV ap = row_grp<E, kChunk>(B.P, 16 * r + c16, s, g);
+          GV ap;
+          if constexpr (PERM)
+            ap = row8_grp<kChunk, kLayLin>(B.P, 16 * r + c16, s, g);
+          else
+            ap = row_grp<E, kChunk>(B.P, 16 * r + c16, s, g);
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) o[ct] = mma<E>(b1[ct][s], ap, o[ct]);
         }
@@ -347,12 +387,13 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       for (int ct = 0; ct < NT; ++ct) store4_rsrc<E>(rout, off + 16 * ct * sizeof(E), o[ct]);
     }
 
+    __builtin_amdgcn_sched_barrier(0);
     // ---- S <- e^{G_C} S + K^T diag(e^{G_C - G}) D' (KDA: Diag(gamma) S + K2^T D') ----
     const float eGC = B.sc[kScEG * kChunk + kChunk - 1];
 #pragma unroll
     for (int r = 0; r < RTK; ++r) {
       if constexpr (KDA) {
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * r + 4 * g]);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[srow(r, 0)]);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) S[r][ct] *= gm;
       } else {
@@ -361,7 +402,11 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
       }
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
-        const GV ak = kt_grp<E, DK>(KDA ? B.K2 : B.K, r, s, g, c16);
+        GV ak;
+        if constexpr (PERM)
+          ak = kt8_grp<DK>(KDA ? B.K2 : B.K, r, s, g, c16);
+        else
+          ak = kt_grp<E, DK>(KDA ? B.K2 : B.K, r, s, g, c16);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) S[r][ct] = mma<E>(ak, b2[ct][s], S[r][ct]);
       }
@@ -400,7 +445,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(int64_t)(16 * r + 4 * g + e) * ld + j0 + cw + 16 * ct + c16] = S[r][ct][e];
+        for (int e = 0; e < 4; ++e) dst[(int64_t)srow(r, e) * ld + j0 + cw + 16 * ct + c16] = S[r][ct][e];
   } else if (p.state_out) {
     float* Sout = p.state_out + head * (int64_t)DK * DV;
 #pragma unroll
@@ -408,7 +453,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sout[(int64_t)(16 * r + 4 * g + e) * DV + j0 + cw + 16 * ct + c16] = S[r][ct][e];
+        for (int e = 0; e < 4; ++e) Sout[(int64_t)srow(r, e) * DV + j0 + cw + 16 * ct + c16] = S[r][ct][e];
   }
 }
 

@@ -75,10 +75,32 @@ __device__ __forceinline__ typename Grp<E>::V acc_grp(const f32x4* tiles, int s)
   }
 }
 
+// Layouts of an operand matrix in LDS (its rows' 16-byte chunks XOR-swizzled by row):
+//   kLaySplit  fragments along a row read as two 8-byte halves (see Grp);
+//   kLayTok    bf16 whole-chunk layout for matrices whose fragments are read along the rows
+//              tok_row(r, 0..15) of a token tile (K, T) or transposed (K for the state update, V);
+//   kLayLin    bf16 whole-chunk layout for matrices read along 16 consecutive rows (Q, P).
+// Each swizzle keeps that matrix's reads free of bank conflicts (measured with the LDS
+// bank-conflict counter on every access pattern of the scan), and depends on as few row bits
+// as that allows, so that reads of different tiles differ by constant offsets.
+enum { kLaySplit = 0, kLayTok = 1, kLayLin = 2 };
+
 // Physical 16-byte chunk of logical chunk cc in row r of a matrix with CPR chunks per row.
-template <typename E, int CPR>
+template <typename E, int CPR, int LAY = kLaySplit>
 __device__ __forceinline__ int swz(int r, int cc) {
-  if constexpr (is_bf16<E>()) {
+  if constexpr (LAY != kLaySplit) {
+    static_assert(is_bf16<E>(), "whole-chunk layouts are bf16 only");
+    static_assert(CPR == 16 || CPR == 8 || CPR == 4, "bf16 row width");
+    const int r0 = r & 1, r1 = (r >> 1) & 1, r3 = (r >> 3) & 1, r4 = (r >> 4) & 1;
+    if constexpr (LAY == kLayLin)
+      return CPR == 16 ? cc ^ (r & 15) : CPR == 8 ? cc ^ ((r >> 1) & 7) : cc ^ (r3 << 1);
+    else if constexpr (CPR == 16)
+      return cc ^ (r0 | (r4 << 1) | (r1 << 2) | (r3 << 3));
+    else if constexpr (CPR == 8)
+      return cc ^ (r1 | (r3 << 1) | (r4 << 2));
+    else
+      return cc ^ (r3 << 1);
+  } else if constexpr (is_bf16<E>()) {
     static_assert(CPR == 16 || CPR == 8 || CPR == 4, "bf16 row width");
     if constexpr (CPR == 16) return cc ^ (((r & 7) << 1) | ((r >> 3) & 1));
     if constexpr (CPR == 8) return cc ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
@@ -90,10 +112,53 @@ __device__ __forceinline__ int swz(int r, int cc) {
 }
 
 // Element offset of (r, col) in a swizzled row-major matrix of NCOL columns.
-template <typename E, int NCOL>
+template <typename E, int NCOL, int LAY = kLaySplit>
 __device__ __forceinline__ int at(int r, int col) {
   constexpr int PER = 16 / sizeof(E), CPR = NCOL / PER;
-  return r * NCOL + PER * swz<E, CPR>(r, col / PER) + col % PER;
+  return r * NCOL + PER * swz<E, CPR, LAY>(r, col / PER) + col % PER;
+}
+
+// ---- whole-chunk layout (bf16) ---------------------------------------------------------------
+// Contraction group s of v_mfma_f32_16x16x32_bf16 feeds lane group g the 8 consecutive indices
+// 32 s + 8 g + 0..7, so a fragment along a row is one 16-byte LDS read. The accumulator tiles
+// that serve as the other operand hold, per lane group g, four consecutive indices each:
+//   token tiles (products over the chunk's tokens), tile r, row m:
+//     tok(r, m) = 32 (r / 2) + 8 (m / 4) + 4 (r % 2) + m % 4
+//   state tiles (products over d_k), tile r, row m = 4 g + e:
+//     krow(r, g, e) = 32 (r / 2) + 8 g + 4 ((g % 2) ^ (r % 2)) + e
+// The state tiles alternate their halves with g, so that the transposing reads of K for the
+// state update touch both 8-byte halves of the 16-byte chunks (no bank conflicts).
+__device__ __forceinline__ int tok_row(int r, int m) { return 32 * (r >> 1) + 8 * (m >> 2) + 4 * (r & 1) + (m & 3); }
+__device__ __forceinline__ int k_row(int r, int g, int e) {
+  return 32 * (r >> 1) + 8 * g + 4 * ((g & 1) ^ (r & 1)) + e;
+}
+
+// A or B operand of group s along row `row`: one 16-byte read.
+template <int NCOL, int LAY>
+__device__ __forceinline__ bf16x8 row8_grp(const bf16* M, int row, int s, int g) {
+  return *reinterpret_cast<const bf16x8*>(M + at<bf16, NCOL, LAY>(row, 32 * s + 8 * g));
+}
+
+// Operand of group s from state tiles 2s and 2s + 1 (the lane's indices 32 s + 8 g + 0..7, in
+// order: the tile holding the lower four depends on g).
+__device__ __forceinline__ bf16x8 state_grp(const f32x4* tiles, int s, int g) {
+  const f32x4 a = tiles[2 * s], b = tiles[2 * s + 1];
+  const bf16x4 ca = {from_f32<bf16>(a[0]), from_f32<bf16>(a[1]), from_f32<bf16>(a[2]), from_f32<bf16>(a[3])};
+  const bf16x4 cb = {from_f32<bf16>(b[0]), from_f32<bf16>(b[1]), from_f32<bf16>(b[2]), from_f32<bf16>(b[3])};
+  const bool swap = g & 1;
+  const bf16x4 lo = swap ? cb : ca, hi = swap ? ca : cb;
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A operand of group s of K^T for state tile rt: A(m, k) = K[k][krow(rt, m / 4, m % 4)],
+// k = tokens 32 s + 8 g + 0..7 (two transposing reads of four tokens each).
+template <int DK>
+__device__ __forceinline__ bf16x8 kt8_grp(const bf16* Ks, int rt, int s, int g, int c) {
+  const int j = c & 3, r0 = 32 * s + 8 * g + (c >> 2);
+  const int col = 32 * (rt >> 1) + 8 * j + 4 * ((j & 1) ^ (rt & 1));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<bf16, DK, kLayTok>(r0, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Ks + at<bf16, DK, kLayTok>(r0 + 4, col)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // A operand of group s along row `row` (k = column index).
@@ -124,13 +189,14 @@ __device__ __forceinline__ typename Grp<E>::V kt_grp(const E* Ks, int rt, int s,
   }
 }
 
-// Rows r0 + 4g + 0..3 of column col0 + c, as fp32.
-template <typename E, int NCOL>
+// Rows r0 + GS g + 0..3 of column col0 + c, as fp32 (GS = 4; 8 in the token-tile layout).
+template <typename E, int NCOL, int LAY = kLaySplit>
 __device__ __forceinline__ f32x4 col4(const E* M, int r0, int col0, int g, int c) {
+  constexpr int GS = LAY == kLayTok ? 8 : 4;
   f32x4 out;
   if constexpr (is_bf16<E>()) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(M + at<E, NCOL>(r0 + 4 * g + (c >> 2), col0 + 4 * (c & 3))));
+        (lds_s16x4*)(M + at<E, NCOL, LAY>(r0 + GS * g + (c >> 2), col0 + 4 * (c & 3))));
     const bf16x4 b = __builtin_bit_cast(bf16x4, v);
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = to_f32(b[j]);

@@ -54,6 +54,14 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
+// Producer waves. In the bf16 forward modes two more waves per workgroup, on the two SIMDs the
+// scan waves leave idle, issue all direct-to-LDS loads; the scan waves then spend no issue
+// cycles on them (about a fifth of a chunk's step when they issued them themselves).
+template <typename E, int DK, int DV, int W, int NT, int MODE>
+constexpr int scan_producers() {
+  return (is_bf16<E>() && MODE != kScanRec && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2 : 0;
+}
+
 // MODE kScanRec (backward recompute): no outputs; instead every chunk's entering state S and its
 // Delta (rs D) are stored to the backward workspace, and Q and P are not loaded.
 // MODE kScanSeg (segment scan, pass 1): workgroups cover (head, segment) pairs and, besides the
@@ -61,7 +69,8 @@ namespace {
 // MODE kScanKda (per-channel decay): K, Q and the update's K2 are the decayed operands of the
 // KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
 template <typename E, int DK, int DV, int W, int NT, int MODE>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(ChunkParams p) {
+__global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(
+    ChunkParams p) {
   constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg, KDA = MODE == kScanKda;
   constexpr bool BF = is_bf16<E>();
   // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
@@ -148,34 +157,38 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   const uint32_t orow = mpart ? DK * sizeof(E) : vrow;                       // bytes per output row
   const uint32_t ocol = mpart ? (j0 + cw) * sizeof(E) : hcol_v + cw * sizeof(E);  // this wave's first column
 
-  // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the waves. Lane l of
-  // block b fills physical chunk 64 b + l; its source is the logical chunk stored there. ----
+  // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the loading waves (the
+  // producers, else the scan waves). Lane l of block b fills physical chunk 64 b + l; its source
+  // is the logical chunk stored there. ----
+  constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
+  constexpr int WD = NP ? NP : W;         // loading waves
+  const int dw = NP ? wave - W : wave;    // this wave's index among them (producers only, if any)
   constexpr int CK = DK / PER, CT = kChunk / PER, CV = DVS / PER;  // 16-byte chunks per row
   constexpr int BK = kChunk * CK / 64, BT = kChunk * CT / 64, BV = kChunk * CV / 64;  // blocks
-  static_assert(BK % W == 0 && BT % W == 0 && BV % W == 0, "block split");
-  constexpr int NBK = BK / W, NBT = BT / W, NBV = BV / W;
+  static_assert(BK % WD == 0 && BT % WD == 0 && BV % WD == 0, "block split");
+  constexpr int NBK = BK / WD, NBT = BT / WD, NBV = BV / WD;
   // Per-lane byte offsets within a row-block, excluding the chunk's base (fixed for the kernel).
   uint32_t offk[NBK], offq[NBK], offt[NBT], offp[NBT], offv[NBV];
 #pragma unroll
   for (int i = 0; i < NBK; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CK;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CK;
     offk[i] = r * krow + hcol_x + 16 * swz<E, CK, LT>(r, ph % CK);
     offq[i] = r * krow + hcol_x + 16 * swz<E, CK, LL>(r, ph % CK);
   }
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CT;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CT;
     offt[i] = (r * CT + swz<E, CT, LT>(r, ph % CT)) * 16;
     offp[i] = (r * CT + swz<E, CT, LL>(r, ph % CT)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < NBV; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CV;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CV;
     offv[i] = r * vrow + hcol_v + 16 * swz<E, CV, LT>(r, ph % CV);
   }
-  // Every wave issues the same NDMA loads per chunk (the factor block is loaded by all of them,
-  // identical bytes), so that the wait counts below are compile-time constants. A chunk past
-  // the end is clamped to the last one (loaded again, never read).
+  // Every loading wave issues the same NDMA loads per chunk (the factor block is loaded by all of
+  // them, identical bytes), so that the wait counts below are compile-time constants. A chunk
+  // past the end is clamped to the last one (loaded again, never read).
   constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : KDA ? 3 * NBK + 2 * NBT + NBV + 2 : 2 * NBK + 2 * NBT + NBV + 1;
   constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
@@ -183,25 +196,44 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     const uint32_t t0 = (uint32_t)(c * kChunk);
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rk, B.K + blk * 64 * PER, t0 * krow + offk[i]);
       if constexpr (!REC) dma16(rq, B.Q + blk * 64 * PER, t0 * krow + offq[i]);
       if constexpr (KDA) dma16(rk2, B.K2 + blk * 64 * PER, t0 * krow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
       if constexpr (!REC) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offp[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rv, B.V + blk * 64 * PER, t0 * vrow + offv[i]);
     }
     dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
     if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
+
+  if constexpr (NP > 0) {
+    static_assert(NB == 2, "producers serve a two-buffer ring");
+    if (wave >= W) {  // producer: the loads of every chunk, one chunk ahead, one barrier per chunk
+      if (ce > cb) fetch(buf0, cb);
+      for (int64_t c = cb; c < ce; c += 2) {
+        wait_vmem<0>();
+        __syncthreads();  // chunk c is in buf0; every wave is done with chunk c - 1 (buf1)
+        fetch(buf1, c + 1);
+        if (c + 1 < ce) {
+          wait_vmem<0>();
+          __syncthreads();
+          fetch(buf0, c + 2);
+        }
+      }
+      wait_vmem<0>();  // no load into LDS outlives the workgroup
+      return;
+    }
+  }
 
   // ---- this wave's state columns: S[rt][ct] lane (g, c) = S[srow(rt, e)][j0 + cw + 16 ct + c] ----
   auto srow = [&](int rt, int e) { return PERM ? k_row(rt, g, e) : 16 * rt + 4 * g + e; };
@@ -236,7 +268,9 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   // must be complete: younger are (DIST - 1) chunks of loads and, from c >= DIST on, the stores
   // of DIST chunks (fewer stores before that: waiting for more is still correct).
   auto step = [&](Buf& B, Buf& Bn, int64_t c) __attribute__((always_inline)) {
-    if constexpr (NB == 1) {
+    if constexpr (NP > 0) {
+      // the producers waited for chunk c's loads before this barrier
+    } else if constexpr (NB == 1) {
       wait_vmem<0>();
     } else {
       if (c - cb < DIST)
@@ -245,7 +279,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
         wait_vmem<(DIST - 1) * NDMA + DIST * NST>();
     }
     __syncthreads();  // chunk c's operands are in LDS; every wave is done with chunk c - 1
-    if constexpr (NB > 1) fetch(Bn, c + DIST);
+    if constexpr (NB > 1 && NP == 0) fetch(Bn, c + DIST);
     const uint32_t t0 = (uint32_t)(c * kChunk);
     if constexpr (REC) {  // the state entering chunk c
 #pragma unroll
@@ -417,7 +451,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
   };
 
-  if (ce > cb) {  // chunks cb .. cb + DIST - 1
+  if (NP == 0 && ce > cb) {  // chunks cb .. cb + DIST - 1
     fetch(buf0, cb);
     if constexpr (NB == 3) fetch(buf1, cb + 1);
   }
@@ -464,7 +498,8 @@ hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   constexpr int NSA = DV / DVS + (MODE == kScanSeg ? DK / DVS : 0);
   const int64_t units = p.heads * (MODE == kScanSeg ? p.nseg : 1);  // (head, segment) pairs
   const int64_t units8 = (units + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3(W * kWave), 0,
+  constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3((W + NP) * kWave), 0,
                      stream, p);
   return hipGetLastError();
 }

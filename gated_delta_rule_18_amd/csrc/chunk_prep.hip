@@ -15,17 +15,17 @@
 // and the per-token factors the scan needs (see chunk_common.h).
 //
 // T is found blockwise on 16 x 16 blocks: the four diagonal blocks by forward substitution in
-// registers (one wave, a lane per column), then the off-diagonal blocks by two doubling steps
-// on fp32 MFMA: T10 = -T11 A10 T00 and T32 = -T33 A32 T22, then
-// T[2:4, 0:2] = -T[2:4, 2:4] (A[2:4, 0:2] T[0:2, 0:2]). T overwrites A in place.
+// registers (one wave, a lane per column), then the off-diagonal blocks by block forward
+// substitution down each block column on fp32 MFMA, one wave per column:
+// T[i][j] = -T[i][i] sum_{j<=k<i} A[i][k] T[k][j]. One barrier separates the two steps.
 #include "tile_ops.h"
 
 namespace kla {
 namespace {
 
 // Ks is dead once every wave holds its B fragments in registers (a barrier follows their
-// loads), so P is staged in the same bytes; once P is stored, the solve's intermediates use
-// them. At 37 KiB (bf16, d_k = 128) four workgroups share a CU.
+// loads), so P is staged in the same bytes; once P is stored, T's off-diagonal blocks use them.
+// At 37 KiB (bf16, d_k = 128) four workgroups share a CU.
 template <typename E, int DK>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(E);
@@ -35,10 +35,7 @@ struct PrepSmem {
   union {
     alignas(16) E Ks[kChunk][LDK];  // K chunk (B operand of K K^T and Q K^T)
     alignas(16) E Ps[kChunk][LDP];
-    struct {
-      alignas(16) float Ms[2][16][20];  // doubling-step intermediates of waves 0 and 1
-      alignas(16) float M2[32][36];     // A[2:4, 0:2] T[0:2, 0:2]
-    };
+    alignas(16) float Tx[6][16][20];  // T's lower off-diagonal blocks (tx_block)
   };
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) float sc[kScRows][kChunk];
@@ -88,7 +85,41 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// T = (I + A)^-1 in place of A in sm.Af, and the chunk's P, T and factor rows to the workspace.
+// Index of the lower off-diagonal 16 x 16 block (i, j), i > j, of T in sm.Tx.
+__device__ __forceinline__ int tx_block(int i, int j) { return i * (i - 1) / 2 + j; }
+
+// acc += A B for 16 x 16 blocks: A row-major in LDS (leading dimension lda), B an accumulator
+// tile in registers (lane (g, c) holds rows 4g .. 4g + 3 of column c). Step s contracts index
+// 4g + s, so B's registers are the MFMA operands as they are.
+__device__ __forceinline__ void mma16_lds_acc(f32x4& acc, const float* A, int lda, const f32x4& b, int lane) {
+  const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + 4 * kq + s], b[s], acc, 0, 0, 0);
+}
+
+// Block column J of T below the diagonal (the diagonal blocks of T and the blocks of A in sm.Af).
+template <int J, typename Sm>
+__device__ __forceinline__ void t_column(Sm& sm, int lane) {
+  constexpr int LDF = Sm::LDF;
+  const int lr = lane & 15, lq = lane >> 4;
+  f32x4 tk[3];
+#pragma unroll
+  for (int i = J + 1; i < 4; ++i) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma16_f32s(acc, &sm.Af[16 * i][16 * J], LDF, 1, &sm.Af[16 * J][16 * J], LDF, 1, 0, 16, lane);
+#pragma unroll
+    for (int k = J + 1; k < i; ++k) mma16_lds_acc(acc, &sm.Af[16 * i][16 * k], LDF, tk[k - J - 1], lane);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    mma16_lds_acc(t, &sm.Af[16 * i][16 * i], LDF, acc, lane);
+    t = -t;
+    tk[i - J - 1] = t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Tx[tx_block(i, J)][4 * lq + e][lr] = t[e];
+  }
+}
+
+// T = (I + A)^-1 (diagonal blocks in place of A in sm.Af, the others in sm.Tx), and the chunk's
+// P, T and factor rows to the workspace.
 // Called by all threads of the workgroup once A (sm.Af, fp32, zero on and above the diagonal),
 // P (sm.Ps) and the factor rows (sm.sc) are in LDS and published by a barrier.
 template <typename E, typename Sm>
@@ -130,38 +161,12 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
   }
   __syncthreads();
 
-  // ---- T10 = -T11 A10 T00 (wave 0), T32 = -T33 A32 T22 (wave 1) ----
-  if (wave < 2) {
-    const int i = 1 + 2 * wave, j = 2 * wave;
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(m, &sm.Af[16 * i][16 * j], LDF, 1, &sm.Af[16 * j][16 * j], LDF, 1, 0, 16, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Ms[wave][4 * lq + e][lr] = m[e];
-    wave_lds_sync();
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(t, &sm.Af[16 * i][16 * i], LDF, 1, &sm.Ms[wave][0][0], 20, 1, 0, 16, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Af[16 * i + 4 * lq + e][16 * j + lr] = -t[e];
-  }
-  __syncthreads();
-
-  // ---- M2 = A[2:4, 0:2] T[0:2, 0:2] (T lower: column block tj starts at row 16 tj) ----
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 m = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(m, &sm.Af[32 + 16 * ti][0], LDF, 1, &sm.Af[0][16 * tj], LDF, 1, 16 * tj, 32, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.M2[16 * ti + 4 * lq + e][16 * tj + lr] = m[e];
-  }
-  __syncthreads();
-  // ---- T[2:4, 0:2] = -T[2:4, 2:4] M2 (T[2:4, 2:4] lower: row block ti needs k < 16 (ti + 1)) ----
-  {
-    const int ti = wave >> 1, tj = wave & 1;
-    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    mma16_f32s(t, &sm.Af[32 + 16 * ti][32], LDF, 1, &sm.M2[0][16 * tj], 36, 1, 0, 16 * (ti + 1), lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Af[32 + 16 * ti + 4 * lq + e][16 * tj + lr] = -t[e];
-  }
+  // ---- off-diagonal blocks, down each block column: wave j forms, for i = j+1 .. 3,
+  //      T[i][j] = -T[i][i] (A[i][j] T[j][j] + sum_{j<k<i} A[i][k] T[k][j]),
+  //      keeping its T[k][j] in registers as operands; results go to sm.Tx ----
+  if (wave == 0) t_column<0>(sm, lane);
+  if (wave == 1) t_column<1>(sm, lane);
+  if (wave == 2) t_column<2>(sm, lane);
   __syncthreads();
 
   // ---- T to the workspace (upper off-diagonal blocks are zero) ----
@@ -171,10 +176,12 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
     for (int i = tid; i < kChunk * VPR; i += kThreads) {
       const int r = i / VPR, c0 = (i % VPR) * VN;
       V16 out;
-      const bool zero = (c0 >> 4) > (r >> 4);  // upper off-diagonal block
+      const int bi = r >> 4, bj = c0 >> 4;
+      const bool zero = bj > bi;  // upper off-diagonal block
+      const float* src = bj == bi ? &sm.Af[r][c0] : &sm.Tx[zero ? 0 : tx_block(bi, bj)][r & 15][c0 & 15];
 #pragma unroll
       for (int e4 = 0; e4 < VN; e4 += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Af[r][c0 + e4]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + e4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
       }
@@ -365,8 +372,7 @@ struct PrepKdaSmem {
   float part[kThreads / DK][DK];      // prefix-scan partial totals
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
-  alignas(16) float Ms[2][16][20];
-  alignas(16) float M2[32][36];
+  alignas(16) float Tx[6][16][20];  // T's lower off-diagonal blocks (tx_block)
   alignas(16) float sc[kScRows][kChunk];
   float n[kChunk], eta[kChunk];
 };

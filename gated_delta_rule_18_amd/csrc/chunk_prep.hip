@@ -556,48 +556,75 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
   }
   // ---- diagonal 16 x 16 blocks ----
   if constexpr (BF) {
-    // thread (s, channel slice): for r = s .. 15 the ratio w = prod_{j = s+1..r} a_j is updated
-    // by one multiply per channel; the 16 channel slices of an s share a DPP row and are summed
-    // there. Every lane runs all 16 r (w = 0 before s), so the DPP sums stay uniform.
+    // Thread (block parity, row pair, channel slice): the rows r2 = 15 - pair and then
+    // r1 = pair of a diagonal block, each summed against s = r, r - 1, .., 0 while the ratio
+    // w = prod_{j = s+1..r} a_j is carried down by one multiply per channel (w *= a_s). Every row
+    // pair takes 17 steps, so no lane idles on the upper triangle; the 16 channel slices of a row
+    // share a DPP row and are summed there.
     constexpr int CS = DK / 16;  // channels per slice: 8 or 4
     typedef typename std::conditional<CS == 8, bf16x8, bf16x4>::type KV;
-    const int ss = tid >> 4 & 15, sl = tid & 15, c0 = CS * sl;
-    for (int I = 0; I < 4; ++I) {
-      const int b = 16 * I, s = b + ss;
-      const KV ks = *reinterpret_cast<const KV*>(&sm.Ks[s][c0]);
-      float w[CS];
+    const int sl = tid & 15, pair = (tid >> 4) & 7, hb = tid >> 7, c0 = CS * sl;
+    static_assert(kThreads == 256, "two blocks of eight row pairs of sixteen slices");
+    for (int I = hb; I < 4; I += 2) {
+      const int b = 16 * I;
+      int r = 15 - pair, s = r;
+      float kr[CS], qr[CS], w[CS];
+      auto row_start = [&]() __attribute__((always_inline)) {
+        const KV kx = *reinterpret_cast<const KV*>(&sm.Ks[b + r][c0]);
+        const KV qx = *reinterpret_cast<const KV*>(&sm.Qs[b + r][c0]);
 #pragma unroll
-      for (int c = 0; c < CS; ++c) w[c] = 0.f;
-      float ra = 0.f, rp = 0.f;  // this lane keeps the sums of row r = b + sl
-#pragma unroll 4
-      for (int rr = 0; rr < 16; ++rr) {
-        const int r = b + rr;
-        float ad[CS];  // read unconditionally (a select below, not a branch per channel)
+        for (int c = 0; c < CS; ++c) {
+          kr[c] = to_f32(kx[c]);
+          qr[c] = to_f32(qx[c]);
+          w[c] = 1.f;
+        }
+      };
+      row_start();
+      KV ks = *reinterpret_cast<const KV*>(&sm.Ks[b + s][c0]);
+      for (int it = 0; it < 17; ++it) {
+        // next step's row and column (the pair's second row after s = 0), its K row read early
+        const bool sw = s == 0;
+        const int s_n = sw ? pair : s - 1;
+        const KV ks_n = *reinterpret_cast<const KV*>(&sm.Ks[b + s_n][c0]);
+        float ad[CS];
 #pragma unroll
         for (int c = 0; c < CS; c += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[r][c0 + c]);
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[b + s][c0 + c]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ad[c + e] = x[e];
         }
-        const KV kr = *reinterpret_cast<const KV*>(&sm.Ks[r][c0]);
-        const KV qr = *reinterpret_cast<const KV*>(&sm.Qs[r][c0]);
-        const bool first = rr == ss;
         float a = 0.f, pq = 0.f;
 #pragma unroll
         for (int c = 0; c < CS; ++c) {
-          w[c] = first ? 1.f : w[c] * ad[c];
           const float x = to_f32(ks[c]) * w[c];
-          a += to_f32(kr[c]) * x;
-          pq += to_f32(qr[c]) * x;
+          a += kr[c] * x;
+          pq += qr[c] * x;
         }
         a = dpp_row16_sum(a);
         pq = dpp_row16_sum(pq);
-        ra = rr == sl ? a : ra;
-        rp = rr == sl ? pq : rp;
+        if (sl == 0) {
+          const int R = b + r, Sc = b + s;
+          sm.Af[R][Sc] = s < r ? sm.eta[R] * sm.sc[kScRs][R] * sm.sc[kScRs][Sc] * a : 0.f;
+          sm.Ps[R][Sc] = from_f32<E>(pq);
+        }
+        if (sw) {  // the row pair's second row
+          r = pair;
+          row_start();
+        } else {  // w for s - 1: times a_s
+#pragma unroll
+          for (int c = 0; c < CS; ++c) w[c] *= ad[c];
+        }
+        s = s_n;
+        ks = ks_n;
       }
-      const int r = b + sl;
-      sm.Af[r][s] = sl > ss ? sm.eta[r] * sm.sc[kScRs][r] * sm.sc[kScRs][s] * ra : 0.f;
-      sm.Ps[r][s] = from_f32<E>(sl >= ss ? rp : 0.f);
+    }
+    // the upper triangles of the diagonal blocks
+    for (int i = tid; i < 4 * 256; i += kThreads) {
+      const int b = 16 * (i >> 8), rr = (i >> 4) & 15, ss = i & 15;
+      if (ss > rr) {
+        sm.Af[b + rr][b + ss] = 0.f;
+        sm.Ps[b + rr][b + ss] = from_f32<E>(0.f);
+      }
     }
   } else {  // one thread per (r, s), summed per channel
     const int rr = tid >> 4, ss = tid & 15;

@@ -32,8 +32,15 @@ hipError_t launch_chunk_grad(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, 
 
 namespace {
 
+// Producer waves (bf16): as in the forward scan, two more waves per workgroup on the idle SIMDs
+// issue all direct-to-LDS loads.
 template <typename E, int DK, int DV, int W, int NT>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_rscan_kernel(
+constexpr int rscan_producers() {
+  return (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT>() == 2) ? 2 : 0;
+}
+
+template <typename E, int DK, int DV, int W, int NT>
+__global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_rscan_kernel(
     ChunkBwdParams p) {
   constexpr int GK = Grp<E>::K;
   typedef typename Grp<E>::V GV;
@@ -84,25 +91,29 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   const rsrc_t rzb = make_rsrc(bw.Zb + chunk0 * kChunk * DV, (uint32_t)(nchunks * kDBytes));
   const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
 
-  // ---- DMA of one chunk's operands (as in the forward scan; dO takes V's place) ----
+  // ---- DMA of one chunk's operands (as in the forward scan; dO takes V's place), by the
+  //      producer waves if there are any, else by the scan waves ----
+  constexpr int NP = rscan_producers<E, DK, DV, W, NT>();
+  constexpr int WD = NP ? NP : W;
+  const int dw = NP ? wave - W : wave;
   constexpr int CK = DK / PER, CT = kChunk / PER, CV = DVS / PER;
   constexpr int BK = kChunk * CK / 64, BT = kChunk * CT / 64, BV = kChunk * CV / 64;
-  static_assert(BK % W == 0 && BT % W == 0 && BV % W == 0, "block split");
-  constexpr int NBK = BK / W, NBT = BT / W, NBV = BV / W;
+  static_assert(BK % WD == 0 && BT % WD == 0 && BV % WD == 0, "block split");
+  constexpr int NBK = BK / WD, NBT = BT / WD, NBV = BV / WD;
   uint32_t offk[NBK], offt[NBT], offv[NBV];
 #pragma unroll
   for (int i = 0; i < NBK; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CK;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CK;
     offk[i] = r * xrow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
   }
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CT;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CT;
     offt[i] = (r * CT + swz<E, CT>(r, ph % CT)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < NBV; ++i) {
-    const int ph = 64 * (wave + W * i) + lane, r = ph / CV;
+    const int ph = 64 * (dw + WD * i) + lane, r = ph / CV;
     offv[i] = r * vrow + hcol_v + 16 * swz<E, CV>(r, ph % CV);
   }
   constexpr int NDMA = 2 * NBK + 2 * NBT + NBV + 1;
@@ -112,23 +123,42 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     const uint32_t t0 = (uint32_t)(c * kChunk);
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rk, B.K + blk * 64 * PER, t0 * xrow + offk[i]);
       dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
       dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
-      const int blk = wave + W * i;
+      const int blk = dw + WD * i;
       dma16(rdo, B.V + blk * 64 * PER, t0 * vrow + offv[i]);
     }
     dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
   };
+
+  if constexpr (NP > 0) {
+    static_assert(NB == 2, "producers serve a two-buffer ring");
+    if (wave >= W) {  // producer: every chunk's loads, one chunk ahead, descending, one barrier per chunk
+      if (nchunks > 0) fetch(buf0, nchunks - 1);
+      for (int64_t c = nchunks - 1; c >= 0; c -= 2) {
+        wait_vmem<0>();
+        __syncthreads();  // chunk c is in buf0; every wave is done with chunk c + 1 (buf1)
+        fetch(buf1, c - 1);
+        if (c - 1 >= 0) {
+          wait_vmem<0>();
+          __syncthreads();
+          fetch(buf0, c - 2);
+        }
+      }
+      wait_vmem<0>();  // no load into LDS outlives the workgroup
+      return;
+    }
+  }
 
   // ---- this wave's columns of dS: lane (g, c) = dS[16 rt + 4g + e][j0 + cw + 16 ct + c] ----
   f32x4 dS[RTK][NT];
@@ -152,7 +182,9 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
   // this chunk's stores, so at most (DIST - 1) chunks of loads and DIST chunks of stores are
   // younger than this chunk's loads when it starts.
   auto step = [&](Buf& B, Buf& Bn, int64_t c, int64_t done) __attribute__((always_inline)) {
-    if constexpr (NB == 1) {
+    if constexpr (NP > 0) {
+      // the producers waited for chunk c's loads before this barrier
+    } else if constexpr (NB == 1) {
       wait_vmem<0>();
     } else {
       if (done < DIST)
@@ -161,7 +193,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
         wait_vmem<(DIST - 1) * NDMA + DIST * NST>();
     }
     __syncthreads();
-    if constexpr (NB > 1) fetch(Bn, c - DIST);
+    if constexpr (NB > 1 && NP == 0) fetch(Bn, c - DIST);
 
     // dS' of this chunk (the gradient of the state leaving it)
 #pragma unroll
@@ -301,7 +333,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
   };
 
-  if (nchunks > 0) fetch(buf0, nchunks - 1);
+  if (NP == 0 && nchunks > 0) fetch(buf0, nchunks - 1);
   if constexpr (NB == 2) {
     int64_t done = 0;
     for (int64_t c = nchunks - 1; c >= 0; c -= 2, done += 2) {
@@ -328,7 +360,8 @@ template <typename E, int DK, int DV, int W, int NT>
 hipError_t launch_wnt(const ChunkBwdParams& p, hipStream_t stream) {
   constexpr int NS = DV / (W * 16 * NT);
   const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((chunk_rscan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3(W * kWave), 0,
+  constexpr int NP = rscan_producers<E, DK, DV, W, NT>();
+  hipLaunchKernelGGL((chunk_rscan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3((W + NP) * kWave), 0,
                      stream, p);
   return hipGetLastError();
 }

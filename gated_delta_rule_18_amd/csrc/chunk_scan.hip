@@ -54,12 +54,12 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
-// Producer waves. In the bf16 forward modes two more waves per workgroup, on the two SIMDs the
-// scan waves leave idle, issue all direct-to-LDS loads; the scan waves then spend no issue
-// cycles on them (about a fifth of a chunk's step when they issued them themselves).
+// Producer waves. For bf16 two more waves per workgroup, on the two SIMDs the scan waves leave
+// idle, issue all direct-to-LDS loads; the scan waves then spend no issue cycles on them (about
+// a fifth of a chunk's step when they issued them themselves).
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_producers() {
-  return (is_bf16<E>() && MODE != kScanRec && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2 : 0;
+  return (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2 : 0;
 }
 
 // MODE kScanRec (backward recompute): no outputs; instead every chunk's entering state S and its

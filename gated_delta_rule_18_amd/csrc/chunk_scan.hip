@@ -41,7 +41,8 @@
 // read). All are row-major without padding, their 16-byte chunks XOR-swizzled by row so that
 // these reads are free of bank conflicts.
 // They arrive by direct-to-LDS buffer loads (no registers), a chunk ahead, into a ring of LDS
-// buffers: one workgroup barrier per chunk. Every global access goes through a buffer resource
+// buffers: one workgroup barrier per chunk. For bf16 the loads are issued by two producer waves
+// of the workgroup, fp32 scan waves issue their own. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
 #include <cstdlib>

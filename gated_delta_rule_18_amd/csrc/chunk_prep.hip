@@ -29,7 +29,11 @@ namespace {
 template <typename E, int DK>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(E);
-  static constexpr int LDK = DK + PAD;
+  // bf16, d_k = 128: K rows unpadded, their 16-byte chunks XOR-swizzled by row (chunk ^ row % 16)
+  // so that the fragment writes and reads (16 rows x 4 chunks per instruction) are free of bank
+  // conflicts; otherwise rows padded by 16 bytes.
+  static constexpr bool KSW = is_bf16<E>() && DK == 128;
+  static constexpr int LDK = KSW ? DK : DK + PAD;
   static constexpr int LDP = kChunk + PAD;
   static constexpr int LDF = kChunk + 4;
   union {
@@ -64,6 +68,14 @@ struct Frag {
         v[i] = valid ? base[r * ld + i * 4 + kq] : 0.f;
       }
     }
+  }
+  // bf16 rows of K 16-byte chunks each, chunk cc of row r stored at cc ^ (r % 16) (16 rows from
+  // base, whose row index is a multiple of 16).
+  __device__ __forceinline__ void load_swz(const E* base, int lane) {
+    static_assert(is_bf16<E>(), "bf16 only");
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const bf16x8*>(base + r * K + 8 * ((4 * i + kq) ^ r));
   }
 };
 
@@ -234,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
 #pragma unroll
       for (int i = 0; i < Frag<E, DK>::N; ++i) {
         if constexpr (BF) {
-          *reinterpret_cast<bf16x8*>(&sm.Ks[row][i * 32 + 8 * kq]) = a.v[i];
+          const int cc = Sm::KSW ? (4 * i + kq) ^ (row & 15) : 4 * i + kq;
+          *reinterpret_cast<bf16x8*>(&sm.Ks[row][8 * cc]) = a.v[i];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = to_f32(a.v[i][e]);
@@ -262,7 +275,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
       acc[0][tj] = acc[1][tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
       if (tj > ti1) continue;
       Frag<E, DK> bk;
-      bk.load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
+      if constexpr (Sm::KSW)
+        bk.load_swz(&sm.Ks[tj * 16][0], lane);
+      else
+        bk.load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
       if (tj <= ti0) mma_frag(acc[0][tj], a0, bk);
       mma_frag(acc[1][tj], a1, bk);
     }

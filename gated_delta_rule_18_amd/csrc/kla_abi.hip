@@ -1,5 +1,6 @@
 // C ABI of the KLA library: argument checks, then stream-ordered launches.
 // Declarations and the contract of every entry point: include/kla.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -151,9 +152,10 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
     return KLA_OK;
   }
   if (B * H * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
-  // The kernels address one batch's rows of q/k/v/o, and one head's workspace, with 32-bit
-  // byte offsets (up to one chunk past T).
-  if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4) >= (int64_t(1) << 31))
+  // The kernels address one batch's rows of q/k/v/o (and, with kda, of the fp32 log a), and one
+  // head's workspace, with 32-bit byte offsets (up to one chunk past T).
+  const int64_t row_bytes = std::max((d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4), kda ? d_k * 4 : int64_t(0));
+  if ((T + kla::kChunk) * H * row_bytes >= (int64_t(1) << 31))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
   if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && (!beta_given || kda)) || !o))
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);

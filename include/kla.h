@@ -174,7 +174,9 @@ size_t kla_kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t
  *              ("Kaczmarz Linear Attention", Abstract) when beta_given = 0, else beta itself
  *              (eps is then ignored).
  *   Everything else (layouts, T, state_in/state_out aliasing, workspace, errors) as for
- *   kla_chunk_fwd. One pass over the chunks (no segment plan).
+ *   kla_chunk_fwd, with the size limit also applied to log a's rows:
+ *   (T + 64) * H * max(d_k, d_v) * element size and (T + 64) * H * d_k * 4 both below 2^31,
+ *   else KLA_ERR_NOT_SUPPORTED. One pass over the chunks (no segment plan).
  */
 kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v,
                                const float* eta, const float* log_a,

@@ -279,6 +279,7 @@ def kda_chunk(dk=128, dv=128, chunk_len=64, eps=1e-6, beta_given=0, dt=K.KLA_BF1
     (dict(ws=0), K.KLA_ERR_INVALID_VALUE),
     (dict(ws_bytes=4096), K.KLA_ERR_INVALID_VALUE),
     (dict(eps=-1.0), K.KLA_ERR_INVALID_VALUE),
+    (dict(T=300000, H=16), K.KLA_ERR_NOT_SUPPORTED),           # fp32 log a of one batch entry past 2 GiB
 ])
 def test_kda_chunk_fwd_rejects(kw, status):
     assert kda_chunk(**kw) == status

@@ -86,8 +86,10 @@ struct Workspace {
 // to the backward workspace, no outputs); the first pass of the segment scan (below).
 enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3 };
 
-// State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four).
-__host__ __device__ constexpr int scan_cols(bool bf16) { return bf16 ? 32 : 64; }
+// State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four). The bf16
+// segment scan uses four waves (64 columns): with half the workgroups per segment, twice the
+// segments fit the compute units.
+__host__ __device__ constexpr int scan_cols(bool bf16, bool seg = false) { return bf16 && !seg ? 32 : 64; }
 
 // Segment scan of the forward, for few heads and long sequences (where one workgroup per head
 // and column slice leaves most compute units idle). The chunks of a head are cut into nseg

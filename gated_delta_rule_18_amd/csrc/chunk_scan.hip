@@ -495,7 +495,7 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   constexpr int DVS = W * 16 * NT;
-  static_assert(DVS == scan_cols(is_bf16<E>()), "column split as planned");
+  static_assert(DVS == scan_cols(is_bf16<E>(), MODE == kScanSeg), "column split as planned");
   constexpr int NSA = DV / DVS + (MODE == kScanSeg ? DK / DVS : 0);
   const int64_t units = p.heads * (MODE == kScanSeg ? p.nseg : 1);  // (head, segment) pairs
   const int64_t units8 = (units + kXcds - 1) / kXcds * kXcds;
@@ -511,7 +511,8 @@ hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
   // head). This split measured fastest: a wave's time per chunk is set by latency, not by
   // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
   // need a single LDS buffer, whose load is not overlapped, so more columns share it).
-  if constexpr (is_bf16<E>())
+  // The segment scan's first pass uses four waves for bf16 too (scan_cols).
+  if constexpr (is_bf16<E>() && MODE != kScanSeg)
     return launch_wnt<E, DK, DV, 2, 1, MODE>(p, stream);
   else
     return launch_wnt<E, DK, DV, 4, 1, MODE>(p, stream);
@@ -538,9 +539,10 @@ hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v,
 // scan's workgroups (heads x column slices) fill the 256 compute units; else enough segments
 // for one workgroup per compute unit over both column kinds, at least eight chunks each. (One
 // scan workgroup fills a compute unit's LDS, and the output correction grows with the number
-// of segments: on B1 H16 T65536, 2 segments measured 1.29 ms, 4 1.32 ms, 8 1.37 ms, against
-// 1.90 ms unsegmented.) KLA_FWD_SEGMENTS, when set, fixes the number of segments (a tuning
-// and testing override).
+// of segments: on B1 H16 T65536 with two-wave segment workgroups, 2 segments measured 1.29 ms,
+// 4 1.32 ms, 8 1.37 ms, against 1.90 ms unsegmented; with the four-wave bf16 segment workgroups
+// the plan gives 4 segments in 224 workgroups, 0.89 ms against 1.14 ms for 2 two-wave ones.)
+// KLA_FWD_SEGMENTS, when set, fixes the number of segments (a tuning and testing override).
 SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool bf16_io) {
   if (nchunks < 2) return SegPlan{1, nchunks};
   const int64_t cols = scan_cols(bf16_io);
@@ -549,7 +551,8 @@ SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool 
   if (const char* env = std::getenv("KLA_FWD_SEGMENTS")) {
     nseg = std::atoll(env);
   } else if (units8 * (d_v / cols) < 256 && nchunks >= 32) {
-    const int64_t per = heads * ((d_v + d_k) / cols);  // workgroups per segment
+    const int64_t scols = scan_cols(bf16_io, true);
+    const int64_t per = heads * ((d_v + d_k) / scols);  // workgroups per segment
     nseg = (256 + per - 1) / per;
     if (nseg > nchunks / 8) nseg = nchunks / 8;
   }

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(ChunkParams p) {
 // One workgroup per run of up to kFixChunks chunks of one segment; wave w takes token tile w of
 // every chunk. The outputs are computed transposed, o^T = S_j^T Y^T, so that each lane holds four
 // consecutive d_v entries of a token; S_j^T (the combine's transposed copy) sits in LDS.
-constexpr int kFixChunks = 16;
+// Eight chunks per workgroup: more workgroups in flight than with 16 (the pass is bound by
+// memory latency, 46 % of HBM bandwidth at 16), for one more 32 KiB read of S_j^T per 8 chunks.
+constexpr int kFixChunks = 8;
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void seg_fix_kernel(ChunkParams p) {

@@ -134,7 +134,7 @@ __device__ __forceinline__ void t_column(Sm& sm, int lane) {
 // P, T and factor rows to the workspace.
 // Called by all threads of the workgroup once A (sm.Af, fp32, zero on and above the diagonal),
 // P (sm.Ps) and the factor rows (sm.sc) are in LDS and published by a barrier.
-template <typename E, typename Sm>
+template <typename E, int NTH = kThreads, typename Sm>
 __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;
@@ -159,7 +159,7 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
     const int t = tid - kWave;  // 0 .. 191
     constexpr int VPR = kChunk / VN;
     E* gP = ws.P + chunk_id * kChunk * kChunk;
-    for (int i = t; i < kChunk * VPR; i += kThreads - kWave) {
+    for (int i = t; i < kChunk * VPR; i += NTH - kWave) {
       const int r = i / VPR, c0 = (i % VPR) * VN;
       V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
       if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
@@ -169,7 +169,7 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
       *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
     }
     float* gS = ws.SC + chunk_id * kScRows * kChunk;
-    for (int i = t; i < kScRows * kChunk; i += kThreads - kWave) gS[i] = (&sm.sc[0][0])[i];
+    for (int i = t; i < kScRows * kChunk; i += NTH - kWave) gS[i] = (&sm.sc[0][0])[i];
   }
   __syncthreads();
 
@@ -185,7 +185,7 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
   {
     constexpr int VPR = kChunk / VN;
     E* gT = ws.T + chunk_id * kChunk * kChunk;
-    for (int i = tid; i < kChunk * VPR; i += kThreads) {
+    for (int i = tid; i < kChunk * VPR; i += NTH) {
       const int r = i / VPR, c0 = (i % VPR) * VN;
       V16 out;
       const int bi = r >> 4, bj = c0 >> 4;
@@ -373,6 +373,10 @@ __device__ __forceinline__ float dpp_row16_sum(float x) {
   return x;
 }
 
+// Eight waves per KDA workgroup: its LDS (about 136 KiB) holds one workgroup per CU, so the
+// waves of the one chunk cover all four SIMDs twice.
+constexpr int kKdaThreads = 512;
+
 template <typename E, int DK>
 struct PrepKdaSmem {
   static constexpr int PAD = 16 / sizeof(E);
@@ -385,7 +389,7 @@ struct PrepKdaSmem {
   alignas(16) float Gm[kChunk][LDG];  // log a, then its chunk-local prefix per channel
   // per-token decays a = e^{log a} (bf16 diagonal blocks; fp32 forms the ratios directly)
   alignas(16) float Ad[is_bf16<E>() ? kChunk : 1][LDG];
-  float part[kThreads / DK][DK];      // prefix-scan partial totals
+  float part[kKdaThreads / DK][DK];   // prefix-scan partial totals
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
   alignas(16) float Tx[6][16][20];  // T's lower off-diagonal blocks (tx_block)
@@ -394,7 +398,8 @@ struct PrepKdaSmem {
 };
 
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams p) {
+  constexpr int NTH = kKdaThreads, NW = NTH / kWave;
   constexpr bool BF = is_bf16<E>();
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
   // ---- K, Q rows, log a and eta of the chunk into LDS: every load issued first, through
   //      buffer resources over this batch entry's rows (rows past T read as zero) ----
   {
-    constexpr int CPR = DK / VN, NKQ = kChunk * CPR / kThreads, NL = kChunk * DK / 4 / kThreads;
+    constexpr int CPR = DK / VN, NKQ = kChunk * CPR / NTH, NL = kChunk * DK / 4 / NTH;
     const int64_t brow = bb * T * p.H;
     const uint32_t xrow = p.H * DK * sizeof(E), lrow = p.H * DK * 4;  // bytes per token
     const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
@@ -423,26 +428,26 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
     i32x4 kx[NKQ], qx[NKQ], lx[NL];
 #pragma unroll
     for (int j = 0; j < NKQ; ++j) {
-      const int i = tid + kThreads * j, r = i / CPR, c0 = (i % CPR) * VN;
+      const int i = tid + NTH * j, r = i / CPR, c0 = (i % CPR) * VN;
       const uint32_t off = (uint32_t)((t0 + r) * xrow + (hh * DK + c0) * sizeof(E));
       kx[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
       qx[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int i = tid + kThreads * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      const int i = tid + NTH * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
       lx[j] = __builtin_amdgcn_raw_buffer_load_b128(rl, (uint32_t)((t0 + r) * lrow + (hh * DK + c4) * 4), 0, 0);
     }
     const float et = tid < kChunk && t0 + tid < T ? p.eta[row_index(t0 + tid)] : 0.f;
 #pragma unroll
     for (int j = 0; j < NKQ; ++j) {
-      const int i = tid + kThreads * j, r = i / CPR, c0 = (i % CPR) * VN;
+      const int i = tid + NTH * j, r = i / CPR, c0 = (i % CPR) * VN;
       *reinterpret_cast<i32x4*>(&sm.Ks[r][c0]) = kx[j];
       *reinterpret_cast<i32x4*>(&sm.Qs[r][c0]) = qx[j];
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int i = tid + kThreads * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      const int i = tid + NTH * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
       *reinterpret_cast<i32x4*>(&sm.Gm[r][c4]) = lx[j];
     }
     if (tid < kChunk) sm.eta[tid] = et;
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
 
   // ---- per-channel prefix of log a over the chunk's tokens: NPART threads per channel, each a
   //      run of tokens in registers, then the runs' totals; the per-token decays e^{log a} ----
-  constexpr int NPART = kThreads / DK, RUN = kChunk / NPART;
+  constexpr int NPART = NTH / DK, RUN = kChunk / NPART;
   const int ch = tid % DK, part = tid / DK;
   float run[RUN];
 #pragma unroll
@@ -509,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
     E* k1 = kw.K1 + chunk_id * kChunk * DK;
     E* q1 = kw.Q1 + chunk_id * kChunk * DK;
     E* k2 = kw.K2 + chunk_id * kChunk * DK;
-    for (int i = tid; i < kChunk * CPR; i += kThreads) {
+    for (int i = tid; i < kChunk * CPR; i += NTH) {
       const int r = i / CPR, c0 = (i % CPR) * VN;
       const V16 kx = *reinterpret_cast<const V16*>(&sm.Ks[r][c0]);
       const V16 qx = *reinterpret_cast<const V16*>(&sm.Qs[r][c0]);
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
   __syncthreads();
 
   // ---- off-diagonal 16 x 16 blocks (I, J), J < I: MFMA on operands decayed to b = 16 I ----
-  for (int t = wave; t < 6; t += 4) {
+  for (int t = wave; t < 6; t += NW) {
     const int I = t >= 3 ? 3 : t >= 1 ? 2 : 1, J = t - (I * (I - 1)) / 2, b = 16 * I;
     const int ra = 16 * I + lr, rb = 16 * J + lr;  // this lane's A row and B row
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
@@ -580,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
     constexpr int CS = DK / 16;  // channels per slice: 8 or 4
     typedef typename std::conditional<CS == 8, bf16x8, bf16x4>::type KV;
     const int sl = tid & 15, pair = (tid >> 4) & 7, hb = tid >> 7, c0 = CS * sl;
-    static_assert(kThreads == 256, "two blocks of eight row pairs of sixteen slices");
-    for (int I = hb; I < 4; I += 2) {
+    static_assert(NTH % 128 == 0 && NTH <= 512, "blocks of eight row pairs of sixteen slices");
+    for (int I = hb; I < 4; I += NTH / 128) {
       const int b = 16 * I;
       int r = 15 - pair, s = r;
       float kr[CS], qr[CS], w[CS];
@@ -635,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
       }
     }
     // the upper triangles of the diagonal blocks
-    for (int i = tid; i < 4 * 256; i += kThreads) {
+    for (int i = tid; i < 4 * 256; i += NTH) {
       const int b = 16 * (i >> 8), rr = (i >> 4) & 15, ss = i & 15;
       if (ss > rr) {
         sm.Af[b + rr][b + ss] = 0.f;
@@ -643,8 +648,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
       }
     }
   } else {  // one thread per (r, s), summed per channel
-    const int rr = tid >> 4, ss = tid & 15;
-    for (int I = 0; I < 4; ++I) {
+    const int rr = (tid >> 4) & 15, ss = tid & 15;
+    static_assert(NTH % 256 == 0, "whole blocks of 16 x 16 threads");
+    for (int I = tid >> 8; I < 4; I += NTH / 256) {
       const int r = 16 * I + rr, s = 16 * I + ss;
       float a = 0.f, pq = 0.f;
       if (s <= r) {
@@ -665,16 +671,16 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda_kernel(ChunkParams p)
   }
   __syncthreads();
 
-  solve_and_store<E>(sm, ws, chunk_id);
+  solve_and_store<E, NTH>(sm, ws, chunk_id);
 }
 
 template <typename E>
 hipError_t launch_kda_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
   const int64_t grid = p.heads * p.nchunks;
   if (d_k == 128)
-    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)grid), dim3(kKdaThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)grid), dim3(kKdaThreads), 0, stream, p);
   return hipGetLastError();
 }
 

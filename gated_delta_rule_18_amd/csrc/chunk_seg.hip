@@ -168,16 +168,17 @@ __global__ __launch_bounds__(kThreads) void seg_fix_kernel(ChunkParams p) {
       }
     }
   };
-  GV yb[2][NGD];
-  f32x4 acc[2][NJT];
+  GV yb[3][NGD];
+  f32x4 acc[3][NJT];
   load(c0, yb[0], acc[0]);
-  // two chunks per iteration, the next chunk's loads in flight while this one is computed
-  for (int64_t c = c0; c < c1; c += 2) {
+  if (c0 + 1 < c1) load(c0 + 1, yb[1], acc[1]);
+  // three chunks per iteration, the next two chunks' loads in flight while one is computed
+  for (int64_t c = c0; c < c1; c += 3) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 3; ++h) {
       const int64_t cc = c + h;
       if (cc >= c1) break;
-      if (cc + 1 < c1) load(cc + 1, yb[h ^ 1], acc[h ^ 1]);
+      if (cc + 2 < c1) load(cc + 2, yb[(h + 2) % 3], acc[(h + 2) % 3]);
       const int64_t row = cc * kChunk + 16 * rt + c16;
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {

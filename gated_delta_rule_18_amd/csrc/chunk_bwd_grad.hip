@@ -61,6 +61,13 @@ constexpr bool grad_fits() {
   return sizeof(GradSmem<E, DK, DV>) <= 160 * 1024;
 }
 
+// One workgroup per CU by its LDS footprint: the kernel then runs persistently and loads the
+// next chunk's register operands during the current chunk.
+template <typename E, int DK, int DV>
+constexpr bool grad_prefetch() {
+  return 2 * sizeof(GradSmem<E, DK, DV>) > 160 * 1024;
+}
+
 // Elements 4h .. 4h + 3 of eight bf16.
 __device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
   return h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
@@ -102,14 +109,56 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   typedef GradSmem<E, DK, DV> Sm;
   __shared__ Sm sm;
 
-  const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
+  const int tid0 = threadIdx.x;
+  const int64_t T = p.T, H = p.H, total = p.heads * p.nchunks;
+  const Workspace<E> ws = Workspace<E>::at(p.ws, total);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, total, DK, DV);
+
+  // Where the LDS footprint leaves one workgroup per CU, nothing else hides a chunk's load
+  // latency: the kernel is persistent (workgroup b works on chunks b, b + gridDim.x, ...; chunk
+  // id = head * nchunks + c) and the register-borne operands of the next chunk go into the
+  // registers of the current one as soon as those are spent: Delta and Zb once they sit in LDS,
+  // S and dS' once both have been put into LDS. With two or more workgroups per CU they overlap
+  // each other instead, the extra live registers would cost that occupancy, and each workgroup
+  // takes one chunk.
+  constexpr bool PF = grad_prefetch<E, DK, DV>();
+  constexpr int NSR = DK * DV / PER / NT_;      // 16-byte pieces of S (and of dS') per thread
+  constexpr int NCH = kChunk * DV / PER / NT_;  // 16-byte pieces of Delta (and of Zb) per thread
+  V16 sreg[NSR], dsreg[NSR], dlreg[NCH], zbreg[NCH];
+  auto load_state = [&](int64_t id) __attribute__((always_inline)) {
+    const E* gS = bw.Sn + id * DK * DV;
+    const E* gdS = bw.dSn + id * DK * DV;
+#pragma unroll
+    for (int i = 0; i < NSR; ++i) {
+      sreg[i] = *reinterpret_cast<const V16*>(gS + (tid0 + NT_ * i) * PER);
+      dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid0 + NT_ * i) * PER);
+    }
+  };
+  auto load_t64 = [&](int64_t id) __attribute__((always_inline)) {
+    const E* gD = bw.Dl + id * kChunk * DV;
+    const E* gZ = bw.Zb + id * kChunk * DV;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      dlreg[i] = *reinterpret_cast<const V16*>(gD + (tid0 + NT_ * i) * PER);
+      zbreg[i] = *reinterpret_cast<const V16*>(gZ + (tid0 + NT_ * i) * PER);
+    }
+  };
+  if ((int64_t)blockIdx.x >= total) return;
+  if constexpr (PF) {
+    load_state(blockIdx.x);
+    load_t64(blockIdx.x);
+  }
+  for (int64_t chunk_id = blockIdx.x; chunk_id < total; chunk_id += gridDim.x) {
+  // Per-thread index arithmetic is redone every chunk rather than kept live across the loop.
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t nid = chunk_id + gridDim.x;
+  const bool more = nid < total;
   const int64_t head = chunk_id / p.nchunks, c = chunk_id % p.nchunks;
   const int64_t bb = head / p.H, hh = head % p.H;
-  const int64_t T = p.T, H = p.H;
   const int64_t t0 = c * kChunk;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, g = lane >> 4;
 
   const int64_t brow = bb * T * H;
   const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);
@@ -122,21 +171,10 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   const rsrc_t rdv = make_rsrc(static_cast<E*>(p.dv) + brow * DV, (uint32_t)(T * vrow));
   const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = hh * DV * sizeof(E);
   const uint32_t x0 = (uint32_t)t0 * xrow, v0 = (uint32_t)t0 * vrow;
-  const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
-  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * p.nchunks, DK, DV);
 
-  // ---- every load of the chunk is issued up front: S and dS' into registers (they are
-  //      needed last), the row-major operands straight into LDS, Delta and Zb through
-  //      registers (transposed on the way into LDS) ----
-  constexpr int NSR = DK * DV / PER / NT_;
-  const E* gS = bw.Sn + chunk_id * DK * DV;
-  const E* gdS = bw.dSn + chunk_id * DK * DV;
-  V16 sreg[NSR], dsreg[NSR];
-#pragma unroll
-  for (int i = 0; i < NSR; ++i) {
-    sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + NT_ * i) * PER);
-    dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + NT_ * i) * PER);
-  }
+  // ---- the row-major operands straight into LDS; Delta and Zb from registers (transposed on
+  //      the way into LDS); S and dS' stay in registers until they are needed ----
+  if constexpr (!PF) load_state(chunk_id);
   auto dma_rows = [&](rsrc_t r, E* dst, uint32_t base, uint32_t rowb, uint32_t hcol, auto ncol_tag) {
     constexpr int NCOL = decltype(ncol_tag)::value;
     constexpr int CPR = NCOL / PER, NBLK = kChunk * CPR / 64;
@@ -154,11 +192,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
 
   // tile-ordered [64 x DV] blocks, transposed into LDS: lane piece (rows 4g..4g+3 of column c of
   // tile (rt, ct)) -> row 16 ct + c, columns 16 rt + 4g .. + 3
-  auto load_t64 = [&](const E* src, E* dst) {
-    constexpr int NCH = kChunk * DV / PER / NT_;  // 16-byte chunks per thread
-    V16 x[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) x[i] = *reinterpret_cast<const V16*>(src + (tid + NT_ * i) * PER);
+  auto put_t64 = [&](const V16* x, E* dst) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ci = tid + NT_ * i;
@@ -175,8 +209,9 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
       }
     }
   };
-  load_t64(bw.Dl + chunk_id * kChunk * DV, sm.Dt);
-  load_t64(bw.Zb + chunk_id * kChunk * DV, sm.Zt);
+  if constexpr (!PF) load_t64(chunk_id);
+  put_t64(dlreg, sm.Dt);
+  put_t64(zbreg, sm.Zt);
 
   // per-token factors; the chunk-local decay prefix G as the forward forms it
   if (wave == 0) {
@@ -204,6 +239,8 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   }
   wait_vmem<0>();
   __syncthreads();
+  // Issued after the barrier: with no load to LDS outstanding, the reads below need no wait.
+  if (PF && more) load_t64(nid);
 
   // ---- C x C tiles: K K^T, Q K^T, Zb Delta^T, dO Delta^T -> Ma, Mp and the decay sums;
   //      on diagonal tiles also Zb V^T, whose diagonal is Zb_r . v_r ----
@@ -318,6 +355,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   }
   __syncthreads();
   put_state(dsreg);
+  if (PF && more) load_state(nid);
   __syncthreads();
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -425,13 +463,27 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
     store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
   }
+  __syncthreads();  // the next chunk overwrites every LDS operand
+  if constexpr (!PF) break;
+  }  // chunk loop
 }
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkBwdParams& p, hipStream_t stream) {
   if constexpr (grad_fits<E, DK, DV>()) {
-    hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)(p.heads * p.nchunks)), dim3(kGradThreads),
-                       0, stream, p);
+    static const int64_t resident = [] {
+      int dev = 0, cus = 0, per = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, chunk_grad_kernel<E, DK, DV>, kGradThreads, 0) !=
+              hipSuccess ||
+          cus <= 0 || per <= 0)
+        return (int64_t)256;
+      return (int64_t)cus * per;
+    }();
+    const int64_t total = p.heads * p.nchunks;
+    const int64_t grid = grad_prefetch<E, DK, DV>() && resident < total ? resident : total;
+    hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)grid), dim3(kGradThreads), 0, stream, p);
     return hipGetLastError();
   } else {
     return hipErrorInvalidConfiguration;

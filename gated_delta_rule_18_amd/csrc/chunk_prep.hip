@@ -268,7 +268,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
   // ---- A from K K^T (waves 0, 1) and P from Q K^T (waves 2, 3): the lower 16 x 16 tiles of
   //      this wave's two row tiles (five tiles per wave) ----
   {
-    // All products first (one B tile of K in registers at a time), then the scaled entries.
+    // All products first (one tile of K in registers at a time), then the scaled entries. The
+    // products are formed transposed (K's rows as the A operand): lane (c, g) holds entries
+    // [16 ti + c][16 tj + 4 g + e], four consecutive columns of one row, written as one vector.
     f32x4 acc[2][4];
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
@@ -279,8 +281,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
         bk.load_swz(&sm.Ks[tj * 16][0], lane);
       else
         bk.load(&sm.Ks[tj * 16][0], Sm::LDK, lane);
-      if (tj <= ti0) mma_frag(acc[0][tj], a0, bk);
-      mma_frag(acc[1][tj], a1, bk);
+      if (tj <= ti0) mma_frag(acc[0][tj], bk, a0);
+      mma_frag(acc[1][tj], bk, a1);
     }
     // ---- per-token factors (wave 0, after its products; the other waves' products overlap) ----
     if (wave == 0) {
@@ -312,37 +314,32 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
       sm.sc[kScD2][r] = rs * __expf(GC - G);
     }
     __syncthreads();  // factors in LDS; K no longer read: P may now overwrite it
-    // Per-token values of the columns (all tiles) and of this lane's rows.
-    float Gs[4], rss[4];
-#pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      Gs[tj] = sm.G[tj * 16 + lr];
-      rss[tj] = sm.sc[kScRs][tj * 16 + lr];
-    }
-    f32x4 Gr[2], cr[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * (half ? ti1 : ti0) + 4 * lq + e;
-        Gr[half][e] = sm.G[r];
-        cr[half][e] = sm.eta[r] * sm.sc[kScRs][r];
-      }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int ti = half ? ti1 : ti0;
+      const int r = ti * 16 + lr;  // this lane's row
+      const float Gr = sm.G[r], cr = sm.eta[r] * sm.sc[kScRs][r];
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
         if (tj > ti) continue;
-        const int s = tj * 16 + lr;
+        const int s0 = tj * 16 + 4 * lq;  // this lane's first column
+        const f32x4 Gs = *reinterpret_cast<const f32x4*>(&sm.G[s0]);
+        f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = ti * 16 + 4 * lq + e;
-          const float dec = __expf(Gr[half][e] - Gs[tj]);
-          if (qwave)
-            sm.Ps[r][s] = from_f32<E>(s <= r ? dec * acc[half][tj][e] : 0.f);
-          else
-            sm.Af[r][s] = s < r ? cr[half][e] * rss[tj] * dec * acc[half][tj][e] : 0.f;
+          const float dec = __expf(Gr - Gs[e]) * acc[half][tj][e];
+          x[e] = qwave ? (s0 + e <= r ? dec : 0.f) : (s0 + e < r ? dec : 0.f);
+        }
+        if (qwave) {
+          if constexpr (BF) {
+            const bf16x4 b = {from_f32<bf16>(x[0]), from_f32<bf16>(x[1]), from_f32<bf16>(x[2]), from_f32<bf16>(x[3])};
+            *reinterpret_cast<bf16x4*>(&sm.Ps[r][s0]) = b;
+          } else {
+            *reinterpret_cast<f32x4*>(&sm.Ps[r][s0]) = x;
+          }
+        } else {
+          const f32x4 rss = *reinterpret_cast<const f32x4*>(&sm.sc[kScRs][s0]);
+          *reinterpret_cast<f32x4*>(&sm.Af[r][s0]) = cr * rss * x;
         }
       }
     }

@@ -118,6 +118,20 @@ def test_chunk_bwd_b8h8_t4096_sampled_heads():
         compare(f"chunk_bwd b8h8_t4096 head {hd[0]}", w, got, oracle_bwd(w, inp, g, hd), hd)
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
+def test_chunk_bwd_partial_last_round(dtype, dk):
+    """More chunks (5 heads x 62) than the gradient kernel keeps resident, and not a multiple of
+    them: with one workgroup per CU (these head sizes) each workgroup walks several chunks and
+    the last round is partial. The oracle on the first head and on the last one, whose chunks
+    fall in that round."""
+    w = wl.custom("bwd_rounds", 313, B=1, H=5, dk=dk, dv=dk, T=64 * 61 + 17, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    g = wl.grad_inputs(w, s0_std=0.05, dst_std=1.0)
+    got = gpu_bwd(w, inp, g)
+    for hd in ([(0, 0)], [(0, 4)]):
+        compare(f"chunk_bwd {dtype} d{dk} rounds head {hd[0]}", w, got, oracle_bwd(w, inp, g, hd), hd)
+
+
 def test_chunk_bwd_mixed_gates_extremes():
     """The mixed workload's gates (eta = sigmoid(N(0, 2)), log alpha in [-0.2, 0]) over a
     few chunks."""

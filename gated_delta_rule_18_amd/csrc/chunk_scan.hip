@@ -55,12 +55,22 @@ hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hi
 
 namespace {
 
-// Producer waves. For bf16 two more waves per workgroup, on the two SIMDs the scan waves leave
+// Producer waves. For bf16, more waves per workgroup, on the two SIMDs the scan waves leave
 // idle, issue all direct-to-LDS loads; the scan waves then spend no issue cycles on them (about
-// a fifth of a chunk's step when they issued them themselves).
+// a fifth of a chunk's step when they issued them themselves). The one-pass bf16 forward loads
+// two chunks ahead into three buffers where they fit, with four producers: a chunk's loads take
+// about a step to issue and as long again to arrive, and each wave can have at most 63 memory
+// operations outstanding (two chunks of loads are 2 x 27 for two producers, 2 x 14 for four).
+// Elsewhere two producers load one chunk ahead.
+template <typename E, int DK, int DV, int W, int NT, int MODE>
+constexpr bool scan_deep() {
+  return is_bf16<E>() && MODE == kScanFwd && 3 * sizeof(ScanBuf<E, DK, W * 16 * NT, false>) <= 160 * 1024;
+}
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_producers() {
-  return (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2 : 0;
+  return scan_deep<E, DK, DV, W, NT, MODE>() ? 4
+         : (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2
+                                                                                    : 0;
 }
 
 // MODE kScanRec (backward recompute): no outputs; instead every chunk's entering state S and its
@@ -69,9 +79,11 @@ constexpr int scan_producers() {
 // DV / DVS slices of the state, DK / DVS slices of identity columns (chunk_common.h).
 // MODE kScanKda (per-channel decay): K, Q and the update's K2 are the decayed operands of the
 // KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
+// (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
-__global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_scan_kernel(
-    ChunkParams p) {
+__global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>()) * kWave) __attribute__((
+    amdgpu_waves_per_eu(scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1, scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1))) void
+chunk_scan_kernel(ChunkParams p) {
   constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg, KDA = MODE == kScanKda;
   constexpr bool BF = is_bf16<E>();
   // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
@@ -89,7 +101,8 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   constexpr int NGT = kChunk / GK;   // groups over the chunk's tokens
   constexpr int PER = 16 / sizeof(E);
   typedef ScanBuf<E, DK, DVS, KDA> Buf;
-  constexpr int NB = scan_ring<E, DK, DVS, KDA>();  // LDS buffers: chunks c .. c + NB - 1 in flight
+  constexpr bool DEEP = scan_deep<E, DK, DV, W, NT, MODE>();
+  constexpr int NB = DEEP ? 3 : scan_ring<E, DK, DVS, KDA>();  // LDS buffers: chunks c .. c + NB - 1 in flight
   constexpr int DIST = NB > 1 ? NB - 1 : 1;     // prefetch distance
   static_assert(DV % DVS == 0, "shape");
   // Distinct LDS objects (not an array indexed by chunk), so that the compiler can tell the
@@ -217,7 +230,33 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
     if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
 
-  if constexpr (NP > 0) {
+  if constexpr (DEEP) {
+    static_assert(NB == 3 && NP == 4, "four producers serve a three-buffer ring");
+    if (wave >= W) {  // producer: the loads of every chunk, two chunks ahead, one barrier per chunk
+      // Before chunk c's barrier, chunk c's loads are complete and those of chunk c + 1 are
+      // younger (the same count for every chunk: a fetch past the end loads the last chunk again).
+      // This wave writes LDS only by these loads, and the wait is all the barrier needs of them:
+      // a workgroup fence there would make the compiler wait for chunk c + 1's loads as well.
+      auto pstep = [&](Buf& Bt, int64_t c) __attribute__((always_inline)) {
+        wait_vmem<NDMA>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1 (Bt)
+        asm volatile("" ::: "memory");
+        fetch(Bt, c + 2);
+      };
+      if (ce > cb) {
+        fetch(buf0, cb);
+        fetch(buf1, cb + 1);
+      }
+      for (int64_t c = cb; c < ce; c += 3) {
+        pstep(buf2, c);
+        if (c + 1 < ce) pstep(buf0, c + 1);
+        if (c + 2 < ce) pstep(buf1, c + 2);
+      }
+      wait_vmem<0>();  // no load into LDS outlives the workgroup
+      return;
+    }
+  } else if constexpr (NP > 0) {
     static_assert(NB == 2, "producers serve a two-buffer ring");
     if (wave >= W) {  // producer: the loads of every chunk, one chunk ahead, one barrier per chunk
       if (ce > cb) fetch(buf0, cb);
@@ -452,15 +491,15 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  if (NP == 0 && ce > cb) {  // chunks cb .. cb + DIST - 1
-    fetch(buf0, cb);
-    if constexpr (NB == 3) fetch(buf1, cb + 1);
-  }
+  if (NP == 0 && ce > cb) fetch(buf0, cb);  // chunk cb (one chunk ahead)
   if constexpr (NB == 3) {
-    for (int64_t c = cb; c < ce; c += 3) {
-      step(buf0, buf2, c);
-      if (c + 1 < ce) step(buf1, buf0, c + 1);
-      if (c + 2 < ce) step(buf2, buf1, c + 2);
+    // One copy of the step, its buffer chosen per chunk: unrolled three ways (a copy per buffer)
+    // the forward measured 20-25 % slower.
+    int k = 0;
+    for (int64_t c = cb; c < ce; ++c) {
+      Buf& B = k == 0 ? buf0 : k == 1 ? buf1 : buf2;
+      step(B, B, c);  // (the producers load; no next buffer is needed here)
+      k = k == 2 ? 0 : k + 1;
     }
   } else if constexpr (NB == 2) {
     for (int64_t c = cb; c < ce; c += 2) {

@@ -235,9 +235,8 @@ struct ScanBuf {
   alignas(16) float gam[KDA ? 256 : 4];
 };
 
-// Buffers in the ring: two where they fit in 160 KiB of LDS, else one. (A third buffer, for a
-// prefetch distance of two chunks, measured slower: the loads are not the bottleneck once they
-// are a chunk ahead, and the three-way unrolled loop costs registers.)
+// Buffers in the ring: two where they fit in 160 KiB of LDS, else one. (The one-pass bf16
+// forward scan uses three, with its own producer count; chunk_scan.hip.)
 template <typename E, int DK, int DVS, bool KDA = false>
 constexpr int scan_ring() {
   return 2 * sizeof(ScanBuf<E, DK, DVS, KDA>) <= 160 * 1024 ? 2 : 1;

@@ -574,19 +574,24 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   }
   // ---- diagonal 16 x 16 blocks ----
   if constexpr (BF) {
-    // Thread (block parity, row pair, channel slice): the rows r2 = 15 - pair and then
-    // r1 = pair of a diagonal block, each summed against s = r, r - 1, .., 0 while the ratio
+    // Thread (block, row pair, channel slice): the rows r2 = 15 - pair and then r1 = pair of a
+    // diagonal block, each summed against s = r, r - 1, .., 0 while the ratio
     // w = prod_{j = s+1..r} a_j is carried down by one multiply per channel (w *= a_s). Every row
     // pair takes 17 steps, so no lane idles on the upper triangle; the 16 channel slices of a row
-    // share a DPP row and are summed there.
+    // share a DPP row and are summed there. Everything a step reads from LDS (the K row, the
+    // decays, the column's factor) is read a step ahead, and the rows' factors before the walk,
+    // so that no step waits on LDS.
     constexpr int CS = DK / 16;  // channels per slice: 8 or 4
     typedef typename std::conditional<CS == 8, bf16x8, bf16x4>::type KV;
     const int sl = tid & 15, pair = (tid >> 4) & 7, hb = tid >> 7, c0 = CS * sl;
     static_assert(NTH % 128 == 0 && NTH <= 512, "blocks of eight row pairs of sixteen slices");
     for (int I = hb; I < 4; I += NTH / 128) {
-      const int b = 16 * I;
-      int r = 15 - pair, s = r;
-      float kr[CS], qr[CS], w[CS];
+      const int b = 16 * I, r2 = 15 - pair;
+      // the rows' factors eta_R rs_R
+      const float f2 = sm.eta[b + r2] * sm.sc[kScRs][b + r2], f1 = sm.eta[b + pair] * sm.sc[kScRs][b + pair];
+      int r = r2, s = r;
+      float fr = f2;
+      float kr[CS], qr[CS], w[CS], ad[CS];
       auto row_start = [&]() __attribute__((always_inline)) {
         const KV kx = *reinterpret_cast<const KV*>(&sm.Ks[b + r][c0]);
         const KV qx = *reinterpret_cast<const KV*>(&sm.Qs[b + r][c0]);
@@ -597,20 +602,26 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
           w[c] = 1.f;
         }
       };
+      auto read_ad = [&](int sr, float* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CS; c += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[b + sr][c0 + c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[c + e] = x[e];
+        }
+      };
       row_start();
       KV ks = *reinterpret_cast<const KV*>(&sm.Ks[b + s][c0]);
+      float rsc = sm.sc[kScRs][b + s];
+      read_ad(s, ad);
       for (int it = 0; it < 17; ++it) {
-        // next step's row and column (the pair's second row after s = 0), its K row read early
+        // next step's row and column (the pair's second row after s = 0), read early
         const bool sw = s == 0;
         const int s_n = sw ? pair : s - 1;
         const KV ks_n = *reinterpret_cast<const KV*>(&sm.Ks[b + s_n][c0]);
-        float ad[CS];
-#pragma unroll
-        for (int c = 0; c < CS; c += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[b + s][c0 + c]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ad[c + e] = x[e];
-        }
+        const float rsc_n = sm.sc[kScRs][b + s_n];
+        float ad_n[CS];
+        read_ad(s_n, ad_n);
         float a = 0.f, pq = 0.f;
 #pragma unroll
         for (int c = 0; c < CS; ++c) {
@@ -622,11 +633,12 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
         pq = dpp_row16_sum(pq);
         if (sl == 0) {
           const int R = b + r, Sc = b + s;
-          sm.Af[R][Sc] = s < r ? sm.eta[R] * sm.sc[kScRs][R] * sm.sc[kScRs][Sc] * a : 0.f;
+          sm.Af[R][Sc] = s < r ? fr * rsc * a : 0.f;
           sm.Ps[R][Sc] = from_f32<E>(pq);
         }
         if (sw) {  // the row pair's second row
           r = pair;
+          fr = f1;
           row_start();
         } else {  // w for s - 1: times a_s
 #pragma unroll
@@ -634,6 +646,9 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
         }
         s = s_n;
         ks = ks_n;
+        rsc = rsc_n;
+#pragma unroll
+        for (int c = 0; c < CS; ++c) ad[c] = ad_n[c];
       }
     }
     // the upper triangles of the diagonal blocks

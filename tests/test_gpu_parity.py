@@ -112,8 +112,10 @@ def test_decode_workload_b64h16_1024_steps():
 
 # ----------------------------------------------------------------------------- chunked forward
 
+# T spans 1 to 8 chunks: every count of chunks modulo the scan's ring of operand buffers (three
+# for the bf16 one-pass forward), with full and ragged last chunks.
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T", [1, 15, 63, 64, 65, 250])
+@pytest.mark.parametrize("T", [1, 15, 63, 64, 65, 192, 250, 300, 449])
 def test_chunk_fwd_small_shapes(dtype, T):
     w = wl.custom("fwd", 202 + T, B=2, H=3, dk=128, dv=128, T=T, dtype=dtype)
     check_fwd(f"chunk_fwd {dtype} T={T}", w, wl.prefill_inputs(w), all_heads(w))

@@ -40,9 +40,10 @@
 // for K^T with the transposing read of gfx950, and V as four rows of one column (transposing
 // read). All are row-major without padding, their 16-byte chunks XOR-swizzled by row so that
 // these reads are free of bank conflicts.
-// They arrive by direct-to-LDS buffer loads (no registers), a chunk ahead, into a ring of LDS
-// buffers: one workgroup barrier per chunk. For bf16 the loads are issued by two producer waves
-// of the workgroup, fp32 scan waves issue their own. Every global access goes through a buffer resource
+// They arrive by direct-to-LDS buffer loads (no registers) into a ring of LDS buffers, one
+// workgroup barrier per chunk: for bf16 issued by producer waves of the workgroup (two chunks
+// ahead by four producers in the one-pass forward, a chunk ahead by two elsewhere), for fp32 a
+// chunk ahead by the scan waves themselves. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
 #include <cstdlib>

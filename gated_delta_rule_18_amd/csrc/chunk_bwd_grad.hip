@@ -244,7 +244,10 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
 
   // ---- C x C tiles: K K^T, Q K^T, Zb Delta^T, dO Delta^T -> Ma, Mp and the decay sums;
   //      on diagonal tiles also Zb V^T, whose diagonal is Zb_r . v_r ----
-  for (int k = wave; k < 10; k += NW) {
+  // Ten tiles on eight waves: waves 0 and 1 take two each, so they get off-diagonal tiles (16
+  // MFMAs; a diagonal tile adds the 4 of Zb V^T). Tile k keeps its slot k in the sums below.
+  for (int j = wave; j < 10; j += NW) {
+    const int k = j == 0 ? 1 : j == 1 ? 3 : j == 2 ? 0 : j == 3 ? 2 : j == 7 ? 9 : j == 8 ? 7 : j == 9 ? 8 : j;
     int ti, tj;
     tri_tile(k, ti, tj);
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, F = kk, dp = kk, zvv = kk;

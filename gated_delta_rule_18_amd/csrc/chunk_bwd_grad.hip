@@ -38,14 +38,20 @@ namespace {
 constexpr int kGradWaves = 8;
 constexpr int kGradThreads = kGradWaves * kWave;
 
+// The row-major operands, loaded straight into LDS: an LDS object of their own, so that the
+// compiler can tell them apart from the rest when the next chunk's loads are in flight.
 template <typename E, int DK, int DV>
-struct GradSmem {
+struct GradOps {
   alignas(16) E Ks[kChunk * DK];
   alignas(16) E Qs[kChunk * DK];
   alignas(16) E dOs[kChunk * DV];
+  alignas(16) E St[DV * DK];      // V ([64][DV]) while the C x C tiles are formed, then S^T, then dS'^T
+};
+
+template <typename E, int DK, int DV>
+struct GradSmem {
   alignas(16) E Dt[DV * kChunk];  // Delta^T
   alignas(16) E Zt[DV * kChunk];  // Zb^T
-  alignas(16) E St[DV * DK];      // V ([64][DV]) while the C x C tiles are formed, then S^T, then dS'^T
   alignas(16) E Ma[kChunk * kChunk];
   alignas(16) E Mp[kChunk * kChunk];
   float G[kChunk], eG[kChunk], cr[kChunk], rs[kChunk], zv[kChunk], kcoef[kChunk];
@@ -58,14 +64,14 @@ struct GradSmem {
 
 template <typename E, int DK, int DV>
 constexpr bool grad_fits() {
-  return sizeof(GradSmem<E, DK, DV>) <= 160 * 1024;
+  return sizeof(GradOps<E, DK, DV>) + sizeof(GradSmem<E, DK, DV>) <= 160 * 1024;
 }
 
 // One workgroup per CU by its LDS footprint: the kernel then runs persistently and loads the
 // next chunk's register operands during the current chunk.
 template <typename E, int DK, int DV>
 constexpr bool grad_prefetch() {
-  return 2 * sizeof(GradSmem<E, DK, DV>) > 160 * 1024;
+  return 2 * (sizeof(GradOps<E, DK, DV>) + sizeof(GradSmem<E, DK, DV>)) > 160 * 1024;
 }
 
 // Elements 4h .. 4h + 3 of eight bf16.
@@ -108,6 +114,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   static_assert(TPW * NW == NIT * 4, "tile split");
   typedef GradSmem<E, DK, DV> Sm;
   __shared__ Sm sm;
+  __shared__ GradOps<E, DK, DV> op;
 
   const int tid0 = threadIdx.x;
   const int64_t T = p.T, H = p.H, total = p.heads * p.nchunks;
@@ -143,10 +150,60 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
       zbreg[i] = *reinterpret_cast<const V16*>(gZ + (tid0 + NT_ * i) * PER);
     }
   };
+  // The row-major operands of chunk id straight into LDS (K, Q, dO, V), and (wave 0) the chunk's
+  // per-token factors into registers.
+  auto dma_rows = [&](rsrc_t r, E* dst, uint32_t base, uint32_t rowb, uint32_t hcol, int wave_, int lane_, auto ncol_tag)
+      __attribute__((always_inline)) {
+    constexpr int NCOL = decltype(ncol_tag)::value;
+    constexpr int CPR = NCOL / PER, NBLK = kChunk * CPR / 64;
+    static_assert(NBLK % NW == 0, "block split");
+#pragma unroll
+    for (int i = 0; i < NBLK / NW; ++i) {
+      const int blk = wave_ + NW * i, ph = 64 * blk + lane_, row = ph / CPR;
+      dma16(r, dst + blk * 64 * PER, base + row * rowb + hcol + 16 * swz<E, CPR>(row, ph % CPR));
+    }
+  };
+  float fla = 0.f, fcr = 0.f, feG = 0.f, frs = 0.f;
+  auto issue_ops = [&](int64_t id, int wave_, int lane_) __attribute__((always_inline)) {
+    const int64_t head = id / p.nchunks, t0 = (id % p.nchunks) * kChunk;
+    const int64_t bb = head / p.H, hh = head % p.H, brow = bb * T * H;
+    const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);
+    const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = hh * DV * sizeof(E);
+    const uint32_t x0 = (uint32_t)t0 * xrow, v0 = (uint32_t)t0 * vrow;
+    dma_rows(make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow)), op.Ks, x0, xrow, hcol_x, wave_,
+             lane_, std::integral_constant<int, DK>());
+    dma_rows(make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow)), op.Qs, x0, xrow, hcol_x, wave_,
+             lane_, std::integral_constant<int, DK>());
+    dma_rows(make_rsrc(static_cast<const E*>(p.dout) + brow * DV, (uint32_t)(T * vrow)), op.dOs, v0, vrow, hcol_v,
+             wave_, lane_, std::integral_constant<int, DV>());
+    dma_rows(make_rsrc(static_cast<const E*>(p.v) + brow * DV, (uint32_t)(T * vrow)), op.St, v0, vrow, hcol_v, wave_,
+             lane_, std::integral_constant<int, DV>());
+    if (wave_ == 0) {
+      const bool valid = t0 + lane_ < T;
+      fla = valid && p.log_alpha ? p.log_alpha[(bb * T + t0 + lane_) * H + hh] : 0.f;
+      const float* sc = ws.SC + id * kScRows * kChunk;
+      fcr = sc[kScCoefR * kChunk + lane_];
+      feG = sc[kScEG * kChunk + lane_];
+      frs = sc[kScRs * kChunk + lane_];
+    }
+  };
+  // A barrier over this wave's LDS operations only: with the next chunk's loads into LDS in
+  // flight, a workgroup fence would make the compiler wait for them.
+  auto lds_barrier = [] __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Stores issued after the next chunk's loads (dk, dq; wave 0's per-token stores come on top,
+  // and waiting for fewer younger operations than there are is still correct).
+  constexpr int NSTO = 2 * TPW;
   if ((int64_t)blockIdx.x >= total) return;
   if constexpr (PF) {
     load_state(blockIdx.x);
     load_t64(blockIdx.x);
+    issue_ops(blockIdx.x, __builtin_amdgcn_readfirstlane(tid0 >> 6), tid0 & 63);
+    wait_vmem<0>();
   }
   for (int64_t chunk_id = blockIdx.x; chunk_id < total; chunk_id += gridDim.x) {
   // Per-thread index arithmetic is redone every chunk rather than kept live across the loop.
@@ -174,21 +231,10 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
 
   // ---- the row-major operands straight into LDS; Delta and Zb from registers (transposed on
   //      the way into LDS); S and dS' stay in registers until they are needed ----
-  if constexpr (!PF) load_state(chunk_id);
-  auto dma_rows = [&](rsrc_t r, E* dst, uint32_t base, uint32_t rowb, uint32_t hcol, auto ncol_tag) {
-    constexpr int NCOL = decltype(ncol_tag)::value;
-    constexpr int CPR = NCOL / PER, NBLK = kChunk * CPR / 64;
-    static_assert(NBLK % NW == 0, "block split");
-#pragma unroll
-    for (int i = 0; i < NBLK / NW; ++i) {
-      const int blk = wave + NW * i, ph = 64 * blk + lane, row = ph / CPR;
-      dma16(r, dst + blk * 64 * PER, base + row * rowb + hcol + 16 * swz<E, CPR>(row, ph % CPR));
-    }
-  };
-  dma_rows(rk, sm.Ks, x0, xrow, hcol_x, std::integral_constant<int, DK>());
-  dma_rows(rq, sm.Qs, x0, xrow, hcol_x, std::integral_constant<int, DK>());
-  dma_rows(rdo, sm.dOs, v0, vrow, hcol_v, std::integral_constant<int, DV>());
-  dma_rows(rv, sm.St, v0, vrow, hcol_v, std::integral_constant<int, DV>());
+  if constexpr (!PF) {
+    load_state(chunk_id);
+    issue_ops(chunk_id, wave, lane);
+  }
 
   // tile-ordered [64 x DV] blocks, transposed into LDS: lane piece (rows 4g..4g+3 of column c of
   // tile (rt, ct)) -> row 16 ct + c, columns 16 rt + 4g .. + 3
@@ -215,13 +261,10 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
 
   // per-token factors; the chunk-local decay prefix G as the forward forms it
   if (wave == 0) {
-    const bool valid = t0 + lane < T;
-    const float la = valid && p.log_alpha ? p.log_alpha[(bb * T + t0 + lane) * H + hh] : 0.f;
-    sm.G[lane] = wave_inclusive_scan(la);
-    const float* sc = ws.SC + chunk_id * kScRows * kChunk;
-    sm.cr[lane] = sc[kScCoefR * kChunk + lane];
-    sm.eG[lane] = sc[kScEG * kChunk + lane];
-    sm.rs[lane] = sc[kScRs * kChunk + lane];
+    sm.G[lane] = wave_inclusive_scan(fla);
+    sm.cr[lane] = fcr;
+    sm.eG[lane] = feG;
+    sm.rs[lane] = frs;
   }
   // Upper off-diagonal tiles of Ma and Mp that the 32-token contraction groups below reach,
   // (0, 1) and (2, 3), are zero (fp32 groups are 16 tokens wide and reach none).
@@ -237,8 +280,14 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
       *reinterpret_cast<V16*>((arr ? sm.Mp : sm.Ma) + at<E, kChunk>(r, col)) = z;
     }
   }
-  wait_vmem<0>();
-  __syncthreads();
+  if constexpr (PF) {
+    // this chunk's operands were loaded during the previous one: younger are its NSTO stores
+    wait_vmem<NSTO>();
+    lds_barrier();
+  } else {
+    wait_vmem<0>();
+    __syncthreads();
+  }
   // Issued after the barrier: with no load to LDS outstanding, the reads below need no wait.
   if (PF && more) load_t64(nid);
 
@@ -253,17 +302,17 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk, F = kk, dp = kk, zvv = kk;
 #pragma unroll
     for (int s = 0; s < NGD; ++s) {
-      const GV bk = row_grp<E, DK>(sm.Ks, 16 * tj + c16, s, g);
-      kk = mma<E>(row_grp<E, DK>(sm.Ks, 16 * ti + c16, s, g), bk, kk);
-      qk = mma<E>(row_grp<E, DK>(sm.Qs, 16 * ti + c16, s, g), bk, qk);
+      const GV bk = row_grp<E, DK>(op.Ks, 16 * tj + c16, s, g);
+      kk = mma<E>(row_grp<E, DK>(op.Ks, 16 * ti + c16, s, g), bk, kk);
+      qk = mma<E>(row_grp<E, DK>(op.Qs, 16 * ti + c16, s, g), bk, qk);
     }
 #pragma unroll
     for (int s = 0; s < NGV; ++s) {
       const GV bd = kt_grp<E, kChunk>(sm.Dt, tj, s, g, c16);
       const GV az = kt_grp<E, kChunk>(sm.Zt, ti, s, g, c16);
       F = mma<E>(az, bd, F);
-      dp = mma<E>(row_grp<E, DV>(sm.dOs, 16 * ti + c16, s, g), bd, dp);
-      if (ti == tj) zvv = mma<E>(az, row_grp<E, DV>(sm.St, 16 * tj + c16, s, g), zvv);
+      dp = mma<E>(row_grp<E, DV>(op.dOs, 16 * ti + c16, s, g), bd, dp);
+      if (ti == tj) zvv = mma<E>(az, row_grp<E, DV>(op.St, 16 * tj + c16, s, g), zvv);
     }
     if (ti == tj && (c16 >> 2) == g) {
       const int e = c16 & 3;
@@ -314,7 +363,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
       for (int h = 0; h < PER / 4; ++h) {
         const int pi = ci * (PER / 4) + h, ti = pi >> 6, l = pi & 63;
         const int rt = ti / (DV / 16), ct = ti % (DV / 16);
-        E* d = sm.St + at<E, DK>(16 * ct + (l & 15), 16 * rt + 4 * (l >> 4));
+        E* d = op.St + at<E, DK>(16 * ct + (l & 15), 16 * rt + 4 * (l >> 4));
         if constexpr (BF) {
           *reinterpret_cast<bf16x4*>(d) = half4(regs[i], h);
         } else {
@@ -334,22 +383,22 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     f32x4 k_ = {0.f, 0.f, 0.f, 0.f}, q_ = k_, zs = k_, os = k_;
 #pragma unroll
     for (int s = 0; s < NGT; ++s) {
-      const GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
+      const GV ak = kt_grp<E, DK>(op.Ks, it, s, g, c16);
       if (GK * s < 16 * (rt + 1)) {  // Ma[r][s], Mp[r][s] vanish for s > r
         k_ = mma<E>(ak, row_grp<E, kChunk>(sm.Ma, 16 * rt + c16, s, g), k_);
         q_ = mma<E>(ak, row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g), q_);
       }
       if (GK * (s + 1) > 16 * rt) {  // Ma[r][s], Mp[r][s] over r >= s
-        const GV aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16);
+        const GV aq = kt_grp<E, DK>(op.Qs, it, s, g, c16);
         k_ = mma<E>(ak, kt_grp<E, kChunk>(sm.Ma, rt, s, g, c16), k_);
         k_ = mma<E>(aq, kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16), k_);
       }
     }
 #pragma unroll
     for (int s = 0; s < NGV; ++s) {
-      const GV as = kt_grp<E, DK>(sm.St, it, s, g, c16);
+      const GV as = kt_grp<E, DK>(op.St, it, s, g, c16);
       zs = mma<E>(as, kt_grp<E, kChunk>(sm.Zt, rt, s, g, c16), zs);
-      os = mma<E>(as, row_grp<E, DV>(sm.dOs, 16 * rt + c16, s, g), os);
+      os = mma<E>(as, row_grp<E, DV>(op.dOs, 16 * rt + c16, s, g), os);
     }
     accK[t] = k_;
     accQ[t] = q_;
@@ -366,7 +415,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     f32x4 ds = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NGV; ++s)
-      ds = mma<E>(kt_grp<E, DK>(sm.St, it, s, g, c16), kt_grp<E, kChunk>(sm.Dt, rt, s, g, c16), ds);
+      ds = mma<E>(kt_grp<E, DK>(op.St, it, s, g, c16), kt_grp<E, kChunk>(sm.Dt, rt, s, g, c16), ds);
     accDS[t] = ds;
   }
 
@@ -378,16 +427,16 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     const int r = 16 * rt + c16, i0 = 16 * it + 4 * g;
     f32x4 kx, qx;
     if constexpr (BF) {
-      const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&sm.Ks[at<E, DK>(r, i0)]);
-      const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&sm.Qs[at<E, DK>(r, i0)]);
+      const bf16x4 kb = *reinterpret_cast<const bf16x4*>(&op.Ks[at<E, DK>(r, i0)]);
+      const bf16x4 qb = *reinterpret_cast<const bf16x4*>(&op.Qs[at<E, DK>(r, i0)]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         kx[e] = to_f32(kb[e]);
         qx[e] = to_f32(qb[e]);
       }
     } else {
-      kx = *reinterpret_cast<const f32x4*>(&sm.Ks[at<E, DK>(r, i0)]);
-      qx = *reinterpret_cast<const f32x4*>(&sm.Qs[at<E, DK>(r, i0)]);
+      kx = *reinterpret_cast<const f32x4*>(&op.Ks[at<E, DK>(r, i0)]);
+      qx = *reinterpret_cast<const f32x4*>(&op.Qs[at<E, DK>(r, i0)]);
     }
     kv[t] = kx;
     float a = 0.f, b = 0.f, d = 0.f;
@@ -407,6 +456,20 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     }
   }
   __syncthreads();
+  // ---- dv = diag(eta rs) Zb: the transposing read of Zb^T gives four consecutive d_v
+  //      entries of one token per lane ----
+  constexpr int NJT = DV / 16;
+#pragma unroll
+  for (int t = 0; t < 4 * NJT / NW; ++t) {
+    const int q = wave * (4 * NJT / NW) + t, rt = q % 4, jt = q / 4;
+    const int r = 16 * rt + c16;
+    const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
+    store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
+  }
+  // The row-major operands are read no more in this chunk: the next chunk's go into LDS now.
+  // (After the transposing reads of Zb^T above: the compiler cannot tell those from the loads'
+  // destination and would wait for the loads before them.)
+  if (PF && more) issue_ops(nid, wave, lane);
 
   // ---- per token: deta, dG, and dlog(alpha) as the within-chunk suffix sum of dG ----
   if (wave == 0) {
@@ -441,7 +504,10 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     }
     sm.kcoef[r] = p.beta_given ? 0.f : -2.f * crr * sm.rs[r] * de;
   }
-  __syncthreads();
+  if constexpr (PF)
+    lds_barrier();
+  else
+    __syncthreads();
 
   // ---- dk, dq: four consecutive d_k entries of one token per lane ----
   const float GC = sm.G[kChunk - 1];
@@ -456,17 +522,11 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
     store4_rsrc<E>(rdk, off, dk);
     store4_rsrc<E>(rdq, off, dq);
   }
-  // ---- dv = diag(eta rs) Zb: the transposing read of Zb^T gives four consecutive d_v
-  //      entries of one token per lane ----
-  constexpr int NJT = DV / 16;
-#pragma unroll
-  for (int t = 0; t < 4 * NJT / NW; ++t) {
-    const int q = wave * (4 * NJT / NW) + t, rt = q % 4, jt = q / 4;
-    const int r = 16 * rt + c16;
-    const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
-    store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
-  }
-  __syncthreads();  // the next chunk overwrites every LDS operand
+  // the next chunk overwrites the LDS this one reads
+  if constexpr (PF)
+    lds_barrier();
+  else
+    __syncthreads();
   if constexpr (!PF) break;
   }  // chunk loop
 }

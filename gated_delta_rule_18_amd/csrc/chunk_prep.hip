@@ -403,39 +403,52 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   typedef PrepKdaSmem<E, DK> Sm;
   __shared__ Sm sm;
 
-  const int64_t chunk_id = blockIdx.x;  // head * nchunks + c
-  const int64_t head = chunk_id / p.nchunks, c = chunk_id % p.nchunks;
-  const int64_t bb = head / p.H, hh = head % p.H;
-  const int64_t T = p.T, t0 = c * kChunk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  auto row_index = [&](int64_t t) { return (bb * T + t) * p.H + hh; };
-  const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * p.nchunks);
-  const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, p.heads * p.nchunks, DK);
+  const int64_t T = p.T, total = p.heads * p.nchunks;
+  const Workspace<E> ws = Workspace<E>::at(p.ws, total);
+  const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, total, DK);
 
-  // ---- K, Q rows, log a and eta of the chunk into LDS: every load issued first, through
-  //      buffer resources over this batch entry's rows (rows past T read as zero) ----
-  {
-    constexpr int CPR = DK / VN, NKQ = kChunk * CPR / NTH, NL = kChunk * DK / 4 / NTH;
-    const int64_t brow = bb * T * p.H;
+  // Persistent: workgroup b takes chunks b, b + gridDim.x, ... (chunk id = head * nchunks + c).
+  // Its LDS holds one workgroup per CU, so nothing else would hide a chunk's loads: the K, Q and
+  // log a rows and eta of the next chunk are loaded into registers (through buffer resources
+  // over the batch entry's rows; rows past T read as zero) as soon as the current chunk's are
+  // in LDS, and arrive during the rest of its work.
+  constexpr int CPR = DK / VN, NKQ = kChunk * CPR / NTH, NL = kChunk * DK / 4 / NTH;
+  const int tid0 = threadIdx.x;
+  i32x4 kx[NKQ], qx[NKQ], lx[NL];
+  float et = 0.f;
+  auto load_chunk = [&](int64_t id, int tid_) __attribute__((always_inline)) {
+    const int64_t head = id / p.nchunks, t0 = (id % p.nchunks) * kChunk;
+    const int64_t bb = head / p.H, hh = head % p.H, brow = bb * T * p.H;
     const uint32_t xrow = p.H * DK * sizeof(E), lrow = p.H * DK * 4;  // bytes per token
     const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
     const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
     const rsrc_t rl = make_rsrc(p.log_alpha + brow * DK, (uint32_t)(T * lrow));
-    i32x4 kx[NKQ], qx[NKQ], lx[NL];
 #pragma unroll
     for (int j = 0; j < NKQ; ++j) {
-      const int i = tid + NTH * j, r = i / CPR, c0 = (i % CPR) * VN;
+      const int i = tid_ + NTH * j, r = i / CPR, c0 = (i % CPR) * VN;
       const uint32_t off = (uint32_t)((t0 + r) * xrow + (hh * DK + c0) * sizeof(E));
       kx[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
       qx[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int i = tid + NTH * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
+      const int i = tid_ + NTH * j, r = i / (DK / 4), c4 = (i % (DK / 4)) * 4;
       lx[j] = __builtin_amdgcn_raw_buffer_load_b128(rl, (uint32_t)((t0 + r) * lrow + (hh * DK + c4) * 4), 0, 0);
     }
-    const float et = tid < kChunk && t0 + tid < T ? p.eta[row_index(t0 + tid)] : 0.f;
+    et = tid_ < kChunk && t0 + tid_ < T ? p.eta[(bb * T + t0 + tid_) * p.H + hh] : 0.f;
+  };
+  if ((int64_t)blockIdx.x >= total) return;
+  load_chunk(blockIdx.x, tid0);
+  for (int64_t chunk_id = blockIdx.x; chunk_id < total; chunk_id += gridDim.x) {
+  // Per-thread index arithmetic is redone every chunk rather than kept live across the loop.
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int64_t t0 = (chunk_id % p.nchunks) * kChunk;
+
+  // ---- K, Q rows, log a and eta of the chunk into LDS, then the next chunk's loads ----
+  {
 #pragma unroll
     for (int j = 0; j < NKQ; ++j) {
       const int i = tid + NTH * j, r = i / CPR, c0 = (i % CPR) * VN;
@@ -448,6 +461,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
       *reinterpret_cast<i32x4*>(&sm.Gm[r][c4]) = lx[j];
     }
     if (tid < kChunk) sm.eta[tid] = et;
+    if (chunk_id + gridDim.x < total) load_chunk(chunk_id + gridDim.x, tid);
   }
   __syncthreads();
 
@@ -684,15 +698,32 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   __syncthreads();
 
   solve_and_store<E, NTH>(sm, ws, chunk_id);
+  __syncthreads();  // the next chunk overwrites the LDS
+  }  // chunk loop
+}
+
+// Workgroups of a kernel resident at once on this device (CUs x occupancy).
+template <typename K>
+int64_t resident_blocks(K kernel, int threads) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || cus <= 0 || per <= 0)
+    return 256;
+  return (int64_t)cus * per;
 }
 
 template <typename E>
 hipError_t launch_kda_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
-  const int64_t grid = p.heads * p.nchunks;
-  if (d_k == 128)
-    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)grid), dim3(kKdaThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)grid), dim3(kKdaThreads), 0, stream, p);
+  const int64_t total = p.heads * p.nchunks;
+  if (d_k == 128) {
+    static const int64_t res = resident_blocks(chunk_prep_kda_kernel<E, 128>, kKdaThreads);
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)(total < res ? total : res)), dim3(kKdaThreads), 0,
+                       stream, p);
+  } else {
+    static const int64_t res = resident_blocks(chunk_prep_kda_kernel<E, 64>, kKdaThreads);
+    hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)(total < res ? total : res)), dim3(kKdaThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -11,7 +11,9 @@
 // [4 cg, 4 cg + 4) in registers between the read and the write, with the k and q entries of
 // those rows. ||k||^2, k.q, S^T k and S^T q are summed over the lane's rows and then reduced in
 // one pass over the row groups (DPP rotations within 16-lane rows, two exchanges across rows).
-// No LDS, no barrier: the only latency is one round trip to memory.
+// No LDS, no barrier, no branch before the stores: every load,
+// the per-head scalars included, is issued at the top, so the only latency is one round trip
+// to memory.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -22,6 +24,8 @@ constexpr int kXcdCount = 8;  // MI355X
 
 // Sum of x over the lanes of the wave whose index is congruent to this lane's mod CG (CG a power
 // of two, 4 <= CG <= 16): DPP row rotations inside each 16-lane row, then exchanges across rows.
+// (The gfx950 row swaps v_permlane16/32_swap would avoid the LDS crossbar here, but this
+// compiler folds the sum of the two results of one swap into twice the first one.)
 template <int CG>
 __device__ __forceinline__ float class_sum(float x) {
   static_assert(CG == 4 || CG == 8 || CG == 16, "class width");
@@ -37,24 +41,30 @@ __device__ __forceinline__ float class_sum(float x) {
 // KDA: log_alpha holds log a [heads][DK], a per-channel decay of the state's rows
 // ("Deep Dive into KDA", section 2.3): u = (Diag(a) S)^T k, p = (Diag(a) S)^T q,
 // delta = beta (v - u), o = p + (k.q) delta, S <- Diag(a) S + k delta^T.
-template <typename E, int DK, int DV, int DVS, bool KDA>
+// BG: eta holds beta itself (gated DeltaNet). The arguments fill one 64-byte line (seven
+// pointers, heads and eps), fetched by one scalar load.
+template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
-    E* __restrict__ o, int64_t heads, float eps, bool beta_given) {
+    E* __restrict__ o, int heads, float eps) {
   constexpr int CG = DVS / 4;        // float4 column groups of the slice
   constexpr int RG = kWave / CG;     // row groups
   constexpr int RPT = DK / RG;       // rows per lane
   constexpr int NS = DV / DVS;       // slices per head
   static_assert(RG * CG == kWave && RPT * RG == DK, "shape");
 
-  // Workgroups are dealt round-robin to the 8 XCDs: give the NS slices of one head ids that are
-  // congruent mod 8, so they share one XCD's L2 (slices narrower than a 128-byte line share lines).
-  const int xcd = blockIdx.x % kXcdCount;
-  const int local = blockIdx.x / kXcdCount;
-  const int64_t head = (int64_t)(local / NS) * kXcdCount + xcd;
-  const int slice = local % NS;
-  if (head >= heads) return;
+  // Workgroups are dealt round-robin to the 8 XCDs: within each full group of 8 heads, give the
+  // NS slices of one head ids that are congruent mod 8, so they share one XCD's L2 (slices
+  // narrower than a 128-byte line share lines). The heads past the last full group take the
+  // remaining ids in order. The grid is exactly heads x NS, so no workgroup idles and nothing
+  // branches ahead of the loads.
+  const unsigned b = blockIdx.x;
+  const unsigned full = (unsigned)heads / kXcdCount * kXcdCount * NS;
+  const bool grouped = b < full;
+  const unsigned r = grouped ? b / kXcdCount : b - full;  // rank within the group / the tail
+  const int64_t head = grouped ? r / NS * kXcdCount + b % kXcdCount : full / NS + r / NS;
+  const int slice = r % NS;
   const int lane = threadIdx.x;
   const int cg = lane % CG, rg = lane / CG;
   const int col0 = slice * DVS + 4 * cg;
@@ -96,7 +106,10 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
   f32x4 vv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[head * DV + col0 + e]);
-  const float alpha = KDA ? 1.f : log_alpha ? __expf(log_alpha[head]) : 1.f;
+  // Without a gate (log_alpha null) the load reads eta's entry instead and alpha = exp(0) = 1:
+  // the load is unconditional, so it need not wait behind a branch.
+  const float la_h = KDA ? 0.f : *(log_alpha ? log_alpha + head : eta + head);
+  const float alpha = KDA ? 1.f : __expf(log_alpha ? la_h : 0.f);
   float ar[RPT];  // per-row decay (KDA)
 #pragma unroll
   for (int m = 0; m < RPT; ++m) ar[m] = KDA ? __expf(lr_[m]) : 1.f;
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
     u[e] = class_sum<CG>(u[e]);
     pq[e] = class_sum<CG>(pq[e]);
   }
-  const float beta = beta_given ? et : et / (nk + eps);
+  const float beta = BG ? et : et / (nk + eps);
   const f32x4 delta = beta * (vv - alpha * u);
   if (rg == 0) {
 #pragma unroll
@@ -136,18 +149,23 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
     *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * (alpha * ar[m]) + delta * kr[m];
 }
 
+template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
+void launch_kernel(const DecodeArgs& a, int heads, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, KDA, BG>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads, a.eps);
+}
+
 template <typename E, int DK, int DV, int DVS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t heads = a.B * a.H;
-  const int64_t grid = (heads + kXcdCount - 1) / kXcdCount * kXcdCount * (DV / DVS);
+  // heads >= 1 and the grid below fit in an int (checked at the C ABI).
+  const int heads = (int)(a.B * a.H);
+  const int64_t grid = (int64_t)heads * (DV / DVS);
   if (a.kda)
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, true>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
-                       a.eps, a.beta_given);
+    a.beta_given ? launch_kernel<E, DK, DV, DVS, true, true>(a, heads, grid, stream)
+                 : launch_kernel<E, DK, DV, DVS, true, false>(a, heads, grid, stream);
   else
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, false>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads,
-                       a.eps, a.beta_given);
+    a.beta_given ? launch_kernel<E, DK, DV, DVS, false, true>(a, heads, grid, stream)
+                 : launch_kernel<E, DK, DV, DVS, false, false>(a, heads, grid, stream);
   return hipGetLastError();
 }
 

@@ -11,9 +11,9 @@
 // [4 cg, 4 cg + 4) in registers between the read and the write, with the k and q entries of
 // those rows. ||k||^2, k.q, S^T k and S^T q are summed over the lane's rows and then reduced in
 // one pass over the row groups (DPP rotations within 16-lane rows, two exchanges across rows).
-// No LDS, no barrier, no branch before the stores: every load,
-// the per-head scalars included, is issued at the top, so the only latency is one round trip
-// to memory.
+// No LDS storage, no barrier, and no source-level branch ahead of the stores: every load, the
+// per-head scalars included, is issued at the top, so the only latency is one round trip to
+// memory.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -41,8 +41,8 @@ __device__ __forceinline__ float class_sum(float x) {
 // KDA: log_alpha holds log a [heads][DK], a per-channel decay of the state's rows
 // ("Deep Dive into KDA", section 2.3): u = (Diag(a) S)^T k, p = (Diag(a) S)^T q,
 // delta = beta (v - u), o = p + (k.q) delta, S <- Diag(a) S + k delta^T.
-// BG: eta holds beta itself (gated DeltaNet). The arguments fill one 64-byte line (seven
-// pointers, heads and eps), fetched by one scalar load.
+// BG: eta holds beta itself (gated DeltaNet). The arguments (seven pointers, heads and eps)
+// fill one 64-byte line, so all their scalar loads hit the line the first one brings in.
 template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,

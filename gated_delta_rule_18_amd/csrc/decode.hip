@@ -171,8 +171,10 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t stream) {
-  // Many heads: 32-column slices (16 rows of float4 per lane). Few heads: 16-column slices, so
-  // that the grid still puts a couple of waves on every CU.
+  // Many heads: wide slices (more rows per lane, fewer waves per byte). Few heads: 16-column
+  // slices, so that the grid still puts a couple of waves on every CU. Measured crossovers
+  // (d = 128, bf16): 64 columns win from 1024 heads on, 32 at 512.
+  if (a.B * a.H >= 1024) return launch<E, DK, DV, 64>(a, stream);
   if (a.B * a.H >= 512) return launch<E, DK, DV, 32>(a, stream);
   return launch<E, DK, DV, 16>(a, stream);
 }

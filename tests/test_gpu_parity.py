@@ -68,7 +68,8 @@ def test_prepare_beta(dtype, dk, T):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv,B,H", [(128, 128, 2, 3), (64, 64, 2, 3), (128, 64, 1, 5), (64, 128, 3, 1),
-                                       (128, 128, 3, 5), (128, 128, 64, 17), (128, 128, 37, 14)])
+                                       (128, 128, 3, 5), (128, 128, 64, 17), (64, 64, 64, 17), (64, 128, 64, 17),
+                                       (128, 128, 37, 14)])
 def test_decode_steps_small(dtype, dk, dv, B, H):
     w = wl.custom("dec", 201, B=B, H=H, dk=dk, dv=dv, steps=12, dtype=dtype, s0_std=0.05)
     inp = wl.decode_inputs(w)

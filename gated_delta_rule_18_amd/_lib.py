@@ -26,6 +26,9 @@ _SIGNATURES = {
     "kla_prepare_beta": (_int, [_c_void_p] * 5 + [_i64] * 5 + [_f32, _int, _c_void_p]),
     "kla_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_chunk_fwd_seg_workspace_size": (ctypes.c_size_t, [_i64] * 7 + [_int]),
+    "kla_chunk_fwd_seg": (_int, [_c_void_p] * 8 + [_i64] * 7 + [_f32, _int, _c_void_p, ctypes.c_size_t,
+                                                                _c_void_p]),
     "kla_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _c_void_p]),
     "kla_gdn_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_gdn_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_int, _c_void_p]),
@@ -137,14 +140,19 @@ def kla_prepare_beta(k, eta, log_alpha, eps=1e-6, chunk=CHUNK, with_gcum=True, b
     return beta_out, gcum_out
 
 
-def kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16) -> int:
-    return int(lib().kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+def kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16, segments=None) -> int:
+    """Workspace bytes of kla_chunk_fwd (segments None) or of kla_chunk_fwd_seg with that plan."""
+    if segments is None:
+        return int(lib().kla_chunk_fwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+    return int(lib().kla_chunk_fwd_seg_workspace_size(B, T, H, d_k, d_v, chunk, segments, dtype_code))
 
 
 def kla_chunk_fwd(q, k, v, eta, log_alpha, eps=1e-6, state_in=None, return_state=True, o=None, state_out=None,
-                  chunk=CHUNK, workspace=None, stream=None):
+                  chunk=CHUNK, workspace=None, stream=None, segments=None):
     """Chunkwise KLA forward. q, k [B, T, H, d_k], v [B, T, H, d_v] (bf16 or fp32, one dtype);
     eta, log_alpha [B, T, H] fp32; state_in [B, H, d_k, d_v] fp32 or None (zeros).
+    segments None calls kla_chunk_fwd (the library's plan); an int calls kla_chunk_fwd_seg with
+    that many sequence segments (0: the library's plan, 1: the one-pass scan).
     Returns (o [B, T, H, d_v] in the input dtype, final state [B, H, d_k, d_v] fp32 or None)."""
     torch = _torch()
     if q.dim() != 4 or v.dim() != 4:
@@ -167,13 +175,17 @@ def kla_chunk_fwd(q, k, v, eta, log_alpha, eps=1e-6, state_in=None, return_state
     if state_out is not None:
         _need(state_out, "state_out", (B, H, dk, dv), torch.float32, dev)
     code = _dtype_code(q)
-    need = kla_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    need = kla_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code, segments)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().kla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state_in),
-                              _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, float(eps), code,
-                              _ptr(workspace), ws_bytes, _stream(dev, stream)))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state_in), _ptr(state_out), _ptr(o),
+            B, T, H, dk, dv, chunk)
+    tail = (float(eps), code, _ptr(workspace), ws_bytes, _stream(dev, stream))
+    if segments is None:
+        check(lib().kla_chunk_fwd(*head, *tail))
+    else:
+        check(lib().kla_chunk_fwd_seg(*head, int(segments), *tail))
     return o, state_out
 
 

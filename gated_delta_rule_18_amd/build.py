@@ -16,7 +16,7 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libkla.so"
-SOURCES = ["kla_abi.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip",
+SOURCES = ["kla_abi.hip", "device_info.hip", "decode.hip", "prepare_beta.hip", "chunk_prep.hip", "chunk_scan.hip",
            "chunk_seg.hip", "chunk_bwd_scan.hip", "chunk_bwd_grad.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -534,16 +534,15 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
 template <typename E, int DK, int DV>
 hipError_t launch_dk_dv(const ChunkBwdParams& p, hipStream_t stream) {
   if constexpr (grad_fits<E, DK, DV>()) {
-    static const int64_t resident = [] {
-      int dev = 0, cus = 0, per = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, chunk_grad_kernel<E, DK, DV>, kGradThreads, 0) !=
-              hipSuccess ||
-          cus <= 0 || per <= 0)
-        return (int64_t)256;
-      return (int64_t)cus * per;
+    // Workgroups resident per compute unit (the same on every gfx950 device), times the device's CUs.
+    static const int64_t per = [] {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_grad_kernel<E, DK, DV>, kGradThreads, 0) !=
+              hipSuccess || n <= 0)
+        return (int64_t)1;
+      return (int64_t)n;
     }();
+    const int64_t resident = device_info().cus * per;
     const int64_t total = p.heads * p.nchunks;
     const int64_t grid = grad_prefetch<E, DK, DV>() && resident < total ? resident : total;
     hipLaunchKernelGGL((chunk_grad_kernel<E, DK, DV>), dim3((unsigned)grid), dim3(kGradThreads), 0, stream, p);

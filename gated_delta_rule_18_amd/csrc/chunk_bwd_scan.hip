@@ -60,9 +60,9 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   __shared__ typename std::conditional<(NB >= 2), Buf, int>::type buf1;
 
   const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int local = bid / kXcds;
-  const int64_t head = (int64_t)(local / NS) * kXcds + xcd;
+  const int xcd = bid % p.xcds;
+  const int local = bid / p.xcds;
+  const int64_t head = (int64_t)(local / NS) * p.xcds + xcd;
   const int slice = local % NS;
   if (head >= p.heads) return;
   const int64_t bb = head / p.H, hh = head % p.H;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 template <typename E, int DK, int DV, int W, int NT>
 hipError_t launch_wnt(const ChunkBwdParams& p, hipStream_t stream) {
   constexpr int NS = DV / (W * 16 * NT);
-  const int64_t heads8 = (p.heads + kXcds - 1) / kXcds * kXcds;
+  const int64_t heads8 = (p.heads + p.xcds - 1) / p.xcds * p.xcds;
   constexpr int NP = rscan_producers<E, DK, DV, W, NT>();
   hipLaunchKernelGGL((chunk_rscan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3((W + NP) * kWave), 0,
                      stream, p);
@@ -402,9 +402,11 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream) {
   ChunkBwdParams bp{a.q,  a.k,    a.v,         a.eta,      a.log_alpha, a.state_in, a.dout, a.dstate_out,
                     a.dq, a.dk,   a.dv,        a.deta,     a.dlog_alpha, a.dstate_in, a.workspace,
                     a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given};
+  bp.xcds = device_info().xcds;
   if (nchunks > 0) {
     ChunkParams fp{a.q,   a.k,       a.v, a.eta,    a.log_alpha, a.state_in, nullptr, nullptr, a.workspace,
                    a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given, a.beta_given};
+    fp.xcds = bp.xcds;
     hipError_t e = launch_chunk_prep(fp, a.d_k, a.bf16, stream);
     if (e == hipSuccess) e = launch_scan_recompute(fp, a.d_k, a.d_v, a.bf16, stream);
     if (e != hipSuccess) return e;

@@ -13,7 +13,6 @@ template <typename E>
 constexpr bool is_bf16() { return std::is_same<E, bf16>::value; }
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
-constexpr int kXcds = 8;       // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 // acc += A[16 x k] * B[k x 16] over k in [0, kend), A stored row-major [16][lda] and B stored
 // as its transpose [16][ldb] (both K-contiguous, in LDS). bf16: v_mfma_f32_16x16x32_bf16
@@ -172,6 +171,7 @@ struct ChunkParams {
   // form d(beta) on tokens whose beta is zero.
   bool unit_rs;
   int64_t nseg = 1, seg_len = 0;  // segment scan (kScanSeg): segments per head, chunks per segment
+  int xcds = 1;  // XCDs of the device: the scan launches keep the workgroups of one head on one XCD
 };
 
 // Backward workspace: the forward workspace above, then per chunk (same chunk ids)
@@ -224,6 +224,7 @@ struct ChunkBwdParams {
   int64_t heads, H, T, nchunks;
   float eps;
   bool beta_given;
+  int xcds = 1;  // as ChunkParams::xcds
 };
 
 }  // namespace kla

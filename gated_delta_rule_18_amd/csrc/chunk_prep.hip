@@ -702,25 +702,25 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   }  // chunk loop
 }
 
-// Workgroups of a kernel resident at once on this device (CUs x occupancy).
+// Workgroups of a kernel resident at once per compute unit (the same on every gfx950 device).
 template <typename K>
-int64_t resident_blocks(K kernel, int threads) {
-  int dev = 0, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || cus <= 0 || per <= 0)
-    return 256;
-  return (int64_t)cus * per;
+int64_t blocks_per_cu(K kernel, int threads) {
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || per <= 0) return 1;
+  return per;
 }
 
 template <typename E>
 hipError_t launch_kda_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
-  const int64_t total = p.heads * p.nchunks;
+  const int64_t total = p.heads * p.nchunks, cus = device_info().cus;
   if (d_k == 128) {
-    static const int64_t res = resident_blocks(chunk_prep_kda_kernel<E, 128>, kKdaThreads);
+    static const int64_t per = blocks_per_cu(chunk_prep_kda_kernel<E, 128>, kKdaThreads);
+    const int64_t res = cus * per;
     hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 128>), dim3((unsigned)(total < res ? total : res)), dim3(kKdaThreads), 0,
                        stream, p);
   } else {
-    static const int64_t res = resident_blocks(chunk_prep_kda_kernel<E, 64>, kKdaThreads);
+    static const int64_t per = blocks_per_cu(chunk_prep_kda_kernel<E, 64>, kKdaThreads);
+    const int64_t res = cus * per;
     hipLaunchKernelGGL((chunk_prep_kda_kernel<E, 64>), dim3((unsigned)(total < res ? total : res)), dim3(kKdaThreads), 0,
                        stream, p);
   }

@@ -46,8 +46,6 @@
 // chunk ahead by the scan waves themselves. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
-#include <cstdlib>
-
 #include "tile_ops.h"
 
 namespace kla {
@@ -119,9 +117,9 @@ chunk_scan_kernel(ChunkParams p) {
   static_assert(!SEG || DK % DVS == 0, "shape");
   const int64_t nseg = SEG ? p.nseg : 1;
   const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int local = bid / kXcds;
-  const int64_t vh = (int64_t)(local / NSA) * kXcds + xcd;  // head * nseg + segment
+  const int xcd = bid % p.xcds;
+  const int local = bid / p.xcds;
+  const int64_t vh = (int64_t)(local / NSA) * p.xcds + xcd;  // head * nseg + segment
   const int slice = local % NSA;
   if (vh >= p.heads * nseg) return;
   const int64_t head = vh / nseg, seg = vh % nseg;
@@ -538,7 +536,7 @@ hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   static_assert(DVS == scan_cols(is_bf16<E>(), MODE == kScanSeg), "column split as planned");
   constexpr int NSA = DV / DVS + (MODE == kScanSeg ? DK / DVS : 0);
   const int64_t units = p.heads * (MODE == kScanSeg ? p.nseg : 1);  // (head, segment) pairs
-  const int64_t units8 = (units + kXcds - 1) / kXcds * kXcds;
+  const int64_t units8 = (units + p.xcds - 1) / p.xcds * p.xcds;
   constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
   hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3((W + NP) * kWave), 0,
                      stream, p);
@@ -575,25 +573,27 @@ hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v,
   return bf16_io ? launch_scan<bf16, kScanRec>(p, d_k, d_v, stream) : launch_scan<float, kScanRec>(p, d_k, d_v, stream);
 }
 
-// Segments for a forward of `heads` heads and `nchunks` chunks. One segment while the one-pass
-// scan's workgroups (heads x column slices) fill the 256 compute units; else enough segments
-// for one workgroup per compute unit over both column kinds, at least eight chunks each. (One
-// scan workgroup fills a compute unit's LDS, and the output correction grows with the number
-// of segments: on B1 H16 T65536 with two-wave segment workgroups, 2 segments measured 1.29 ms,
-// 4 1.32 ms, 8 1.37 ms, against 1.90 ms unsegmented; with the four-wave bf16 segment workgroups
-// the plan gives 4 segments in 224 workgroups, 0.89 ms against 1.14 ms for 2 two-wave ones.)
-// KLA_FWD_SEGMENTS, when set, fixes the number of segments (a tuning and testing override).
-SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool bf16_io) {
+// Segments for a forward of `heads` heads and `nchunks` chunks on a device with `dev.cus` compute
+// units. One segment while the one-pass scan's workgroups (heads x column slices) fill the
+// compute units; else enough segments for one workgroup per compute unit over both column kinds,
+// at least eight chunks each. (One scan workgroup fills a compute unit's LDS, and the output
+// correction grows with the number of segments: on B1 H16 T65536 with two-wave segment
+// workgroups, 2 segments measured 1.29 ms, 4 1.32 ms, 8 1.37 ms, against 1.90 ms unsegmented;
+// with the four-wave bf16 segment workgroups the plan gives 4 segments in 224 workgroups,
+// 0.89 ms against 1.14 ms for 2 two-wave ones.) `forced` > 0 fixes the number of segments
+// instead (the caller's explicit plan), clipped to the chunks.
+SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool bf16_io, int64_t forced,
+                 const DeviceInfo& dev) {
   if (nchunks < 2) return SegPlan{1, nchunks};
   const int64_t cols = scan_cols(bf16_io);
-  const int64_t units8 = (heads + kXcds - 1) / kXcds * kXcds;
+  const int64_t units = (heads + dev.xcds - 1) / dev.xcds * dev.xcds;
   int64_t nseg = 1;
-  if (const char* env = std::getenv("KLA_FWD_SEGMENTS")) {
-    nseg = std::atoll(env);
-  } else if (units8 * (d_v / cols) < 256 && nchunks >= 32) {
+  if (forced > 0) {
+    nseg = forced;
+  } else if (units * (d_v / cols) < dev.cus && nchunks >= 32) {
     const int64_t scols = scan_cols(bf16_io, true);
     const int64_t per = heads * ((d_v + d_k) / scols);  // workgroups per segment
-    nseg = (256 + per - 1) / per;
+    nseg = (dev.cus + per - 1) / per;
     if (nseg > nchunks / 8) nseg = nchunks / 8;
   }
   if (nseg < 1) nseg = 1;
@@ -613,6 +613,7 @@ size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_
 hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
   ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
                 a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
+  p.xcds = device_info().xcds;
   if (p.nchunks > 0) {
     const hipError_t e = launch_chunk_prep_kda(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;
@@ -621,9 +622,10 @@ hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
                 : launch_scan<float, kScanKda>(p, a.d_k, a.d_v, stream);
 }
 
-size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io) {
+size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io,
+                                 int64_t segments) {
   const int64_t nch = (T + kChunk - 1) / kChunk, n = B * H * nch;
-  const SegPlan sp = seg_plan(B * H, nch, d_k, d_v, bf16_io);
+  const SegPlan sp = seg_plan(B * H, nch, d_k, d_v, bf16_io, segments, device_info());
   if (sp.nseg > 1)
     return bf16_io ? SegSpace<bf16>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v)
                    : SegSpace<float>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v);
@@ -633,11 +635,13 @@ size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, i
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
   ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
                 a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
+  const DeviceInfo dev = device_info();
+  p.xcds = dev.xcds;
   if (p.nchunks > 0) {
     const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;
   }
-  const SegPlan sp = seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16);
+  const SegPlan sp = seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev);
   if (sp.nseg <= 1)
     return a.bf16 ? launch_scan<bf16>(p, a.d_k, a.d_v, stream) : launch_scan<float>(p, a.d_k, a.d_v, stream);
   p.nseg = sp.nseg;

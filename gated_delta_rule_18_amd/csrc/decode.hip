@@ -20,8 +20,6 @@
 namespace kla {
 namespace {
 
-constexpr int kXcdCount = 8;  // MI355X
-
 // Sum of x over the lanes of the wave whose index is congruent to this lane's mod CG (CG a power
 // of two, 4 <= CG <= 16): DPP row rotations inside each 16-lane row, then exchanges across rows.
 // (The gfx950 row swaps v_permlane16/32_swap would avoid the LDS crossbar here, but this
@@ -41,29 +39,32 @@ __device__ __forceinline__ float class_sum(float x) {
 // KDA: log_alpha holds log a [heads][DK], a per-channel decay of the state's rows
 // ("Deep Dive into KDA", section 2.3): u = (Diag(a) S)^T k, p = (Diag(a) S)^T q,
 // delta = beta (v - u), o = p + (k.q) delta, S <- Diag(a) S + k delta^T.
-// BG: eta holds beta itself (gated DeltaNet). The arguments (seven pointers, heads and eps)
+// BG: eta holds beta itself (gated DeltaNet). The arguments (seven pointers, heads_x and eps)
 // fill one 64-byte line, so all their scalar loads hit the line the first one brings in.
+// heads_x packs the head count (bits 0..27; the C ABI bounds it below 2^28) and log2 of the
+// XCD grouping width X (bits 28..31), X the largest power of two not above the device's XCDs.
 template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
-    E* __restrict__ o, int heads, float eps) {
+    E* __restrict__ o, unsigned heads_x, float eps) {
   constexpr int CG = DVS / 4;        // float4 column groups of the slice
   constexpr int RG = kWave / CG;     // row groups
   constexpr int RPT = DK / RG;       // rows per lane
   constexpr int NS = DV / DVS;       // slices per head
   static_assert(RG * CG == kWave && RPT * RG == DK, "shape");
 
-  // Workgroups are dealt round-robin to the 8 XCDs: within each full group of 8 heads, give the
-  // NS slices of one head ids that are congruent mod 8, so they share one XCD's L2 (slices
+  // Workgroups are dealt round-robin to the XCDs: within each full group of X heads, give the
+  // NS slices of one head ids that are congruent mod X, so they share one XCD's L2 (slices
   // narrower than a 128-byte line share lines). The heads past the last full group take the
   // remaining ids in order. The grid is exactly heads x NS, so no workgroup idles and nothing
   // branches ahead of the loads.
+  const unsigned heads = heads_x & 0x0fffffffu, xs = heads_x >> 28;
   const unsigned b = blockIdx.x;
-  const unsigned full = (unsigned)heads / kXcdCount * kXcdCount * NS;
+  const unsigned full = (heads >> xs << xs) * NS;
   const bool grouped = b < full;
-  const unsigned r = grouped ? b / kXcdCount : b - full;  // rank within the group / the tail
-  const int64_t head = grouped ? r / NS * kXcdCount + b % kXcdCount : full / NS + r / NS;
+  const unsigned r = grouped ? b >> xs : b - full;  // rank within the group / the tail
+  const int64_t head = grouped ? ((r / NS) << xs) + (b & ((1u << xs) - 1)) : full / NS + r / NS;
   const int slice = r % NS;
   const int lane = threadIdx.x;
   const int cg = lane % CG, rg = lane / CG;
@@ -150,22 +151,26 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
 }
 
 template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
-void launch_kernel(const DecodeArgs& a, int heads, int64_t grid, hipStream_t stream) {
+void launch_kernel(const DecodeArgs& a, unsigned heads_x, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, KDA, BG>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads, a.eps);
+                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads_x,
+                     a.eps);
 }
 
 template <typename E, int DK, int DV, int DVS>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  // heads >= 1 and the grid below fit in an int (checked at the C ABI).
-  const int heads = (int)(a.B * a.H);
-  const int64_t grid = (int64_t)heads * (DV / DVS);
+  // 1 <= heads < 2^28 and the grid below fit in an int (checked at the C ABI).
+  const int64_t heads = a.B * a.H;
+  const int64_t grid = heads * (DV / DVS);
+  unsigned xs = 0;
+  for (int x = device_info().xcds; x > 1 && xs < 7; x >>= 1) ++xs;
+  const unsigned heads_x = (unsigned)heads | (xs << 28);
   if (a.kda)
-    a.beta_given ? launch_kernel<E, DK, DV, DVS, true, true>(a, heads, grid, stream)
-                 : launch_kernel<E, DK, DV, DVS, true, false>(a, heads, grid, stream);
+    a.beta_given ? launch_kernel<E, DK, DV, DVS, true, true>(a, heads_x, grid, stream)
+                 : launch_kernel<E, DK, DV, DVS, true, false>(a, heads_x, grid, stream);
   else
-    a.beta_given ? launch_kernel<E, DK, DV, DVS, false, true>(a, heads, grid, stream)
-                 : launch_kernel<E, DK, DV, DVS, false, false>(a, heads, grid, stream);
+    a.beta_given ? launch_kernel<E, DK, DV, DVS, false, true>(a, heads_x, grid, stream)
+                 : launch_kernel<E, DK, DV, DVS, false, false>(a, heads_x, grid, stream);
   return hipGetLastError();
 }
 

@@ -113,6 +113,14 @@ size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
   return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
 }
 
+size_t kla_chunk_fwd_seg_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                        int64_t segments, kla_dtype_t dt) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk ||
+      segments < 0)
+    return 0;
+  return kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
+}
+
 size_t kla_kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                                         kla_dtype_t dt) {
   if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
@@ -134,12 +142,15 @@ namespace {
 // kla_chunk_fwd, kla_gdn_chunk_fwd and kla_kda_chunk_fwd: eta is eta (Kaczmarz step) or beta itself
 // (beta_given, where a scalar log_alpha may be null for alpha = 1); with kda, log_alpha is the
 // per-channel log a [B, T, H, d_k] and required.
+// segments: the scan's sequence segments (0: the library's plan).
 kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                             const float* eta, const float* log_alpha, const float* state_in, float* state_out,
                             void* o, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
-                            float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream) {
+                            float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream,
+                            int64_t segments = 0) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
+  if (segments < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative segment count", fn);
   if (!supported_head(d_k) || !supported_head(d_v))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k and d_v must be 64 or 128", fn);
   if (chunk != kla::kChunk) return fail(KLA_ERR_NOT_SUPPORTED, "%s: chunk must be 64", fn);
@@ -163,7 +174,7 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
       !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, kda ? 16 : 4))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
   const size_t need = kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
-                          : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+                          : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
   if (T > 0 && need > 0 && (!workspace || workspace_bytes < need))
     return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
   const int64_t es = dt == KLA_BF16 ? 2 : 4;
@@ -189,7 +200,7 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
     return KLA_OK;
   }
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
-                   workspace, workspace_bytes, beta_given};
+                   workspace, workspace_bytes, beta_given, segments};
   return launched(kda ? kla::launch_chunk_kda_fwd(a, static_cast<hipStream_t>(stream))
                       : kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)),
                   fn);
@@ -312,6 +323,14 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl("kla_chunk_fwd", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v,
                         chunk, eps, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_chunk_fwd_seg(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                               const float* state_in, float* state_out, void* o, int64_t B, int64_t T, int64_t H,
+                               int64_t d_k, int64_t d_v, int64_t chunk, int64_t segments, float eps, kla_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_chunk_fwd_seg", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H,
+                        d_k, d_v, chunk, eps, dt, workspace, workspace_bytes, stream, segments);
 }
 
 kla_status_t kla_gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* beta,

@@ -10,6 +10,16 @@ namespace kla {
 
 constexpr int kChunk = 64;  // chunk length of the chunkwise algorithm
 
+// Compute units and XCDs of the current device, queried once per device ordinal (the full
+// MI355X's 256 and 8 when there is no device to ask, e.g. for a host-only size query).
+// Workgroups are dealt round-robin to the XCDs; the launches use the count to keep the
+// workgroups of one head on one XCD (one L2), and the plans size grids to the compute units.
+struct DeviceInfo {
+  int cus;
+  int xcds;
+};
+DeviceInfo device_info();
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -51,6 +61,7 @@ struct ChunkArgs {
   void* workspace;
   size_t workspace_bytes;
   bool beta_given;  // eta holds beta itself; log_alpha may be null (alpha = 1)
+  int64_t segments = 0;  // sequence segments of the scan; 0: the library's plan
 };
 
 struct ChunkBwdArgs {
@@ -79,7 +90,9 @@ struct ChunkBwdArgs {
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prepare_beta(const PrepareArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
-size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+// segments: as ChunkArgs::segments (0: the library's plan for the current device).
+size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,
+                                 int64_t segments = 0);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
 // Per-channel decay (KDA): ChunkArgs.log_alpha / DecodeArgs.log_alpha hold log a [.., d_k].
 hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);

@@ -72,7 +72,9 @@ kla_status_t kla_prepare_beta(const void* k, const float* eta, const float* log_
 
 /*
  * kla_chunk_fwd_workspace_size — bytes of device workspace kla_chunk_fwd needs for
- * these sizes (0 when it needs none). Host-only; never fails.
+ * these sizes on the current device (0 when it needs none). The amount depends on the scan's
+ * plan, which the library sizes to the current device's compute units (the full MI355X's when
+ * no device is present). Host-only; never fails.
  */
 size_t kla_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
                                     int64_t chunk, kla_dtype_t dt);
@@ -102,6 +104,31 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v,
                            int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                            float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * kla_chunk_fwd_seg_workspace_size / kla_chunk_fwd_seg — kla_chunk_fwd with the scan's plan given
+ * by the caller instead of chosen by the library.
+ * Source: "Deep Dive into KDA", section 3 (each chunk maps the entering state to an affine
+ * function of it, so a head's chunks can be cut into segments scanned at the same time and joined
+ * by composing those maps); "Kaczmarz Linear Attention", Abstract (KLA keeps the chunkwise
+ * parallel algorithm). Segments change the result only by rounding.
+ *   segments   0: the library's plan for the current device (exactly kla_chunk_fwd);
+ *              n >= 1: the chunks of every head are cut into about n segments of equal length
+ *              (n is clipped to the number of chunks; segments of ceil(chunks / n) chunks, so the
+ *              count actually used may be lower); n = 1 is the one-pass scan. Negative:
+ *              KLA_ERR_INVALID_VALUE (the size query returns 0).
+ * The workspace size depends on the plan: size it with kla_chunk_fwd_seg_workspace_size for the
+ * same segments and current device. Everything else is as for kla_chunk_fwd. For tuning and for
+ * tests that force the segmented scan; kla_chunk_fwd is the entry point for other callers.
+ */
+size_t kla_chunk_fwd_seg_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                        int64_t chunk, int64_t segments, kla_dtype_t dt);
+kla_status_t kla_chunk_fwd_seg(const void* q, const void* k, const void* v,
+                               const float* eta, const float* log_alpha,
+                               const float* state_in, float* state_out, void* o,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                               int64_t segments, float eps, kla_dtype_t dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * kla_decode_step — one recurrent decode step for B x H heads (one new token each).

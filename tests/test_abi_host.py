@@ -18,7 +18,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kla_prepare_beta", "kla_chunk_fwd_workspace_size", "kla_chunk_fwd",
                           "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
                           "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd",
-                          "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step"}
+                          "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step",
+                          "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -80,30 +81,41 @@ def test_chunk_fwd_empty_batch_is_a_no_op():
     assert chunk(T=0) == K.KLA_OK  # no state requested: nothing to write, nothing launched
 
 
-@pytest.mark.parametrize("segments", [None, "3", "0", "-2", "100000"])
-def test_chunk_fwd_plan_is_host_only_and_total(segments, monkeypatch):
-    """The workspace size (which depends on the segment plan) is defined for every length,
-    and KLA_FWD_SEGMENTS only changes it, never breaks it."""
-    if segments is None:
-        monkeypatch.delenv("KLA_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("KLA_FWD_SEGMENTS", segments)
+@pytest.mark.parametrize("segments", [None, 0, 1, 3, 100000])
+def test_chunk_fwd_plan_is_host_only_and_total(segments):
+    """The workspace size (which depends on the segment plan) is defined for every length and
+    every segment count the caller may ask for."""
     for T in (1, 2, 63, 64, 65, 129, 4096, 65536):
         for H in (1, 16, 64):
-            assert K.lib().kla_chunk_fwd_workspace_size(1, T, H, 128, 128, 64, K.KLA_BF16) > 0
+            if segments is None:
+                assert K.lib().kla_chunk_fwd_workspace_size(1, T, H, 128, 128, 64, K.KLA_BF16) > 0
+            else:
+                assert K.lib().kla_chunk_fwd_seg_workspace_size(1, T, H, 128, 128, 64, segments, K.KLA_BF16) > 0
     assert chunk(T=0) == K.KLA_OK
 
 
-def test_long_few_head_forward_plans_segments(monkeypatch):
-    """B1 H16 T65536: the one-pass scan would occupy 64 of 256 compute units, so the plan
-    segments the sequence and the workspace grows by the segment buffers; B8 H8 T4096 does not."""
-    monkeypatch.delenv("KLA_FWD_SEGMENTS", raising=False)
+def test_segment_plan_argument():
+    """segments = 0 is the library's plan (kla_chunk_fwd's workspace); 1 is the one-pass scan;
+    a negative count is rejected before anything else, and its size query gives 0."""
     ws = lambda B, T, H: K.lib().kla_chunk_fwd_workspace_size(B, T, H, 128, 128, 64, K.KLA_BF16)
-    monkeypatch.setenv("KLA_FWD_SEGMENTS", "1")
-    one_long, one_b8 = ws(1, 65536, 16), ws(8, 4096, 8)
-    monkeypatch.delenv("KLA_FWD_SEGMENTS")
-    assert ws(1, 65536, 16) > one_long
-    assert ws(8, 4096, 8) == one_b8
+    seg = lambda B, T, H, n: K.lib().kla_chunk_fwd_seg_workspace_size(B, T, H, 128, 128, 64, n, K.KLA_BF16)
+    for B, T, H in ((1, 65536, 16), (8, 4096, 8), (1, 1000, 3)):
+        assert seg(B, T, H, 0) == ws(B, T, H)
+    assert seg(1, 1000, 3, 4) > seg(1, 1000, 3, 1)
+    assert seg(1, 1000, 3, -1) == 0
+    st = L().kla_chunk_fwd_seg(p(A16), p(A16 * 2), p(A16 * 3), p(A16 * 4), p(A16 * 5), None, None, p(A16 * 6),
+                               1, 64, 1, 128, 128, 64, -1, 1e-6, K.KLA_BF16, None, 0, None)
+    assert st == K.KLA_ERR_INVALID_VALUE and b"segment" in L().kla_last_error()
+
+
+def test_long_few_head_forward_plans_segments():
+    """B1 H16 T65536: the one-pass scan would occupy 64 of the full chip's 256 compute units, so the
+    plan segments the sequence and the workspace grows by the segment buffers; B8 H8 T4096 does not.
+    (With no device present the plan is made for the full MI355X.)"""
+    ws = lambda B, T, H: K.lib().kla_chunk_fwd_workspace_size(B, T, H, 128, 128, 64, K.KLA_BF16)
+    one = lambda B, T, H: K.lib().kla_chunk_fwd_seg_workspace_size(B, T, H, 128, 128, 64, 1, K.KLA_BF16)
+    assert ws(1, 65536, 16) > one(1, 65536, 16)
+    assert ws(8, 4096, 8) == one(8, 4096, 8)
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -1,9 +1,10 @@
-"""Pins for the fp64 gradient oracle (CPU only).
+"""Pins for the fp64 gradient oracles (CPU only).
 
-The gradients come from reverse-mode autodiff of the token loop. They are tied to
-things other than that autodiff: central finite differences of the NumPy forward
-oracle (itself pinned in test_oracle.py), hand-derived closed forms for a single token
-and for a pure-decay sequence, and exact homogeneity identities of the recurrence.
+The gradients come from two implementations of the same derivative of the token loop:
+reverse-mode autodiff (kla_grad, PyTorch) and the adjoint recurrence written out by hand
+(adjoint, NumPy). Each is tied to things other than itself: central finite differences
+of the NumPy forward oracle (itself pinned in test_oracle.py), hand-derived closed forms for a
+single token and for a pure-decay sequence, and exact homogeneity identities of the recurrence.
 """
 import math
 
@@ -11,9 +12,17 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import kla_grad
+from oracle import adjoint, kla_grad
 
 pytestmark = pytest.mark.filterwarnings("error::RuntimeWarning")
+
+# (KLA vjp, beta-given vjp) of each implementation; the adjoint checkpoints every 4 tokens here,
+# so that the short cases below still cross several recompute blocks.
+IMPLS = {
+    "autodiff": (oracle.kla_vjp, oracle.gated_delta_vjp),
+    "adjoint": (lambda *a: oracle.kla_adjoint(*a, block=4), lambda *a: oracle.gated_delta_adjoint(*a, block=4)),
+}
+impls = pytest.mark.parametrize("impl", sorted(IMPLS))
 
 
 def rand_case(rng, N, T, dk, dv, la=(0.001, 0.3)):
@@ -57,22 +66,24 @@ def _fd(fun, args, i, h=1e-6):
     return g
 
 
+@impls
 @pytest.mark.parametrize("eps", [0.3, 1e-6])
-def test_kla_gradients_match_finite_differences(eps):
+def test_kla_gradients_match_finite_differences(impl, eps):
     rng = np.random.default_rng(100)
     q, k, v, eta, la, S0, do, dST = rand_case(rng, 2, 7, 3, 4)
-    g = oracle.kla_vjp(q, k, v, eta, la, eps, S0, do, dST)
+    g = IMPLS[impl][0](q, k, v, eta, la, eps, S0, do, dST)
     args = (q, k, v, eta, la, eps, S0, do, dST)
     for name, i in (("dq", 0), ("dk", 1), ("dv", 2), ("deta", 3), ("dlog_alpha", 4), ("dS0", 6)):
         fd = _fd(_loss_kla, args, i)
         np.testing.assert_allclose(g[name], fd, rtol=1e-6, atol=1e-7, err_msg=name)
 
 
-def test_gdn_gradients_match_finite_differences():
+@impls
+def test_gdn_gradients_match_finite_differences(impl):
     rng = np.random.default_rng(101)
     q, k, v, eta, la, S0, do, dST = rand_case(rng, 2, 6, 4, 3)
     beta = rng.uniform(-0.5, 1.5, eta.shape)
-    g = oracle.gated_delta_vjp(q, k, v, beta, la, S0, do, dST)
+    g = IMPLS[impl][1](q, k, v, beta, la, S0, do, dST)
     args = (q, k, v, beta, la, S0, do, dST)
     for name, i in (("dq", 0), ("dk", 1), ("dv", 2), ("dbeta", 3), ("dlog_alpha", 4), ("dS0", 5)):
         fd = _fd(_loss_gdn, args, i)
@@ -92,7 +103,8 @@ def test_autodiff_loop_is_the_forward_oracle():
     np.testing.assert_allclose(S.numpy(), S_ref, rtol=0, atol=1e-13)
 
 
-def test_single_token_closed_forms():
+@impls
+def test_single_token_closed_forms(impl):
     """T = 1: o = alpha S0^T q + beta (k.q) (v - alpha S0^T k). By hand, for L = do.o:
     dq = S_1 do; dv = beta (k.q) do; dbeta = (k.q) (v - alpha S0^T k).do;
     dlog_alpha = alpha (S0^T q - beta (k.q) S0^T k).do; dS0 = alpha (q - beta (k.q) k) do^T;
@@ -118,20 +130,21 @@ def test_single_token_closed_forms():
             "dk": beta * (v @ do) * q - alpha * beta * ((k @ S0 @ do) * q + kq * S0 @ do)
                   - 2 * dbeta * eta / (n + eps) ** 2 * k,
         }
-        g = oracle.kla_vjp(q[None, None], k[None, None], v[None, None], np.array([[eta]]),
+        g = IMPLS[impl][0](q[None, None], k[None, None], v[None, None], np.array([[eta]]),
                            np.array([[math.log(alpha)]]), eps, S0[None], do[None, None])
         for name, val in exp.items():
             np.testing.assert_allclose(np.squeeze(g[name]), val, rtol=1e-12, atol=1e-14, err_msg=name)
 
 
-def test_pure_decay_closed_forms():
+@impls
+def test_pure_decay_closed_forms(impl):
     """eta = 0: o_t = e^{c_t} S0^T q_t with c_t = sum_{j<=t} log alpha_j and S_T = e^{c_T} S0, so
     dlog_alpha_j = sum_{t>=j} e^{c_t} do_t.(S0^T q_t) + e^{c_T} <S0, dS_T>, dq_t = e^{c_t} S0 do_t,
     dS0 = sum_t e^{c_t} q_t do_t^T + e^{c_T} dS_T, and dv = dk = 0."""
     rng = np.random.default_rng(104)
     q, k, v, _, la, S0, do, dST = rand_case(rng, 2, 9, 4, 3)
     eta = np.zeros((2, 9))
-    g = oracle.kla_vjp(q, k, v, eta, la, 1e-6, S0, do, dST)
+    g = IMPLS[impl][0](q, k, v, eta, la, 1e-6, S0, do, dST)
     c = np.cumsum(la, axis=1)
     a = np.einsum("ntj,nij,nti->nt", do, S0, q)
     ec = np.exp(c)
@@ -144,19 +157,20 @@ def test_pure_decay_closed_forms():
     assert np.abs(g["dv"]).max() == 0 and np.abs(g["dk"]).max() == 0
 
 
-def test_homogeneity_identities():
+@impls
+def test_homogeneity_identities(impl):
     """o is linear in q; (o, S_T) are jointly linear in (v, S0); with eps = 0 and S0 = 0,
     scaling every key by c scales (o, S_T) by 1/c. Euler's identity for each gives
     <q, dq> = <o, do>, <v, dv> + <S0, dS0> = L and <k, dk> = -L, where L = <o, do> + <S_T, dS_T>."""
     rng = np.random.default_rng(105)
     q, k, v, eta, la, S0, do, dST = rand_case(rng, 3, 30, 6, 5)
     o, S = oracle.kla_recurrent(q, k, v, eta, la, 1e-6, S0)
-    g = oracle.kla_vjp(q, k, v, eta, la, 1e-6, S0, do, dST)
+    g = IMPLS[impl][0](q, k, v, eta, la, 1e-6, S0, do, dST)
     L = np.sum(o * do) + np.sum(S * dST)
     assert np.sum(q * g["dq"]) == pytest.approx(np.sum(o * do), rel=1e-11)
     assert np.sum(v * g["dv"]) + np.sum(S0 * g["dS0"]) == pytest.approx(L, rel=1e-11)
     o, S = oracle.kla_recurrent(q, k, v, eta, la, 0.0)
-    g = oracle.kla_vjp(q, k, v, eta, la, 0.0, None, do, dST)
+    g = IMPLS[impl][0](q, k, v, eta, la, 0.0, None, do, dST)
     L = np.sum(o * do) + np.sum(S * dST)
     assert np.sum(k * g["dk"]) == pytest.approx(-L, rel=1e-11)
 
@@ -198,3 +212,29 @@ def test_planted_mistake_fails_a_pin():
     assert not np.allclose(wrong, fd, rtol=1e-6, atol=1e-7)
     right = oracle.kla_vjp(q, k, v, eta, la, eps, S0, do, dST)["dk"]
     np.testing.assert_allclose(right, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_adjoint_planted_mistake_fails_a_pin(monkeypatch):
+    """States recomputed without the decay (a slip in the adjoint's forward and block recompute)
+    leave the key gradients, which read those states, wrong, and the finite-difference pin sees it."""
+    rng = np.random.default_rng(108)
+    q, k, v, eta, la, S0, do, dST = rand_case(rng, 1, 9, 3, 3)
+    fd = _fd(_loss_kla, (q, k, v, eta, la, 0.3, S0, do, dST), 1)
+    right = oracle.kla_adjoint(q, k, v, eta, la, 0.3, S0, do, dST, block=4)["dk"]
+    np.testing.assert_allclose(right, fd, rtol=1e-6, atol=1e-7)
+    step = adjoint._step
+    monkeypatch.setattr(adjoint, "_step", lambda S, q_, k_, v_, b_, a_: step(S, q_, k_, v_, b_, np.ones_like(a_)))
+    wrong = oracle.kla_adjoint(q, k, v, eta, la, 0.3, S0, do, dST, block=4)["dk"]
+    assert not np.allclose(wrong, fd, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("block", [1, 5, 64])
+def test_adjoint_block_size_only_changes_rounding(block):
+    """The checkpoint spacing is a memory/time trade only: the gradients agree to rounding for
+    block sizes that do and do not divide T."""
+    rng = np.random.default_rng(109)
+    q, k, v, eta, la, S0, do, dST = rand_case(rng, 2, 23, 4, 3)
+    ref = oracle.kla_adjoint(q, k, v, eta, la, 1e-6, S0, do, dST, block=23)
+    g = oracle.kla_adjoint(q, k, v, eta, la, 1e-6, S0, do, dST, block=block)
+    for n in ref:
+        np.testing.assert_allclose(g[n], ref[n], rtol=1e-12, atol=1e-14, err_msg=n)

@@ -180,33 +180,50 @@ def custom(name: str, wid: int, **kw) -> Workload:
     return Workload(name=name, wid=wid, **kw)
 
 
+def head_grad(w: Workload, b: int, h: int, s0_std: float = 0.0, dst_std: float = 0.0) -> dict:
+    """Cotangents of one head: do [T, dv] (bf16-rounded for bf16 workloads), and, when the std is
+    positive, an initial state S0 and a final-state cotangent dST [dk, dv] fp32 (else None)."""
+    x = _rng(w, "do", b, h).standard_normal((w.T, w.dv), dtype=np.float32)
+    return {
+        "do": round_to_bf16(x) if w.dtype == "bf16" else x,
+        "S0": _rng(w, "S0_prefill", b, h).normal(0.0, s0_std, (w.dk, w.dv)).astype(np.float32) if s0_std > 0 else None,
+        "dST": _rng(w, "dST", b, h).normal(0.0, dst_std, (w.dk, w.dv)).astype(np.float32) if dst_std > 0 else None,
+    }
+
+
 def grad_inputs(w: Workload, s0_std: float = 0.0, dst_std: float = 0.0) -> dict:
-    """Cotangents for gradient checks, all heads: do [B, T, H, dv] (bf16-rounded for bf16
-    workloads), and, when the std is positive, an initial state S0 and a final-state cotangent
-    dST [B, H, dk, dv] fp32 (else None)."""
+    """Cotangents for gradient checks, all heads: do [B, T, H, dv] and, when the std is positive,
+    S0 and dST [B, H, dk, dv] (else None), as head_grad."""
     do = np.empty((w.B, w.T, w.H, w.dv), np.float32)
     S0 = np.empty((w.B, w.H, w.dk, w.dv), np.float32) if s0_std > 0 else None
     dST = np.empty((w.B, w.H, w.dk, w.dv), np.float32) if dst_std > 0 else None
     for b in range(w.B):
         for h in range(w.H):
-            x = _rng(w, "do", b, h).standard_normal((w.T, w.dv), dtype=np.float32)
-            do[b, :, h] = round_to_bf16(x) if w.dtype == "bf16" else x
+            d = head_grad(w, b, h, s0_std, dst_std)
+            do[b, :, h] = d["do"]
             if S0 is not None:
-                S0[b, h] = _rng(w, "S0_prefill", b, h).normal(0.0, s0_std, (w.dk, w.dv))
+                S0[b, h] = d["S0"]
             if dST is not None:
-                dST[b, h] = _rng(w, "dST", b, h).normal(0.0, dst_std, (w.dk, w.dv))
+                dST[b, h] = d["dST"]
     return {"do": do, "S0": S0, "dST": dST}
+
+
+def head_channel_log_decay(w: Workload, b: int, h: int, decode: bool = False) -> np.ndarray:
+    """Per-channel log decays of one head: [T, dk] (prefill) or [steps, dk] (decode), each element
+    -U(a_lo, a_hi) with the workload's scalar-gate range."""
+    a_lo, a_hi = w.log_alpha_range
+    n = w.steps if decode else w.T
+    return (-_rng(w, "dec_log_a" if decode else "log_a", b, h).uniform(a_lo, a_hi, (n, w.dk))).astype(np.float32)
 
 
 def channel_log_decay(w: Workload, decode: bool = False) -> np.ndarray:
     """Per-channel log decays for all heads: [B, T, H, dk] (prefill) or [steps, B, H, dk]
-    (decode), each element -U(a_lo, a_hi) with the workload's scalar-gate range."""
-    a_lo, a_hi = w.log_alpha_range
+    (decode), as head_channel_log_decay."""
     n = w.steps if decode else w.T
     out = np.empty((n, w.B, w.H, w.dk) if decode else (w.B, n, w.H, w.dk), np.float32)
     for b in range(w.B):
         for h in range(w.H):
-            x = -_rng(w, "dec_log_a" if decode else "log_a", b, h).uniform(a_lo, a_hi, (n, w.dk))
+            x = head_channel_log_decay(w, b, h, decode)
             if decode:
                 out[:, b, h] = x
             else:

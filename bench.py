@@ -16,6 +16,13 @@ are launched through the C ABI with pre-marshalled pointers on torch's current
 stream; the decode steps of a bench step are replayed from a HIP graph captured
 once before timing (--decode-launch eager issues them one call at a time). HIP
 events on that stream time each part. Prints one JSON line.
+
+After the timed steps, the default run also times, each alone and outside `value`, the
+other named workloads (B8 H8 T4096 and B1 H16 T65536 prefill behind a 512 MiB cache-evicting
+write, the B64 H16 1024-step decode) and a decode whose 512 MiB state exceeds the
+last-level cache, under parts["extra:<name>"] (--no-extras skips them). The CPU baseline
+times the fp64 oracle on the host's cores (worker processes, at most 16) on a bounded
+sample of the prefill and of the decode steps.
 """
 from __future__ import annotations
 
@@ -128,73 +135,119 @@ def unit_keys(k):
     return (k / np.maximum(n, 1e-3)).astype(np.float32)
 
 
-def cpu_baseline(w, head_tokens, mode="kla"):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload: every head
-    of the batch over the first head_tokens / (B H) prefill tokens (or decode steps). Single
-    threaded; the recurrence costs the same per token at any position."""
+def _oracle_leg(w, heads, n, leg, mode):
+    """One worker of the CPU baseline: regenerates the inputs of `heads` (the first n prefill tokens,
+    or n decode steps) and times the fp64 oracle on them alone. Returns (seconds, head-tokens)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    n = max(1, min(head_tokens // w.heads, w.T if w.T else w.steps))
-    if w.T and mode == "kda":
-        x = wl.prefill_inputs(w.with_(T=n))
-        la = wl.channel_log_decay(w.with_(T=n))
-        args = (x["q"], x["k"], x["v"], x["eta"], la, w.eps)
-        run = lambda: oracle.kda_forward(*args)
-        what = f"oracle kda_forward on all {w.heads} heads (B={w.B}, H={w.H}) of the first {n} prefill tokens"
-    elif w.T and mode != "kla":
-        x = wl.prefill_inputs(w.with_(T=n))
-        heads = lambda a: np.moveaxis(a, 2, 1).reshape(w.heads, n, *a.shape[3:])  # [B, T, H, ...] -> [BH, T, ...]
-        la = x["log_alpha"] if mode == "gdn" else np.zeros_like(x["log_alpha"])
-        args = (heads(x["q"]), heads(unit_keys(x["k"])), heads(x["v"]), heads(x["eta"]), heads(la))
-        run = lambda: oracle.gated_delta_recurrent(*args)
-        what = (f"oracle gated_delta_recurrent ({mode}) on all {w.heads} heads (B={w.B}, H={w.H}) of the first "
-                f"{n} prefill tokens")
-    elif w.T:
-        x = wl.prefill_inputs(w.with_(T=n))
-        args = (x["q"], x["k"], x["v"], x["eta"], x["log_alpha"], w.eps)
-        run = lambda: oracle.kla_forward(*args)
-        what = f"oracle kla_forward on all {w.heads} heads (B={w.B}, H={w.H}) of the first {n} prefill tokens"
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    if leg == "decode":
+        d = [wl.head_decode(w.with_(steps=n), b, h) for b, h in heads]
+        st = lambda key: np.stack([x[key] for x in d])
+        args = (st("q"), st("k"), st("v"), st("eta"), st("log_alpha"), w.eps, st("S0"))
+        run = lambda: oracle.kla_recurrent(*args)
     else:
-        x = wl.decode_inputs(w.with_(steps=n))
-        args = (x["q"], x["k"], x["v"], x["eta"], x["log_alpha"], w.eps, x["S0"])
-        run = lambda: oracle.kla_decode_steps(*args)
-        what = f"oracle decode on all {w.heads} heads (B={w.B}, H={w.H}) for the first {n} steps"
-    ctx = threadpool_limits(1) if threadpool_limits else None
+        ws = w.with_(T=n)
+        d = [wl.head_prefill(ws, b, h) for b, h in heads]
+        st = lambda key: np.stack([x[key] for x in d])
+        if mode == "kda":
+            la = np.stack([wl.head_channel_log_decay(ws, b, h) for b, h in heads])
+            k = st("k")
+            args = (st("q"), k, st("v"), oracle.kaczmarz_step_size(k, st("eta"), w.eps), la)
+            run = lambda: oracle.kda_recurrent(*args)
+        elif mode in ("gdn", "deltanet"):
+            la = st("log_alpha") if mode == "gdn" else np.zeros((len(heads), n))
+            args = (st("q"), unit_keys(st("k")), st("v"), st("eta"), la)
+            run = lambda: oracle.gated_delta_recurrent(*args)
+        else:
+            args = (st("q"), st("k"), st("v"), st("eta"), st("log_alpha"), w.eps)
+            run = lambda: oracle.kla_recurrent(*args)
     t0 = time.perf_counter()
-    if ctx:
-        with ctx:
-            run()
-    else:
-        run()
-    dt = time.perf_counter() - t0
-    tokens = w.B * n
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}: {tokens} tokens in {dt:.2f} s (fp64 numpy, one thread)"}
+    run()
+    return time.perf_counter() - t0, len(heads) * n
+
+
+def _oracle_pool_time(w, n, leg, mode, cores):
+    """Times the oracle over every head of w (n tokens or steps each), split over `cores` worker
+    processes that run at once. The leg's time is that of the slowest worker (input generation
+    excluded); also returns the mean rate of one worker, in head-tokens per second per core."""
+    import concurrent.futures
+    import multiprocessing
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    groups = [heads[i::cores] for i in range(cores) if heads[i::cores]]
+    with concurrent.futures.ProcessPoolExecutor(len(groups), mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_leg, [w] * len(groups), groups, [n] * len(groups), [leg] * len(groups),
+                          [mode] * len(groups)))
+    secs = max(t for t, _ in res)
+    per_core = sum(ht / t for t, ht in res) / len(res)
+    return secs, len(heads) * n, per_core, len(groups)
+
+
+def cpu_baseline(w, head_tokens, mode="kla"):
+    """The fp64 oracle, as it stands, timed on the host's cores (at most 16 worker processes, one
+    thread each) on a bounded sample of the same workload: every head over the first
+    head_tokens / (B H) prefill tokens, and every head over the workload's decode steps (at most
+    head_tokens / (B H)). The recurrence costs the same per token at any position, so each leg's
+    rate scales to the whole workload; value is one bench step's tokens (prefill B T plus decode
+    B steps) over the oracle time those rates give."""
+    avail = len(os.sched_getaffinity(0))
+    cores = max(1, min(avail, 16, w.heads))
+    legs, what = {}, []
+    if w.T:
+        n = max(1, min(head_tokens // w.heads, w.T))
+        secs, ht, per_core, used = _oracle_pool_time(w, n, "prefill", mode, cores)
+        legs["prefill"] = {"tokens_per_s": w.B * n / secs, "head_tokens": ht, "seconds": secs,
+                           "head_tokens_per_s_per_core": per_core}
+        what.append(f"prefill: all {w.heads} heads x the first {n} tokens ({ht} head-tokens) in {secs:.2f} s")
+    if w.steps:
+        n = max(1, min(head_tokens // w.heads, w.steps))
+        secs, ht, per_core, used = _oracle_pool_time(w, n, "decode", "kla", cores)
+        legs["decode"] = {"tokens_per_s": w.B * n / secs, "head_tokens": ht, "seconds": secs,
+                          "head_tokens_per_s_per_core": per_core}
+        what.append(f"decode: all {w.heads} heads x {n} steps ({ht} head-steps) in {secs:.2f} s")
+    t_step = (w.B * w.T / legs["prefill"]["tokens_per_s"] if w.T else 0.0) + (
+        w.B * w.steps / legs["decode"]["tokens_per_s"] if w.steps else 0.0)
+    single = 1.0 / ((w.heads * w.T / legs["prefill"]["head_tokens_per_s_per_core"] if w.T else 0.0) +
+                    (w.heads * w.steps / legs["decode"]["head_tokens_per_s_per_core"] if w.steps else 0.0))
+    return {"value": (w.B * w.T + w.B * w.steps) / t_step, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cores_available": avail, "legs": legs,
+            "single_core_value": (w.B * w.T + w.B * w.steps) * single,
+            "sample": (f"fp64 oracle ({'kda_recurrent' if mode == 'kda' else 'gated_delta_recurrent' if mode != 'kla' else 'kla_recurrent'}"
+                       f", numpy) in {cores} worker processes of one thread each, heads split between them; "
+                       + "; ".join(what) + "; a leg's time is its slowest worker's, input generation excluded")}
 
 
 def cpu_baseline_bwd(w, head_tokens):
-    """The fp64 gradient oracle (autodiff of the token loop), as it stands, on a bounded sample:
-    the first 8 heads (or all, if fewer) over the first head_tokens / 8 prefill tokens."""
+    """The fp64 gradient oracle (the adjoint of the token loop), as it stands, on a bounded sample:
+    every head over the first head_tokens / (B H) prefill tokens, in worker processes."""
+    import concurrent.futures
+    import multiprocessing
+    avail = len(os.sched_getaffinity(0))
+    cores = max(1, min(avail, 16, w.heads))
+    n = max(1, min(head_tokens // w.heads, w.T))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    groups = [heads[i::cores] for i in range(cores) if heads[i::cores]]
+    with concurrent.futures.ProcessPoolExecutor(len(groups), mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_bwd_leg, [w] * len(groups), groups, [n] * len(groups)))
+    secs = max(t for t, _ in res)
+    return {"value": w.B * n / secs, "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "cores_available": avail,
+            "sample": f"oracle kla_adjoint (fp64 numpy, one thread per worker) on all {w.heads} heads x the first "
+                      f"{n} prefill tokens in {len(groups)} worker processes: {len(heads) * n} head-tokens in "
+                      f"{secs:.2f} s (slowest worker; input generation excluded)"}
+
+
+def _oracle_bwd_leg(w, heads, n):
     import oracle
-    import torch
-    torch.set_num_threads(1)
-    nh = min(8, w.heads)
-    n = max(1, min(head_tokens // nh, w.T))
-    sub = w.with_(T=n)
-    x = wl.prefill_inputs(sub)
-    g = wl.grad_inputs(sub)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:nh]
-    sel = lambda a: np.stack([a[b, :, h] for b, h in heads])
-    args = (sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["eta"]), sel(x["log_alpha"]), w.eps, None, sel(g["do"]))
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    ws = w.with_(T=n)
+    d = [wl.head_prefill(ws, b, h) for b, h in heads]
+    g = [wl.head_grad(ws, b, h) for b, h in heads]
+    st = lambda key, src=d: np.stack([x[key] for x in src])
     t0 = time.perf_counter()
-    oracle.kla_vjp(*args)
-    dt = time.perf_counter() - t0
-    return {"value": nh * n / dt / w.H, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle kla_vjp (fp64 autodiff of the token loop, one thread) on {nh} heads x the first {n} "
-                      f"prefill tokens: {nh * n} head-tokens in {dt:.2f} s, reported per token of all {w.H} heads"}
+    oracle.kla_adjoint(st("q"), st("k"), st("v"), st("eta"), st("log_alpha"), w.eps, None, st("do", g))
+    return time.perf_counter() - t0, len(heads) * n
 
 
 def run_bwd(args, w):
@@ -279,6 +332,146 @@ def run_bwd(args, w):
     print(json.dumps(result), flush=True)
 
 
+# Extra workloads timed after the default step (in its JSON line, under parts["extra:<name>"]): the
+# other named workloads, each in its own launch configuration, and one decode whose state exceeds
+# the 256 MB last-level cache. Prefill launches follow a 512 MiB write that evicts the caches.
+EXTRAS = ("fwd_b8h8_t4096", "fwd_long_t65536", "decode_b64h16", "decode_b512h16")
+BIG_DECODE = wl.Workload("decode_b512h16", 5, B=512, H=16, dk=128, dv=128, steps=16, s0_std=0.02,
+                         note="KLA decode B512 H16 d128: 512 MiB fp32 state, twice the last-level cache")
+FLUSH_BYTES = 512 << 20
+
+
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def launch_floor_us(torch, device, n=512):
+    """Per-launch time of n graph-replayed kernels that do almost nothing (a 64-element add): the
+    floor under any one-kernel decode step on this stack."""
+    z = torch.zeros(64, device=device)
+    z.add_(1.0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            z.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = _events(torch, 3)
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return min(a.elapsed_time(b) for a, b in ev) * 1e3 / n
+
+
+def prefill_part(w, ms_list, es, extra=False):
+    ms = float(np.median(ms_list))
+    tokens = w.B * w.T
+    flops = chunk_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
+    nbytes = chunk_bytes(w, es)
+    peak = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
+    part = {"kernel": "chunk_prep_kernel + chunk_scan_kernel (+ seg_combine_kernel + seg_fix_kernel when the plan "
+                      "segments)", "launches_per_step": 1, "ms_per_step": ms, "kernel_avg_us": ms * 1e3,
+            "tokens": tokens, "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops,
+            "algorithmic_bytes": nbytes, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak, "hbm_gbs": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if extra:
+        part.update({"extra": True, "launches_timed": len(ms_list), "ms_min": float(min(ms_list)),
+                     "timing": "median of launches each preceded by a 512 MiB write (caches cold), HIP events"})
+    return part
+
+
+def decode_part(w, per_ms, es, launch, extra=False, launches=None):
+    nbytes = decode_bytes(w, es)
+    part = {"kernel": "decode_step_kernel", "launches_per_step": w.steps, "launch": launch,
+            "ms_per_step": per_ms * w.steps, "kernel_avg_us": per_ms * 1e3, "tokens": w.B * w.steps,
+            "tokens_per_s": w.B / (per_ms * 1e-3), "algorithmic_bytes_per_launch": nbytes,
+            "hbm_gbs": nbytes / (per_ms * 1e-3) / 1e9, "hbm_frac": nbytes / (per_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "state_bytes": w.heads * w.dk * w.dv * 4}
+    if extra:
+        part.update({"extra": True, "launches_timed": launches,
+                     "timing": "graph-replayed consecutive steps, best of 3 replays, HIP events"})
+    return part
+
+
+def time_extra(name, torch, K, L, device, stream, flush):
+    """Times one extra workload alone (kla mode) and returns its part."""
+    w = BIG_DECODE if name == BIG_DECODE.name else wl.WORKLOADS[name]
+    es = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
+    on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    log(f"[bench] extra {name}: generating ...")
+    if w.T:
+        x = wl.prefill_inputs(w)
+        t = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
+        del x
+        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
+        state = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=device)
+        ws_bytes = int(L.kla_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+        args = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), P(t["log_alpha"]), None, P(state), P(o),
+                w.B, w.T, w.H, w.dk, w.dv, 64, ctypes.c_float(w.eps), code, P(ws), ws_bytes, sp)
+        for _ in range(2):
+            K.check(L.kla_chunk_fwd(*args))
+        iters = 10 if w.heads * w.T <= (1 << 19) else 6
+        ev = _events(torch, iters)
+        for a, b in ev:
+            flush.fill_(1)
+            a.record(stream)
+            st = L.kla_chunk_fwd(*args)
+            b.record(stream)
+            K.check(st)
+        torch.cuda.synchronize()
+        part = prefill_part(w, [a.elapsed_time(b) for a, b in ev], es, extra=True)
+        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, "chunk_fwd")
+        part["workspace_bytes"] = ws_bytes
+        del t, o, state, ws
+    else:
+        x = wl.decode_inputs(w)
+        t = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
+        del x
+        state = t["S0"].clone()
+        out = torch.empty((w.steps, w.B, w.H, w.dv), dtype=tdt, device=device)
+        # 1024 steps for the named decode workload; the large-state one cycles its 16 input sets
+        # through 64 steps (the state still changes every step).
+        nlaunch = w.steps if w.steps >= 64 else 64
+        calls = []
+        for i in range(nlaunch):
+            s_ = i % w.steps
+            calls.append((P(t["q"][s_]), P(t["k"][s_]), P(t["v"][s_]), P(t["eta"][s_]), P(t["log_alpha"][s_]),
+                          P(state), P(out[s_]), w.B, w.H, w.dk, w.dv, ctypes.c_float(w.eps), code))
+        for c in calls[:2]:
+            K.check(L.kla_decode_step(*c, sp))
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gs = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+            for c in calls:
+                K.check(L.kla_decode_step(*c, gs))
+        torch.cuda.synchronize()
+        g.replay()
+        ev = _events(torch, 3)
+        for a, b in ev:
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = min(a.elapsed_time(b) for a, b in ev) / nlaunch
+        part = decode_part(w, per, es, "graph", extra=True, launches=nlaunch)
+        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, "decode")
+        del t, state, out, g
+    part["sources_sha"] = sources_sha("chunk_fwd" if w.T else "decode")
+    part["workload"] = w.note
+    torch.cuda.empty_cache()
+    return part
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +479,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the chosen workload (the default run also times " + ", ".join(EXTRAS) + ")")
     ap.add_argument("--mode", default="kla", choices=("kla", "gdn", "deltanet", "kda"),
                     help="kla: Kaczmarz step from eta (the headline); gdn: beta given (kla_gdn_* entry points, "
                          "beta drawn like eta, unit-norm keys); deltanet: gdn without the gate; kda: the Kaczmarz "
@@ -297,7 +492,7 @@ def main():
                     help="size of the oracle's bounded sample, in head-tokens")
     ap.add_argument("--pass", dest="pass_", default="fwd", choices=("fwd", "bwd"),
                     help="fwd: the hot path (default); bwd: the chunkwise backward over a prefill workload")
-    ap.add_argument("--cpu-bwd-head-tokens", type=int, default=8192,
+    ap.add_argument("--cpu-bwd-head-tokens", type=int, default=65536,
                     help="size of the gradient oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counter scaling)")
@@ -309,7 +504,7 @@ def main():
         sys.exit(2)
 
     import torch
-    import gated_delta_rule_18_amd as kla
+    import gated_delta_rule_18_amd as kla  # noqa: F401  (loads the library or raises)
     from gated_delta_rule_18_amd import _lib as K
 
     device = torch.device("cuda:0")
@@ -458,29 +653,13 @@ def main():
     dec_tokens = w.B * w.steps
     if fwd_args is not None:
         ms = sum(e["fwd"][0].elapsed_time(e["fwd"][1]) for e in evs) / args.steps
-        flops = chunk_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
-        nbytes = chunk_bytes(w, es)
-        segs = 1 if w.heads * (w.dv // (32 if es == 2 else 64)) >= 256 or w.T < 32 * 64 else None
-        parts["chunk_fwd"] = {
-            "kernel": "chunk_prep_kda_kernel + chunk_scan_kernel (KDA mode)" if args.mode == "kda" else
-                      "chunk_prep_kernel + chunk_scan_kernel" + (
-                          "" if segs == 1 else " (+ seg_combine_kernel + seg_fix_kernel when the plan segments)"),
-            "launches_per_step": 1, "ms_per_step": ms,
-            "kernel_avg_us": ms * 1e3, "tokens": fwd_tokens, "tokens_per_s": fwd_tokens / (ms * 1e-3),
-            "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
-            "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-            "mfma_frac": flops / (ms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS),
-            "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        part = prefill_part(w, [ms], es)
+        if kda:
+            part["kernel"] = "chunk_prep_kda_kernel + chunk_scan_kernel (KDA mode)"
+        parts["chunk_fwd"] = part
     if dec_args:
         ms = sum(e["dec"][0].elapsed_time(e["dec"][1]) for e in evs) / args.steps
-        per = ms / w.steps
-        nbytes = decode_bytes(w, es)
-        parts["decode"] = {
-            "kernel": "decode_step_kernel", "launches_per_step": w.steps, "launch": args.decode_launch,
-            "ms_per_step": ms,
-            "kernel_avg_us": per * 1e3, "tokens": dec_tokens, "tokens_per_s": dec_tokens / (ms * 1e-3),
-            "algorithmic_bytes_per_launch": nbytes,
-            "hbm_gbs": nbytes / (per * 1e-3) / 1e9, "hbm_frac": nbytes / (per * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        parts["decode"] = decode_part(w, ms / w.steps, es, args.decode_launch)
 
     for name, part in parts.items():
         part["sources_sha"] = sources_sha(name)
@@ -493,6 +672,15 @@ def main():
         roof["mfma_view"] = {"achieved": dom["mfma_tflops"],
                              "peak": PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS,
                              "unit": "TFLOP/s", "frac": dom["mfma_frac"]}
+    else:
+        # A graph-replayed kernel cannot take less than the launch floor measured here; state it
+        # beside the roofline so that the fraction is read against it.
+        floor = launch_floor_us(torch, device)
+        roof["launch_floor_us"] = floor
+        roof["kernel_avg_us"] = dom["kernel_avg_us"]
+        roof["note"] = (f"{dom['kernel_avg_us']:.2f} us per launch against a {floor:.2f} us per-launch floor (512 "
+                        f"graph-replayed 64-element adds); the HBM time of its algorithmic bytes is "
+                        f"{dom['algorithmic_bytes_per_launch'] / PEAK_HBM_GBS / 1e3:.2f} us")
 
     tokens_per_step = fwd_tokens + dec_tokens
     ms_step = elapsed * 1e3 / args.steps
@@ -514,6 +702,17 @@ def main():
         "parts": parts,
         "roofline": roof,
     }
+
+    # The other workloads, each alone (the default run only; they are not part of `value`).
+    if not args.no_extras and args.mode == "kla" and args.workload == "mixed_b4h16":
+        del pre, dec, workspace, dec_graph
+        torch.cuda.empty_cache()
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+        for name in EXTRAS:
+            parts["extra:" + name] = time_extra(name, torch, K, L, device, stream, flush)
+        del flush
+        torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on a bounded sample ({args.cpu_head_tokens} head-tokens)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_head_tokens, args.mode)

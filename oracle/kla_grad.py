@@ -26,16 +26,23 @@ Layouts follow ``kla_oracle``: head-major [N, T, d] inside, library layout
 from __future__ import annotations
 
 import numpy as np
-import torch
+
+
+def _torch():
+    # Imported on first use, so that importing the oracle package does not load PyTorch.
+    import torch
+    return torch
 
 
 def _t(x):
+    torch = _torch()
     return torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float64, requires_grad=True)
 
 
 def _loop(q, k, v, beta, log_alpha, S0):
     """The token recurrence ("Deep Dive into KDA", section 2.2, state stored [d_k, d_v]):
     S <- alpha_t S;  u = S^T k_t;  S <- S + beta_t k_t (v_t - u)^T;  o_t = S^T q_t."""
+    torch = _torch()
     T = k.shape[1]
     alpha = torch.exp(log_alpha)
     S = S0
@@ -55,6 +62,7 @@ def gated_delta_vjp(q, k, v, beta, log_alpha, S0, do, dST=None):
     per-token beta, head-major: q, k [N, T, d_k]; v, do [N, T, d_v]; beta, log_alpha [N, T];
     S0, dST [N, d_k, d_v] or None (zeros). Returns a dict of fp64 arrays:
     dq, dk, dv, dbeta, dlog_alpha, dS0."""
+    torch = _torch()
     N, T, dk = np.shape(k)
     dv = np.shape(v)[-1]
     q_, k_, v_, b_, la_ = map(_t, (q, k, v, beta, log_alpha))
@@ -73,6 +81,7 @@ def kla_vjp(q, k, v, eta, log_alpha, eps, S0, do, dST=None):
     """KLA gradients, head-major. beta_t = eta_t / (||k_t||^2 + eps) ("Kaczmarz Linear
     Attention", Abstract) is formed inside the differentiated graph, so dk includes the
     path through the step size. Returns dq, dk, dv, deta, dlog_alpha, dS0."""
+    torch = _torch()
     N, T, dk = np.shape(k)
     dv = np.shape(v)[-1]
     q_, k_, v_, e_, la_ = map(_t, (q, k, v, eta, log_alpha))

@@ -32,3 +32,20 @@ def rel_l2(x, ref):
 
 def report(name, **errs):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" for k, v in errs.items()), flush=True)
+
+
+def host32(t):
+    """A device tensor on the host as fp32 (exact for bf16 and fp32 values)."""
+    return t.float().cpu().numpy()
+
+
+def heads_of(x, heads, time_axis=1):
+    """[B, T, H, ...] (time_axis 1) or [steps, B, H, ...] (time_axis 0) -> [n, T, ...] for the listed heads."""
+    if time_axis == 1:
+        return np.stack([x[b, :, h] for b, h in heads])
+    return np.stack([x[:, b, h] for b, h in heads])
+
+
+def states_of(x, heads):
+    """[B, H, dk, dv] -> [n, dk, dv] for the listed heads."""
+    return np.stack([x[b, h] for b, h in heads])

@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.kla_testutil import TOL, dev, host, rel_l2, report
+from tests import oracle_pool as op
+from tests.kla_testutil import TOL, dev, heads_of, host, rel_l2, report, states_of
 
 pytestmark = pytest.mark.gpu
 
@@ -107,15 +108,19 @@ def test_chunk_bwd_tiny_f32_workload():
     compare("chunk_bwd fwd_tiny_f32", w, gpu_bwd(w, inp, g), oracle_bwd(w, inp, g, all_heads(w)), all_heads(w))
 
 
-def test_chunk_bwd_b8h8_t4096_sampled_heads():
-    """The B8 H8 T4096 d128 bf16 workload at full size, in the benchmark's launch; the oracle on
-    two sampled heads."""
+def test_chunk_bwd_b8h8_t4096_all_heads():
+    """The B8 H8 T4096 d128 bf16 workload at full size, in the benchmark's launch: every gradient of
+    every head against the oracle (the adjoint of the token loop; whole tensor, worst head, worst
+    64-token chunk)."""
     w = wl.WORKLOADS["fwd_b8h8_t4096"]
     inp = wl.prefill_inputs(w)
     g = wl.grad_inputs(w)
     got = gpu_bwd(w, inp, g)
-    for hd in ([(0, 0)], [(7, 5)]):
-        compare(f"chunk_bwd b8h8_t4096 head {hd[0]}", w, got, oracle_bwd(w, inp, g, hd), hd)
+    del inp, g
+    got_for = lambda hd: {**{n: heads_of(got[n], hd) for n in ("dq", "dk", "dv", "deta", "dlog_alpha")},
+                          "dS0": states_of(got["dS0"], hd)}
+    merged, heads = op.run("backward", w, got_for, (0.0, 0.0))
+    op.check("chunk_bwd b8h8_t4096", merged, heads, TOL[w.dtype])
 
 
 @pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])

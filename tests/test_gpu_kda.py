@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.kla_testutil import TOL, dev, host, rel_l2, report
+from tests import oracle_pool as op
+from tests.kla_testutil import TOL, dev, heads_of, host, host32, rel_l2, report, states_of
 
 pytestmark = pytest.mark.gpu
 
@@ -85,17 +86,28 @@ def test_kda_strong_and_mixed_decay(dtype):
     compare_fwd(f"kda strong/mixed decay {dtype}", w, inp, la)
 
 
-def test_kda_b8h8_t4096_sampled_heads():
-    """The B8 H8 T4096 d128 bf16 shape at full size with per-channel decays; two sampled heads."""
+def test_kda_b8h8_t4096_all_heads():
+    """The B8 H8 T4096 d128 bf16 shape at full size with per-channel decays: every head against the
+    oracle (whole tensor, worst head, worst 64-token chunk), on o and S_T."""
     w = wl.WORKLOADS["fwd_b8h8_t4096"]
     inp = wl.prefill_inputs(w)
-    compare_fwd("kda b8h8_t4096", w, inp, wl.channel_log_decay(w), heads=[(0, 0), (7, 5)])
+    o, S = kla.kla_kda_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                                 dev(inp["eta"]), dev(wl.channel_log_decay(w)), eps=w.eps)
+    del inp
+    torch.cuda.synchronize()
+    o_h, S_h = host32(o), host32(S)
+    merged, heads = op.run("forward", w, lambda g: {"o": heads_of(o_h, g), "S": states_of(S_h, g)}, ("kda",))
+    op.check("kda b8h8_t4096", merged, heads, TOL[w.dtype])
 
 
+# Head counts: 15 (16-column slices), 518 (32-column slices: a lane holds 16 rows, so k, q and
+# log a rows arrive by shuffle) and 1088 (64-column slices, 32 rows per lane).
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("beta_given", [False, True], ids=["kaczmarz", "beta"])
-def test_kda_decode_steps(dtype, beta_given):
-    w = wl.custom("kda_dec", 513, B=3, H=5, dk=128, dv=128, steps=20, dtype=dtype, s0_std=0.05)
+@pytest.mark.parametrize("B,H", [(3, 5), (37, 14), (64, 17)])
+def test_kda_decode_steps(dtype, beta_given, B, H):
+    w = wl.custom("kda_dec", 513, B=B, H=H, dk=128, dv=128, steps=20 if B * H < 256 else 6, dtype=dtype,
+                  s0_std=0.05)
     inp = wl.decode_inputs(w)
     la = wl.channel_log_decay(w, decode=True)
     kk = inp["k"]
@@ -117,7 +129,7 @@ def test_kda_decode_steps(dtype, beta_given):
                                   inp["S0"].reshape(N, w.dk, w.dv))
     eo = rel_l2(flat(np.stack(outs)), ro)
     eS = rel_l2(host(S).reshape(N, w.dk, w.dv), rS)
-    report(f"kda decode {dtype} {'beta' if beta_given else 'kaczmarz'}", o=eo, S=eS)
+    report(f"kda decode {dtype} {'beta' if beta_given else 'kaczmarz'} B={B} H={H}", o=eo, S=eS)
     assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
 
 

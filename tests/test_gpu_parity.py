@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.kla_testutil import TOL, dev, host, rel_l2, report
+from tests import oracle_pool as op
+from tests.kla_testutil import TOL, dev, heads_of, host, host32, rel_l2, report, states_of
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def test_prepare_beta(dtype, dk, T):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv,B,H", [(128, 128, 2, 3), (64, 64, 2, 3), (128, 64, 1, 5), (64, 128, 3, 1),
                                        (128, 128, 3, 5), (128, 128, 64, 17), (64, 64, 64, 17), (64, 128, 64, 17),
-                                       (128, 128, 37, 14)])
+                                       (128, 64, 64, 17), (128, 128, 37, 14)])
 def test_decode_steps_small(dtype, dk, dv, B, H):
     w = wl.custom("dec", 201, B=B, H=H, dk=dk, dv=dv, steps=12, dtype=dtype, s0_std=0.05)
     inp = wl.decode_inputs(w)
@@ -87,28 +88,21 @@ def test_decode_steps_small(dtype, dk, dv, B, H):
 
 
 def test_decode_workload_b64h16_1024_steps():
-    """Decode B64 H16 d128, 1024 consecutive steps from S0 ~ N(0, 0.02); oracle on sampled heads."""
+    """Decode B64 H16 d128, 1024 consecutive steps from S0 ~ N(0, 0.02): every one of the 1024 heads
+    against the oracle (whole tensor, worst head, worst 64-step window)."""
     w = wl.WORKLOADS["decode_b64h16"]
     inp = wl.decode_inputs(w)
     S = dev(inp["S0"])
     q, k, v = dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype)
     eta, la = dev(inp["eta"]), dev(inp["log_alpha"])
+    del inp
     o_all = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda:0")
     for s in range(w.steps):
         kla.kla_decode_step(q[s], k[s], v[s], eta[s], la[s], S, eps=w.eps, o=o_all[s])
     torch.cuda.synchronize()
-    heads = [(0, 0), (17, 5), (40, 9), (63, 15)]
-    o_h = host(o_all)
-    S_h = host(S)
-    for i, (b, h) in enumerate(heads):
-        ro, rS = oracle.kla_decode_steps(inp["q"][:, b:b + 1, h:h + 1], inp["k"][:, b:b + 1, h:h + 1],
-                                         inp["v"][:, b:b + 1, h:h + 1], inp["eta"][:, b:b + 1, h:h + 1],
-                                         inp["log_alpha"][:, b:b + 1, h:h + 1], w.eps, inp["S0"][b:b + 1, h:h + 1])
-        eo = rel_l2(o_h[:, b, h], ro[:, 0, 0])
-        eS = rel_l2(S_h[b, h], rS[0, 0])
-        report(f"decode_b64h16 head ({b},{h})", o=eo, S=eS)
-        assert eo <= TOL["bf16"] and eS <= TOL["bf16"]
-    assert np.isfinite(o_h).all() and np.isfinite(S_h).all()
+    o_h, S_h = host32(o_all), host32(S)
+    merged, heads = op.run("decode", w, lambda g: {"od": heads_of(o_h, g, 0), "S": states_of(S_h, g)})
+    op.check("decode_b64h16", merged, heads, TOL["bf16"])
 
 
 # ----------------------------------------------------------------------------- chunked forward
@@ -161,40 +155,49 @@ def test_chunk_fwd_fwd_tiny_f32_workload():
     check_fwd("fwd_tiny_f32", w, wl.prefill_inputs(w), all_heads(w))
 
 
+def full_size_fwd(name, w):
+    """A prefill workload at full size, in the launch the benchmark times (kla_chunk_fwd with the
+    library's plan): every head against the oracle (whole tensor, worst head, worst 64-token chunk),
+    on o and S_T."""
+    inp = wl.prefill_inputs(w)
+    o, S = kla.kla_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                             dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps)
+    del inp
+    torch.cuda.synchronize()
+    o_h, S_h = host32(o), host32(S)
+    merged, heads = op.run("forward", w, lambda g: {"o": heads_of(o_h, g), "S": states_of(S_h, g)})
+    op.check(name, merged, heads, TOL[w.dtype])
+
+
 def test_chunk_fwd_b8h8_t4096_workload():
-    w = wl.WORKLOADS["fwd_b8h8_t4096"]
-    check_fwd("fwd_b8h8_t4096 (sampled heads)", w, wl.prefill_inputs(w), [(0, 0), (3, 5), (7, 7)])
+    full_size_fwd("fwd_b8h8_t4096", wl.WORKLOADS["fwd_b8h8_t4096"])
 
 
 def test_chunk_fwd_long_t65536_workload():
-    w = wl.WORKLOADS["fwd_long_t65536"]
-    check_fwd("fwd_long_t65536 (sampled heads)", w, wl.prefill_inputs(w), [(0, 3), (0, 12)])
+    """B1 H16 T65536: the plan segments this one (few heads, long sequence)."""
+    full_size_fwd("fwd_long_t65536", wl.WORKLOADS["fwd_long_t65536"])
 
 
 def test_mixed_prefill_then_decode_workload():
-    """Prefill B4 H16 T32768, then 512 decode steps from its final states; sampled heads are
-    checked against one uninterrupted oracle recurrence over T + 512 tokens."""
+    """Prefill B4 H16 T32768, then 512 decode steps from its final states: every head against one
+    uninterrupted oracle recurrence over T + 512 tokens (prefill o, decode o, final state)."""
     w = wl.WORKLOADS["mixed_b4h16"]
     inp = wl.prefill_inputs(w)
     o, S = kla.kla_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
                              dev(inp["eta"]), dev(inp["log_alpha"]), eps=w.eps)
+    del inp
     dec = wl.decode_inputs(w)
     q, k, v = dev(dec["q"], w.dtype), dev(dec["k"], w.dtype), dev(dec["v"], w.dtype)
     eta, la = dev(dec["eta"]), dev(dec["log_alpha"])
+    del dec
     od = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.bfloat16, device="cuda:0")
     for s in range(w.steps):
         kla.kla_decode_step(q[s], k[s], v[s], eta[s], la[s], S, eps=w.eps, o=od[s])
     torch.cuda.synchronize()
-    o_h, od_h, S_h = host(o), host(od), host(S)
-    for b, h in [(0, 0), (3, 11)]:
-        cat = lambda a, d: np.concatenate([a[b, :, h], d[:, b, h]])[None]
-        ro, rS = oracle.kla_recurrent(cat(inp["q"], dec["q"]), cat(inp["k"], dec["k"]), cat(inp["v"], dec["v"]),
-                                      cat(inp["eta"], dec["eta"]), cat(inp["log_alpha"], dec["log_alpha"]), w.eps)
-        e_pre = rel_l2(o_h[b, :, h], ro[0, :w.T])
-        e_dec = rel_l2(od_h[:, b, h], ro[0, w.T:])
-        e_S = rel_l2(S_h[b, h], rS[0])
-        report(f"mixed_b4h16 head ({b},{h})", prefill_o=e_pre, decode_o=e_dec, S=e_S)
-        assert max(e_pre, e_dec, e_S) <= TOL["bf16"]
+    o_h, od_h, S_h = host32(o), host32(od), host32(S)
+    merged, heads = op.run("forward", w, lambda g: {"o": heads_of(o_h, g), "od": heads_of(od_h, g, 0),
+                                                   "S": states_of(S_h, g)})
+    op.check("mixed_b4h16", merged, heads, TOL["bf16"])
 
 
 # ----------------------------------------------------------------------------- edge cases
@@ -385,10 +388,13 @@ def test_gdn_with_the_kaczmarz_step_equals_kla():
     assert eo <= 1e-2 and eS <= 1e-2, (eo, eS)
 
 
+# Head counts: 15 (16-column slices), 518 (32-column slices) and 1088 (64-column slices).
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gated", [True, False], ids=["gdn", "deltanet"])
-def test_gdn_decode_steps(dtype, gated):
-    w = wl.custom("gdn_dec", 253, B=3, H=5, dk=128, dv=128, steps=20, dtype=dtype, s0_std=0.05)
+@pytest.mark.parametrize("B,H", [(3, 5), (37, 14), (64, 17)])
+def test_gdn_decode_steps(dtype, gated, B, H):
+    w = wl.custom("gdn_dec", 253, B=B, H=H, dk=128, dv=128, steps=20 if B * H < 256 else 6, dtype=dtype,
+                  s0_std=0.05)
     inp = wl.decode_inputs(w)
     kk = _unit_keys(inp["k"])
     kk = wl.round_to_bf16(kk) if dtype == "bf16" else kk
@@ -408,5 +414,5 @@ def test_gdn_decode_steps(dtype, gated):
                                           inp["S0"].reshape(N, w.dk, w.dv))
     eo = rel_l2(flat(np.stack(outs)), ro)
     eS = rel_l2(host(S).reshape(N, w.dk, w.dv), rS)
-    report(f"gdn decode {dtype} {'gated' if gated else 'deltanet'}", o=eo, S=eS)
+    report(f"gdn decode {dtype} {'gated' if gated else 'deltanet'} B={B} H={H}", o=eo, S=eS)
     assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)

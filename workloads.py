@@ -25,7 +25,10 @@ stream: step s is row s.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import math
+import multiprocessing
+import os
 from dataclasses import dataclass, field, replace
 
 import numpy as np
@@ -136,6 +139,24 @@ def head_decode(w: Workload, b: int, h: int) -> dict:
     return d
 
 
+def _heads_block(fn, w: Workload, heads) -> list:
+    return [fn(w, b, h) for b, h in heads]
+
+
+def _per_head(fn, w: Workload, elements: int) -> list:
+    """fn(w, b, h) for every head in (b, h) order. Large workloads (more than 2^26 drawn elements)
+    are drawn in worker processes, one block of heads each; every head has its own stream, so the
+    values do not depend on how the heads are split."""
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    nw = min(len(os.sched_getaffinity(0)), 16, len(heads))
+    if elements < (1 << 26) or nw < 2:
+        return _heads_block(fn, w, heads)
+    blocks = [heads[i * len(heads) // nw:(i + 1) * len(heads) // nw] for i in range(nw)]
+    with concurrent.futures.ProcessPoolExecutor(nw, mp_context=multiprocessing.get_context("spawn")) as ex:
+        parts = ex.map(_heads_block, [fn] * nw, [w] * nw, blocks)
+        return [d for part in parts for d in part]
+
+
 def prefill_inputs(w: Workload) -> dict:
     """All heads in the library layout: q, k [B, T, H, dk], v [B, T, H, dv], eta, log_alpha [B, T, H]."""
     out = {
@@ -145,11 +166,10 @@ def prefill_inputs(w: Workload) -> dict:
         "eta": np.empty((w.B, w.T, w.H), np.float32),
         "log_alpha": np.empty((w.B, w.T, w.H), np.float32),
     }
-    for b in range(w.B):
-        for h in range(w.H):
-            d = head_prefill(w, b, h)
-            for name, arr in d.items():
-                out[name][b, :, h] = arr
+    for i, d in enumerate(_per_head(head_prefill, w, w.heads * w.T * (2 * w.dk + w.dv))):
+        b, h = divmod(i, w.H)
+        for name, arr in d.items():
+            out[name][b, :, h] = arr
     return out
 
 
@@ -164,14 +184,13 @@ def decode_inputs(w: Workload) -> dict:
         "log_alpha": np.empty((w.steps, w.B, w.H), np.float32),
         "S0": np.empty((w.B, w.H, w.dk, w.dv), np.float32),
     }
-    for b in range(w.B):
-        for h in range(w.H):
-            d = head_decode(w, b, h)
-            for name, arr in d.items():
-                if name == "S0":
-                    out[name][b, h] = arr
-                else:
-                    out[name][:, b, h] = arr
+    for i, d in enumerate(_per_head(head_decode, w, w.heads * (w.steps * (2 * w.dk + w.dv) + w.dk * w.dv))):
+        b, h = divmod(i, w.H)
+        for name, arr in d.items():
+            if name == "S0":
+                out[name][b, h] = arr
+            else:
+                out[name][:, b, h] = arr
     return out
 
 

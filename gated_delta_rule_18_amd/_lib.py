@@ -51,11 +51,20 @@ class KLAError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded C library (loaded on first use). Raises if it has not been built."""
+    """The loaded C library (loaded on first use). Raises if it has not been built.
+
+    PyTorch is imported first when it is installed: it ships its own HIP runtime, and the
+    library's dependency on libamdhip64.so.7 must resolve to that same, already loaded runtime
+    (one runtime per process, so torch's device pointers and streams are the library's). Loaded
+    the other way round, the system runtime comes in first and torch then finds no GPU."""
     global _lib
     if _lib is None:
         if not LIB_PATH.exists():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_18_amd.build`")
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover
+            pass
         handle = ctypes.CDLL(str(LIB_PATH))
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 import gated_delta_rule_18_amd as kla  # noqa: E402
 
 
-def heads_of(w):
+def all_heads_of(w):
     return [(b, h) for b in range(w.B) for h in range(w.H)]
 
 
@@ -25,7 +25,7 @@ def compare_fwd(name, w, inp, log_a, beta_given=False, S0=None, heads=None, tol=
                                  dev(inp["eta"]), dev(log_a), eps=w.eps, beta_given=beta_given,
                                  state_in=None if S0 is None else dev(S0))
     torch.cuda.synchronize()
-    heads = heads_of(w) if heads is None else heads
+    heads = all_heads_of(w) if heads is None else heads
     sub = lambda x: np.stack([x[b, :, h] for b, h in heads])[:, :, None]  # [n, T, 1, ...] (library layout, B=n H=1)
     s0 = None if S0 is None else np.stack([S0[b, h] for b, h in heads])[:, None]
     ro, rS = oracle.kda_forward(sub(inp["q"]), sub(inp["k"]), sub(inp["v"]), sub(inp["eta"]), sub(log_a), w.eps, s0,

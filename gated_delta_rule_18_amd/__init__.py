@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     kla_chunk_bwd,
     kla_chunk_bwd_workspace_size,
     kla_chunk_fwd,
+    kla_chunk_fwd_noalloc,
     kla_chunk_fwd_workspace_size,
     kla_decode_step,
     kla_gdn_chunk_bwd,

@@ -26,6 +26,7 @@ _SIGNATURES = {
     "kla_prepare_beta": (_int, [_c_void_p] * 5 + [_i64] * 5 + [_f32, _int, _c_void_p]),
     "kla_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_chunk_fwd_noalloc": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p]),
     "kla_chunk_fwd_seg_workspace_size": (ctypes.c_size_t, [_i64] * 7 + [_int]),
     "kla_chunk_fwd_seg": (_int, [_c_void_p] * 8 + [_i64] * 7 + [_f32, _int, _c_void_p, ctypes.c_size_t,
                                                                 _c_void_p]),
@@ -195,6 +196,19 @@ def kla_chunk_fwd(q, k, v, eta, log_alpha, eps=1e-6, state_in=None, return_state
         check(lib().kla_chunk_fwd(*head, *tail))
     else:
         check(lib().kla_chunk_fwd_seg(*head, int(segments), *tail))
+    return o, state_out
+
+
+def kla_chunk_fwd_noalloc(q, k, v, eta, log_alpha, o, eps=1e-6, state_in=None, state_out=None, chunk=CHUNK,
+                          stream=None):
+    """kla_chunk_fwd through the entry point that allocates nothing (its workspace is the library's
+    static scratch): the caller passes every output (o, and state_out or None). Returns (o, state_out)."""
+    torch = _torch()
+    B, T, H, dk, dv, dev, o, state_out = _fwd_tensors(q, k, v, "eta", eta, log_alpha, False, state_in, False, o,
+                                                      state_out)
+    check(lib().kla_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_alpha), _ptr(state_in),
+                                      _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, float(eps), _dtype_code(q),
+                                      _stream(dev, stream)))
     return o, state_out
 
 

@@ -4,9 +4,15 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kla.h"
 #include "kla_launch.h"
+
+// Workspace of kla_chunk_fwd_noalloc, for callers that cannot allocate: one copy per device, held
+// from the library's first use of that device until the process ends. In host code `scratch` only
+// names the symbol; its device address on each device comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -53,6 +59,29 @@ bool mul_ok(int64_t& acc, int64_t x) {
   if (x != 0 && acc > (int64_t(1) << 62) / x) return false;
   acc *= x;
   return true;
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current device: looked up on the first call on each device,
+// with that device current, and kept per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -142,12 +171,13 @@ namespace {
 // kla_chunk_fwd, kla_gdn_chunk_fwd and kla_kda_chunk_fwd: eta is eta (Kaczmarz step) or beta itself
 // (beta_given, where a scalar log_alpha may be null for alpha = 1); with kda, log_alpha is the
 // per-channel log a [B, T, H, d_k] and required.
-// segments: the scan's sequence segments (0: the library's plan).
+// segments: the scan's sequence segments (0: the library's plan). use_scratch: the workspace is the
+// library's static `scratch` (workspace and workspace_bytes are ignored).
 kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                             const float* eta, const float* log_alpha, const float* state_in, float* state_out,
                             void* o, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                             float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream,
-                            int64_t segments = 0) {
+                            int64_t segments = 0, bool use_scratch = false) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (segments < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative segment count", fn);
@@ -175,6 +205,21 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
   const size_t need = kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
                           : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (T > 0 && need > KLA_NOALLOC_SCRATCH_BYTES) {
+      char msg[160];
+      std::snprintf(msg, sizeof(msg), "these sizes need %zu bytes of workspace, more than the %zu of the static scratch",
+                    need, (size_t)KLA_NOALLOC_SCRATCH_BYTES);
+      return fail(KLA_ERR_NOT_SUPPORTED, "%s: %s", fn, msg);
+    }
+    if (T > 0 && need > 0) {
+      const hipError_t e = scratch_address(&workspace);
+      if (e != hipSuccess) return launched(e, fn);
+      workspace_bytes = KLA_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (T > 0 && need > 0 && (!workspace || workspace_bytes < need))
     return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
   const int64_t es = dt == KLA_BF16 ? 2 : 4;
@@ -323,6 +368,14 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl("kla_chunk_fwd", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v,
                         chunk, eps, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* eta,
+                                   const float* log_alpha, const float* state_in, float* state_out, void* o, int64_t B,
+                                   int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps,
+                                   kla_dtype_t dt, void* stream) {
+  return chunk_fwd_impl("kla_chunk_fwd_noalloc", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T,
+                        H, d_k, d_v, chunk, eps, dt, nullptr, 0, stream, 0, true);
 }
 
 kla_status_t kla_chunk_fwd_seg(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,

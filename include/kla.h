@@ -106,6 +106,29 @@ kla_status_t kla_chunk_fwd(const void* q, const void* k, const void* v,
                            void* stream);
 
 /*
+ * kla_chunk_fwd_noalloc — kla_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. The caller passes
+ * inputs and outputs only; the workspace is a static device array of KLA_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) inside the library, one per device, held from the first call on that device until the
+ * process ends. The call allocates nothing (no hipMalloc, no hipFree, no allocating routine).
+ *   Sizes: accepted while kla_chunk_fwd_workspace_size(...) <= KLA_NOALLOC_SCRATCH_BYTES (for bf16
+ *   and d_k = d_v = 128 about 17 KiB per 64-token chunk of one head: B * H * ceil(T / 64) up to
+ *   7 710 on the one-pass plan); larger ones return KLA_ERR_NOT_SUPPORTED, with both sizes in
+ *   kla_last_error(), and enqueue nothing.
+ *   Every call on one device shares that device's array, which keeps the last call's contents (no
+ *   part of it needs clearing: a call writes every byte it reads). Calls that overlap in time on
+ *   one device (on different streams, or from different host threads) race on it and give wrong
+ *   results: serialise them.
+ * Otherwise exactly kla_chunk_fwd (same plan, same kernels, the same results bit for bit).
+ */
+#define KLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kla_status_t kla_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* eta, const float* log_alpha,
+                                   const float* state_in, float* state_out, void* o,
+                                   int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                   float eps, kla_dtype_t dt, void* stream);
+
+/*
  * kla_chunk_fwd_seg_workspace_size / kla_chunk_fwd_seg — kla_chunk_fwd with the scan's plan given
  * by the caller instead of chosen by the library.
  * Source: "Deep Dive into KDA", section 3 (each chunk maps the entering state to an affine

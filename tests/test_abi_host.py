@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol():
                           "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
                           "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd",
                           "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step",
-                          "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg"}
+                          "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg", "kla_chunk_fwd_noalloc"}
     for n in names:
         assert hasattr(L(), n), n
 

@@ -262,7 +262,7 @@ def run_bwd(args, w):
     gdn = args.mode != "kla"
     log(f"[bench] generating {w.name} ({w.note}) and its output cotangent ...")
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
-    x = wl.prefill_inputs(w)
+    x = wl.prefill_inputs(w, GEN_WORKERS)
     if gdn:
         x["k"] = unit_keys(x["k"])
     x["do"] = wl.grad_inputs(w)["do"]
@@ -339,6 +339,7 @@ EXTRAS = ("fwd_b8h8_t4096", "fwd_long_t65536", "decode_b64h16", "decode_b512h16"
 BIG_DECODE = wl.Workload("decode_b512h16", 5, B=512, H=16, dk=128, dv=128, steps=16, s0_std=0.02,
                          note="KLA decode B512 H16 d128: 512 MiB fp32 state, twice the last-level cache")
 FLUSH_BYTES = 512 << 20
+GEN_WORKERS = None  # --gen-workers
 
 
 def _events(torch, n):
@@ -408,7 +409,7 @@ def time_extra(name, torch, K, L, device, stream, flush):
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     log(f"[bench] extra {name}: generating ...")
     if w.T:
-        x = wl.prefill_inputs(w)
+        x = wl.prefill_inputs(w, GEN_WORKERS)
         t = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         o = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
@@ -433,7 +434,7 @@ def time_extra(name, torch, K, L, device, stream, flush):
         part["workspace_bytes"] = ws_bytes
         del t, o, state, ws
     else:
-        x = wl.decode_inputs(w)
+        x = wl.decode_inputs(w, GEN_WORKERS)
         t = {n: on(x[n], tdt if n in ("q", "k", "v") else torch.float32) for n in x}
         del x
         state = t["S0"].clone()
@@ -496,7 +497,13 @@ def main():
                     help="size of the gradient oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM counter scaling)")
+    ap.add_argument("--gen-workers", type=int, default=None,
+                    help="processes that draw the inputs (default: the CPUs available, up to 16); 1 draws them "
+                         "in this process, as profiled runs need (a profiler's preload would open the GPU in "
+                         "every worker)")
     args = ap.parse_args()
+    global GEN_WORKERS
+    GEN_WORKERS = args.gen_workers
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -540,7 +547,7 @@ def main():
     gdn = args.mode in ("gdn", "deltanet")
     kda = args.mode == "kda"
     if w.T:
-        x = wl.prefill_inputs(w)
+        x = wl.prefill_inputs(w, GEN_WORKERS)
         if gdn:
             x["k"] = unit_keys(x["k"])
         if kda:
@@ -550,7 +557,7 @@ def main():
         pre["o"] = torch.empty((w.B, w.T, w.H, w.dv), dtype=tdt, device=device)
     state = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=device)
     if w.steps:
-        x = wl.decode_inputs(w)
+        x = wl.decode_inputs(w, GEN_WORKERS)
         if gdn:
             x["k"] = unit_keys(x["k"])
         if kda:

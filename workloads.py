@@ -143,12 +143,13 @@ def _heads_block(fn, w: Workload, heads) -> list:
     return [fn(w, b, h) for b, h in heads]
 
 
-def _per_head(fn, w: Workload, elements: int) -> list:
+def _per_head(fn, w: Workload, elements: int, workers=None) -> list:
     """fn(w, b, h) for every head in (b, h) order. Large workloads (more than 2^26 drawn elements)
-    are drawn in worker processes, one block of heads each; every head has its own stream, so the
-    values do not depend on how the heads are split."""
+    are drawn in worker processes (`workers`, default the CPUs available up to 16; 1 draws in this
+    process), one block of heads each; every head has its own stream, so the values do not depend
+    on how the heads are split."""
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    nw = min(len(os.sched_getaffinity(0)), 16, len(heads))
+    nw = min(len(os.sched_getaffinity(0)) if workers is None else workers, 16, len(heads))
     if elements < (1 << 26) or nw < 2:
         return _heads_block(fn, w, heads)
     blocks = [heads[i * len(heads) // nw:(i + 1) * len(heads) // nw] for i in range(nw)]
@@ -157,7 +158,7 @@ def _per_head(fn, w: Workload, elements: int) -> list:
         return [d for part in parts for d in part]
 
 
-def prefill_inputs(w: Workload) -> dict:
+def prefill_inputs(w: Workload, workers=None) -> dict:
     """All heads in the library layout: q, k [B, T, H, dk], v [B, T, H, dv], eta, log_alpha [B, T, H]."""
     out = {
         "q": np.empty((w.B, w.T, w.H, w.dk), np.float32),
@@ -166,14 +167,14 @@ def prefill_inputs(w: Workload) -> dict:
         "eta": np.empty((w.B, w.T, w.H), np.float32),
         "log_alpha": np.empty((w.B, w.T, w.H), np.float32),
     }
-    for i, d in enumerate(_per_head(head_prefill, w, w.heads * w.T * (2 * w.dk + w.dv))):
+    for i, d in enumerate(_per_head(head_prefill, w, w.heads * w.T * (2 * w.dk + w.dv), workers)):
         b, h = divmod(i, w.H)
         for name, arr in d.items():
             out[name][b, :, h] = arr
     return out
 
 
-def decode_inputs(w: Workload) -> dict:
+def decode_inputs(w: Workload, workers=None) -> dict:
     """All heads, all steps: q, k [steps, B, H, dk], v [steps, B, H, dv], eta, log_alpha [steps, B, H],
     S0 [B, H, dk, dv]. Step s is the slice [s]."""
     out = {
@@ -184,7 +185,8 @@ def decode_inputs(w: Workload) -> dict:
         "log_alpha": np.empty((w.steps, w.B, w.H), np.float32),
         "S0": np.empty((w.B, w.H, w.dk, w.dv), np.float32),
     }
-    for i, d in enumerate(_per_head(head_decode, w, w.heads * (w.steps * (2 * w.dk + w.dv) + w.dk * w.dv))):
+    for i, d in enumerate(_per_head(head_decode, w, w.heads * (w.steps * (2 * w.dk + w.dv) + w.dk * w.dv),
+                                    workers)):
         b, h = divmod(i, w.H)
         for name, arr in d.items():
             if name == "S0":

@@ -344,27 +344,88 @@ chunk_scan_kernel(ChunkParams p) {
       }
     }
     f32x4 X[4][NT], Y[NT][4];
+    // One-pass bf16 forward (EARLY): the operands of the later products are read early: T and P
+    // fragments (the groups below the diagonal), the V columns and the per-token factors. (The
+    // other modes keep their reads beside their products: the segment pass would spill.)
+    constexpr bool EARLY = PERM && MODE == kScanFwd;
+    constexpr int NTF = EARLY ? 6 : 1;  // T / P fragments: row tiles 0, 1 need group 0; 2, 3 groups 0, 1
+    GV ft[NTF], fp[NTF];
+    f32x4 fv[4][NT], fcoef[4], feg[4];
+    auto tp_slot = [](int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; };
+    if constexpr (EARLY) {
+      // X = K S and Y^T = S^T Q^T as a two-stage pipeline over the four token tiles: the eight
+      // fragment reads of tile r + 1 are issued before the eight products of tile r, so that each
+      // product finds its operands in registers (issued one or two ahead, every product waited
+      // for its read). The fences keep the scheduler from pulling the reads back to their uses.
+      GV fk[2][NGD], fq[2][NGD];
+      auto load_xy = [&](int r, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+        for (int s = 0; s < NGD; ++s) {
+          fk[slot][s] = row8_grp<DK, kLayTok>(B.K, tok_row(r, c16), s, g);
+          if constexpr (!REC) fq[slot][s] = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+        }
+      };
+      load_xy(0, 0);
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) X[r][ct] = Y[ct][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) {
+        if (r + 1 < 4) {
+          load_xy(r + 1, (r + 1) & 1);
+        } else {
+          // The last tile's products cover the reads of everything the rest of the step reads
+          // from this chunk's buffer, except K^T for the state update (read with its products).
 #pragma unroll
-      for (int s = 0; s < NGD; ++s) {
-        GV ak;
-        if constexpr (PERM)
-          ak = row8_grp<DK, kLayTok>(B.K, tok_row(r, c16), s, g);
-        else
-          ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
+          for (int rr = 0; rr < 4; ++rr) {
+            fcoef[rr] = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + trow4(rr)]);
+            feg[rr] = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + trow4(rr)]);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
-        if constexpr (!REC) {
-          GV aq;
+            for (int ct = 0; ct < NT; ++ct) fv[rr][ct] = col4<E, DVS, LT>(B.V, tok_row(rr, 0), cw + 16 * ct, g, c16);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              if (GK * s2 < 16 * (rr + 1)) {
+                ft[tp_slot(rr, s2)] = row8_grp<kChunk, kLayTok>(B.T, tok_row(rr, c16), s2, g);
+                if constexpr (!REC) fp[tp_slot(rr, s2)] = row8_grp<kChunk, kLayLin>(B.P, 16 * rr + c16, s2, g);
+              }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) X[r][ct] = Y[ct][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NGD; ++s) {
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(fk[r & 1][s], sb[s][ct], X[r][ct]);
+          if constexpr (!REC) {
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], fq[r & 1][s], Y[ct][r]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) X[r][ct] = Y[ct][r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NGD; ++s) {
+          GV ak;
           if constexpr (PERM)
-            aq = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+            ak = row8_grp<DK, kLayTok>(B.K, tok_row(r, c16), s, g);
           else
-            aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
+            ak = row_grp<E, DK>(B.K, 16 * r + c16, s, g);
 #pragma unroll
-          for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
+          for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(ak, sb[s][ct], X[r][ct]);
+          if constexpr (!REC) {
+            GV aq;
+            if constexpr (PERM)
+              aq = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+            else
+              aq = row_grp<E, DK>(B.Q, 16 * r + c16, s, g);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], aq, Y[ct][r]);
+          }
         }
       }
     }
@@ -377,11 +438,12 @@ chunk_scan_kernel(ChunkParams p) {
     const float vscale = mpart ? 0.f : 1.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const f32x4 coefR = *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + trow4(r)]);
-      const f32x4 eG = *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + trow4(r)]);
+      const f32x4 coefR = EARLY ? fcoef[r] : *reinterpret_cast<const f32x4*>(&B.sc[kScCoefR * kChunk + trow4(r)]);
+      const f32x4 eG = EARLY ? feg[r] : *reinterpret_cast<const f32x4*>(&B.sc[kScEG * kChunk + trow4(r)]);
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct) {
-        const f32x4 v = vscale * col4<E, DVS, LT>(B.V, PERM ? tok_row(r, 0) : 16 * r, cw + 16 * ct, g, c16);
+        const f32x4 v = vscale * (EARLY ? fv[r][ct]
+                                        : col4<E, DVS, LT>(B.V, PERM ? tok_row(r, 0) : 16 * r, cw + 16 * ct, g, c16));
         X[r][ct] = coefR * (v - eG * X[r][ct]);
       }
     }
@@ -404,7 +466,9 @@ chunk_scan_kernel(ChunkParams p) {
       for (int s = 0; s < NGT; ++s) {
         if (GK * s < 16 * (r + 1)) {
           GV at_;
-          if constexpr (PERM)
+          if constexpr (EARLY)
+            at_ = ft[tp_slot(r, s)];
+          else if constexpr (PERM)
             at_ = row8_grp<kChunk, kLayTok>(B.T, tok_row(r, c16), s, g);
           else
             at_ = row_grp<E, kChunk>(B.T, 16 * r + c16, s, g);
@@ -447,7 +511,9 @@ chunk_scan_kernel(ChunkParams p) {
       for (int s = 0; s < NGT; ++s) {
         if (GK * s < 16 * (r + 1)) {
           GV ap;
-          if constexpr (PERM)
+          if constexpr (EARLY)
+            ap = fp[tp_slot(r, s)];
+          else if constexpr (PERM)
             ap = row8_grp<kChunk, kLayLin>(B.P, 16 * r + c16, s, g);
           else
             ap = row_grp<E, kChunk>(B.P, 16 * r + c16, s, g);

@@ -82,8 +82,9 @@ struct Workspace {
 };
 
 // Modes of the scan kernel: the forward; the backward's recompute (entering states and Delta
-// to the backward workspace, no outputs); the first pass of the segment scan (below).
-enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3 };
+// to the backward workspace, no outputs); the first pass of the segment scan (below); the
+// forward with the per-channel decay (KDA); and the first segment pass with that decay.
+enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3, kScanKdaSeg = 4 };
 
 // State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four). The bf16
 // segment scan uses four waves (64 columns): with half the workgroups per segment, twice the
@@ -106,6 +107,8 @@ struct SegPlan {
   int64_t nseg, seg_len;
 };
 
+// The segment buffers follow the forward's workspace (ChunkParams::seg_off bytes into it: the
+// scalar gate's Workspace, or with the per-channel decay the KdaSpace below).
 template <typename E>
 struct SegSpace {
   E* Y;         // [n][64][DK]: outputs of the identity columns
@@ -113,11 +116,10 @@ struct SegSpace {
   float* Mseg;  // [heads * nseg][DK][DK]: state transition of each segment
   E* SinT;      // [heads * nseg][DV][DK]: entering state of each segment, transposed (pass 2)
   __host__ __device__ static size_t bytes(int64_t n, int64_t nsegs, int dk, int dv) {
-    return Workspace<E>::bytes(n) + (size_t)n * kChunk * dk * sizeof(E) +
-           (size_t)nsegs * ((dk * dv + dk * dk) * sizeof(float) + dk * dv * sizeof(E));
+    return (size_t)n * kChunk * dk * sizeof(E) + (size_t)nsegs * ((dk * dv + dk * dk) * sizeof(float) + dk * dv * sizeof(E));
   }
-  __host__ __device__ static SegSpace at(void* base, int64_t n, int64_t nsegs, int dk, int dv) {
-    char* p = static_cast<char*>(base) + Workspace<E>::bytes(n);
+  __host__ __device__ static SegSpace at(void* base, size_t off, int64_t n, int64_t nsegs, int dk, int dv) {
+    char* p = static_cast<char*>(base) + off;
     SegSpace w;
     w.Y = reinterpret_cast<E*>(p);
     p += (size_t)n * kChunk * dk * sizeof(E);
@@ -171,6 +173,7 @@ struct ChunkParams {
   // form d(beta) on tokens whose beta is zero.
   bool unit_rs;
   int64_t nseg = 1, seg_len = 0;  // segment scan (kScanSeg): segments per head, chunks per segment
+  size_t seg_off = 0;             // bytes of the workspace ahead of the segment buffers (SegSpace)
   int xcds = 1;  // XCDs of the device: the scan launches keep the workgroups of one head on one XCD
 };
 

@@ -68,7 +68,7 @@ constexpr bool scan_deep() {
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_producers() {
   return scan_deep<E, DK, DV, W, NT, MODE>() ? 4
-         : (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda>() == 2) ? 2
+         : (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda || MODE == kScanKdaSeg>() == 2) ? 2
                                                                                     : 0;
 }
 
@@ -78,12 +78,14 @@ constexpr int scan_producers() {
 // DV / DVS slices of the state, DK / DVS slices of identity columns (chunk_common.h).
 // MODE kScanKda (per-channel decay): K, Q and the update's K2 are the decayed operands of the
 // KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
+// MODE kScanKdaSeg: the segment pass with the per-channel decay (both of the above).
 // (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>()) * kWave) __attribute__((
     amdgpu_waves_per_eu(scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1, scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1))) void
 chunk_scan_kernel(ChunkParams p) {
-  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg, KDA = MODE == kScanKda;
+  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg || MODE == kScanKdaSeg,
+                 KDA = MODE == kScanKda || MODE == kScanKdaSeg;
   constexpr bool BF = is_bf16<E>();
   // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
   // fragment along a row is one 16-byte LDS read. The recompute keeps the row-split layout, in
@@ -165,7 +167,7 @@ chunk_scan_kernel(ChunkParams p) {
   // Output rows: o (the state columns; after the first segment of a segment scan these are
   // outputs from a zero entering state, corrected in place later), or, for identity columns, Y
   // in the segment workspace ([chunk][64][DK] per head). One store form for both.
-  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.heads * nchunks, p.heads * nseg, DK, DV);
+  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.seg_off, p.heads * nchunks, p.heads * nseg, DK, DV);
   const rsrc_t rout = mpart ? make_rsrc(sg.Y + chunk0 * kChunk * DK, (uint32_t)(nchunks * kChunk * DK * sizeof(E))) : ro;
   const uint32_t orow = mpart ? DK * sizeof(E) : vrow;                       // bytes per output row
   const uint32_t ocol = mpart ? (j0 + cw) * sizeof(E) : hcol_v + cw * sizeof(E);  // this wave's first column
@@ -599,9 +601,10 @@ chunk_scan_kernel(ChunkParams p) {
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   constexpr int DVS = W * 16 * NT;
-  static_assert(DVS == scan_cols(is_bf16<E>(), MODE == kScanSeg), "column split as planned");
-  constexpr int NSA = DV / DVS + (MODE == kScanSeg ? DK / DVS : 0);
-  const int64_t units = p.heads * (MODE == kScanSeg ? p.nseg : 1);  // (head, segment) pairs
+  constexpr bool SEG = MODE == kScanSeg || MODE == kScanKdaSeg;
+  static_assert(DVS == scan_cols(is_bf16<E>(), SEG), "column split as planned");
+  constexpr int NSA = DV / DVS + (SEG ? DK / DVS : 0);
+  const int64_t units = p.heads * (SEG ? p.nseg : 1);  // (head, segment) pairs
   const int64_t units8 = (units + p.xcds - 1) / p.xcds * p.xcds;
   constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
   hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3((W + NP) * kWave), 0,
@@ -616,7 +619,7 @@ hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
   // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
   // need a single LDS buffer, whose load is not overlapped, so more columns share it).
   // The segment scan's first pass uses four waves for bf16 too (scan_cols).
-  if constexpr (is_bf16<E>() && MODE != kScanSeg)
+  if constexpr (is_bf16<E>() && MODE != kScanSeg && MODE != kScanKdaSeg)
     return launch_wnt<E, DK, DV, 2, 1, MODE>(p, stream);
   else
     return launch_wnt<E, DK, DV, 4, 1, MODE>(p, stream);
@@ -670,32 +673,61 @@ SegPlan seg_plan(int64_t heads, int64_t nchunks, int64_t d_k, int64_t d_v, bool 
 
 hipError_t launch_chunk_prep_kda(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream);
 
-size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t, bool bf16_io) {
-  const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
-  return bf16_io ? KdaSpace<bf16>::bytes(n, (int)d_k) : KdaSpace<float>::bytes(n, (int)d_k);
+// Bytes of the forward's workspace: the per-chunk factors (scalar gate) or the KDA prep's
+// operands, followed by the segment buffers when the plan has more than one segment.
+template <typename E>
+size_t fwd_space_bytes(int64_t n, int64_t heads, const SegPlan& sp, int d_k, int d_v, bool kda) {
+  const size_t head = kda ? KdaSpace<E>::bytes(n, d_k) : Workspace<E>::bytes(n);
+  return head + (sp.nseg > 1 ? SegSpace<E>::bytes(n, heads * sp.nseg, d_k, d_v) : 0);
 }
 
-// KDA forward: the per-channel prep, then the scan in its KDA mode (one pass; no segments).
-hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
-  ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
-                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
-  p.xcds = device_info().xcds;
-  if (p.nchunks > 0) {
-    const hipError_t e = launch_chunk_prep_kda(p, a.d_k, a.bf16, stream);
-    if (e != hipSuccess) return e;
-  }
-  return a.bf16 ? launch_scan<bf16, kScanKda>(p, a.d_k, a.d_v, stream)
-                : launch_scan<float, kScanKda>(p, a.d_k, a.d_v, stream);
+size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io,
+                                     int64_t segments) {
+  const int64_t nch = (T + kChunk - 1) / kChunk, n = B * H * nch;
+  const SegPlan sp = seg_plan(B * H, nch, d_k, d_v, bf16_io, segments, device_info());
+  return bf16_io ? fwd_space_bytes<bf16>(n, B * H, sp, (int)d_k, (int)d_v, true)
+                 : fwd_space_bytes<float>(n, B * H, sp, (int)d_k, (int)d_v, true);
 }
 
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io,
                                  int64_t segments) {
   const int64_t nch = (T + kChunk - 1) / kChunk, n = B * H * nch;
   const SegPlan sp = seg_plan(B * H, nch, d_k, d_v, bf16_io, segments, device_info());
-  if (sp.nseg > 1)
-    return bf16_io ? SegSpace<bf16>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v)
-                   : SegSpace<float>::bytes(n, B * H * sp.nseg, (int)d_k, (int)d_v);
-  return bf16_io ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n);
+  return bf16_io ? fwd_space_bytes<bf16>(n, B * H, sp, (int)d_k, (int)d_v, false)
+                 : fwd_space_bytes<float>(n, B * H, sp, (int)d_k, (int)d_v, false);
+}
+
+// Launches the scan (one pass, or the segment passes when the plan has several segments) after
+// the prep. KDA selects the per-channel decay's scan modes and workspace.
+template <bool KDA>
+hipError_t launch_scan_plan(ChunkParams& p, const ChunkArgs& a, const SegPlan& sp, hipStream_t stream) {
+  constexpr int ONE = KDA ? kScanKda : kScanFwd, SEGM = KDA ? kScanKdaSeg : kScanSeg;
+  if (sp.nseg <= 1)
+    return a.bf16 ? launch_scan<bf16, ONE>(p, a.d_k, a.d_v, stream) : launch_scan<float, ONE>(p, a.d_k, a.d_v, stream);
+  const int64_t n = p.heads * p.nchunks;
+  p.nseg = sp.nseg;
+  p.seg_len = sp.seg_len;
+  p.seg_off = KDA ? (a.bf16 ? KdaSpace<bf16>::bytes(n, (int)a.d_k) : KdaSpace<float>::bytes(n, (int)a.d_k))
+                  : (a.bf16 ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n));
+  hipError_t e = a.bf16 ? launch_scan<bf16, SEGM>(p, a.d_k, a.d_v, stream)
+                        : launch_scan<float, SEGM>(p, a.d_k, a.d_v, stream);
+  if (e == hipSuccess) e = launch_seg_combine(p, a.d_k, a.d_v, a.bf16, stream);
+  if (e == hipSuccess) e = launch_seg_fix(p, a.d_k, a.d_v, a.bf16, stream);
+  return e;
+}
+
+// KDA forward: the per-channel prep, then the scan in its KDA modes (segmented like the scalar
+// gate's when few heads would leave compute units idle).
+hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
+  ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
+                a.B * a.H, a.H, a.T, (a.T + kChunk - 1) / kChunk, a.eps, a.beta_given, false};
+  const DeviceInfo dev = device_info();
+  p.xcds = dev.xcds;
+  if (p.nchunks > 0) {
+    const hipError_t e = launch_chunk_prep_kda(p, a.d_k, a.bf16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_scan_plan<true>(p, a, seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev), stream);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
@@ -707,16 +739,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
     const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
     if (e != hipSuccess) return e;
   }
-  const SegPlan sp = seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev);
-  if (sp.nseg <= 1)
-    return a.bf16 ? launch_scan<bf16>(p, a.d_k, a.d_v, stream) : launch_scan<float>(p, a.d_k, a.d_v, stream);
-  p.nseg = sp.nseg;
-  p.seg_len = sp.seg_len;
-  hipError_t e = a.bf16 ? launch_scan<bf16, kScanSeg>(p, a.d_k, a.d_v, stream)
-                        : launch_scan<float, kScanSeg>(p, a.d_k, a.d_v, stream);
-  if (e == hipSuccess) e = launch_seg_combine(p, a.d_k, a.d_v, a.bf16, stream);
-  if (e == hipSuccess) e = launch_seg_fix(p, a.d_k, a.d_v, a.bf16, stream);
-  return e;
+  return launch_scan_plan<false>(p, a, seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev), stream);
 }
 
 }  // namespace kla

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(ChunkParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int64_t nseg = p.nseg, u0 = head * nseg;
-  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.heads * p.nchunks, p.heads * nseg, DK, DV);
+  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.seg_off, p.heads * p.nchunks, p.heads * nseg, DK, DV);
 
   {
     float x[DK * CW / kThreads];
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void seg_fix_kernel(ChunkParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int64_t bb = head / p.H, hh = head % p.H, T = p.T, H = p.H;
-  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.heads * nchunks, p.heads * nseg, DK, DV);
+  const SegSpace<E> sg = SegSpace<E>::at(p.ws, p.seg_off, p.heads * nchunks, p.heads * nseg, DK, DV);
 
   // S_j^T into LDS (rows swizzled for conflict-free fragment reads), from the combine's copy
   constexpr int PER = 16 / sizeof(E), NCH = DV * DK / PER / kThreads;

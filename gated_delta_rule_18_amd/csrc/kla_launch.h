@@ -96,7 +96,8 @@ size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, i
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
 // Per-channel decay (KDA): ChunkArgs.log_alpha / DecodeArgs.log_alpha hold log a [.., d_k].
 hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);
-size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,
+                                     int64_t segments = 0);
 size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
 bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16);
 

@@ -226,7 +226,9 @@ size_t kla_kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t
  *   Everything else (layouts, T, state_in/state_out aliasing, workspace, errors) as for
  *   kla_chunk_fwd, with the size limit also applied to log a's rows:
  *   (T + 64) * H * max(d_k, d_v) * element size and (T + 64) * H * d_k * 4 both below 2^31,
- *   else KLA_ERR_NOT_SUPPORTED. One pass over the chunks (no segment plan).
+ *   else KLA_ERR_NOT_SUPPORTED. The scan is planned as kla_chunk_fwd's: cut into sequence
+ *   segments when few heads would leave compute units idle (kla_kda_chunk_fwd_workspace_size
+ *   includes the segment buffers then).
  */
 kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v,
                                const float* eta, const float* log_a,

@@ -318,3 +318,17 @@ def test_kda_decode_step_rejects(kw, status):
                                  p(A16 * 8), p(d["o"]), 1, 1, d["dk"], d["dv"], 1e-6, 0, K.KLA_BF16, None)
     assert st == status
 
+
+
+def test_kda_forward_plans_segments_like_the_scalar_gate():
+    """The per-channel decay's forward takes the same segment plan: a few-head long sequence gets
+    the segment buffers on top of the KDA prep's workspace; B8 H8 T4096 stays one pass."""
+    kda = lambda B, T, H: K.lib().kla_kda_chunk_fwd_workspace_size(B, T, H, 128, 128, 64, K.KLA_BF16)
+    one = lambda B, T, H: K.lib().kla_chunk_fwd_seg_workspace_size(B, T, H, 128, 128, 64, 1, K.KLA_BF16)
+    seg = lambda B, T, H: K.lib().kla_chunk_fwd_workspace_size(B, T, H, 128, 128, 64, K.KLA_BF16)
+    # KDA adds K o e^G, Q o e^G, K o e^{G_C - G} (bf16) and gamma (fp32) per chunk to the scalar
+    # gate's per-chunk factors; the segment buffers of a plan are the same for both gates.
+    kda_ops = lambda B, T, H: B * H * (T // 64) * 128 * (3 * 64 * 2 + 4)
+    for B, T, H in ((1, 65536, 16), (8, 4096, 8)):
+        assert kda(B, T, H) - kda_ops(B, T, H) - one(B, T, H) == seg(B, T, H) - one(B, T, H)
+    assert seg(1, 65536, 16) > one(1, 65536, 16) and seg(8, 4096, 8) == one(8, 4096, 8)

@@ -154,3 +154,33 @@ def test_kda_decode_continues_the_chunked_forward():
     eS = rel_l2(host(S), host(S_all))
     report("kda decode after chunked", o=eo, S=eS)
     assert eo <= 1e-2 and eS <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kda_segmented_plan(dtype):
+    """Two heads over 32 chunks: the plan cuts each head into segments (pass 1 in the scan's KDA
+    segment mode, then the combine and the output correction), with an initial state."""
+    w = wl.custom("kda_seg", 515, B=1, H=2, dk=128, dv=128, T=2048, dtype=dtype, log_alpha_range=(0.0, 0.2))
+    inp = wl.prefill_inputs(w)
+    S0 = np.random.default_rng(515).normal(0, 0.05, (1, 2, 128, 128)).astype(np.float32)
+    compare_fwd(f"kda segmented {dtype}", w, inp, wl.channel_log_decay(w), S0=S0)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 64)])
+def test_kda_segmented_head_sizes(dk, dv):
+    w = wl.custom("kda_seg_hs", 516, B=1, H=3, dk=dk, dv=dv, T=2100, dtype="bf16")
+    compare_fwd(f"kda segmented dk={dk} dv={dv}", w, wl.prefill_inputs(w), wl.channel_log_decay(w))
+
+
+def test_kda_long_few_heads_all_heads():
+    """B1 H4 T16384 d128 bf16 with per-channel decays (the plan takes 16 segments of 16 chunks):
+    every head against the oracle (whole tensor, worst head, worst 64-token chunk)."""
+    w = wl.custom("kda_long", 517, B=1, H=4, dk=128, dv=128, T=16384, dtype="bf16")
+    inp = wl.prefill_inputs(w)
+    o, S = kla.kla_kda_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                                 dev(inp["eta"]), dev(wl.channel_log_decay(w)), eps=w.eps)
+    del inp
+    torch.cuda.synchronize()
+    o_h, S_h = host32(o), host32(S)
+    merged, heads = op.run("forward", w, lambda g: {"o": heads_of(o_h, g), "S": states_of(S_h, g)}, ("kda",))
+    op.check("kda long b1h4_t16384", merged, heads, TOL[w.dtype])

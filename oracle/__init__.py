@@ -19,6 +19,8 @@ Sources (titles as the pages give them):
     the CPU), for the chunkwise backward; the pages give no backward formulas.
   * adjoint: the same gradients as the loop's adjoint recurrence written out by
     hand in NumPy (linear memory in T, for full-size comparisons).
+  * kda_vjp / kda_backward / kda_adjoint: the gradients of the per-channel decay's
+    loop (kda_recurrent), by both routes.
 
 Every function here is pinned by tests that do not call back into it alone:
 hand-derived golden values, exact invariants, brute-force products, the
@@ -39,5 +41,5 @@ from .kla_oracle import (  # noqa: F401
     kda_forward,
     kda_chunked,
 )
-from .adjoint import gated_delta_adjoint, kla_adjoint  # noqa: F401,E402
-from .kla_grad import gated_delta_vjp, kla_vjp, kla_backward  # noqa: F401,E402
+from .adjoint import gated_delta_adjoint, kla_adjoint, kda_adjoint  # noqa: F401,E402
+from .kla_grad import gated_delta_vjp, kla_vjp, kla_backward, kda_vjp, kda_backward  # noqa: F401,E402

@@ -26,9 +26,13 @@ Abstract): deta_t = dbeta_t / (||k_t||^2 + eps) and dk_t += -2 eta_t dbeta_t k_t
 The states entering the tokens are recomputed block by block from checkpoints taken every
 ``block`` tokens during a first forward pass (the same loop as ``gated_delta_recurrent``).
 
-Pinned in tests/test_oracle_grad.py by the same pins as the autodiff oracle: central finite
-differences of the NumPy forward oracle, single-token and pure-decay closed forms and the
-homogeneity identities, plus a planted mistake.
+The per-channel decay of KDA ("Deep Dive into KDA", section 2.3: P = Diag(a_t) S_{t-1}, the
+rows that the keys index) changes only the decay's two lines of the reverse step:
+    dlog_a_t[i] = sum_j P[i, j] dP[i, j];   dL/dS_{t-1} = Diag(a_t) dP     (kda_adjoint)
+
+Pinned in tests/test_oracle_grad.py (KDA: tests/test_oracle_kda_grad.py) by the same pins as
+the autodiff oracle: central finite differences of the NumPy forward oracle, single-token and
+pure-decay closed forms and the homogeneity identities, plus a planted mistake.
 """
 from __future__ import annotations
 
@@ -98,3 +102,59 @@ def kla_adjoint(q, k, v, eta, log_alpha, eps, S0, do, dST=None, block=64):
     g["deta"] = dbeta / den
     g["dk"] = g["dk"] - (2.0 * eta * dbeta / den ** 2)[..., None] * k
     return g
+
+
+def _kda_step(S, k_t, v_t, beta_t, a_t):
+    """One token of the per-channel-decay loop from S_{t-1}: returns (P, e, S_t)."""
+    P = a_t[:, :, None] * S
+    u = np.einsum("nij,ni->nj", P, k_t)
+    e = v_t - u
+    S_t = P + beta_t[:, None, None] * (k_t[:, :, None] * e[:, None, :])
+    return P, e, S_t
+
+
+def kda_adjoint(q, k, v, eta, log_a, eps, S0, do, dST=None, block=64, beta_given=False):
+    """Gradients of L = sum(do * o) + sum(dST * S_T) through ``kda_recurrent``, head-major:
+    q, k [N, T, d_k]; v, do [N, T, d_v]; eta [N, T]; log_a [N, T, d_k]; S0, dST [N, d_k, d_v] or
+    None. The step is beta = eta / (||k||^2 + eps) unless ``beta_given`` (eta is beta). Returns
+    dq, dk, dv, deta (d beta when beta_given), dlog_a [N, T, d_k] and dS0 (fp64)."""
+    q, k, v, eta, log_a, do = map(_f64, (q, k, v, eta, log_a, do))
+    N, T, dk = k.shape
+    dv = v.shape[-1]
+    den = np.sum(k * k, axis=-1) + float(eps)
+    beta = eta if beta_given else eta / den
+    a = np.exp(log_a)
+    S = np.zeros((N, dk, dv)) if S0 is None else _f64(S0).copy()
+    ckpt = []
+    for t in range(T):
+        if t % block == 0:
+            ckpt.append(S.copy())
+        S = _kda_step(S, k[:, t], v[:, t], beta[:, t], a[:, t])[2]
+    G = np.zeros((N, dk, dv)) if dST is None else _f64(dST).copy()
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dbeta, dla = np.zeros((N, T)), np.zeros((N, T, dk))
+    for b0 in reversed(range(0, T, block)):
+        b1 = min(b0 + block, T)
+        entering = [ckpt[b0 // block]]
+        for t in range(b0, b1 - 1):
+            entering.append(_kda_step(entering[-1], k[:, t], v[:, t], beta[:, t], a[:, t])[2])
+        for t in reversed(range(b0, b1)):
+            kt, bt = k[:, t], beta[:, t]
+            P, e, S_t = _kda_step(entering[t - b0], kt, v[:, t], bt, a[:, t])
+            G = G + q[:, t][:, :, None] * do[:, t][:, None, :]
+            dq[:, t] = np.einsum("nij,nj->ni", S_t, do[:, t])
+            Ge = np.einsum("nij,nj->ni", G, e)
+            dbeta[:, t] = np.einsum("ni,ni->n", kt, Ge)
+            de = bt[:, None] * np.einsum("nij,ni->nj", G, kt)
+            dv_[:, t] = de
+            dP = G - kt[:, :, None] * de[:, None, :]
+            dk_[:, t] = bt[:, None] * Ge - np.einsum("nij,nj->ni", P, de)
+            dla[:, t] = np.einsum("nij,nij->ni", P, dP)
+            G = a[:, t][:, :, None] * dP
+    out = {"dq": dq, "dk": dk_, "dv": dv_, "dlog_a": dla, "dS0": G}
+    if beta_given:
+        out["deta"] = dbeta
+    else:
+        out["deta"] = dbeta / den
+        out["dk"] = dk_ - (2.0 * eta * dbeta / den ** 2)[..., None] * k
+    return out

@@ -20,6 +20,9 @@ pure-decay sequence, and homogeneity identities of the recurrence (o is linear i
 (o, S_T) are jointly linear in (v, S_0); with eps = 0 and S_0 = 0 they scale as 1/c
 when every key is scaled by c).
 
+The per-channel decay of KDA ("Deep Dive into KDA", section 2.3) is differentiated the same
+way, through the loop of ``kla_oracle.kda_recurrent`` (``kda_vjp``, ``kda_backward``).
+
 Layouts follow ``kla_oracle``: head-major [N, T, d] inside, library layout
 [B, T, H, d] (state [B, H, d_k, d_v]) in the wrappers.
 """
@@ -124,5 +127,61 @@ def kla_backward(q, k, v, eta, log_alpha, eps, S0, do, dST=None, beta_given=Fals
     else:
         g = kla_vjp(*args, eps, s0, _to_heads(do), dst)
     out = {n: _from_heads(g[n], B, H) for n in ("dq", "dk", "dv", "deta", "dlog_alpha")}
+    out["dS0"] = g["dS0"].reshape(B, H, dk, dv)
+    return out
+
+
+def _kda_loop(q, k, v, beta, log_a, S0):
+    """The token recurrence with the per-channel decay ("Deep Dive into KDA", section 2.3, state
+    stored [d_k, d_v], so Diag(a_t) scales the rows the keys index):
+    S <- Diag(a_t) S;  u = S^T k_t;  S <- S + beta_t k_t (v_t - u)^T;  o_t = S^T q_t."""
+    torch = _torch()
+    T = k.shape[1]
+    a = torch.exp(log_a)
+    S = S0
+    outs = []
+    for t in range(T):
+        kt = k[:, t]
+        S = a[:, t, :, None] * S
+        u = torch.einsum("nij,ni->nj", S, kt)
+        S = S + beta[:, t, None, None] * (kt[:, :, None] * (v[:, t] - u)[:, None, :])
+        outs.append(torch.einsum("nij,ni->nj", S, q[:, t]))
+    o = torch.stack(outs, 1) if outs else torch.zeros(v.shape, dtype=torch.float64)
+    return o, S
+
+
+def kda_vjp(q, k, v, eta, log_a, eps, S0, do, dST=None, beta_given=False):
+    """Gradients of L = sum(do * o) + sum(dST * S_T) through the per-channel-decay loop,
+    head-major: q, k [N, T, d_k]; v, do [N, T, d_v]; eta [N, T]; log_a [N, T, d_k];
+    S0, dST [N, d_k, d_v] or None (zeros). The step is beta = eta / (||k||^2 + eps), formed inside
+    the differentiated graph, unless ``beta_given`` (eta is then beta itself and eps unused).
+    Returns dq, dk, dv, deta (d beta when beta_given), dlog_a [N, T, d_k] and dS0, fp64."""
+    torch = _torch()
+    N, T, dk = np.shape(k)
+    dv = np.shape(v)[-1]
+    q_, k_, v_, e_, la_ = map(_t, (q, k, v, eta, log_a))
+    S0_ = _t(np.zeros((N, dk, dv)) if S0 is None else S0)
+    beta = e_ if beta_given else e_ / ((k_ * k_).sum(-1) + float(eps))
+    o, S = _kda_loop(q_, k_, v_, beta, la_, S0_)
+    loss = (o * torch.as_tensor(np.asarray(do, np.float64))).sum()
+    if dST is not None:
+        loss = loss + (S * torch.as_tensor(np.asarray(dST, np.float64))).sum()
+    grads = torch.autograd.grad(loss, (q_, k_, v_, e_, la_, S0_), allow_unused=True)
+    names = ("dq", "dk", "dv", "deta", "dlog_a", "dS0")
+    shapes = ((N, T, dk), (N, T, dk), (N, T, dv), (N, T), (N, T, dk), (N, dk, dv))
+    return {n: (np.zeros(s) if g is None else g.numpy()) for n, g, s in zip(names, grads, shapes)}
+
+
+def kda_backward(q, k, v, eta, log_a, eps, S0, do, dST=None, beta_given=False):
+    """Library-layout KDA gradients: q, k, log_a [B, T, H, d_k]; v, do [B, T, H, d_v]; eta (or beta
+    when ``beta_given``) [B, T, H]; S0, dST [B, H, d_k, d_v] or None. Returns dq, dk, dlog_a
+    [B, T, H, d_k], dv [B, T, H, d_v], deta [B, T, H] and dS0 [B, H, d_k, d_v], all fp64."""
+    B, T, H, dk = np.shape(k)
+    dv = np.shape(v)[-1]
+    s0 = None if S0 is None else np.asarray(S0, np.float64).reshape(B * H, dk, dv)
+    dst = None if dST is None else np.asarray(dST, np.float64).reshape(B * H, dk, dv)
+    g = kda_vjp(_to_heads(q), _to_heads(k), _to_heads(v), _to_heads(eta), _to_heads(log_a), eps, s0,
+                _to_heads(do), dst, beta_given)
+    out = {n: _from_heads(g[n], B, H) for n in ("dq", "dk", "dv", "deta", "dlog_a")}
     out["dS0"] = g["dS0"].reshape(B, H, dk, dv)
     return out

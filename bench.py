@@ -70,10 +70,12 @@ def bwd_flops_per_head_token(dk, dv, C=64):
     return C * (16 * dk + 10 * dv) + 16 * dk * dv
 
 
-def bwd_bytes(w, es):
+def bwd_bytes(w, es, kda=False):
     """Algorithmic HBM bytes of one backward launch: q, k, v, do, eta, log_alpha read once;
-    dq, dk, dv, deta, dlog_alpha written once (no initial state, no state cotangent)."""
-    return w.heads * w.T * ((3 * w.dk + 3 * w.dv) * es + 16)
+    dq, dk, dv, deta, dlog_alpha written once (no initial state, no state cotangent). With the
+    per-channel decay, log a and dlog a are d_k fp32 per head-token."""
+    gate = 8 + (8 * w.dk if kda else 8)
+    return w.heads * w.T * ((3 * w.dk + 3 * w.dv) * es + gate)
 
 
 def decode_bytes(w, es):
@@ -217,7 +219,7 @@ def cpu_baseline(w, head_tokens, mode="kla"):
                        + "; ".join(what) + "; a leg's time is its slowest worker's, input generation excluded")}
 
 
-def cpu_baseline_bwd(w, head_tokens):
+def cpu_baseline_bwd(w, head_tokens, kda=False):
     """The fp64 gradient oracle (the adjoint of the token loop), as it stands, on a bounded sample:
     every head over the first head_tokens / (B H) prefill tokens, in worker processes."""
     import concurrent.futures
@@ -228,16 +230,16 @@ def cpu_baseline_bwd(w, head_tokens):
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     groups = [heads[i::cores] for i in range(cores) if heads[i::cores]]
     with concurrent.futures.ProcessPoolExecutor(len(groups), mp_context=multiprocessing.get_context("spawn")) as ex:
-        res = list(ex.map(_oracle_bwd_leg, [w] * len(groups), groups, [n] * len(groups)))
+        res = list(ex.map(_oracle_bwd_leg, [w] * len(groups), groups, [n] * len(groups), [kda] * len(groups)))
     secs = max(t for t, _ in res)
     return {"value": w.B * n / secs, "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
             "cores_available": avail,
-            "sample": f"oracle kla_adjoint (fp64 numpy, one thread per worker) on all {w.heads} heads x the first "
+            "sample": f"oracle {'kda' if kda else 'kla'}_adjoint (fp64 numpy, one thread per worker) on all {w.heads} heads x the first "
                       f"{n} prefill tokens in {len(groups)} worker processes: {len(heads) * n} head-tokens in "
                       f"{secs:.2f} s (slowest worker; input generation excluded)"}
 
 
-def _oracle_bwd_leg(w, heads, n):
+def _oracle_bwd_leg(w, heads, n, kda=False):
     import oracle
     from threadpoolctl import threadpool_limits
     threadpool_limits(1)
@@ -245,13 +247,18 @@ def _oracle_bwd_leg(w, heads, n):
     d = [wl.head_prefill(ws, b, h) for b, h in heads]
     g = [wl.head_grad(ws, b, h) for b, h in heads]
     st = lambda key, src=d: np.stack([x[key] for x in src])
-    t0 = time.perf_counter()
-    oracle.kla_adjoint(st("q"), st("k"), st("v"), st("eta"), st("log_alpha"), w.eps, None, st("do", g))
+    if kda:
+        la = np.stack([wl.head_channel_log_decay(ws, b, h) for b, h in heads])
+        t0 = time.perf_counter()
+        oracle.kda_adjoint(st("q"), st("k"), st("v"), st("eta"), la, w.eps, None, st("do", g))
+    else:
+        t0 = time.perf_counter()
+        oracle.kla_adjoint(st("q"), st("k"), st("v"), st("eta"), st("log_alpha"), w.eps, None, st("do", g))
     return time.perf_counter() - t0, len(heads) * n
 
 
 def run_bwd(args, w):
-    """--pass bwd: time kla_chunk_bwd (or kla_gdn_chunk_bwd) over the workload's prefill."""
+    """--pass bwd: time kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd) over the workload's prefill."""
     import torch
     from gated_delta_rule_18_amd import _lib as K
     device = torch.device("cuda:0")
@@ -259,18 +266,22 @@ def run_bwd(args, w):
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
     L = K.lib()
-    gdn = args.mode != "kla"
+    gdn = args.mode in ("gdn", "deltanet")
+    kda = args.mode == "kda"
     log(f"[bench] generating {w.name} ({w.note}) and its output cotangent ...")
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
     x = wl.prefill_inputs(w, GEN_WORKERS)
     if gdn:
         x["k"] = unit_keys(x["k"])
     x["do"] = wl.grad_inputs(w)["do"]
+    if kda:
+        x["log_alpha"] = wl.channel_log_decay(w)
     t = {n: on(x[n], tdt if n in ("q", "k", "v", "do") else torch.float32) for n in x}
     del x
     out = {"dq": torch.empty_like(t["q"]), "dk": torch.empty_like(t["k"]), "dv": torch.empty_like(t["v"]),
            "deta": torch.empty_like(t["eta"]), "dla": torch.empty_like(t["log_alpha"])}
-    ws_bytes = int(L.kla_chunk_bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, 64, code))
+    ws_fn = L.kla_kda_chunk_bwd_workspace_size if kda else L.kla_chunk_bwd_workspace_size
+    ws_bytes = int(ws_fn(w.B, w.T, w.H, w.dk, w.dv, 64, code))
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(device)
@@ -282,6 +293,8 @@ def run_bwd(args, w):
             P(out["dv"]), P(out["deta"]), dla, None, w.B, w.T, w.H, w.dk, w.dv, 64)
     if gdn:
         call = lambda: L.kla_gdn_chunk_bwd(*head, code, P(workspace), ws_bytes, sp)
+    elif kda:
+        call = lambda: L.kla_kda_chunk_bwd(*head, ctypes.c_float(w.eps), 0, code, P(workspace), ws_bytes, sp)
     else:
         call = lambda: L.kla_chunk_bwd(*head, ctypes.c_float(w.eps), code, P(workspace), ws_bytes, sp)
     ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -305,9 +318,11 @@ def run_bwd(args, w):
     ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     tokens = w.B * w.T
     flops = bwd_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
-    nbytes = bwd_bytes(w, es)
+    nbytes = bwd_bytes(w, es, kda)
     peak_mfma = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
-    part = {"kernel": "chunk_prep_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + chunk_grad_kernel",
+    part = {"kernel": ("chunk_prep_kda_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + "
+                       "chunk_grad_kda_kernel") if kda else
+                      "chunk_prep_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + chunk_grad_kernel",
             "launches_per_step": 1, "ms_per_step": ms, "kernel_avg_us": ms * 1e3, "tokens": tokens,
             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
@@ -328,7 +343,7 @@ def run_bwd(args, w):
         "parts": {"chunk_bwd": part}, "roofline": roof}
     if not args.no_cpu_baseline and not gdn:
         log("[bench] cpu baseline: gradient oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_bwd_head_tokens)
+        result["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_bwd_head_tokens, kda)
     print(json.dumps(result), flush=True)
 
 

@@ -40,6 +40,9 @@ _SIGNATURES = {
     "kla_kda_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
                                                                _c_void_p]),
     "kla_kda_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "kla_kda_chunk_bwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
+    "kla_kda_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
+                                                                   _c_void_p]),
     "kla_status_string": (ctypes.c_char_p, [_int]),
     "kla_last_error": (ctypes.c_char_p, []),
 }
@@ -419,3 +422,54 @@ def kla_kda_decode_step(q, k, v, eta, log_a, state, eps=1e-6, beta_given=False, 
                                     _stream(dev, stream)))
     return o
 
+
+
+def kla_kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk=CHUNK, dtype_code=KLA_BF16) -> int:
+    return int(lib().kla_kda_chunk_bwd_workspace_size(B, T, H, d_k, d_v, chunk, dtype_code))
+
+
+def kla_kda_chunk_bwd(q, k, v, eta, log_a, do, eps=1e-6, beta_given=False, state_in=None, dstate_out=None,
+                      want_dstate_in=True, chunk=CHUNK, workspace=None, stream=None, out=None):
+    """Gradients of L = sum(do * o) + sum(dstate_out * S_T) through kla_kda_chunk_fwd on the same
+    inputs: log_a [B, T, H, d_k] fp32, eta [B, T, H] fp32 (beta itself when beta_given), the rest as
+    kla_chunk_bwd. Returns a dict with dq, dk, dv (input dtype), deta (d beta when beta_given),
+    dlog_a [B, T, H, d_k] (fp32) and dstate_in (fp32, or None when not wanted); tensors given in
+    ``out`` under those names are written in place."""
+    torch = _torch()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(do, "do", (B, T, H, dv), dt, dev)
+    _need(eta, "eta", (B, T, H), torch.float32, dev)
+    _need(log_a, "log_a", (B, T, H, dk), torch.float32, dev)
+    if state_in is not None:
+        _need(state_in, "state_in", (B, H, dk, dv), torch.float32, dev)
+    if dstate_out is not None:
+        _need(dstate_out, "dstate_out", (B, H, dk, dv), torch.float32, dev)
+    out = dict(out or {})
+    shapes = {"dq": ((B, T, H, dk), dt), "dk": ((B, T, H, dk), dt), "dv": ((B, T, H, dv), dt),
+              "deta": ((B, T, H), torch.float32), "dlog_a": ((B, T, H, dk), torch.float32),
+              "dstate_in": ((B, H, dk, dv), torch.float32)}
+    for name, (shape, dtype) in shapes.items():
+        if name == "dstate_in" and not want_dstate_in:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+        _need(out[name], name, shape, dtype, dev)
+    code = _dtype_code(q)
+    need = kla_kda_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().kla_kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in), _ptr(do),
+                                  _ptr(dstate_out), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                  _ptr(out["deta"]), _ptr(out["dlog_a"]), _ptr(out["dstate_in"]), B, T, H, dk, dv,
+                                  chunk, float(eps), int(bool(beta_given)), code, _ptr(workspace), ws_bytes,
+                                  _stream(dev, stream)))
+    return out

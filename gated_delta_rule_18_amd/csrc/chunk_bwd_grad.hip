@@ -74,32 +74,6 @@ constexpr bool grad_prefetch() {
   return 2 * (sizeof(GradOps<E, DK, DV>) + sizeof(GradSmem<E, DK, DV>)) > 160 * 1024;
 }
 
-// Elements 4h .. 4h + 3 of eight bf16.
-__device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
-  return h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
-}
-
-// Sum over the 16 lanes of a DPP row (lanes with equal lane / 16), in every lane of the row.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-  return x;
-}
-
-// Sum over the four lanes c, c + 16, c + 32, c + 48.
-__device__ __forceinline__ float col4_sum(float x) {
-  x += __shfl_xor(x, 16, kWave);
-  return x + __shfl_xor(x, 32, kWave);
-}
-
-// lower-triangular tile k (0..9) -> (ti, tj), ti >= tj
-__device__ __forceinline__ void tri_tile(int k, int& ti, int& tj) {
-  ti = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
-  tj = k - ti * (ti + 1) / 2;
-}
-
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams p) {
   constexpr bool BF = is_bf16<E>();
@@ -119,7 +93,7 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   const int tid0 = threadIdx.x;
   const int64_t T = p.T, H = p.H, total = p.heads * p.nchunks;
   const Workspace<E> ws = Workspace<E>::at(p.ws, total);
-  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, total, DK, DV);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.bwd_off, total, DK, DV);
 
   // Where the LDS footprint leaves one workgroup per CU, nothing else hides a chunk's load
   // latency: the kernel is persistent (workgroup b works on chunks b, b + gridDim.x, ...; chunk

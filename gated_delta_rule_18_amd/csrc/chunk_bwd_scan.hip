@@ -17,6 +17,12 @@
 // Zb = T^T R'. Every chunk's dS' and Zb go to the backward workspace for the chunk-parallel
 // gradient kernel; dS after the first chunk is dL/dS_0.
 //
+// With the per-channel decay (KDA, "Deep Dive into KDA", sections 2.3 and 3) the decays sit in
+// the operands that the KDA prep wrote (K1 = K o e^G, Q1 = Q o e^G, K2 = K o e^{G_C - G}, gamma =
+// e^{G_C} per d_k row; its factor rows carry e^G = 1 and rs e^{G_C - G} = rs):
+//   X = K2 dS',  R' = rs o X + rs o (P^T dO),  Zb = T^T R',
+//   dS = Diag(gamma) dS' + Q1^T dO - K1^T diag(eta rs) Zb.
+//
 // The structure mirrors the forward scan (chunk_scan.hip): a workgroup of W waves owns DVS
 // columns of one head's dS for every d_k row, each wave 16 NT of them, in fp32 MFMA
 // accumulators; the chain dS -> X -> R' -> Zb -> dS never leaves the wave. Operands (K, Q, T, P,
@@ -27,19 +33,26 @@
 namespace kla {
 
 hipError_t launch_chunk_prep(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream);
+hipError_t launch_chunk_prep_kda(const ChunkParams& p, int64_t d_k, bool bf16_io, hipStream_t stream);
 hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream);
+hipError_t launch_scan_recompute_kda(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io,
+                                     hipStream_t stream);
 hipError_t launch_chunk_grad(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream);
+hipError_t launch_chunk_grad_kda(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io,
+                                 hipStream_t stream);
 
 namespace {
 
 // Producer waves (bf16): as in the forward scan, two more waves per workgroup on the idle SIMDs
 // issue all direct-to-LDS loads.
-template <typename E, int DK, int DV, int W, int NT>
+template <typename E, int DK, int DV, int W, int NT, bool KDA>
 constexpr int rscan_producers() {
-  return (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT>() == 2) ? 2 : 0;
+  return (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, KDA>() == 2) ? 2 : 0;
 }
 
-template <typename E, int DK, int DV, int W, int NT>
+// KDA: the buffer's K holds K2 (the rows of X = K2 dS'), its K2 slot K1 (read transposed for the
+// state update), Q holds Q1, and gam the chunk's gamma.
+template <typename E, int DK, int DV, int W, int NT, bool KDA>
 __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_rscan_kernel(
     ChunkBwdParams p) {
   constexpr int GK = Grp<E>::K;
@@ -51,8 +64,8 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   constexpr int NGD = DK / GK;       // groups over d_k
   constexpr int NGT = kChunk / GK;   // groups over the chunk's tokens
   constexpr int PER = 16 / sizeof(E);
-  typedef ScanBuf<E, DK, DVS> Buf;
-  constexpr int NB = scan_ring<E, DK, DVS>();
+  typedef ScanBuf<E, DK, DVS, KDA> Buf;
+  constexpr int NB = scan_ring<E, DK, DVS, KDA>();
   constexpr int DIST = NB > 1 ? NB - 1 : 1;
   static_assert(NB <= 2, "ring of at most two buffers");
   static_assert(DV % DVS == 0, "shape");
@@ -76,12 +89,21 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 
   const int64_t brow = bb * T * H;
   const uint32_t xrow = H * DK * sizeof(E), vrow = H * DV * sizeof(E);
-  const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
-  const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
   const rsrc_t rdo = make_rsrc(static_cast<const E*>(p.dout) + brow * DV, (uint32_t)(T * vrow));
   const Workspace<E> ws = Workspace<E>::at(p.ws, p.heads * nchunks);
-  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * nchunks, DK, DV);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.bwd_off, p.heads * nchunks, DK, DV);
   const int64_t chunk0 = head * nchunks;
+  // K and Q rows: the k/q tensors (token stride H DK), or with KDA the decayed operands of the
+  // KDA workspace (chunk-contiguous rows of DK): K2 in K's place, Q1 in Q's, K1 for the update.
+  const KdaSpace<E> kw = KdaSpace<E>::at(p.ws, p.heads * nchunks, DK);
+  const uint32_t krow = KDA ? DK * sizeof(E) : xrow;
+  const uint32_t kspan = KDA ? (uint32_t)(nchunks * kChunk * DK * sizeof(E)) : (uint32_t)(T * xrow);
+  const rsrc_t rk = make_rsrc(KDA ? (const void*)(kw.K2 + chunk0 * kChunk * DK)
+                                  : (const void*)(static_cast<const E*>(p.k) + brow * DK), kspan);
+  const rsrc_t rq = make_rsrc(KDA ? (const void*)(kw.Q1 + chunk0 * kChunk * DK)
+                                  : (const void*)(static_cast<const E*>(p.q) + brow * DK), kspan);
+  const rsrc_t rk1 = make_rsrc(kw.K1 + chunk0 * kChunk * DK, KDA ? kspan : 0u);
+  const rsrc_t rgam = make_rsrc(kw.gamma + chunk0 * DK, KDA ? (uint32_t)(nchunks * DK * 4) : 0u);
   constexpr uint32_t kMatBytes = kChunk * kChunk * sizeof(E), kScBytes = kScRows * kChunk * sizeof(float);
   constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
   const rsrc_t rt = make_rsrc(ws.T + chunk0 * kChunk * kChunk, (uint32_t)(nchunks * kMatBytes));
@@ -89,11 +111,11 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   const rsrc_t rsc = make_rsrc(ws.SC + chunk0 * kScRows * kChunk, (uint32_t)(nchunks * kScBytes));
   const rsrc_t rds = make_rsrc(bw.dSn + chunk0 * DK * DV, (uint32_t)(nchunks * kSBytes));
   const rsrc_t rzb = make_rsrc(bw.Zb + chunk0 * kChunk * DV, (uint32_t)(nchunks * kDBytes));
-  const uint32_t hcol_x = hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
+  const uint32_t hcol_x = KDA ? 0u : hh * DK * sizeof(E), hcol_v = (hh * DV + j0) * sizeof(E);
 
   // ---- DMA of one chunk's operands (as in the forward scan; dO takes V's place), by the
   //      producer waves if there are any, else by the scan waves ----
-  constexpr int NP = rscan_producers<E, DK, DV, W, NT>();
+  constexpr int NP = rscan_producers<E, DK, DV, W, NT, KDA>();
   constexpr int WD = NP ? NP : W;
   const int dw = NP ? wave - W : wave;
   constexpr int CK = DK / PER, CT = kChunk / PER, CV = DVS / PER;
@@ -104,7 +126,7 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int i = 0; i < NBK; ++i) {
     const int ph = 64 * (dw + WD * i) + lane, r = ph / CK;
-    offk[i] = r * xrow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
+    offk[i] = r * krow + hcol_x + 16 * swz<E, CK>(r, ph % CK);
   }
 #pragma unroll
   for (int i = 0; i < NBT; ++i) {
@@ -116,7 +138,7 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
     const int ph = 64 * (dw + WD * i) + lane, r = ph / CV;
     offv[i] = r * vrow + hcol_v + 16 * swz<E, CV>(r, ph % CV);
   }
-  constexpr int NDMA = 2 * NBK + 2 * NBT + NBV + 1;
+  constexpr int NDMA = (2 + KDA) * NBK + 2 * NBT + NBV + 1 + KDA;
   constexpr int NST = (RTK + 4) * NT;  // stores per chunk and wave: dS' tiles, Zb tiles
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < 0 ? 0 : c;  // a chunk before the first is clamped (loaded again, never read)
@@ -124,8 +146,9 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < NBK; ++i) {
       const int blk = dw + WD * i;
-      dma16(rk, B.K + blk * 64 * PER, t0 * xrow + offk[i]);
-      dma16(rq, B.Q + blk * 64 * PER, t0 * xrow + offk[i]);
+      dma16(rk, B.K + blk * 64 * PER, t0 * krow + offk[i]);
+      dma16(rq, B.Q + blk * 64 * PER, t0 * krow + offk[i]);
+      if constexpr (KDA) dma16(rk1, B.K2 + blk * 64 * PER, t0 * krow + offk[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
@@ -139,6 +162,7 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
       dma16(rdo, B.V + blk * 64 * PER, t0 * vrow + offv[i]);
     }
     dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
+    if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
 
   if constexpr (NP > 0) {
@@ -310,16 +334,23 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int s = 0; s < NGT; ++s) b2[ct][s] = acc_grp<E>(Z2[ct], s);
 
-    // ---- dS <- e^{G_C} dS' + Q^T (e^G o dO) - K^T (eta rs e^G o Zb) ----
+    // ---- dS <- e^{G_C} dS' + Q^T (e^G o dO) - K^T (eta rs e^G o Zb)
+    //      (KDA: Diag(gamma) dS' + Q1^T dO - K1^T (eta rs o Zb)) ----
     const float eGC = B.sc[kScEG * kChunk + kChunk - 1];
 #pragma unroll
     for (int r = 0; r < RTK; ++r) {
+      if constexpr (KDA) {
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * r + 4 * g]);
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) dS[r][ct] *= eGC;
+        for (int ct = 0; ct < NT; ++ct) dS[r][ct] *= gm;
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) dS[r][ct] *= eGC;
+      }
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
         const GV aq = kt_grp<E, DK>(B.Q, r, s, g, c16);
-        const GV ak = kt_grp<E, DK>(B.K, r, s, g, c16);
+        const GV ak = kt_grp<E, DK>(KDA ? B.K2 : B.K, r, s, g, c16);
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
           dS[r][ct] = mma<E>(aq, boe[ct][s], dS[r][ct]);
@@ -356,63 +387,78 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   }
 }
 
-template <typename E, int DK, int DV, int W, int NT>
+template <typename E, int DK, int DV, int W, int NT, bool KDA>
 hipError_t launch_wnt(const ChunkBwdParams& p, hipStream_t stream) {
   constexpr int NS = DV / (W * 16 * NT);
   const int64_t heads8 = (p.heads + p.xcds - 1) / p.xcds * p.xcds;
-  constexpr int NP = rscan_producers<E, DK, DV, W, NT>();
-  hipLaunchKernelGGL((chunk_rscan_kernel<E, DK, DV, W, NT>), dim3((unsigned)(heads8 * NS)), dim3((W + NP) * kWave), 0,
-                     stream, p);
+  constexpr int NP = rscan_producers<E, DK, DV, W, NT, KDA>();
+  hipLaunchKernelGGL((chunk_rscan_kernel<E, DK, DV, W, NT, KDA>), dim3((unsigned)(heads8 * NS)),
+                     dim3((W + NP) * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, bool KDA>
 hipError_t launch_dk_dv(const ChunkBwdParams& p, hipStream_t stream) {
   // The forward scan's split: bf16 two waves of 16 columns, fp32 four.
   if constexpr (is_bf16<E>())
-    return launch_wnt<E, DK, DV, 2, 1>(p, stream);
+    return launch_wnt<E, DK, DV, 2, 1, KDA>(p, stream);
   else
-    return launch_wnt<E, DK, DV, 4, 1>(p, stream);
+    return launch_wnt<E, DK, DV, 4, 1, KDA>(p, stream);
 }
 
-template <typename E>
+template <typename E, bool KDA>
 hipError_t launch_e(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, hipStream_t stream) {
-  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128>(p, stream);
-  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64>(p, stream);
-  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64>(p, stream);
-  return launch_dk_dv<E, 64, 128>(p, stream);
+  if (d_k == 128 && d_v == 128) return launch_dk_dv<E, 128, 128, KDA>(p, stream);
+  if (d_k == 64 && d_v == 64) return launch_dk_dv<E, 64, 64, KDA>(p, stream);
+  if (d_k == 128 && d_v == 64) return launch_dk_dv<E, 128, 64, KDA>(p, stream);
+  return launch_dk_dv<E, 64, 128, KDA>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_reverse_scan(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
-  return bf16_io ? launch_e<bf16>(p, d_k, d_v, stream) : launch_e<float>(p, d_k, d_v, stream);
+hipError_t launch_reverse_scan(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io, bool kda,
+                               hipStream_t stream) {
+  if (kda) return bf16_io ? launch_e<bf16, true>(p, d_k, d_v, stream) : launch_e<float, true>(p, d_k, d_v, stream);
+  return bf16_io ? launch_e<bf16, false>(p, d_k, d_v, stream) : launch_e<float, false>(p, d_k, d_v, stream);
 }
 
 size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io) {
   const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
-  return bf16_io ? BwdSpace<bf16>::bytes(n, (int)d_k, (int)d_v) : BwdSpace<float>::bytes(n, (int)d_k, (int)d_v);
+  return bf16_io ? Workspace<bf16>::bytes(n) + BwdSpace<bf16>::bytes(n, (int)d_k, (int)d_v)
+                 : Workspace<float>::bytes(n) + BwdSpace<float>::bytes(n, (int)d_k, (int)d_v);
+}
+
+size_t chunk_kda_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16_io) {
+  const int64_t n = B * H * ((T + kChunk - 1) / kChunk);
+  return bf16_io ? KdaSpace<bf16>::bytes(n, (int)d_k) + BwdSpace<bf16>::bytes(n, (int)d_k, (int)d_v)
+                 : KdaSpace<float>::bytes(n, (int)d_k) + BwdSpace<float>::bytes(n, (int)d_k, (int)d_v);
 }
 
 // The backward: the forward's per-chunk factors again (prep), the forward scan once more to
 // record every chunk's entering state and Delta, the reverse scan for the state gradients, then
 // the chunk-parallel gradients. With beta given the factors are taken unbalanced (rs = 1).
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream) {
-  const int64_t nchunks = (a.T + kChunk - 1) / kChunk;
+  const int64_t nchunks = (a.T + kChunk - 1) / kChunk, n = a.B * a.H * nchunks;
   ChunkBwdParams bp{a.q,  a.k,    a.v,         a.eta,      a.log_alpha, a.state_in, a.dout, a.dstate_out,
                     a.dq, a.dk,   a.dv,        a.deta,     a.dlog_alpha, a.dstate_in, a.workspace,
                     a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given};
   bp.xcds = device_info().xcds;
+  bp.bwd_off = a.kda ? (a.bf16 ? KdaSpace<bf16>::bytes(n, (int)a.d_k) : KdaSpace<float>::bytes(n, (int)a.d_k))
+                     : (a.bf16 ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n));
   if (nchunks > 0) {
     ChunkParams fp{a.q,   a.k,       a.v, a.eta,    a.log_alpha, a.state_in, nullptr, nullptr, a.workspace,
                    a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given, a.beta_given};
     fp.xcds = bp.xcds;
-    hipError_t e = launch_chunk_prep(fp, a.d_k, a.bf16, stream);
-    if (e == hipSuccess) e = launch_scan_recompute(fp, a.d_k, a.d_v, a.bf16, stream);
+    fp.bwd_off = bp.bwd_off;
+    hipError_t e = a.kda ? launch_chunk_prep_kda(fp, a.d_k, a.bf16, stream) : launch_chunk_prep(fp, a.d_k, a.bf16, stream);
+    if (e == hipSuccess)
+      e = a.kda ? launch_scan_recompute_kda(fp, a.d_k, a.d_v, a.bf16, stream)
+                : launch_scan_recompute(fp, a.d_k, a.d_v, a.bf16, stream);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_reverse_scan(bp, a.d_k, a.d_v, a.bf16, stream);
-  if (e == hipSuccess && nchunks > 0) e = launch_chunk_grad(bp, a.d_k, a.d_v, a.bf16, stream);
+  hipError_t e = launch_reverse_scan(bp, a.d_k, a.d_v, a.bf16, a.kda, stream);
+  if (e == hipSuccess && nchunks > 0)
+    e = a.kda ? launch_chunk_grad_kda(bp, a.d_k, a.d_v, a.bf16, stream) : launch_chunk_grad(bp, a.d_k, a.d_v, a.bf16, stream);
   return e;
 }
 

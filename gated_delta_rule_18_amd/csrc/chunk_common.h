@@ -83,8 +83,14 @@ struct Workspace {
 
 // Modes of the scan kernel: the forward; the backward's recompute (entering states and Delta
 // to the backward workspace, no outputs); the first pass of the segment scan (below); the
-// forward with the per-channel decay (KDA); and the first segment pass with that decay.
-enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3, kScanKdaSeg = 4 };
+// forward with the per-channel decay (KDA); the first segment pass with that decay; and the
+// backward's recompute with that decay.
+enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3, kScanKdaSeg = 4, kScanKdaRec = 5 };
+__host__ __device__ constexpr bool scan_kda(int mode) {
+  return mode == kScanKda || mode == kScanKdaSeg || mode == kScanKdaRec;
+}
+__host__ __device__ constexpr bool scan_rec(int mode) { return mode == kScanRec || mode == kScanKdaRec; }
+__host__ __device__ constexpr bool scan_seg(int mode) { return mode == kScanSeg || mode == kScanKdaSeg; }
 
 // State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four). The bf16
 // segment scan uses four waves (64 columns): with half the workgroups per segment, twice the
@@ -174,10 +180,12 @@ struct ChunkParams {
   bool unit_rs;
   int64_t nseg = 1, seg_len = 0;  // segment scan (kScanSeg): segments per head, chunks per segment
   size_t seg_off = 0;             // bytes of the workspace ahead of the segment buffers (SegSpace)
+  size_t bwd_off = 0;             // bytes of the workspace ahead of the backward buffers (BwdSpace)
   int xcds = 1;  // XCDs of the device: the scan launches keep the workgroups of one head on one XCD
 };
 
-// Backward workspace: the forward workspace above, then per chunk (same chunk ids)
+// Backward workspace: the forward workspace above (the scalar gate's Workspace, or with the
+// per-channel decay the KdaSpace), then, bwd_off bytes into it, per chunk (same chunk ids)
 //   Sn  [DK x DV] of E : the state entering the chunk
 //   dSn [DK x DV] of E : the gradient of the state leaving the chunk
 //   Dl  [64 x DV] of E : Delta = U - W S of the chunk (the page's new-value term)
@@ -192,10 +200,10 @@ struct BwdSpace {
   E* Dl;
   E* Zb;
   __host__ __device__ static size_t bytes(int64_t n, int dk, int dv) {
-    return Workspace<E>::bytes(n) + (size_t)n * (2 * dk * dv + 2 * kChunk * dv) * sizeof(E);
+    return (size_t)n * (2 * dk * dv + 2 * kChunk * dv) * sizeof(E);
   }
-  __host__ __device__ static BwdSpace at(void* base, int64_t n, int dk, int dv) {
-    E* p = reinterpret_cast<E*>(static_cast<char*>(base) + Workspace<E>::bytes(n));
+  __host__ __device__ static BwdSpace at(void* base, size_t off, int64_t n, int dk, int dv) {
+    E* p = reinterpret_cast<E*>(static_cast<char*>(base) + off);
     BwdSpace w;
     w.Sn = p;
     w.dSn = w.Sn + (size_t)n * dk * dv;
@@ -227,7 +235,8 @@ struct ChunkBwdParams {
   int64_t heads, H, T, nchunks;
   float eps;
   bool beta_given;
-  int xcds = 1;  // as ChunkParams::xcds
+  int xcds = 1;        // as ChunkParams::xcds
+  size_t bwd_off = 0;  // as ChunkParams::bwd_off
 };
 
 }  // namespace kla

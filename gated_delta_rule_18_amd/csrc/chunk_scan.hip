@@ -68,7 +68,7 @@ constexpr bool scan_deep() {
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_producers() {
   return scan_deep<E, DK, DV, W, NT, MODE>() ? 4
-         : (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, MODE == kScanKda || MODE == kScanKdaSeg>() == 2) ? 2
+         : (is_bf16<E>() && scan_ring<E, DK, W * 16 * NT, scan_kda(MODE)>() == 2) ? 2
                                                                                     : 0;
 }
 
@@ -79,13 +79,13 @@ constexpr int scan_producers() {
 // MODE kScanKda (per-channel decay): K, Q and the update's K2 are the decayed operands of the
 // KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
 // MODE kScanKdaSeg: the segment pass with the per-channel decay (both of the above).
+// MODE kScanKdaRec: the backward's recompute with the per-channel decay.
 // (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>()) * kWave) __attribute__((
     amdgpu_waves_per_eu(scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1, scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1))) void
 chunk_scan_kernel(ChunkParams p) {
-  constexpr bool REC = MODE == kScanRec, SEG = MODE == kScanSeg || MODE == kScanKdaSeg,
-                 KDA = MODE == kScanKda || MODE == kScanKdaSeg;
+  constexpr bool REC = scan_rec(MODE), SEG = scan_seg(MODE), KDA = scan_kda(MODE);
   constexpr bool BF = is_bf16<E>();
   // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
   // fragment along a row is one 16-byte LDS read. The recompute keeps the row-split layout, in
@@ -160,7 +160,7 @@ chunk_scan_kernel(ChunkParams p) {
   const uint32_t hcol_x = KDA ? 0u : hh * DK * sizeof(E), hcol_v = (hh * DV + (mpart ? 0 : j0)) * sizeof(E);
   // Backward recompute: this head's state and Delta blocks, tile-ordered (chunk_common.h).
   constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
-  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.heads * nchunks, DK, DV);
+  const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.bwd_off, p.heads * nchunks, DK, DV);
   const rsrc_t rsn = make_rsrc(bw.Sn + chunk0 * DK * DV, REC ? (uint32_t)(nchunks * kSBytes) : 0u);
   const rsrc_t rdl = make_rsrc(bw.Dl + chunk0 * kChunk * DV, REC ? (uint32_t)(nchunks * kDBytes) : 0u);
   const int ct0 = (j0 + cw) / 16;  // first global 16-column tile of this wave
@@ -204,7 +204,7 @@ chunk_scan_kernel(ChunkParams p) {
   // Every loading wave issues the same NDMA loads per chunk (the factor block is loaded by all of
   // them, identical bytes), so that the wait counts below are compile-time constants. A chunk
   // past the end is clamped to the last one (loaded again, never read).
-  constexpr int NDMA = REC ? NBK + NBT + NBV + 1 : KDA ? 3 * NBK + 2 * NBT + NBV + 2 : 2 * NBK + 2 * NBT + NBV + 1;
+  constexpr int NDMA = (1 + !REC + KDA) * NBK + (1 + !REC) * NBT + NBV + 1 + KDA;
   constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < ce ? c : ce - 1;
@@ -601,7 +601,7 @@ chunk_scan_kernel(ChunkParams p) {
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   constexpr int DVS = W * 16 * NT;
-  constexpr bool SEG = MODE == kScanSeg || MODE == kScanKdaSeg;
+  constexpr bool SEG = scan_seg(MODE);
   static_assert(DVS == scan_cols(is_bf16<E>(), SEG), "column split as planned");
   constexpr int NSA = DV / DVS + (SEG ? DK / DVS : 0);
   const int64_t units = p.heads * (SEG ? p.nseg : 1);  // (head, segment) pairs
@@ -619,7 +619,7 @@ hipError_t launch_dk_dv(const ChunkParams& p, hipStream_t stream) {
   // throughput, so more workgroups per head beat wider ones. fp32: four waves (its operands
   // need a single LDS buffer, whose load is not overlapped, so more columns share it).
   // The segment scan's first pass uses four waves for bf16 too (scan_cols).
-  if constexpr (is_bf16<E>() && MODE != kScanSeg && MODE != kScanKdaSeg)
+  if constexpr (is_bf16<E>() && !scan_seg(MODE))
     return launch_wnt<E, DK, DV, 2, 1, MODE>(p, stream);
   else
     return launch_wnt<E, DK, DV, 4, 1, MODE>(p, stream);
@@ -640,6 +640,12 @@ hipError_t launch_seg_fix(const ChunkParams& p, int64_t d_k, int64_t d_v, bool b
 
 hipError_t launch_scan_recompute(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
   return bf16_io ? launch_scan<bf16, kScanRec>(p, d_k, d_v, stream) : launch_scan<float, kScanRec>(p, d_k, d_v, stream);
+}
+
+hipError_t launch_scan_recompute_kda(const ChunkParams& p, int64_t d_k, int64_t d_v, bool bf16_io,
+                                     hipStream_t stream) {
+  return bf16_io ? launch_scan<bf16, kScanKdaRec>(p, d_k, d_v, stream)
+                 : launch_scan<float, kScanKdaRec>(p, d_k, d_v, stream);
 }
 
 // Segments for a forward of `heads` heads and `nchunks` chunks on a device with `dev.cus` compute

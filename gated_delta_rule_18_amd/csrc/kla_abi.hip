@@ -164,6 +164,13 @@ size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
   return kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
 }
 
+size_t kla_kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                        kla_dtype_t dt) {
+  if (B <= 0 || T <= 0 || H <= 0 || !supported_head(d_k) || !supported_head(d_v) || chunk != kla::kChunk)
+    return 0;
+  return kla::chunk_kda_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+}
+
 }  // extern "C"
 
 namespace {
@@ -251,8 +258,9 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
                   fn);
 }
 
-// kla_chunk_bwd and kla_gdn_chunk_bwd (as chunk_fwd_impl; deta receives dL/dbeta when beta_given).
-kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, const void* k, const void* v,
+// kla_chunk_bwd, kla_gdn_chunk_bwd and kla_kda_chunk_bwd (as chunk_fwd_impl; deta receives dL/dbeta
+// when beta_given; with kda, log_alpha / dlog_alpha are log a / dlog a [B, T, H, d_k] and required).
+kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                             const float* eta, const float* log_alpha, const float* state_in, const void* dout,
                             const float* dstate_out, void* dq, void* dk, void* dv, float* deta, float* dlog_alpha,
                             float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
@@ -262,7 +270,7 @@ kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, cons
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (!supported_head(d_k) || !supported_head(d_v))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: d_k and d_v must be 64 or 128", fn);
-  if (!kla::chunk_grad_supported(d_k, d_v, dt == KLA_BF16))
+  if (!(kda ? kla::chunk_grad_kda_supported(d_k, d_v, dt == KLA_BF16) : kla::chunk_grad_supported(d_k, d_v, dt == KLA_BF16)))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: fp32 gradients need d_k = d_v = 64", fn);
   if (chunk != kla::kChunk) return fail(KLA_ERR_NOT_SUPPORTED, "%s: chunk must be 64", fn);
   if (!std::isfinite(eps) || eps < 0.f) return fail(KLA_ERR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
@@ -279,30 +287,33 @@ kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, cons
     return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
   // 32-bit byte offsets within one batch entry's rows and within one head's workspace blocks.
   if ((T + kla::kChunk) * H * (d_k > d_v ? d_k : d_v) * es >= (int64_t(1) << 31) ||
-      (nchunks + 1) * d_k * d_v * es >= (int64_t(1) << 31))
+      (kda && (T + kla::kChunk) * H * d_k * 4 >= (int64_t(1) << 31)) ||
+      (nchunks + 1) * d_k * d_v * es >= (int64_t(1) << 31) ||
+      (kda && (nchunks + 1) * kla::kChunk * d_k * es >= (int64_t(1) << 31)))
     return fail(KLA_ERR_NOT_SUPPORTED, "%s: T * H * d of one batch entry must stay below 2 GiB", fn);
-  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && !beta_given) || !dout || !dq || !dk || !dv || !deta ||
-                (log_alpha && !dlog_alpha)))
+  if (T > 0 && (!q || !k || !v || !eta || (!log_alpha && (!beta_given || kda)) || !dout || !dq || !dk || !dv ||
+                !deta || (log_alpha && !dlog_alpha)))
     return fail(KLA_ERR_INVALID_VALUE, "%s: null pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
       !aligned(dk, 16) || !aligned(dv, 16) || !aligned(state_in, 16) || !aligned(dstate_out, 16) ||
-      !aligned(dstate_in, 16) || !aligned(eta, 4) || !aligned(log_alpha, 4) || !aligned(deta, 4) ||
+      !aligned(dstate_in, 16) || !aligned(eta, 4) || !aligned(log_alpha, kda ? 16 : 4) || !aligned(deta, 4) ||
       !aligned(dlog_alpha, 4) || !aligned(workspace, 16))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
-  const size_t need = kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
+  const size_t need = kda ? kla::chunk_kda_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+                          : kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16);
   if (T > 0 && (!workspace || workspace_bytes < need))
     return fail(KLA_ERR_INVALID_VALUE, "%s: workspace missing or too small", fn);
   const int64_t tok = B * T * H;
   const int64_t sbytes = B * H * d_k * d_v * 4;
   const Range ins[8] = {range("q", q, tok * d_k * es),          range("k", k, tok * d_k * es),
                         range("v", v, tok * d_v * es),          range("eta", eta, tok * 4),
-                        range("log_alpha", log_alpha, tok * 4), range("state_in", state_in, sbytes),
+                        range("log_alpha", log_alpha, tok * 4 * (kda ? d_k : 1)), range("state_in", state_in, sbytes),
                         range("do", dout, tok * d_v * es),      range("dstate_out", dstate_out, sbytes)};
   const Range outs[7] = {range("dq", dq, T > 0 ? tok * d_k * es : 0),
                          range("dk", dk, T > 0 ? tok * d_k * es : 0),
                          range("dv", dv, T > 0 ? tok * d_v * es : 0),
                          range("deta", deta, T > 0 ? tok * 4 : 0),
-                         range("dlog_alpha", dlog_alpha, T > 0 ? tok * 4 : 0),
+                         range("dlog_alpha", dlog_alpha, T > 0 ? tok * 4 * (kda ? d_k : 1) : 0),
                          range("dstate_in", dstate_in, sbytes),
                          range("workspace", workspace, T > 0 ? (int64_t)workspace_bytes : 0)};
   for (int i = 0; i < 7; ++i) {
@@ -318,7 +329,7 @@ kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, const void* q, cons
   }
   kla::ChunkBwdArgs a{q,  k,  v,    eta,        log_alpha, state_in, dout, dstate_out, dq,  dk,
                       dv, deta, dlog_alpha, dstate_in, B,  T,        H,    d_k,        d_v, eps,
-                      dt == KLA_BF16, workspace, workspace_bytes, beta_given};
+                      dt == KLA_BF16, workspace, workspace_bytes, beta_given, kda};
   return launched(kla::launch_chunk_bwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -412,7 +423,7 @@ kla_status_t kla_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            void* dv, float* deta, float* dlog_alpha, float* dstate_in, int64_t B, int64_t T,
                            int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return chunk_bwd_impl("kla_chunk_bwd", false, q, k, v, eta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
+  return chunk_bwd_impl("kla_chunk_bwd", false, false, q, k, v, eta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
                         deta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, eps, dt, workspace, workspace_bytes,
                         stream);
 }
@@ -423,7 +434,7 @@ kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v, cons
                                float* dlog_alpha, float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k,
                                int64_t d_v, int64_t chunk, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  return chunk_bwd_impl("kla_gdn_chunk_bwd", true, q, k, v, beta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
+  return chunk_bwd_impl("kla_gdn_chunk_bwd", true, false, q, k, v, beta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
                         dbeta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, 0.f, dt, workspace, workspace_bytes,
                         stream);
 }
@@ -434,6 +445,16 @@ kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v, cons
                                void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl("kla_kda_chunk_fwd", beta_given != 0, true, q, k, v, eta, log_a, state_in, state_out, o, B,
                         T, H, d_k, d_v, chunk, beta_given ? 0.f : eps, dt, workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_kda_chunk_bwd(const void* q, const void* k, const void* v, const float* eta, const float* log_a,
+                               const float* state_in, const void* dout, const float* dstate_out, void* dq, void* dk,
+                               void* dv, float* deta, float* dlog_a, float* dstate_in, int64_t B, int64_t T, int64_t H,
+                               int64_t d_k, int64_t d_v, int64_t chunk, float eps, int beta_given, kla_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kla_kda_chunk_bwd", beta_given != 0, true, q, k, v, eta, log_a, state_in, dout, dstate_out,
+                        dq, dk, dv, deta, dlog_a, dstate_in, B, T, H, d_k, d_v, chunk, beta_given ? 0.f : eps, dt,
+                        workspace, workspace_bytes, stream);
 }
 
 kla_status_t kla_kda_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_a,

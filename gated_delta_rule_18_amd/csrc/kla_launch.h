@@ -85,6 +85,7 @@ struct ChunkBwdArgs {
   void* workspace;
   size_t workspace_bytes;
   bool beta_given;
+  bool kda = false;  // per-channel decay: log_alpha holds log a [B, T, H, d_k], dlog_alpha d log a
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
@@ -99,6 +100,8 @@ hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,
                                      int64_t segments = 0);
 size_t chunk_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
+size_t chunk_kda_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16);
 bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16);
+bool chunk_grad_kda_supported(int64_t d_k, int64_t d_v, bool bf16);
 
 }  // namespace kla

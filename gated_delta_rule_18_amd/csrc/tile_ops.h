@@ -220,6 +220,54 @@ __device__ __forceinline__ void store4_rsrc(rsrc_t r, uint32_t off, f32x4 v) {
   }
 }
 
+// ---- helpers of the chunk-parallel gradient kernels --------------------------------------------
+// Elements 4h .. 4h + 3 of eight bf16.
+__device__ __forceinline__ bf16x4 half4(bf16x8 x, int h) {
+  return h ? __builtin_shufflevector(x, x, 4, 5, 6, 7) : __builtin_shufflevector(x, x, 0, 1, 2, 3);
+}
+
+// Sum over the 16 lanes of a DPP row (lanes with equal lane / 16), in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
+// Sum over the four lanes c, c + 16, c + 32, c + 48.
+__device__ __forceinline__ float col4_sum(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  return x + __shfl_xor(x, 32, kWave);
+}
+
+// lower-triangular tile k (0..9) -> (ti, tj), ti >= tj
+__device__ __forceinline__ void tri_tile(int k, int& ti, int& tj) {
+  ti = k >= 6 ? 3 : k >= 3 ? 2 : k >= 1 ? 1 : 0;
+  tj = k - ti * (ti + 1) / 2;
+}
+
+// Contraction index of element j of a lane's operand in group s (lane group g): see Grp.
+template <typename E>
+__device__ __forceinline__ int grp_index(int s, int g, int j) {
+  if constexpr (is_bf16<E>())
+    return 32 * s + 4 * g + (j & 3) + 16 * (j >> 2);
+  else
+    return 16 * s + 4 * g + j;
+}
+
+// Four consecutive entries col .. col + 3 (col a multiple of 4) of row r of a swizzled
+// row-major matrix of NCOL columns, as fp32.
+template <typename E, int NCOL>
+__device__ __forceinline__ f32x4 row4(const E* M, int r, int col) {
+  if constexpr (is_bf16<E>()) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(M + at<E, NCOL>(r, col));
+    return (f32x4){to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
+  } else {
+    return *reinterpret_cast<const f32x4*>(M + at<E, NCOL>(r, col));
+  }
+}
+
 // One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz). With the
 // per-channel decay (KDA) the buffer also holds the state-update operand K2 and the chunk's
 // state decay gamma (a 1 KiB block, of which the first DK entries are this chunk's).

@@ -308,6 +308,49 @@ kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v,
                                int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                                kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * kla_kda_chunk_bwd_workspace_size — bytes of device workspace kla_kda_chunk_bwd needs (0 when
+ * T = 0 or the sizes are not supported). Host-only; never fails. For bf16 and d_k = d_v = 128 it
+ * is about 162 KiB per chunk of 64 tokens per head: the KDA forward's per-chunk factors and
+ * decayed operands plus every chunk's entering state, state gradient, Delta and solve gradient.
+ */
+size_t kla_kda_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                        int64_t chunk, kla_dtype_t dt);
+
+/*
+ * kla_kda_chunk_bwd — gradients of kla_kda_chunk_fwd (training with the per-channel decay).
+ * Source: "Deep Dive into KDA", section 2.3 (S_t = (I - beta_t k_t k_t^T) Diag(a_t) S_{t-1}
+ * + beta_t v_t k_t^T, here with the state stored [d_k, d_v]) and section 3 (the chunkwise form
+ * that is differentiated, decay ratios in the log domain); "Kaczmarz Linear Attention",
+ * Abstract (beta_t = eta_t / (||k_t||^2 + eps)). The pages give no backward formulas: the result
+ * is the exact gradient of the token recurrence, up to rounding.
+ * For L = sum(do * o) + sum(dstate_out * S_T), with o and S_T the outputs of kla_kda_chunk_fwd on
+ * the same inputs, computes
+ *   dq, dk     [B,T,H,d_k] of type dt   (dk includes the path through beta unless beta_given)
+ *   dv         [B,T,H,d_v] of type dt
+ *   deta       [B,T,H] fp32             dL/deta, or dL/dbeta when beta_given
+ *   dlog_a     [B,T,H,d_k] fp32         dL/dlog a, per channel
+ *   dstate_in  [B,H,d_k,d_v] fp32       dL/dS_0, or NULL if not wanted
+ * Inputs: q, k, v, eta, log_a (16-byte aligned), state_in (NULL for S_0 = 0), eps and beta_given
+ * exactly as given to kla_kda_chunk_fwd; do [B,T,H,d_v] of type dt; dstate_out [B,H,d_k,d_v]
+ * fp32 or NULL (zero). The forward is recomputed inside.
+ *   Supported: bf16 with d_k, d_v in {64, 128}; fp32 with d_k = d_v = 64 (else
+ *   KLA_ERR_NOT_SUPPORTED). chunk must be 64. Any T >= 0; T = 0 writes dstate_in = dstate_out
+ *   (or zeros) and nothing else. Size limits as kla_kda_chunk_fwd. No output may overlap an
+ *   input or another output (KLA_ERR_INVALID_VALUE).
+ *   workspace  device buffer of at least kla_kda_chunk_bwd_workspace_size(...) bytes (NULL when
+ *              T = 0); its contents on entry do not matter.
+ * Stream-ordered and asynchronous; the library allocates nothing and keeps no pointer.
+ */
+kla_status_t kla_kda_chunk_bwd(const void* q, const void* k, const void* v,
+                               const float* eta, const float* log_a, const float* state_in,
+                               const void* dout, const float* dstate_out,
+                               void* dq, void* dk, void* dv, float* deta, float* dlog_a,
+                               float* dstate_in,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                               float eps, int beta_given, kla_dtype_t dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* kla_status_string(kla_status_t status);
 

@@ -110,7 +110,22 @@ def _job_backward(w, heads, got, s0_std, dst_std):
     return out
 
 
-_JOBS = {"forward": _job_forward, "decode": _job_decode, "backward": _job_backward}
+def _job_kda_backward(w, heads, got, s0_std, dst_std):
+    """Gradients of `heads` with the per-channel decay (Kaczmarz step): dq, dk, dv, deta [n, T, ...],
+    dlog_a [n, T, d_k], dS0."""
+    pre = [wl.head_prefill(w, b, h) for b, h in heads]
+    gr = [wl.head_grad(w, b, h, s0_std, dst_std) for b, h in heads]
+    la = np.stack([wl.head_channel_log_decay(w, b, h) for b, h in heads])
+    S0 = _stack(gr, "S0") if s0_std > 0 else None
+    dST = _stack(gr, "dST") if dst_std > 0 else None
+    g = oracle.kda_adjoint(*(_stack(pre, n) for n in ("q", "k", "v", "eta")), la, w.eps, S0, _stack(gr, "do"), dST)
+    out = {n: _chunk_sums(got[n], g[n]) for n in ("dq", "dk", "dv", "deta", "dlog_a")}
+    out["dS0"] = _state_sums(got["dS0"], g["dS0"])
+    return out
+
+
+_JOBS = {"forward": _job_forward, "decode": _job_decode, "backward": _job_backward,
+         "kda_backward": _job_kda_backward}
 
 
 def run(job, w, got_for, extra=(), heads=None):

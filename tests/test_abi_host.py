@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
                           "kla_decode_step", "kla_gdn_chunk_fwd", "kla_gdn_decode_step", "kla_status_string",
                           "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd",
                           "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step",
-                          "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg", "kla_chunk_fwd_noalloc"}
+                          "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg", "kla_chunk_fwd_noalloc",
+                          "kla_kda_chunk_bwd_workspace_size", "kla_kda_chunk_bwd"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -270,6 +271,47 @@ def test_bwd_workspace_size():
     # the forward's per-chunk factors, then per chunk two bf16 states and two 64 x 128 blocks
     assert need == fwd + 8 * 8 * 64 * (2 * 128 * 128 + 2 * 64 * 128) * 2
     assert K.lib().kla_chunk_bwd_workspace_size(8, 0, 8, 128, 128, 64, K.KLA_BF16) == 0
+
+
+def kda_bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, beta_given=0, dt=K.KLA_BF16, B=1, T=64, H=1, la=A16 * 5,
+            dla=A16 * 16, dq=A16 * 7, ws=WS, ws_bytes=None):
+    """kla_kda_chunk_bwd with fake device addresses (rejected before anything is enqueued).
+    log a and dlog a are [B, T, H, d_k] fp32: 32 KiB apart at T = 64, d_k = 128."""
+    if ws_bytes is None:
+        ws_bytes = max(K.lib().kla_kda_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk_len, dt), 0)
+    opt = lambda x: p(x) if x else None
+    return L().kla_kda_chunk_bwd(p(A16), p(A16 * 2), p(A16 * 3), p(A16 * 4), opt(la), None, p(A16 * 6), None,
+                                 opt(dq), p(A16 * 8), p(A16 * 9), p(A16 * 10), opt(dla), None, B, T, H, dk, dv,
+                                 chunk_len, eps, beta_given, dt, opt(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(dt=K.KLA_F32), K.KLA_ERR_NOT_SUPPORTED),             # fp32 gradients need d = 64
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),                     # the per-channel decay is required
+    (dict(la=0, beta_given=1), K.KLA_ERR_INVALID_VALUE),       # ... also with beta given
+    (dict(dla=0), K.KLA_ERR_INVALID_VALUE),                    # and its gradient
+    (dict(la=A16 * 5 + 4), K.KLA_ERR_INVALID_VALUE),           # log a rows are read 16 bytes at a time
+    (dict(dq=A16 * 5 + 4096), K.KLA_ERR_INVALID_VALUE),        # dq inside log a
+    (dict(dla=A16 * 5 + 8192), K.KLA_ERR_INVALID_VALUE),       # dlog a overlapping log a
+    (dict(ws=0), K.KLA_ERR_INVALID_VALUE),
+    (dict(ws_bytes=4096), K.KLA_ERR_INVALID_VALUE),
+    (dict(T=300000, H=16), K.KLA_ERR_NOT_SUPPORTED),           # fp32 log a of one batch entry past 2 GiB
+])
+def test_kda_chunk_bwd_rejects(kw, status):
+    assert kda_bwd(**kw) == status
+    assert L().kla_last_error().startswith(b"kla_kda_chunk_bwd")
+
+
+def test_kda_bwd_workspace_and_empty():
+    need = K.lib().kla_kda_chunk_bwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16)
+    kfwd = K.lib().kla_kda_chunk_fwd_workspace_size(8, 4096, 8, 128, 128, 64, K.KLA_BF16)
+    # the KDA forward's per-chunk factors and decayed operands, then per chunk two bf16 states and
+    # two 64 x 128 blocks (as for the scalar gate's backward)
+    assert need == kfwd + 8 * 8 * 64 * (2 * 128 * 128 + 2 * 64 * 128) * 2
+    assert K.lib().kla_kda_chunk_bwd_workspace_size(8, 0, 8, 128, 128, 64, K.KLA_BF16) == 0
+    assert kda_bwd(B=0) == K.KLA_OK
+    assert kda_bwd(T=0, ws=0) == K.KLA_OK
 
 
 def kda_chunk(dk=128, dv=128, chunk_len=64, eps=1e-6, beta_given=0, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16,

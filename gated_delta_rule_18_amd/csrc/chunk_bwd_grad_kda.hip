@@ -43,6 +43,10 @@ namespace {
 
 constexpr int kKgWaves = 8;
 constexpr int kKgThreads = kKgWaves * kWave;
+// Largest decay span (in log units, per channel) over a 16-token diagonal block that the MFMA
+// path takes: its operands are then at most e^32 (about 8e13) times the keys or queries, far
+// inside bf16's range for any key whose squares fit fp32 (which the recurrence itself needs).
+constexpr float kSpan = 32.f;
 
 template <typename E, int DK, int DV>
 struct KgSmem {
@@ -134,31 +138,37 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
       dma16(r, dst + blk * 64 * PER, base + row * rowb + hcol + 16 * swz<E, CPR>(row, ph % CPR));
     }
   };
-  dma_rows(rk, sm.Ks, x0, xrow, hcol_x, std::integral_constant<int, DK>());
-  dma_rows(rq, sm.Qs, x0, xrow, hcol_x, std::integral_constant<int, DK>());
+  // Issue order: what the C x C tiles need first (dO and V into LDS, Delta and Zb into
+  // registers), then K and Q (first read by the decayed products), S, dS' and log a, so that the
+  // first phase waits only for its own operands.
   dma_rows(rdo, sm.u.a.dOs, v0, vrow, hcol_v, std::integral_constant<int, DV>());
   dma_rows(rv, sm.u.a.St, v0, vrow, hcol_v, std::integral_constant<int, DV>());
 
   constexpr int NSR = DK * DV / PER / NT_;      // 16-byte pieces of S (and of dS') per thread
   constexpr int NCH = kChunk * DV / PER / NT_;  // 16-byte pieces of Delta (and of Zb) per thread
   constexpr int NL = kChunk * DK / 4 / NT_;     // 16-byte pieces of log a per thread
+  constexpr int NKQ = kChunk * DK / PER / 64 / NW;  // direct-to-LDS loads per wave for K (and Q)
   static_assert(NSR >= 1 && NCH >= 1 && NL >= 1, "piece split");
   V16 sreg[NSR], dsreg[NSR], dlreg[NCH], zbreg[NCH];
   i32x4 lx[NL];
   {
-    const E* gS = bw.Sn + chunk_id * DK * DV;
-    const E* gdS = bw.dSn + chunk_id * DK * DV;
     const E* gD = bw.Dl + chunk_id * kChunk * DV;
     const E* gZ = bw.Zb + chunk_id * kChunk * DV;
-#pragma unroll
-    for (int i = 0; i < NSR; ++i) {
-      sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + NT_ * i) * PER);
-      dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + NT_ * i) * PER);
-    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       dlreg[i] = *reinterpret_cast<const V16*>(gD + (tid + NT_ * i) * PER);
       zbreg[i] = *reinterpret_cast<const V16*>(gZ + (tid + NT_ * i) * PER);
+    }
+  }
+  dma_rows(rk, sm.Ks, x0, xrow, hcol_x, std::integral_constant<int, DK>());
+  dma_rows(rq, sm.Qs, x0, xrow, hcol_x, std::integral_constant<int, DK>());
+  {
+    const E* gS = bw.Sn + chunk_id * DK * DV;
+    const E* gdS = bw.dSn + chunk_id * DK * DV;
+#pragma unroll
+    for (int i = 0; i < NSR; ++i) {
+      sreg[i] = *reinterpret_cast<const V16*>(gS + (tid + NT_ * i) * PER);
+      dsreg[i] = *reinterpret_cast<const V16*>(gdS + (tid + NT_ * i) * PER);
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
@@ -166,6 +176,7 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
       lx[j] = __builtin_amdgcn_raw_buffer_load_b128(rla, (uint32_t)((t0 + r) * lrow + (hh * DK + c4) * 4), 0, 0);
     }
   }
+  constexpr int NLATER = 2 * NKQ + 2 * NSR + NL;  // loads issued after Zb, per wave (wave 0 adds two)
   if (wave == 0) {
     const float* sc = ws.SC + chunk_id * kScRows * kChunk;
     sm.cr[lane] = sc[kScCoefR * kChunk + lane];
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
       *reinterpret_cast<V16*>((arr ? sm.Mp : sm.Na) + at<E, kChunk>(r, col)) = z;
     }
   }
-  wait_vmem<0>();
+  wait_vmem<NLATER>();  // dO and V are in LDS (the loads complete in issue order)
   __syncthreads();
 
   // ---- C x C tiles: Na = -(Zb Delta^T), Mp = dO Delta^T; on diagonal tiles Zb V^T for Zb_r.v_r ----
@@ -311,6 +322,7 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
       store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
     }
   }
+  wait_vmem<0>();   // K and Q are in LDS
   __syncthreads();  // the d_v products are done: their LDS now holds G and a
 
   // ---- G = chunk-local prefix of log a per channel (NPART threads per channel, each a run of
@@ -355,22 +367,37 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
     const int b = 16 * rt, ce = 16 * rt + 15;
     const int tok = b + c16;          // this lane's output token
     f32x4 r1 = {0.f, 0.f, 0.f, 0.f}, r2 = r1, cc = r1;  // R1, R2, C1 + C2
+    // The diagonal block joins the MFMA products when the block's decay span (G_b - G_{b+15}, per
+    // channel) is at most kSpan on every channel of the tile: its operand factors then lie in
+    // [1, e^kSpan] (row side e^{G_b - G_s}, column side e^{G_r - G_ce}) and the output factors
+    // stay at most 1. Otherwise (channels that forget faster) the block is walked exactly.
+    const bool fast = __all(Gm[b * LDG + chA] - Gm[ce * LDG + chA] <= kSpan);
+    const int rlim = fast ? ce : b - 1;   // row side: contracted tokens s <= rlim
+    const int clim = fast ? b : ce + 1;   // column side: contracted tokens r >= clim
 
-    // row side, blocks left of the diagonal: reference token b
-    if (rt > 0) {
+    // row side: reference token b
+    {
       const float Gb = Gm[b * LDG + chA];
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
-        if (GK * s < b) {
-          GV a = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
+        if (GK * s <= rlim) {
+          GV a = kt_grp<E, DK>(sm.Ks, it, s, g, c16), alo;
 #pragma unroll
           for (int j = 0; j < (BF ? 8 : 4); ++j) {
             const int sk = grp_index<E>(s, g, j);
-            const float f = sk < b ? __expf(Gb - Gm[sk * LDG + chA]) : 0.f;
-            a[j] = from_f32<E>(to_f32(a[j]) * f);
+            const float f = sk <= rlim ? __expf(Gb - Gm[sk * LDG + chA]) : 0.f;
+            const float x = to_f32(a[j]) * f;
+            a[j] = from_f32<E>(x);
+            if constexpr (BF) alo[j] = from_f32<E>(x - to_f32(a[j]));
           }
-          r1 = mma<E>(a, row_grp<E, kChunk>(sm.Na, 16 * rt + c16, s, g), r1);
-          r2 = mma<E>(a, row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g), r2);
+          const GV bn = row_grp<E, kChunk>(sm.Na, 16 * rt + c16, s, g);
+          const GV bm = row_grp<E, kChunk>(sm.Mp, 16 * rt + c16, s, g);
+          r1 = mma<E>(a, bn, r1);
+          r2 = mma<E>(a, bm, r2);
+          if constexpr (BF) {
+            r1 = mma<E>(alo, bn, r1);
+            r2 = mma<E>(alo, bm, r2);
+          }
         }
       }
       const f32x4 Gr = *reinterpret_cast<const f32x4*>(&Gm[tok * LDG + ch0]);
@@ -382,10 +409,10 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
         r2[e] *= f;
       }
     }
-    // row side, the diagonal block: token tok walks s = b + 15 .. b with E = prod_{s < j <= tok} a_j
-    // (a loop with per-step LDS reads, partly unrolled: fully unrolled, the reads of all steps
-    // were hoisted and spilled)
-    {
+    // row side, the diagonal block walked: token tok goes s = b + 15 .. b with
+    // E = prod_{s < j <= tok} a_j (a loop with per-step LDS reads, partly unrolled: fully
+    // unrolled, the reads of all steps were hoisted and spilled)
+    if (!fast) {
       f32x4 Ew = {0.f, 0.f, 0.f, 0.f}, w1 = Ew, w2 = Ew;
 #pragma unroll 4
       for (int j = 15; j >= 0; --j) {
@@ -400,24 +427,34 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
       r2 += w2;
     }
 
-    // column side, blocks below the diagonal: reference token ce
-    if (rt < 3) {
+    // column side: reference token ce
+    {
       const float Gc = Gm[ce * LDG + chA];
 #pragma unroll
       for (int s = 0; s < NGT; ++s) {
-        if (GK * (s + 1) > ce + 1) {
-          GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16);
-          GV aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16);
+        if (GK * (s + 1) > clim) {
+          GV ak = kt_grp<E, DK>(sm.Ks, it, s, g, c16), aq = kt_grp<E, DK>(sm.Qs, it, s, g, c16), aklo, aqlo;
 #pragma unroll
           for (int j = 0; j < (BF ? 8 : 4); ++j) {
             const int rk_ = grp_index<E>(s, g, j);
-            const float f = rk_ > ce ? __expf(Gm[rk_ * LDG + chA] - Gc) : 0.f;
-            ak[j] = from_f32<E>(to_f32(ak[j]) * (f * sm.cr[rk_]));
-            aq[j] = from_f32<E>(to_f32(aq[j]) * f);
+            const float f = rk_ >= clim ? __expf(Gm[rk_ * LDG + chA] - Gc) : 0.f;
+            const float xk = to_f32(ak[j]) * (f * sm.cr[rk_]), xq = to_f32(aq[j]) * f;
+            ak[j] = from_f32<E>(xk);
+            aq[j] = from_f32<E>(xq);
+            if constexpr (BF) {
+              aklo[j] = from_f32<E>(xk - to_f32(ak[j]));
+              aqlo[j] = from_f32<E>(xq - to_f32(aq[j]));
+            }
           }
+          const GV bn = kt_grp<E, kChunk>(sm.Na, rt, s, g, c16);
+          const GV bm = kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16);
           f32x4 c = {0.f, 0.f, 0.f, 0.f};
-          c = mma<E>(ak, kt_grp<E, kChunk>(sm.Na, rt, s, g, c16), c);
-          c = mma<E>(aq, kt_grp<E, kChunk>(sm.Mp, rt, s, g, c16), c);
+          c = mma<E>(ak, bn, c);
+          c = mma<E>(aq, bm, c);
+          if constexpr (BF) {
+            c = mma<E>(aklo, bn, c);
+            c = mma<E>(aqlo, bm, c);
+          }
           cc += c;
         }
       }
@@ -426,8 +463,9 @@ __global__ __launch_bounds__(kKgThreads) void chunk_grad_kda_kernel(ChunkBwdPara
 #pragma unroll
       for (int e = 0; e < 4; ++e) cc[e] *= __expf(Gcv[e] - Gs[e]);
     }
-    // column side, the diagonal block: token tok walks r = b .. b + 15 with E = prod_{tok < j <= r} a_j
-    {
+    // column side, the diagonal block walked: token tok goes r = b .. b + 15 with
+    // E = prod_{tok < j <= r} a_j
+    if (!fast) {
       f32x4 Ew = {0.f, 0.f, 0.f, 0.f}, w = Ew;
 #pragma unroll 4
       for (int j = 0; j < 16; ++j) {

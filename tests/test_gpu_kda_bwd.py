@@ -111,6 +111,21 @@ def test_kda_bwd_strong_and_mixed_decay(dtype):
             oracle_bwd(w, inp, la, g, all_heads(w)), all_heads(w))
 
 
+def test_kda_bwd_diagonal_block_paths():
+    """The gradient kernel's two ways with a diagonal 16-token block: inside the matrix products
+    when the block's decay span is bounded, walked exactly when some channel forgets faster.
+    Here every block near the span bound (log a = -2 per token: e^30 over a block) next to
+    blocks where one channel forgets at -6 per token (tokens 70..99), in one chunk sequence."""
+    w = wl.custom("kda_bwd_paths", 615, B=1, H=2, dk=128, dv=128, T=192)
+    inp = wl.prefill_inputs(w)
+    la = np.full((1, w.T, 2, w.dk), -2.0, np.float32)
+    la[:, :, 1] = wl.channel_log_decay(w)[:, :, 1]
+    la[:, 70:100, :, 5] = -6.0
+    g = wl.grad_inputs(w, s0_std=0.05, dst_std=1.0)
+    compare("kda_bwd diagonal-block paths", w, gpu_bwd(w, inp, la, g), oracle_bwd(w, inp, la, g, all_heads(w)),
+            all_heads(w))
+
+
 def test_kda_bwd_equal_channels_equal_the_scalar_gate():
     """Every channel with the token's scalar log alpha: kla_kda_chunk_bwd reproduces kla_chunk_bwd,
     and its d log a summed over the channels is the scalar gate's d log alpha."""

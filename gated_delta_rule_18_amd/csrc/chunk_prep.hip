@@ -373,6 +373,10 @@ __device__ __forceinline__ float dpp_row16_sum(float x) {
 // Eight waves per KDA workgroup: its LDS (about 136 KiB) holds one workgroup per CU, so the
 // waves of the one chunk cover all four SIMDs twice.
 constexpr int kKdaThreads = 512;
+// Largest decay span (log units, per channel) of a 16-token diagonal block that its MFMA path
+// takes: its column operands are then at most e^32 (about 8e13) times the keys, far inside
+// bf16's range for any key whose squares fit fp32 (which the recurrence itself needs).
+constexpr float kKdaSpan = 32.f;
 
 template <typename E, int DK>
 struct PrepKdaSmem {
@@ -392,6 +396,7 @@ struct PrepKdaSmem {
   alignas(16) float Tx[6][16][20];  // T's lower off-diagonal blocks (tx_block)
   alignas(16) float sc[kScRows][kChunk];
   float n[kChunk], eta[kChunk];
+  int fast[4];  // diagonal block I within the decay span of its MFMA path (see kKdaSpan)
 };
 
 template <typename E, int DK>
@@ -543,28 +548,55 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     }
     if (tid < DK) kw.gamma[chunk_id * DK + tid] = __expf(sm.Gm[kChunk - 1][tid]);
   }
+  // Waves 4..7: whether diagonal block I = wave - 4 decays by at most kKdaSpan (log units) over
+  // its 16 tokens on every channel.
+  if (wave >= 4 && wave < 8) {
+    const int b = 16 * (wave - 4);
+    bool ok = true;
+    for (int ch = lane; ch < DK; ch += kWave) ok = ok && sm.Gm[b][ch] - sm.Gm[b + 15][ch] <= kKdaSpan;
+    const bool all = __all(ok);
+    if (lane == 0) sm.fast[wave - 4] = all;
+  }
   __syncthreads();
 
-  // ---- off-diagonal 16 x 16 blocks (I, J), J < I: MFMA on operands decayed to b = 16 I ----
-  for (int t = wave; t < 6; t += NW) {
-    const int I = t >= 3 ? 3 : t >= 1 ? 2 : 1, J = t - (I * (I - 1)) / 2, b = 16 * I;
+  // ---- 16 x 16 blocks (I, J), J <= I, as MFMA products of operands decayed to b = 16 I: the
+  //      six off the diagonal (row factors e^{G_r - G_b} <= 1, column factors e^{G_b - G_s} <= 1),
+  //      and the four diagonal ones whose decay span is bounded (column factors then in
+  //      [1, e^kKdaSpan]; in bf16 both operands are split into high and low parts, so that these
+  //      blocks, which dominate A and P, keep fp32-level accuracy). The other diagonal blocks are
+  //      walked below. ----
+  for (int t = wave; t < 10; t += NW) {
+    const bool diag = t >= 6;
+    if (diag && !sm.fast[t - 6]) continue;
+    const int I = diag ? t - 6 : t >= 3 ? 3 : t >= 1 ? 2 : 1, J = diag ? I : t - (I * (I - 1)) / 2, b = 16 * I;
     const int ra = 16 * I + lr, rb = 16 * J + lr;  // this lane's A row and B row
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
     if constexpr (BF) {
 #pragma unroll
       for (int i = 0; i < DK / 32; ++i) {
-        bf16x8 ak, aq, bk;
+        bf16x8 ak, aq, bk, akl, aql, bkl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int ch = 32 * i + 8 * lq + e;
           const float Gb = sm.Gm[b][ch];
           const float fa = __expf(sm.Gm[ra][ch] - Gb), fb = __expf(Gb - sm.Gm[rb][ch]);
-          ak[e] = from_f32<bf16>(to_f32(sm.Ks[ra][ch]) * fa);
-          aq[e] = from_f32<bf16>(to_f32(sm.Qs[ra][ch]) * fa);
-          bk[e] = from_f32<bf16>(to_f32(sm.Ks[rb][ch]) * fb);
+          const float xa = to_f32(sm.Ks[ra][ch]) * fa, xq = to_f32(sm.Qs[ra][ch]) * fa;
+          const float xb = to_f32(sm.Ks[rb][ch]) * fb;
+          ak[e] = from_f32<bf16>(xa);
+          aq[e] = from_f32<bf16>(xq);
+          bk[e] = from_f32<bf16>(xb);
+          akl[e] = from_f32<bf16>(xa - to_f32(ak[e]));
+          aql[e] = from_f32<bf16>(xq - to_f32(aq[e]));
+          bkl[e] = from_f32<bf16>(xb - to_f32(bk[e]));
         }
         kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, kk, 0, 0, 0);
         qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, qk, 0, 0, 0);
+        if (diag) {
+          kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akl, bk, kk, 0, 0, 0);
+          kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bkl, kk, 0, 0, 0);
+          qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aql, bk, qk, 0, 0, 0);
+          qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bkl, qk, 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll 4
@@ -582,8 +614,8 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * I + 4 * lq + e;
-      sm.Af[r][s] = sm.eta[r] * sm.sc[kScRs][r] * rss * kk[e];
-      sm.Ps[r][s] = from_f32<E>(qk[e]);
+      sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * rss * kk[e] : 0.f;
+      sm.Ps[r][s] = from_f32<E>(s <= r ? qk[e] : 0.f);
     }
   }
   // ---- diagonal 16 x 16 blocks ----
@@ -600,6 +632,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     const int sl = tid & 15, pair = (tid >> 4) & 7, hb = tid >> 7, c0 = CS * sl;
     static_assert(NTH % 128 == 0 && NTH <= 512, "blocks of eight row pairs of sixteen slices");
     for (int I = hb; I < 4; I += NTH / 128) {
+      if (sm.fast[I]) continue;
       const int b = 16 * I, r2 = 15 - pair;
       // the rows' factors eta_R rs_R
       const float f2 = sm.eta[b + r2] * sm.sc[kScRs][b + r2], f1 = sm.eta[b + pair] * sm.sc[kScRs][b + pair];
@@ -665,10 +698,10 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
         for (int c = 0; c < CS; ++c) ad[c] = ad_n[c];
       }
     }
-    // the upper triangles of the diagonal blocks
+    // the upper triangles of the walked diagonal blocks
     for (int i = tid; i < 4 * 256; i += NTH) {
       const int b = 16 * (i >> 8), rr = (i >> 4) & 15, ss = i & 15;
-      if (ss > rr) {
+      if (ss > rr && !sm.fast[i >> 8]) {
         sm.Af[b + rr][b + ss] = 0.f;
         sm.Ps[b + rr][b + ss] = from_f32<E>(0.f);
       }
@@ -677,6 +710,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     const int rr = (tid >> 4) & 15, ss = tid & 15;
     static_assert(NTH % 256 == 0, "whole blocks of 16 x 16 threads");
     for (int I = tid >> 8; I < 4; I += NTH / 256) {
+      if (sm.fast[I]) continue;
       const int r = 16 * I + rr, s = 16 * I + ss;
       float a = 0.f, pq = 0.f;
       if (s <= r) {

@@ -86,6 +86,19 @@ def test_kda_strong_and_mixed_decay(dtype):
     compare_fwd(f"kda strong/mixed decay {dtype}", w, inp, la)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kda_diagonal_block_paths(dtype):
+    """The prep's two ways with a diagonal 16-token block: matrix products when the block's decay
+    span is bounded (here log a = -2 per token: factors up to e^30 inside a block), the exact walk
+    when one channel forgets faster (channel 5 at -6 per token over tokens 70..99)."""
+    w = wl.custom("kda_paths", 515, B=1, H=2, dk=128 if dtype == "bf16" else 64, dv=64, T=192, dtype=dtype)
+    inp = wl.prefill_inputs(w)
+    la = np.full((1, w.T, 2, w.dk), -2.0, np.float32)
+    la[:, :, 1] = wl.channel_log_decay(w)[:, :, 1]
+    la[:, 70:100, :, 5] = -6.0
+    compare_fwd(f"kda diagonal-block paths {dtype}", w, inp, la)
+
+
 def test_kda_b8h8_t4096_all_heads():
     """The B8 H8 T4096 d128 bf16 shape at full size with per-channel decays: every head against the
     oracle (whole tensor, worst head, worst 64-token chunk), on o and S_T."""

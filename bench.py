@@ -481,6 +481,22 @@ def time_extra(name, torch, K, L, device, stream, flush):
         per = min(a.elapsed_time(b) for a, b in ev) / nlaunch
         part = decode_part(w, per, es, "graph", extra=True, launches=nlaunch)
         part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, "decode")
+        if w is BIG_DECODE:
+            # What a plain device copy of the state (read and write once, beyond the last-level
+            # cache) reaches on this device: the practical ceiling for a state read and rewritten.
+            dst = torch.empty_like(state)
+            dst.copy_(state)
+            ev = _events(torch, 5)
+            for a, b in ev:
+                a.record(stream)
+                dst.copy_(state)
+                b.record(stream)
+            torch.cuda.synchronize()
+            cms = min(a.elapsed_time(b) for a, b in ev)
+            cgbs = 2 * state.numel() * 4 / (cms * 1e-3) / 1e9
+            part["copy_reference"] = {"bytes": 2 * state.numel() * 4, "us": cms * 1e3, "gbs": cgbs,
+                                      "hbm_frac": cgbs / PEAK_HBM_GBS, "decode_frac_of_copy": part["hbm_gbs"] / cgbs}
+            del dst
         del t, state, out, g
     part["sources_sha"] = sources_sha("chunk_fwd" if w.T else "decode")
     part["workload"] = w.note

@@ -20,6 +20,12 @@
 namespace kla {
 namespace {
 
+// States of at least this many bytes (twice the MI355X's 256 MB last-level cache) are rewritten
+// with streaming stores: cache policy bits SC1 | NT of the buffer store (system scope,
+// non-temporal).
+constexpr int64_t kStreamStateBytes = int64_t(512) << 20;
+constexpr int kStreamStore = 16 | 2;
+
 // Sum of x over the lanes of the wave whose index is congruent to this lane's mod CG (CG a power
 // of two, 4 <= CG <= 16): DPP row rotations inside each 16-lane row, then exchanges across rows.
 // (The gfx950 row swaps v_permlane16/32_swap would avoid the LDS crossbar here, but this
@@ -43,7 +49,11 @@ __device__ __forceinline__ float class_sum(float x) {
 // fill one 64-byte line, so all their scalar loads hit the line the first one brings in.
 // heads_x packs the head count (bits 0..27; the C ABI bounds it below 2^28) and log2 of the
 // XCD grouping width X (bits 28..31), X the largest power of two not above the device's XCDs.
-template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
+// STREAM: the state is far larger than the last-level cache, so its rewrite is stored
+// non-temporally at system scope (it would only evict the next step's reads): measured on a
+// 512 MiB state 208 -> 196 us per step; on states the cache holds it is slower (64 MiB: 19.9 ->
+// 27.2 us), so it is chosen by state size.
+template <typename E, int DK, int DV, int DVS, bool KDA, bool BG, bool STREAM = false>
 __global__ __launch_bounds__(kWave) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ eta, const float* __restrict__ log_alpha, float* __restrict__ state,
@@ -145,16 +155,31 @@ __global__ __launch_bounds__(kWave) void decode_step_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[head * DV + col0 + e] = from_f32<E>(alpha * pq[e] + kq * delta[e]);
   }
+  if constexpr (STREAM) {
+    typedef int i32x4v __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, DK * DV * 4, 0x00020000);
 #pragma unroll
-  for (int m = 0; m < RPT; ++m)
-    *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * (alpha * ar[m]) + delta * kr[m];
+    for (int m = 0; m < RPT; ++m)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4v, s[m] * (alpha * ar[m]) + delta * kr[m]), rs,
+                                             (int)(((rg + RG * m) * DV + col0) * 4), 0, kStreamStore);
+  } else {
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+      *reinterpret_cast<f32x4*>(S + (int64_t)(rg + RG * m) * DV + col0) = s[m] * (alpha * ar[m]) + delta * kr[m];
+  }
 }
 
 template <typename E, int DK, int DV, int DVS, bool KDA, bool BG>
 void launch_kernel(const DecodeArgs& a, unsigned heads_x, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, KDA, BG>), dim3((unsigned)grid), dim3(kWave), 0, stream,
-                     (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads_x,
-                     a.eps);
+  const bool stream_state = DVS == 64 && (a.B * a.H) * (int64_t)DK * DV * 4 >= kStreamStateBytes;
+  if (stream_state)
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, KDA, BG, DVS == 64>), dim3((unsigned)grid), dim3(kWave),
+                       0, stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o,
+                       heads_x, a.eps);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, DVS, KDA, BG>), dim3((unsigned)grid), dim3(kWave), 0, stream,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, a.eta, a.log_alpha, a.state, (E*)a.o, heads_x,
+                       a.eps);
 }
 
 template <typename E, int DK, int DV, int DVS>

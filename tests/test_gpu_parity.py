@@ -87,6 +87,27 @@ def test_decode_steps_small(dtype, dk, dv, B, H):
     assert eo <= TOL[dtype] and eS <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
+def test_decode_state_beyond_the_cache(dtype, dk):
+    """A state of 512 MiB or more (twice the last-level cache) is rewritten with streaming stores:
+    8 192 heads at d = 128 bf16 (512 MiB) and 32 768 heads at d = 64 fp32 (512 MiB), four steps,
+    every head against the oracle."""
+    B, H = (512, 16) if dk == 128 else (2048, 16)
+    w = wl.custom("dec_big", 204, B=B, H=H, dk=dk, dv=dk, steps=4, dtype=dtype, s0_std=0.02)
+    inp = wl.decode_inputs(w)
+    S = dev(inp["S0"])
+    outs = []
+    for s in range(w.steps):
+        o = kla.kla_decode_step(dev(inp["q"][s], dtype), dev(inp["k"][s], dtype), dev(inp["v"][s], dtype),
+                                dev(inp["eta"][s]), dev(inp["log_alpha"][s]), S, eps=w.eps)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    ro, rS = oracle.kla_decode_steps(inp["q"], inp["k"], inp["v"], inp["eta"], inp["log_alpha"], w.eps, inp["S0"])
+    eo, eS = rel_l2(np.stack(outs), ro), rel_l2(host(S), rS)
+    report(f"decode {dtype} d={dk} B={B} H={H} (streaming state stores)", o=eo, S=eS)
+    assert eo <= TOL[dtype] and eS <= TOL[dtype]
+
+
 def test_decode_workload_b64h16_1024_steps():
     """Decode B64 H16 d128, 1024 consecutive steps from S0 ~ N(0, 0.02): every one of the 1024 heads
     against the oracle (whole tensor, worst head, worst 64-step window)."""

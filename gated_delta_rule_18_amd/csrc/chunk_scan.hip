@@ -346,10 +346,12 @@ chunk_scan_kernel(ChunkParams p) {
       }
     }
     f32x4 X[4][NT], Y[NT][4];
-    // One-pass bf16 forward (EARLY): the operands of the later products are read early: T and P
-    // fragments (the groups below the diagonal), the V columns and the per-token factors. (The
-    // other modes keep their reads beside their products: the segment pass would spill.)
-    constexpr bool EARLY = PERM && MODE == kScanFwd;
+    // One-pass bf16 forward, scalar gate or per-channel decay (EARLY): the operands of the later
+    // products are read early: T and P fragments (the groups below the diagonal), the V columns
+    // and the per-token factors. (The segment pass keeps its reads beside its products: it would
+    // spill. With the per-channel decay: bit-identical outputs, within noise on B8 H8 T4096 and
+    // the B4 H16 T32768 prefill.)
+    constexpr bool EARLY = PERM && (MODE == kScanFwd || MODE == kScanKda);
     constexpr int NTF = EARLY ? 6 : 1;  // T / P fragments: row tiles 0, 1 need group 0; 2, 3 groups 0, 1
     GV ft[NTF], fp[NTF];
     f32x4 fv[4][NT], fcoef[4], feg[4];

@@ -536,12 +536,14 @@ hipError_t launch_e(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, hipStream
 
 }  // namespace
 
-bool chunk_grad_supported(int64_t d_k, int64_t d_v, bool bf16_io) {
-  if (bf16_io) return true;
-  return d_k == 64 && d_v == 64;  // fp32 operands of 128-wide heads exceed 160 KiB of LDS
-}
+bool chunk_grad_supported(int64_t, int64_t, bool) { return true; }
 
+hipError_t launch_chunk_grad_split(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, hipStream_t stream);
+
+// fp32 operands of 128-wide heads exceed 160 KiB of LDS in this kernel: those shapes take the
+// kernel of chunk_bwd_grad_f32.hip, which forms the products over d_v in parts.
 hipError_t launch_chunk_grad(const ChunkBwdParams& p, int64_t d_k, int64_t d_v, bool bf16_io, hipStream_t stream) {
+  if (!bf16_io && !(d_k == 64 && d_v == 64)) return launch_chunk_grad_split(p, d_k, d_v, stream);
   return bf16_io ? launch_e<bf16>(p, d_k, d_v, stream) : launch_e<float>(p, d_k, d_v, stream);
 }
 

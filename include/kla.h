@@ -276,9 +276,9 @@ size_t kla_chunk_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k
  * Inputs: q, k, v, eta, log_alpha, state_in (NULL for S_0 = 0) exactly as given to
  * kla_chunk_fwd; do [B,T,H,d_v] of type dt; dstate_out [B,H,d_k,d_v] fp32 or NULL (zero).
  * The forward is recomputed inside; o is not needed.
- *   Supported: bf16 with d_k, d_v in {64, 128}; fp32 with d_k = d_v = 64 (else
- *   KLA_ERR_NOT_SUPPORTED). chunk must be 64. Any T >= 0 (a last partial chunk is handled);
- *   T = 0 writes dstate_in = dstate_out (or zeros) and nothing else.
+ *   Supported: d_k, d_v in {64, 128}, bf16 or fp32 (else KLA_ERR_NOT_SUPPORTED). chunk must
+ *   be 64. Any T >= 0 (a last partial chunk is handled); T = 0 writes dstate_in = dstate_out (or
+ *   zeros) and nothing else.
  *   No output may overlap an input or another output (KLA_ERR_INVALID_VALUE).
  *   workspace  device buffer of at least kla_chunk_bwd_workspace_size(...) bytes (NULL when
  *              T = 0); its contents on entry do not matter.

@@ -82,6 +82,7 @@ def all_heads(w):
 @pytest.mark.parametrize("dtype,dk,dv,T", [
     ("bf16", 128, 128, 250), ("bf16", 128, 128, 64), ("bf16", 64, 64, 131), ("bf16", 128, 64, 100),
     ("bf16", 64, 128, 1), ("f32", 64, 64, 256), ("f32", 64, 64, 77),
+    ("f32", 128, 128, 250), ("f32", 128, 128, 64), ("f32", 128, 64, 100), ("f32", 64, 128, 131),
 ])
 def test_chunk_bwd_shapes(dtype, dk, dv, T):
     w = wl.custom("bwd", 300 + T, B=2, H=2, dk=dk, dv=dv, T=T, dtype=dtype)
@@ -196,6 +197,25 @@ def test_gdn_chunk_bwd(dtype, gated):
     got = gpu_bwd(w, inp, g, beta=beta, la_given=gated)
     ref = oracle_bwd(w, inp, g, all_heads(w), beta=beta, la_given=gated)
     compare(f"gdn_chunk_bwd {dtype} {'gated' if gated else 'deltanet'}", w, got, ref, all_heads(w), la_given=gated)
+
+
+@pytest.mark.parametrize("gated", [True, False], ids=["gdn", "deltanet"])
+def test_gdn_chunk_bwd_f32_d128(gated):
+    """fp32 with 128-wide heads (the gradient kernel that forms the products over d_v in two
+    parts), beta given, signed and zero; also bitwise reproducible."""
+    w = wl.custom("gdn_bwd128", 317, B=1, H=2, dk=128, dv=128, T=150, dtype="f32")
+    inp = wl.prefill_inputs(w)
+    inp["k"] = _unit_keys(inp["k"])
+    beta = (inp["eta"] * np.where(np.arange(w.T) % 4 == 0, -0.5, 1.0)[None, :, None]).astype(np.float32)
+    beta[:, 30:70] = 0.0
+    g = wl.grad_inputs(w, s0_std=0.05, dst_std=1.0)
+    got = gpu_bwd(w, inp, g, beta=beta, la_given=gated)
+    again = gpu_bwd(w, inp, g, beta=beta, la_given=gated)
+    for n in NAMES:
+        if got[n] is not None:
+            np.testing.assert_array_equal(got[n], again[n], err_msg=n)
+    ref = oracle_bwd(w, inp, g, all_heads(w), beta=beta, la_given=gated)
+    compare(f"gdn_chunk_bwd f32 d128 {'gated' if gated else 'deltanet'}", w, got, ref, all_heads(w), la_given=gated)
 
 
 def test_bwd_agrees_with_forward_by_directional_derivative():

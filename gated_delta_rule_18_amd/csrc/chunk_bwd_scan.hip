@@ -80,9 +80,9 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   if (head >= p.heads) return;
   const int64_t bb = head / p.H, hh = head % p.H;
   const int64_t T = p.T, nchunks = p.nchunks, H = p.H;
-  const int tid = threadIdx.x, lane = tid & 63;
+  int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, g = lane >> 4;
+  int c16 = lane & 15, g = lane >> 4;
   const int j0 = slice * DVS;
   const int cw = wave * NC;
   const int ct0 = (j0 + cw) / 16;  // first global 16-column tile of this wave
@@ -206,6 +206,16 @@ __global__ __launch_bounds__((W + 2) * kWave) __attribute__((amdgpu_waves_per_eu
   // this chunk's stores, so at most (DIST - 1) chunks of loads and DIST chunks of stores are
   // younger than this chunk's loads when it starts.
   auto step = [&](Buf& B, Buf& Bn, int64_t c, int64_t done) __attribute__((always_inline)) {
+    if constexpr (!is_bf16<E>() && DK == 128) {
+      // fp32 with d_k = 128: per-lane index arithmetic is redone every chunk (the lane id passed
+      // through an empty asm) rather than hoisted out of the chunk loop: hoisted, it stayed live
+      // across the loop and spilled 136-169 VGPRs; now none (B2 H8 T4096 backward 2.06 ->
+      // 1.54 ms). At d_k = 64 (15 spilled) the redone arithmetic cost more than it saved.
+      asm volatile("" : "+v"(tid));
+      lane = tid & 63;
+      c16 = lane & 15;
+      g = lane >> 4;
+    }
     if constexpr (NP > 0) {
       // the producers waited for chunk c's loads before this barrier
     } else if constexpr (NB == 1) {

@@ -98,6 +98,10 @@ PART_SOURCES = {
     "chunk_bwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "chunk_bwd_scan.hip", "chunk_bwd_grad.hip",
                   "tile_ops.h", "kla_device.h", "kla_launch.h"],
 }
+# The per-channel decay runs other kernels (or other instantiations) of the same files.
+PART_SOURCES["chunk_fwd_kda"] = PART_SOURCES["chunk_fwd"]
+PART_SOURCES["decode_kda"] = PART_SOURCES["decode"]
+PART_SOURCES["chunk_bwd_kda"] = PART_SOURCES["chunk_bwd"] + ["chunk_bwd_grad_kda.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -112,6 +116,11 @@ def sources_sha(part):
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def traffic_key(part, mode):
+    """Name under which the traffic of `part` in decay mode `mode` is recorded."""
+    return part if mode == "kla" else part + "_kda"
 
 
 def recorded_traffic(workload, part):
@@ -327,8 +336,9 @@ def run_bwd(args, w):
             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "workspace_bytes": ws_bytes, "sources_sha": sources_sha("chunk_bwd")}
-    part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, "chunk_bwd") if args.mode == "kla" else None
+            "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key("chunk_bwd", args.mode))}
+    part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key("chunk_bwd", args.mode))
+                                            if args.mode in ("kla", "kda") else None)
     roof = {"bound": "mfma", "kernel": part["kernel"], "achieved": part["mfma_tflops"], "peak": peak_mfma,
             "unit": "TFLOP/s", "frac": part["mfma_frac"], "traffic": part["hbm_traffic_bytes_per_launch"],
             "hbm_view": {"achieved": part["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -700,8 +710,9 @@ def main():
         parts["decode"] = decode_part(w, ms / w.steps, es, args.decode_launch)
 
     for name, part in parts.items():
-        part["sources_sha"] = sources_sha(name)
-        part["hbm_traffic_bytes_per_launch"] = recorded_traffic(w.name, name) if args.mode == "kla" else None
+        part["sources_sha"] = sources_sha(traffic_key(name, args.mode))
+        part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key(name, args.mode))
+                                                if args.mode in ("kla", "kda") else None)
     dom_name = max(parts, key=lambda p: parts[p]["ms_per_step"])
     dom = parts[dom_name]
     roof = {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["hbm_gbs"], "peak": PEAK_HBM_GBS,

@@ -130,47 +130,81 @@ __device__ __forceinline__ void t_column(Sm& sm, int lane) {
   }
 }
 
+// Diagonal 16 x 16 blocks of T = (I + A)^-1 by forward substitution, in place of A's in sm.Af
+// (wave 0: lane group g takes block g, lane c of it column c).
+template <typename Sm>
+__device__ __forceinline__ void t_diag(Sm& sm, int lane) {
+  const int base = (lane >> 4) * 16, col = lane & 15;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float* arow = &sm.Af[base + i][base];
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
+    x[i] = (i == col) ? 1.f : -s;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
+}
+
+// P (sm.Ps; upper off-diagonal blocks written as zero) and the factor rows (sm.sc) of chunk
+// chunk_id to the workspace, by threads t = 0 .. nt - 1.
+template <typename E, typename Sm>
+__device__ __forceinline__ void store_p_sc(const Sm& sm, const Workspace<E>& ws, int64_t chunk_id, int t, int nt) {
+  constexpr int VN = Vec16<E>::N;
+  typedef typename Vec16<E>::type V16;
+  constexpr int VPR = kChunk / VN;
+  E* gP = ws.P + chunk_id * kChunk * kChunk;
+  for (int i = t; i < kChunk * VPR; i += nt) {
+    const int r = i / VPR, c0 = (i % VPR) * VN;
+    V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
+    if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
+#pragma unroll
+      for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
+    }
+    *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
+  }
+  float* gS = ws.SC + chunk_id * kScRows * kChunk;
+  for (int i = t; i < kScRows * kChunk; i += nt) gS[i] = (&sm.sc[0][0])[i];
+}
+
+// T of chunk chunk_id to the workspace (diagonal blocks from sm.Af, lower off-diagonal ones
+// from sm.Tx, upper ones zero), by all NTH threads.
+template <typename E, int NTH, typename Sm>
+__device__ __forceinline__ void store_t(const Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
+  constexpr int VN = Vec16<E>::N;
+  typedef typename Vec16<E>::type V16;
+  constexpr int VPR = kChunk / VN;
+  E* gT = ws.T + chunk_id * kChunk * kChunk;
+  for (int i = threadIdx.x; i < kChunk * VPR; i += NTH) {
+    const int r = i / VPR, c0 = (i % VPR) * VN;
+    V16 out;
+    const int bi = r >> 4, bj = c0 >> 4;
+    const bool zero = bj > bi;  // upper off-diagonal block
+    const float* src = bj == bi ? &sm.Af[r][c0] : &sm.Tx[zero ? 0 : tx_block(bi, bj)][r & 15][c0 & 15];
+#pragma unroll
+    for (int e4 = 0; e4 < VN; e4 += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + e4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
+    }
+    *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
+  }
+}
+
 // T = (I + A)^-1 (diagonal blocks in place of A in sm.Af, the others in sm.Tx), and the chunk's
 // P, T and factor rows to the workspace.
 // Called by all threads of the workgroup once A (sm.Af, fp32, zero on and above the diagonal),
 // P (sm.Ps) and the factor rows (sm.sc) are in LDS and published by a barrier.
 template <typename E, int NTH = kThreads, typename Sm>
 __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
-  constexpr int VN = Vec16<E>::N;
-  typedef typename Vec16<E>::type V16;
-  constexpr int LDF = Sm::LDF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  // ---- diagonal blocks of T by forward substitution (wave 0); waves 1-3 store P and the factors ----
-  if (wave == 0) {
-    const int base = (lane >> 4) * 16, col = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float* arow = &sm.Af[base + i][base];
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
-      x[i] = (i == col) ? 1.f : -s;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
-  } else {
-    const int t = tid - kWave;  // 0 .. 191
-    constexpr int VPR = kChunk / VN;
-    E* gP = ws.P + chunk_id * kChunk * kChunk;
-    for (int i = t; i < kChunk * VPR; i += NTH - kWave) {
-      const int r = i / VPR, c0 = (i % VPR) * VN;
-      V16 out = *reinterpret_cast<const V16*>(&sm.Ps[r][c0]);
-      if ((c0 >> 4) > (r >> 4)) {  // upper off-diagonal blocks were never computed
-#pragma unroll
-        for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
-      }
-      *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
-    }
-    float* gS = ws.SC + chunk_id * kScRows * kChunk;
-    for (int i = t; i < kScRows * kChunk; i += NTH - kWave) gS[i] = (&sm.sc[0][0])[i];
-  }
+  // ---- diagonal blocks of T (wave 0) while the other waves store P and the factors ----
+  if (wave == 0)
+    t_diag(sm, lane);
+  else
+    store_p_sc<E>(sm, ws, chunk_id, tid - kWave, NTH - kWave);
   __syncthreads();
 
   // ---- off-diagonal blocks, down each block column: wave j forms, for i = j+1 .. 3,
@@ -182,24 +216,7 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
   __syncthreads();
 
   // ---- T to the workspace (upper off-diagonal blocks are zero) ----
-  {
-    constexpr int VPR = kChunk / VN;
-    E* gT = ws.T + chunk_id * kChunk * kChunk;
-    for (int i = tid; i < kChunk * VPR; i += NTH) {
-      const int r = i / VPR, c0 = (i % VPR) * VN;
-      V16 out;
-      const int bi = r >> 4, bj = c0 >> 4;
-      const bool zero = bj > bi;  // upper off-diagonal block
-      const float* src = bj == bi ? &sm.Af[r][c0] : &sm.Tx[zero ? 0 : tx_block(bi, bj)][r & 15][c0 & 15];
-#pragma unroll
-      for (int e4 = 0; e4 < VN; e4 += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + e4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
-      }
-      *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
-    }
-  }
+  store_t<E, NTH>(sm, ws, chunk_id);
 }
 
 template <typename E, int DK>
@@ -370,6 +387,11 @@ __device__ __forceinline__ float dpp_row16_sum(float x) {
   return x;
 }
 
+// The KDA prep keeps the prefixes of log a in log2 units, so that every decay factor is one
+// hardware exp2 of a difference.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Eight waves per KDA workgroup: its LDS (about 136 KiB) holds one workgroup per CU, so the
 // waves of the one chunk cover all four SIMDs twice.
 constexpr int kKdaThreads = 512;
@@ -387,9 +409,10 @@ struct PrepKdaSmem {
   static constexpr int LDF = kChunk + 4;
   alignas(16) E Ks[kChunk][LDK];
   alignas(16) E Qs[kChunk][LDK];
-  alignas(16) float Gm[kChunk][LDG];  // log a, then its chunk-local prefix per channel
-  // per-token decays a = e^{log a} (bf16 diagonal blocks; fp32 forms the ratios directly)
-  alignas(16) float Ad[is_bf16<E>() ? kChunk : 1][LDG];
+  alignas(16) float Gm[kChunk][LDG];  // log a, then its chunk-local prefix per channel in log2 units
+  // bf16: the row factors e^{G_r - G_b} of the 16 x 16 blocks' MFMA products (b = the row's
+  // block start), formed once per chunk (fp32 forms them in the products: its LDS has no room)
+  alignas(16) float FR[is_bf16<E>() ? kChunk : 1][LDG];
   float part[kKdaThreads / DK][DK];   // prefix-scan partial totals
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
@@ -422,8 +445,11 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   i32x4 kx[NKQ], qx[NKQ], lx[NL];
   float et = 0.f;
   auto load_chunk = [&](int64_t id, int tid_) __attribute__((always_inline)) {
-    const int64_t head = id / p.nchunks, t0 = (id % p.nchunks) * kChunk;
-    const int64_t bb = head / p.H, hh = head % p.H, brow = bb * T * p.H;
+    // (chunk ids and head counts fit 32 bits: the entry points reject larger grids)
+    const uint32_t idu = (uint32_t)id, ncu = (uint32_t)p.nchunks, Hu = (uint32_t)p.H;
+    const uint32_t head = idu / ncu, bbu = head / Hu;
+    const int64_t t0 = (int64_t)(idu - head * ncu) * kChunk;
+    const int64_t bb = bbu, hh = head - bbu * Hu, brow = bb * T * p.H;
     const uint32_t xrow = p.H * DK * sizeof(E), lrow = p.H * DK * 4;  // bytes per token
     const rsrc_t rk = make_rsrc(static_cast<const E*>(p.k) + brow * DK, (uint32_t)(T * xrow));
     const rsrc_t rq = make_rsrc(static_cast<const E*>(p.q) + brow * DK, (uint32_t)(T * xrow));
@@ -444,13 +470,14 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   };
   if ((int64_t)blockIdx.x >= total) return;
   load_chunk(blockIdx.x, tid0);
+  int64_t prev_id = -1;  // the previous chunk, whose P, factor rows and T are still in LDS
   for (int64_t chunk_id = blockIdx.x; chunk_id < total; chunk_id += gridDim.x) {
   // Per-thread index arithmetic is redone every chunk rather than kept live across the loop.
   int tid = tid0;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int64_t t0 = (chunk_id % p.nchunks) * kChunk;
+  const int64_t t0 = (int64_t)((uint32_t)chunk_id % (uint32_t)p.nchunks) * kChunk;
 
   // ---- K, Q rows, log a and eta of the chunk into LDS, then the next chunk's loads ----
   {
@@ -469,29 +496,39 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     if (chunk_id + gridDim.x < total) load_chunk(chunk_id + gridDim.x, tid);
   }
   __syncthreads();
+  // ---- the previous chunk's P, factor rows and T to the workspace: stored here, behind the
+  //      loads just issued, so that waiting for those loads does not wait for these stores ----
+  if (prev_id >= 0) {
+    store_p_sc<E>(sm, ws, prev_id, tid, NTH);
+    store_t<E, NTH>(sm, ws, prev_id);
+  }
 
-  // ---- per-channel prefix of log a over the chunk's tokens: NPART threads per channel, each a
-  //      run of tokens in registers, then the runs' totals; the per-token decays e^{log a} ----
+  // ---- per-channel prefix of log a over the chunk's tokens, in log2 units (every exponential
+  //      below is one exp2 of a difference of these): NPART threads per channel, each a run of
+  //      tokens in registers, then the runs' totals; squared key norms, TPR threads per token ----
   constexpr int NPART = NTH / DK, RUN = kChunk / NPART;
   const int ch = tid % DK, part = tid / DK;
   float run[RUN];
 #pragma unroll
-  for (int j = 0; j < RUN; ++j) run[j] = sm.Gm[part * RUN + j][ch];
-  if constexpr (BF) {
-#pragma unroll
-    for (int j = 0; j < RUN; ++j) sm.Ad[part * RUN + j][ch] = __expf(run[j]);
-  }
+  for (int j = 0; j < RUN; ++j) run[j] = sm.Gm[part * RUN + j][ch] * kLog2e;
 #pragma unroll
   for (int j = 1; j < RUN; ++j) run[j] += run[j - 1];
   sm.part[part][ch] = run[RUN - 1];
-  if (tid < kChunk) {  // squared key norms
+  {
+    constexpr int TPR = NTH / kChunk, CPT = DK / TPR;
+    static_assert(TPR == 8 && CPT % VN == 0, "eight threads per token");
+    const int r = tid / TPR, c0 = (tid % TPR) * CPT;
     float nn = 0.f;
-    for (int i = 0; i < DK; i += VN) {
-      const V16 x = *reinterpret_cast<const V16*>(&sm.Ks[tid][i]);
+#pragma unroll
+    for (int i = 0; i < CPT; i += VN) {
+      const V16 x = *reinterpret_cast<const V16*>(&sm.Ks[r][c0 + i]);
 #pragma unroll
       for (int e = 0; e < VN; ++e) nn += to_f32(x[e]) * to_f32(x[e]);
     }
-    sm.n[tid] = nn;
+    nn += __shfl_xor(nn, 1);
+    nn += __shfl_xor(nn, 2);
+    nn += __shfl_xor(nn, 4);
+    if (tid % TPR == 0) sm.n[r] = nn;
   }
   __syncthreads();
   {
@@ -500,7 +537,6 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
 #pragma unroll
     for (int j = 0; j < RUN; ++j) sm.Gm[part * RUN + j][ch] = run[j] + off;
   }
-  __syncthreads();
 
   // ---- factors (wave 0): as for the scalar gate, with e^G = 1 and rs e^{G_C - G} = rs ----
   if (wave == 0) {
@@ -524,36 +560,51 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     sm.sc[kScRs][r] = rs;
     sm.sc[kScD2][r] = rs;
   }
-  // ---- decayed scan operands and gamma to the workspace ----
+  __syncthreads();
+
+  // ---- decayed scan operands and gamma to the workspace; (bf16) the row factors ----
   {
     constexpr int CPR = DK / VN;
     E* k1 = kw.K1 + chunk_id * kChunk * DK;
     E* q1 = kw.Q1 + chunk_id * kChunk * DK;
     E* k2 = kw.K2 + chunk_id * kChunk * DK;
     for (int i = tid; i < kChunk * CPR; i += NTH) {
-      const int r = i / CPR, c0 = (i % CPR) * VN;
+      const int r = i / CPR, c0 = (i % CPR) * VN, b = r & ~15;
       const V16 kx = *reinterpret_cast<const V16*>(&sm.Ks[r][c0]);
       const V16 qx = *reinterpret_cast<const V16*>(&sm.Qs[r][c0]);
-      V16 a, b, d;
+      V16 a, bq, d;
+      float fr[VN];
 #pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        const float G = sm.Gm[r][c0 + e], eg = __expf(G), ed = __expf(sm.Gm[kChunk - 1][c0 + e] - G);
-        a[e] = from_f32<E>(to_f32(kx[e]) * eg);
-        b[e] = from_f32<E>(to_f32(qx[e]) * eg);
-        d[e] = from_f32<E>(to_f32(kx[e]) * ed);
+      for (int e4 = 0; e4 < VN; e4 += 4) {
+        const f32x4 G = *reinterpret_cast<const f32x4*>(&sm.Gm[r][c0 + e4]);
+        const f32x4 GC = *reinterpret_cast<const f32x4*>(&sm.Gm[kChunk - 1][c0 + e4]);
+        const f32x4 Gb = *reinterpret_cast<const f32x4*>(&sm.Gm[b][c0 + e4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float eg = exp2_fast(G[e]), ed = exp2_fast(GC[e] - G[e]);
+          a[e4 + e] = from_f32<E>(to_f32(kx[e4 + e]) * eg);
+          bq[e4 + e] = from_f32<E>(to_f32(qx[e4 + e]) * eg);
+          d[e4 + e] = from_f32<E>(to_f32(kx[e4 + e]) * ed);
+          fr[e4 + e] = exp2_fast(G[e] - Gb[e]);
+        }
       }
       *reinterpret_cast<V16*>(k1 + r * DK + c0) = a;
-      *reinterpret_cast<V16*>(q1 + r * DK + c0) = b;
+      *reinterpret_cast<V16*>(q1 + r * DK + c0) = bq;
       *reinterpret_cast<V16*>(k2 + r * DK + c0) = d;
+      if constexpr (BF) {
+#pragma unroll
+        for (int e4 = 0; e4 < VN; e4 += 4)
+          *reinterpret_cast<f32x4*>(&sm.FR[r][c0 + e4]) = f32x4{fr[e4], fr[e4 + 1], fr[e4 + 2], fr[e4 + 3]};
+      }
     }
-    if (tid < DK) kw.gamma[chunk_id * DK + tid] = __expf(sm.Gm[kChunk - 1][tid]);
+    if (tid < DK) kw.gamma[chunk_id * DK + tid] = exp2_fast(sm.Gm[kChunk - 1][tid]);
   }
   // Waves 4..7: whether diagonal block I = wave - 4 decays by at most kKdaSpan (log units) over
   // its 16 tokens on every channel.
   if (wave >= 4 && wave < 8) {
     const int b = 16 * (wave - 4);
     bool ok = true;
-    for (int ch = lane; ch < DK; ch += kWave) ok = ok && sm.Gm[b][ch] - sm.Gm[b + 15][ch] <= kKdaSpan;
+    for (int ch = lane; ch < DK; ch += kWave) ok = ok && sm.Gm[b][ch] - sm.Gm[b + 15][ch] <= kKdaSpan * kLog2e;
     const bool all = __all(ok);
     if (lane == 0) sm.fast[wave - 4] = all;
   }
@@ -565,33 +616,42 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   //      [1, e^kKdaSpan]; in bf16 both operands are split into high and low parts, so that these
   //      blocks, which dominate A and P, keep fp32-level accuracy). The other diagonal blocks are
   //      walked below. ----
-  for (int t = wave; t < 10; t += NW) {
-    const bool diag = t >= 6;
-    if (diag && !sm.fast[t - 6]) continue;
-    const int I = diag ? t - 6 : t >= 3 ? 3 : t >= 1 ? 2 : 1, J = diag ? I : t - (I * (I - 1)) / 2, b = 16 * I;
+  auto block = [&](auto diag_c, int I, int J) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_c)::value;
+    const int b = 16 * I;
     const int ra = 16 * I + lr, rb = 16 * J + lr;  // this lane's A row and B row
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
     if constexpr (BF) {
 #pragma unroll
       for (int i = 0; i < DK / 32; ++i) {
+        const int c = 32 * i + 8 * lq;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.Ks[ra][c]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.Qs[ra][c]);
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&sm.Ks[rb][c]);
         bf16x8 ak, aq, bk, akl, aql, bkl;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = 32 * i + 8 * lq + e;
-          const float Gb = sm.Gm[b][ch];
-          const float fa = __expf(sm.Gm[ra][ch] - Gb), fb = __expf(Gb - sm.Gm[rb][ch]);
-          const float xa = to_f32(sm.Ks[ra][ch]) * fa, xq = to_f32(sm.Qs[ra][ch]) * fa;
-          const float xb = to_f32(sm.Ks[rb][ch]) * fb;
-          ak[e] = from_f32<bf16>(xa);
-          aq[e] = from_f32<bf16>(xq);
-          bk[e] = from_f32<bf16>(xb);
-          akl[e] = from_f32<bf16>(xa - to_f32(ak[e]));
-          aql[e] = from_f32<bf16>(xq - to_f32(aq[e]));
-          bkl[e] = from_f32<bf16>(xb - to_f32(bk[e]));
+        for (int h = 0; h < 8; h += 4) {
+          const f32x4 fa = *reinterpret_cast<const f32x4*>(&sm.FR[ra][c + h]);
+          const f32x4 gb = *reinterpret_cast<const f32x4*>(&sm.Gm[b][c + h]);
+          const f32x4 gs = *reinterpret_cast<const f32x4*>(&sm.Gm[rb][c + h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float fb = exp2_fast(gb[e] - gs[e]);
+            const float xa = to_f32(ka[h + e]) * fa[e], xq = to_f32(qa[h + e]) * fa[e];
+            const float xb = to_f32(kb[h + e]) * fb;
+            ak[h + e] = from_f32<bf16>(xa);
+            aq[h + e] = from_f32<bf16>(xq);
+            bk[h + e] = from_f32<bf16>(xb);
+            if constexpr (DIAG) {
+              akl[h + e] = from_f32<bf16>(xa - to_f32(ak[h + e]));
+              aql[h + e] = from_f32<bf16>(xq - to_f32(aq[h + e]));
+              bkl[h + e] = from_f32<bf16>(xb - to_f32(bk[h + e]));
+            }
+          }
         }
         kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, kk, 0, 0, 0);
         qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, qk, 0, 0, 0);
-        if (diag) {
+        if constexpr (DIAG) {
           kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(akl, bk, kk, 0, 0, 0);
           kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bkl, kk, 0, 0, 0);
           qk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aql, bk, qk, 0, 0, 0);
@@ -603,7 +663,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
       for (int i = 0; i < DK / 4; ++i) {
         const int ch = 4 * i + lq;
         const float Gb = sm.Gm[b][ch];
-        const float fa = __expf(sm.Gm[ra][ch] - Gb), fb = __expf(Gb - sm.Gm[rb][ch]);
+        const float fa = exp2_fast(sm.Gm[ra][ch] - Gb), fb = exp2_fast(Gb - sm.Gm[rb][ch]);
         const float bk = sm.Ks[rb][ch] * fb;
         kk = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.Ks[ra][ch] * fa, bk, kk, 0, 0, 0);
         qk = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.Qs[ra][ch] * fa, bk, qk, 0, 0, 0);
@@ -617,6 +677,20 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
       sm.Af[r][s] = s < r ? sm.eta[r] * sm.sc[kScRs][r] * rss * kk[e] : 0.f;
       sm.Ps[r][s] = from_f32<E>(s <= r ? qk[e] : 0.f);
     }
+  };
+  // Waves 0..3 take diagonal block I = wave, waves 4..7 off-diagonal block t = wave - 4 and
+  // (t < 2) t + 4, so that each SIMD (waves w and w + 4) carries one diagonal block and one or
+  // two off-diagonal ones. Off-diagonal block t is (I, J) = (1,0), (2,0), (2,1), (3,0), (3,1), (3,2).
+  if (wave < 4) {
+    if (sm.fast[wave]) block(std::true_type{}, wave, wave);
+  } else if (wave < 8) {
+    auto off = [&](int t) __attribute__((always_inline)) {
+      const int I = t >= 3 ? 3 : t >= 1 ? 2 : 1, J = t - (I * (I - 1)) / 2;
+      block(std::false_type{}, I, J);
+    };
+    const int t = wave - 4;
+    off(t);
+    if (t < 2) off(t + 4);
   }
   // ---- diagonal 16 x 16 blocks ----
   if constexpr (BF) {
@@ -649,12 +723,15 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
           w[c] = 1.f;
         }
       };
+      // a_sr = e^{G_sr - G_{sr-1}} (unused for sr = 0, where it reads as 1)
       auto read_ad = [&](int sr, float* dst) __attribute__((always_inline)) {
+        const int sp = sr > 0 ? sr - 1 : 0;
 #pragma unroll
         for (int c = 0; c < CS; c += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Ad[b + sr][c0 + c]);
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.Gm[b + sr][c0 + c]);
+          const f32x4 y = *reinterpret_cast<const f32x4*>(&sm.Gm[b + sp][c0 + c]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[c + e] = x[e];
+          for (int e = 0; e < 4; ++e) dst[c + e] = exp2_fast(x[e] - y[e]);
         }
       };
       row_start();
@@ -719,7 +796,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
           const f32x4 Gs = *reinterpret_cast<const f32x4*>(&sm.Gm[s][i]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float w = __expf(Gr[e] - Gs[e]) * to_f32(sm.Ks[s][i + e]);
+            const float w = exp2_fast(Gr[e] - Gs[e]) * to_f32(sm.Ks[s][i + e]);
             a += to_f32(sm.Ks[r][i + e]) * w;
             pq += to_f32(sm.Qs[r][i + e]) * w;
           }
@@ -731,9 +808,21 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   }
   __syncthreads();
 
-  solve_and_store<E, NTH>(sm, ws, chunk_id);
-  __syncthreads();  // the next chunk overwrites the LDS
+  // ---- T = (I + A)^-1 in LDS: diagonal blocks (wave 0), then the blocks below them (waves
+  //      0..2, as in solve_and_store). The other waves go on to the next chunk's rows, which
+  //      t_column does not read; its results are read after the next chunk's first barrier. ----
+  if (wave == 0) t_diag(sm, lane);
+  __syncthreads();
+  if (wave == 0) t_column<0>(sm, lane);
+  if (wave == 1) t_column<1>(sm, lane);
+  if (wave == 2) t_column<2>(sm, lane);
+  prev_id = chunk_id;
   }  // chunk loop
+  __syncthreads();
+  if (prev_id >= 0) {
+    store_p_sc<E>(sm, ws, prev_id, threadIdx.x, NTH);
+    store_t<E, NTH>(sm, ws, prev_id);
+  }
 }
 
 // Workgroups of a kernel resident at once per compute unit (the same on every gfx950 device).

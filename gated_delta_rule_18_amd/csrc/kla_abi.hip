@@ -199,7 +199,8 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
     g_last_error[0] = '\0';
     return KLA_OK;
   }
-  if (B * H * 8 > 0x7fffffffLL) return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
+  if (B * H * 8 > 0x7fffffffLL || B * H * ((T + kla::kChunk - 1) / kla::kChunk) > 0x7fffffffLL)
+    return fail(KLA_ERR_INVALID_VALUE, "%s: grid too large", fn);
   // The kernels address one batch's rows of q/k/v/o (and, with kda, of the fp32 log a), and one
   // head's workspace, with 32-bit byte offsets (up to one chunk past T).
   const int64_t row_bytes = std::max((d_k > d_v ? d_k : d_v) * (dt == KLA_BF16 ? 2 : 4), kda ? d_k * 4 : int64_t(0));

@@ -138,10 +138,14 @@ __device__ __forceinline__ void t_diag(Sm& sm, int lane) {
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
+    // sum_{m < i} A[i][m] x[m] as four interleaved partial sums over m < i - 1 plus the last
+    // term, so that each row waits on the one before it for a single fma
     const float* arow = &sm.Af[base + i][base];
-    float s = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
+    for (int m = 0; m + 1 < i; ++m) ps[m & 3] = fmaf(arow[m], x[m], ps[m & 3]);
+    float s = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (i > 0) s = fmaf(arow[i - 1], x[i - 1], s);
     x[i] = (i == col) ? 1.f : -s;
   }
 #pragma unroll
@@ -414,6 +418,7 @@ struct PrepKdaSmem {
   // block start), formed once per chunk (fp32 forms them in the products: its LDS has no room)
   alignas(16) float FR[is_bf16<E>() ? kChunk : 1][LDG];
   float part[kKdaThreads / DK][DK];   // prefix-scan partial totals
+  float EB[4][DK];                    // e^{G_b} at the four block starts b
   alignas(16) float Af[kChunk][LDF];  // A, then T in place
   alignas(16) E Ps[kChunk][LDP];
   alignas(16) float Tx[6][16][20];  // T's lower off-diagonal blocks (tx_block)
@@ -536,6 +541,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     for (int j = 0; j < part; ++j) off += sm.part[j][ch];
 #pragma unroll
     for (int j = 0; j < RUN; ++j) sm.Gm[part * RUN + j][ch] = run[j] + off;
+    if ((part * RUN) % 16 == 0) sm.EB[part * RUN / 16][ch] = exp2_fast(run[0] + off);
   }
 
   // ---- factors (wave 0): as for the scalar gate, with e^G = 1 and rs e^{G_C - G} = rs ----
@@ -579,13 +585,15 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
         const f32x4 G = *reinterpret_cast<const f32x4*>(&sm.Gm[r][c0 + e4]);
         const f32x4 GC = *reinterpret_cast<const f32x4*>(&sm.Gm[kChunk - 1][c0 + e4]);
         const f32x4 Gb = *reinterpret_cast<const f32x4*>(&sm.Gm[b][c0 + e4]);
+        const f32x4 eb = *reinterpret_cast<const f32x4*>(&sm.EB[b >> 4][c0 + e4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float eg = exp2_fast(G[e]), ed = exp2_fast(GC[e] - G[e]);
+          // e^G = e^{G - G_b} e^{G_b}, both factors <= 1
+          fr[e4 + e] = exp2_fast(G[e] - Gb[e]);
+          const float eg = fr[e4 + e] * eb[e], ed = exp2_fast(GC[e] - G[e]);
           a[e4 + e] = from_f32<E>(to_f32(kx[e4 + e]) * eg);
           bq[e4 + e] = from_f32<E>(to_f32(qx[e4 + e]) * eg);
           d[e4 + e] = from_f32<E>(to_f32(kx[e4 + e]) * ed);
-          fr[e4 + e] = exp2_fast(G[e] - Gb[e]);
         }
       }
       *reinterpret_cast<V16*>(k1 + r * DK + c0) = a;
@@ -616,14 +624,16 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   //      [1, e^kKdaSpan]; in bf16 both operands are split into high and low parts, so that these
   //      blocks, which dominate A and P, keep fp32-level accuracy). The other diagonal blocks are
   //      walked below. ----
-  auto block = [&](auto diag_c, int I, int J) __attribute__((always_inline)) {
+  // Block (I, J) over channel steps [i0, i1) (32 channels a step in bf16, 4 in fp32) into kk
+  // (K K^T) and qk (Q K^T), accumulated.
+  constexpr int NI = BF ? DK / 32 : DK / 4;
+  auto block = [&](auto diag_c, int I, int J, int i0, int i1, f32x4& kk, f32x4& qk) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(diag_c)::value;
     const int b = 16 * I;
     const int ra = 16 * I + lr, rb = 16 * J + lr;  // this lane's A row and B row
-    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
     if constexpr (BF) {
 #pragma unroll
-      for (int i = 0; i < DK / 32; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const int c = 32 * i + 8 * lq;
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sm.Ks[ra][c]);
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&sm.Qs[ra][c]);
@@ -660,7 +670,7 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
       }
     } else {
 #pragma unroll 4
-      for (int i = 0; i < DK / 4; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const int ch = 4 * i + lq;
         const float Gb = sm.Gm[b][ch];
         const float fa = exp2_fast(sm.Gm[ra][ch] - Gb), fb = exp2_fast(Gb - sm.Gm[rb][ch]);
@@ -669,6 +679,9 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
         qk = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.Qs[ra][ch] * fa, bk, qk, 0, 0, 0);
       }
     }
+  };
+  // A and P of block (I, J) from its products.
+  auto block_out = [&](int I, int J, const f32x4& kk, const f32x4& qk) __attribute__((always_inline)) {
     const int s = 16 * J + lr;
     const float rss = sm.sc[kScRs][s];
 #pragma unroll
@@ -678,19 +691,43 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
       sm.Ps[r][s] = from_f32<E>(s <= r ? qk[e] : 0.f);
     }
   };
-  // Waves 0..3 take diagonal block I = wave, waves 4..7 off-diagonal block t = wave - 4 and
-  // (t < 2) t + 4, so that each SIMD (waves w and w + 4) carries one diagonal block and one or
-  // two off-diagonal ones. Off-diagonal block t is (I, J) = (1,0), (2,0), (2,1), (3,0), (3,1), (3,2).
+  auto off_ij = [](int t, int& I, int& J) __attribute__((always_inline)) {
+    I = t >= 3 ? 3 : t >= 1 ? 2 : 1;
+    J = t - (I * (I - 1)) / 2;
+  };
+  // Waves 0..3 take diagonal block I = wave; waves 4..7 off-diagonal block t = wave - 4 and one
+  // half of the channels of block 4 + (t & 1) (waves 4, 5 the first, 6, 7 the second), so that
+  // each SIMD (waves w and w + 4) carries one diagonal block and one and a half off-diagonal
+  // ones. Off-diagonal block t is (I, J) = (1,0), (2,0), (2,1), (3,0), (3,1), (3,2). The second
+  // halves go through sm.Tx (free until T's blocks are formed) and are added by waves 4, 5 after
+  // the barrier below.
+  f32x4 hk = {0.f, 0.f, 0.f, 0.f}, hq = hk;
   if (wave < 4) {
-    if (sm.fast[wave]) block(std::true_type{}, wave, wave);
+    if (sm.fast[wave]) {
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+      block(std::true_type{}, wave, wave, 0, NI, kk, qk);
+      block_out(wave, wave, kk, qk);
+    }
   } else if (wave < 8) {
-    auto off = [&](int t) __attribute__((always_inline)) {
-      const int I = t >= 3 ? 3 : t >= 1 ? 2 : 1, J = t - (I * (I - 1)) / 2;
-      block(std::false_type{}, I, J);
-    };
     const int t = wave - 4;
-    off(t);
-    if (t < 2) off(t + 4);
+    int I, J;
+    off_ij(t, I, J);
+    {
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+      block(std::false_type{}, I, J, 0, NI, kk, qk);
+      block_out(I, J, kk, qk);
+    }
+    off_ij(4 + (t & 1), I, J);
+    const int h = t >> 1;
+    block(std::false_type{}, I, J, h * (NI / 2), (h + 1) * (NI / 2), hk, hq);
+    if (h == 1) {
+      float* part2 = &sm.Tx[0][0][0] + (t & 1) * 8 * kWave;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part2[e * kWave + lane] = hk[e];
+        part2[(4 + e) * kWave + lane] = hq[e];
+      }
+    }
   }
   // ---- diagonal 16 x 16 blocks ----
   if constexpr (BF) {
@@ -807,6 +844,18 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
     }
   }
   __syncthreads();
+  // the split blocks: second halves (from waves 6, 7) added to the first (waves 4, 5)
+  if (wave == 4 || wave == 5) {
+    const float* part2 = &sm.Tx[0][0][0] + (wave - 4) * 8 * kWave;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hk[e] += part2[e * kWave + lane];
+      hq[e] += part2[(4 + e) * kWave + lane];
+    }
+    int I, J;
+    off_ij(wave, I, J);
+    block_out(I, J, hk, hq);
+  }
 
   // ---- T = (I + A)^-1 in LDS: diagonal blocks (wave 0), then the blocks below them (waves
   //      0..2, as in solve_and_store). The other waves go on to the next chunk's rows, which

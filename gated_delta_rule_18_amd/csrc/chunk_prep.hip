@@ -152,9 +152,22 @@ __device__ __forceinline__ void t_diag(Sm& sm, int lane) {
   for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
 }
 
+// Cache policy of the streaming stores: SC1 | NT (system scope, non-temporal). Workspace blocks
+// that the scan reads only after the whole prep has written far more than the caches hold go
+// out this way.
+constexpr int kStreamPolicy = 16 | 2;
+
+// 16 bytes at byte offset off of the block at base (block_bytes long), with the streaming policy.
+template <typename V>
+__device__ __forceinline__ void store16_stream(void* base, uint32_t block_bytes, uint32_t off, const V& v) {
+  static_assert(sizeof(V) == 16, "16-byte vectors");
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), make_rsrc(base, block_bytes), off, 0,
+                                         kStreamPolicy);
+}
+
 // P (sm.Ps; upper off-diagonal blocks written as zero) and the factor rows (sm.sc) of chunk
-// chunk_id to the workspace, by threads t = 0 .. nt - 1.
-template <typename E, typename Sm>
+// chunk_id to the workspace, by threads t = 0 .. nt - 1 (P with streaming stores if STREAM).
+template <typename E, bool STREAM = false, typename Sm>
 __device__ __forceinline__ void store_p_sc(const Sm& sm, const Workspace<E>& ws, int64_t chunk_id, int t, int nt) {
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;
@@ -167,15 +180,18 @@ __device__ __forceinline__ void store_p_sc(const Sm& sm, const Workspace<E>& ws,
 #pragma unroll
       for (int e = 0; e < VN; ++e) out[e] = from_f32<E>(0.f);
     }
-    *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
+    if constexpr (STREAM)
+      store16_stream(gP, kChunk * kChunk * sizeof(E), (uint32_t)((r * kChunk + c0) * sizeof(E)), out);
+    else
+      *reinterpret_cast<V16*>(gP + r * kChunk + c0) = out;
   }
   float* gS = ws.SC + chunk_id * kScRows * kChunk;
   for (int i = t; i < kScRows * kChunk; i += nt) gS[i] = (&sm.sc[0][0])[i];
 }
 
 // T of chunk chunk_id to the workspace (diagonal blocks from sm.Af, lower off-diagonal ones
-// from sm.Tx, upper ones zero), by all NTH threads.
-template <typename E, int NTH, typename Sm>
+// from sm.Tx, upper ones zero), by all NTH threads (with streaming stores if STREAM).
+template <typename E, int NTH, bool STREAM = false, typename Sm>
 __device__ __forceinline__ void store_t(const Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;
@@ -193,7 +209,10 @@ __device__ __forceinline__ void store_t(const Sm& sm, const Workspace<E>& ws, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e4 + e] = from_f32<E>(zero ? 0.f : x[e]);
     }
-    *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
+    if constexpr (STREAM)
+      store16_stream(gT, kChunk * kChunk * sizeof(E), (uint32_t)((r * kChunk + c0) * sizeof(E)), out);
+    else
+      *reinterpret_cast<V16*>(gT + r * kChunk + c0) = out;
   }
 }
 
@@ -504,8 +523,8 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   // ---- the previous chunk's P, factor rows and T to the workspace: stored here, behind the
   //      loads just issued, so that waiting for those loads does not wait for these stores ----
   if (prev_id >= 0) {
-    store_p_sc<E>(sm, ws, prev_id, tid, NTH);
-    store_t<E, NTH>(sm, ws, prev_id);
+    store_p_sc<E, true>(sm, ws, prev_id, tid, NTH);
+    store_t<E, NTH, true>(sm, ws, prev_id);
   }
 
   // ---- per-channel prefix of log a over the chunk's tokens, in log2 units (every exponential
@@ -568,7 +587,8 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   }
   __syncthreads();
 
-  // ---- decayed scan operands and gamma to the workspace; (bf16) the row factors ----
+  // ---- decayed scan operands (streaming stores) and gamma to the workspace; (bf16) the row
+  //      factors ----
   {
     constexpr int CPR = DK / VN;
     E* k1 = kw.K1 + chunk_id * kChunk * DK;
@@ -596,9 +616,10 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
           d[e4 + e] = from_f32<E>(to_f32(kx[e4 + e]) * ed);
         }
       }
-      *reinterpret_cast<V16*>(k1 + r * DK + c0) = a;
-      *reinterpret_cast<V16*>(q1 + r * DK + c0) = bq;
-      *reinterpret_cast<V16*>(k2 + r * DK + c0) = d;
+      const uint32_t off = (uint32_t)((r * DK + c0) * sizeof(E)), blk = kChunk * DK * sizeof(E);
+      store16_stream(k1, blk, off, a);
+      store16_stream(q1, blk, off, bq);
+      store16_stream(k2, blk, off, d);
       if constexpr (BF) {
 #pragma unroll
         for (int e4 = 0; e4 < VN; e4 += 4)
@@ -869,8 +890,8 @@ __global__ __launch_bounds__(kKdaThreads) void chunk_prep_kda_kernel(ChunkParams
   }  // chunk loop
   __syncthreads();
   if (prev_id >= 0) {
-    store_p_sc<E>(sm, ws, prev_id, threadIdx.x, NTH);
-    store_t<E, NTH>(sm, ws, prev_id);
+    store_p_sc<E, true>(sm, ws, prev_id, threadIdx.x, NTH);
+    store_t<E, NTH, true>(sm, ws, prev_id);
   }
 }
 

@@ -15,9 +15,11 @@
 //
 // Work split. A workgroup of W waves owns DVS = 16 W NT columns of one head's state and walks
 // the chunks in order; each wave owns 16 NT of those columns for every d_k row and every token,
-// so the chain S -> X -> R -> D -> (O, S) of its columns never leaves the wave and needs no
-// barrier. The slice of S lives in fp32 MFMA accumulators for the whole sequence. The
-// workgroups of one head get ids congruent mod 8, so they run on one XCD and share its L2.
+// so the chain S -> X -> R -> D -> S of its columns never leaves the wave and needs no barrier.
+// The outputs O of its columns are formed by the wave itself, or, in the one-pass bf16 forward,
+// by an output wave of its own from the state fragments and D' handed over in LDS. The slice of
+// S lives in fp32 MFMA accumulators for the whole sequence. The workgroups of one head get ids
+// congruent mod 8, so they run on one XCD and share its L2.
 //
 // Chaining without data movement. The contraction index of every product is enumerated in
 // the order in which an MFMA accumulator holds its rows, so that the accumulators of one
@@ -41,9 +43,10 @@
 // read). All are row-major without padding, their 16-byte chunks XOR-swizzled by row so that
 // these reads are free of bank conflicts.
 // They arrive by direct-to-LDS buffer loads (no registers) into a ring of LDS buffers, one
-// workgroup barrier per chunk: for bf16 issued by producer waves of the workgroup (two chunks
-// ahead by four producers in the one-pass forward, a chunk ahead by two elsewhere), for fp32 a
-// chunk ahead by the scan waves themselves. Every global access goes through a buffer resource
+// workgroup barrier per chunk (two in the one-pass bf16 forward, the second handing D' to the
+// output waves): for bf16 issued by producer waves of the workgroup (two chunks ahead by four
+// producers in the one-pass forward, P there one chunk ahead in a ring of its own; a chunk ahead
+// by two elsewhere), for fp32 a chunk ahead by the scan waves themselves. Every global access goes through a buffer resource
 // (rows past T read as zeros, stores past T are dropped), so there are no per-lane branches
 // around memory operations.
 #include "tile_ops.h"
@@ -61,9 +64,27 @@ namespace {
 // about a step to issue and as long again to arrive, and each wave can have at most 63 memory
 // operations outstanding (two chunks of loads are 2 x 27 for two producers, 2 x 14 for four).
 // Elsewhere two producers load one chunk ahead.
+//
+// Output waves (the same one-pass forward): one more wave per scan wave, on the SIMDs the scan
+// waves leave idle, forms that scan wave's outputs, Y^T = S^T Q^T and O^T = e^G Y^T + D'^T P^T
+// (a third of its products), from the bf16 state fragments and D' the scan wave hands over in
+// LDS. The scan wave's chain then holds only X, R, D and the state update. The hand-over needs
+// a second barrier per chunk and room in LDS: P then has a two-slot ring of its own, loaded a
+// chunk ahead, instead of a slot in each of the three operand buffers; D' goes into the scan
+// wave's own V bytes of the chunk's buffer, dead once R is formed. (Measured: the B4 H16 T32768
+// prefill 1.19 -> 1.17 ms, B8 H8 T4096 192 -> 185 us from cold caches; outputs bit-identical.)
+template <typename E, int DK, int W, int NT>
+constexpr size_t deep_lds() {
+  return 3 * sizeof(ScanBuf<E, DK, W * 16 * NT, false, false>) + 2 * kChunk * kChunk * sizeof(E) +
+         (size_t)W * NT * (DK / 32) * kWave * 16;
+}
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr bool scan_deep() {
-  return is_bf16<E>() && MODE == kScanFwd && 3 * sizeof(ScanBuf<E, DK, W * 16 * NT, false>) <= 160 * 1024;
+  return is_bf16<E>() && MODE == kScanFwd && NT == 1 && deep_lds<E, DK, W, NT>() <= 160 * 1024;
+}
+template <typename E, int DK, int DV, int W, int NT, int MODE>
+constexpr int scan_outwaves() {
+  return scan_deep<E, DK, DV, W, NT, MODE>() ? W : 0;
 }
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_producers() {
@@ -82,7 +103,8 @@ constexpr int scan_producers() {
 // MODE kScanKdaRec: the backward's recompute with the per-channel decay.
 // (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
-__global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>()) * kWave) __attribute__((
+__global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>() + scan_outwaves<E, DK, DV, W, NT, MODE>()) *
+                             kWave) __attribute__((
     amdgpu_waves_per_eu(scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1, scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1))) void
 chunk_scan_kernel(ChunkParams p) {
   constexpr bool REC = scan_rec(MODE), SEG = scan_seg(MODE), KDA = scan_kda(MODE);
@@ -101,8 +123,8 @@ chunk_scan_kernel(ChunkParams p) {
   constexpr int NGD = DK / GK;       // groups over d_k
   constexpr int NGT = kChunk / GK;   // groups over the chunk's tokens
   constexpr int PER = 16 / sizeof(E);
-  typedef ScanBuf<E, DK, DVS, KDA> Buf;
   constexpr bool DEEP = scan_deep<E, DK, DV, W, NT, MODE>();
+  typedef ScanBuf<E, DK, DVS, KDA, !DEEP> Buf;  // (DEEP: P in a ring of its own)
   constexpr int NB = DEEP ? 3 : scan_ring<E, DK, DVS, KDA>();  // LDS buffers: chunks c .. c + NB - 1 in flight
   constexpr int DIST = NB > 1 ? NB - 1 : 1;     // prefetch distance
   static_assert(DV % DVS == 0, "shape");
@@ -111,6 +133,16 @@ chunk_scan_kernel(ChunkParams p) {
   __shared__ Buf buf0;
   __shared__ typename std::conditional<(NB >= 2), Buf, int>::type buf1;
   __shared__ typename std::conditional<(NB >= 3), Buf, int>::type buf2;
+  // DEEP: the two slots of P's ring, and the scan waves' state fragments for their output waves
+  // (wave w's fragment (s, ct) of lane l at v[((w NT + ct) NGD + s) 64 + l]).
+  struct PSlot {
+    alignas(16) E P[kChunk * kChunk];
+  };
+  struct HSlot {
+    alignas(16) GV v[W * NT * NGD * kWave];
+  };
+  __shared__ typename std::conditional<DEEP, PSlot, int>::type pr0, pr1;
+  __shared__ typename std::conditional<DEEP, HSlot, int>::type hs;
 
   // Workgroup -> (head, segment) and slice. The workgroups of one (head, segment) get ids
   // congruent mod 8, so they run on one XCD and share its L2.
@@ -135,7 +167,10 @@ chunk_scan_kernel(ChunkParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, g = lane >> 4;
   const int j0 = (mpart ? slice - NS : slice) * DVS;  // first state (or identity) column of this workgroup
-  const int cw = wave * NC;                          // first column of this wave within the slice
+  constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();  // producer waves W .. W + NP - 1
+  constexpr int NO = scan_outwaves<E, DK, DV, W, NT, MODE>();   // output waves W + NP .. W + NP + NO - 1
+  const bool outw = NO > 0 && wave >= W + NP;                   // output wave of scan wave wave - W - NP
+  const int cw = (outw ? wave - W - NP : wave) * NC;  // first column of this (or its scan) wave within the slice
 
   // ---- resources: this batch's rows of q/k/v/o, this head's workspace chunks ----
   const int64_t brow = bb * T * H;
@@ -175,7 +210,6 @@ chunk_scan_kernel(ChunkParams p) {
   // ---- DMA of one chunk's operands: 1 KiB LDS blocks dealt round-robin to the loading waves (the
   // producers, else the scan waves). Lane l of block b fills physical chunk 64 b + l; its source
   // is the logical chunk stored there. ----
-  constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
   constexpr int WD = NP ? NP : W;         // loading waves
   const int dw = NP ? wave - W : wave;    // this wave's index among them (producers only, if any)
   constexpr int CK = DK / PER, CT = kChunk / PER, CV = DVS / PER;  // 16-byte chunks per row
@@ -204,7 +238,7 @@ chunk_scan_kernel(ChunkParams p) {
   // Every loading wave issues the same NDMA loads per chunk (the factor block is loaded by all of
   // them, identical bytes), so that the wait counts below are compile-time constants. A chunk
   // past the end is clamped to the last one (loaded again, never read).
-  constexpr int NDMA = (1 + !REC + KDA) * NBK + (1 + !REC) * NBT + NBV + 1 + KDA;
+  constexpr int NDMA = (1 + !REC + KDA) * NBK + (1 + (!REC && !DEEP)) * NBT + NBV + 1 + KDA;
   constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < ce ? c : ce - 1;
@@ -220,7 +254,7 @@ chunk_scan_kernel(ChunkParams p) {
     for (int i = 0; i < NBT; ++i) {
       const int blk = dw + WD * i;
       dma16(rt, B.T + blk * 64 * PER, (uint32_t)c * kMatBytes + offt[i]);
-      if constexpr (!REC) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offp[i]);
+      if constexpr (!REC && !DEEP) dma16(rp, B.P + blk * 64 * PER, (uint32_t)c * kMatBytes + offp[i]);
     }
 #pragma unroll
     for (int i = 0; i < NBV; ++i) {
@@ -230,31 +264,118 @@ chunk_scan_kernel(ChunkParams p) {
     dma16(rsc, B.sc, (uint32_t)c * kScBytes + 16 * lane);
     if constexpr (KDA) dma16(rgam, B.gam, (uint32_t)c * DK * 4 + 16 * lane);
   };
+  // DEEP: chunk c's P into a slot of P's ring (NBT loads per producer).
+  auto fetch_p = [&](E* Pd, int64_t c) {
+    c = c < ce ? c : ce - 1;
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) {
+      const int blk = dw + WD * i;
+      dma16(rp, Pd + blk * 64 * PER, (uint32_t)c * kMatBytes + offp[i]);
+    }
+  };
+
+  // DEEP: element offset in V of hand-over piece idx (0 .. 64 NGT - 1) of scan wave wv's D': the
+  // 16-byte chunks of the wave's own columns (2 per row), dead in V once the wave has formed R.
+  auto dpos = [&](int wv, int idx) { return at<E, DVS, LT>(idx >> 1, 16 * wv + 8 * (idx & 1)); };
+  // Slot of the T and P fragments (row tile r, group s) read early: row tiles 0, 1 need group 0.
+  auto tp_slot = [](int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; };
 
   if constexpr (DEEP) {
-    static_assert(NB == 3 && NP == 4, "four producers serve a three-buffer ring");
-    if (wave >= W) {  // producer: the loads of every chunk, two chunks ahead, one barrier per chunk
-      // Before chunk c's barrier, chunk c's loads are complete and those of chunk c + 1 are
-      // younger (the same count for every chunk: a fetch past the end loads the last chunk again).
-      // This wave writes LDS only by these loads, and the wait is all the barrier needs of them:
-      // a workgroup fence there would make the compiler wait for chunk c + 1's loads as well.
-      auto pstep = [&](Buf& Bt, int64_t c) __attribute__((always_inline)) {
+    static_assert(NB == 3 && NP == 4 && NO == W, "four producers serve a three-buffer ring and P's ring");
+    if (wave >= W && !outw) {  // producer: the loads of every chunk, two chunks ahead (P one)
+      // Issue order: after chunk c's first barrier, chunk c + 1's P, then the rest of chunk
+      // c + 2. Before chunk c's first barrier, chunk c's loads and its P are complete and younger
+      // are only the rest of chunk c + 1 (the same count for every chunk: a fetch past the end
+      // loads the last chunk again). This wave writes LDS only by these loads, and the wait is all
+      // the barrier needs of them: a workgroup fence there would make the compiler wait for chunk
+      // c + 1's loads as well.
+      auto pstep = [&](Buf& Bt, E* Pn, int64_t c) __attribute__((always_inline)) {
         wait_vmem<NDMA>();
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1 (Bt)
+        __builtin_amdgcn_s_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1 (Bt, Pn)
         asm volatile("" ::: "memory");
+        fetch_p(Pn, c + 1);
         fetch(Bt, c + 2);
+        __builtin_amdgcn_s_barrier();  // chunk c's second barrier (D' handed to the output waves)
       };
       if (ce > cb) {
+        fetch_p(pr0.P, cb);
         fetch(buf0, cb);
         fetch(buf1, cb + 1);
       }
-      for (int64_t c = cb; c < ce; c += 3) {
-        pstep(buf2, c);
-        if (c + 1 < ce) pstep(buf0, c + 1);
-        if (c + 2 < ce) pstep(buf1, c + 2);
+      int k = 0;
+      for (int64_t c = cb; c < ce; ++c) {
+        Buf& Bt = k == 0 ? buf2 : k == 1 ? buf0 : buf1;  // held chunk c - 1, receives chunk c + 2
+        pstep(Bt, ((c + 1 - cb) & 1) ? pr1.P : pr0.P, c);
+        k = k == 2 ? 0 : k + 1;
       }
       wait_vmem<0>();  // no load into LDS outlives the workgroup
+      return;
+    }
+    if (outw) {  // output wave of scan wave ow: two barriers per chunk, as every wave
+      const int ow = wave - W - NP;
+      // Its LDS reads are complete before each barrier (the scan wave overwrites what it read
+      // after the next one); no workgroup fence, which would also wait for its output stores.
+      auto obarrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      };
+      int k = 0;
+      for (int64_t c = cb; c < ce; ++c) {
+        const Buf& B = k == 0 ? buf0 : k == 1 ? buf1 : buf2;
+        const E* Pc = ((c - cb) & 1) ? pr1.P : pr0.P;
+        obarrier();  // chunk c's operands, its P and the scan wave's state fragments are in LDS
+        GV so[NGD];
+#pragma unroll
+        for (int s = 0; s < NGD; ++s) so[s] = hs.v[(ow * NGD + s) * kWave + lane];
+        // Y^T = S^T Q^T over the four token tiles, the Q fragments of tile r + 1 read during the
+        // products of tile r; P's fragments and e^G with the last tile.
+        GV fq[2][NGD], fp[6];
+        float eGt[4];
+        f32x4 Y[4];
+        auto load_q = [&](int r, int slot) __attribute__((always_inline)) {
+#pragma unroll
+          for (int s = 0; s < NGD; ++s) fq[slot][s] = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+        };
+        load_q(0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (r + 1 < 4) {
+            load_q(r + 1, (r + 1) & 1);
+          } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              eGt[rr] = B.sc[kScEG * kChunk + 16 * rr + c16];
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2)
+                if (GK * s2 < 16 * (rr + 1)) fp[tp_slot(rr, s2)] = row8_grp<kChunk, kLayLin>(Pc, 16 * rr + c16, s2, g);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          Y[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < NGD; ++s) Y[r] = mma<E>(so[s], fq[r & 1][s], Y[r]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        obarrier();  // chunk c's D' is in the scan wave's V bytes
+        GV d1[NGT];
+#pragma unroll
+        for (int s = 0; s < NGT; ++s) d1[s] = *reinterpret_cast<const GV*>(B.V + dpos(ow, s * kWave + lane));
+        // O^T = e^G Y^T + D'^T P^T, each lane four consecutive columns of one token row
+        const uint32_t t0 = (uint32_t)(c * kChunk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f32x4 o = eGt[r] * Y[r];
+#pragma unroll
+          for (int s = 0; s < NGT; ++s)
+            if (GK * s < 16 * (r + 1)) o = mma<E>(d1[s], fp[tp_slot(r, s)], o);
+          store4_rsrc<E>(rout, (t0 + 16 * r + c16) * orow + ocol + 4 * g * sizeof(E), o);
+        }
+        k = k == 2 ? 0 : k + 1;
+      }
+      wait_vmem<0>();
       return;
     }
   } else if constexpr (NP > 0) {
@@ -303,6 +424,24 @@ chunk_scan_kernel(ChunkParams p) {
       for (int ct = 0; ct < NT; ++ct) S[r][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
+  // The state's bf16 fragments (operand of X; DEEP: formed at the end of the previous chunk's
+  // step and handed to the output wave through hs).
+  GV sb[NGD][NT];
+  auto state_frags = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 tiles[RTK];
+#pragma unroll
+      for (int r = 0; r < RTK; ++r) tiles[r] = S[r][ct];
+#pragma unroll
+      for (int s = 0; s < NGD; ++s) {
+        if constexpr (PERM)
+          sb[s][ct] = state_grp(tiles, s, g);
+        else
+          sb[s][ct] = acc_grp<E>(tiles, s);
+      }
+    }
+  };
   // One chunk: B holds its operands; chunk c + DIST is loaded into Bn meanwhile (Bn held chunk
   // c - 1). Issue order per wave: the loads of chunks 0 .. DIST - 1, then per chunk k the loads
   // of chunk k + DIST and the k's output stores. Before chunk c's barrier the loads of chunk c
@@ -330,21 +469,8 @@ chunk_scan_kernel(ChunkParams p) {
           store4_rsrc<E>(rsn, (uint32_t)c * kSBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), S[r][ct]);
     }
 
-    // ---- X = K S (token rows x this wave's columns) and Y^T = S^T Q^T ----
-    GV sb[NGD][NT];
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      f32x4 tiles[RTK];
-#pragma unroll
-      for (int r = 0; r < RTK; ++r) tiles[r] = S[r][ct];
-#pragma unroll
-      for (int s = 0; s < NGD; ++s) {
-        if constexpr (PERM)
-          sb[s][ct] = state_grp(tiles, s, g);
-        else
-          sb[s][ct] = acc_grp<E>(tiles, s);
-      }
-    }
+    // ---- X = K S (token rows x this wave's columns) and Y^T = S^T Q^T (DEEP: the output wave's) ----
+    if constexpr (!DEEP) state_frags();
     f32x4 X[4][NT], Y[NT][4];
     // One-pass bf16 forward, scalar gate or per-channel decay (EARLY): the operands of the later
     // products are read early: T and P fragments (the groups below the diagonal), the V columns
@@ -355,7 +481,6 @@ chunk_scan_kernel(ChunkParams p) {
     constexpr int NTF = EARLY ? 6 : 1;  // T / P fragments: row tiles 0, 1 need group 0; 2, 3 groups 0, 1
     GV ft[NTF], fp[NTF];
     f32x4 fv[4][NT], fcoef[4], feg[4];
-    auto tp_slot = [](int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; };
     if constexpr (EARLY) {
       // X = K S and Y^T = S^T Q^T as a two-stage pipeline over the four token tiles: the eight
       // fragment reads of tile r + 1 are issued before the eight products of tile r, so that each
@@ -366,7 +491,7 @@ chunk_scan_kernel(ChunkParams p) {
 #pragma unroll
         for (int s = 0; s < NGD; ++s) {
           fk[slot][s] = row8_grp<DK, kLayTok>(B.K, tok_row(r, c16), s, g);
-          if constexpr (!REC) fq[slot][s] = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
+          if constexpr (!REC && !DEEP) fq[slot][s] = row8_grp<DK, kLayLin>(B.Q, 16 * r + c16, s, g);
         }
       };
       load_xy(0, 0);
@@ -390,7 +515,7 @@ chunk_scan_kernel(ChunkParams p) {
             for (int s2 = 0; s2 < 2; ++s2)
               if (GK * s2 < 16 * (rr + 1)) {
                 ft[tp_slot(rr, s2)] = row8_grp<kChunk, kLayTok>(B.T, tok_row(rr, c16), s2, g);
-                if constexpr (!REC) fp[tp_slot(rr, s2)] = row8_grp<kChunk, kLayLin>(B.P, 16 * rr + c16, s2, g);
+                if constexpr (!REC && !DEEP) fp[tp_slot(rr, s2)] = row8_grp<kChunk, kLayLin>(B.P, 16 * rr + c16, s2, g);
               }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -400,7 +525,7 @@ chunk_scan_kernel(ChunkParams p) {
         for (int s = 0; s < NGD; ++s) {
 #pragma unroll
           for (int ct = 0; ct < NT; ++ct) X[r][ct] = mma<E>(fk[r & 1][s], sb[s][ct], X[r][ct]);
-          if constexpr (!REC) {
+          if constexpr (!REC && !DEEP) {
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) Y[ct][r] = mma<E>(sb[s][ct], fq[r & 1][s], Y[ct][r]);
           }
@@ -505,8 +630,15 @@ chunk_scan_kernel(ChunkParams p) {
         for (int ct = 0; ct < NT; ++ct)
           store4_rsrc<E>(rdl, (uint32_t)c * kDBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), D1[ct][r]);
     }
+    if constexpr (DEEP) {
+      // D' to this wave's own V bytes of the chunk's buffer, then the chunk's second barrier: the
+      // output wave forms O from it.
 #pragma unroll
-    for (int r = 0; r < 4 && !REC; ++r) {
+      for (int s = 0; s < NGT; ++s) *reinterpret_cast<GV*>(B.V + dpos(wave, s * kWave + lane)) = b1[0][s];
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4 && !REC && !DEEP; ++r) {
       const float eGt = B.sc[kScEG * kChunk + 16 * r + c16];
       f32x4 o[NT];
 #pragma unroll
@@ -554,6 +686,11 @@ chunk_scan_kernel(ChunkParams p) {
         for (int ct = 0; ct < NT; ++ct) S[r][ct] = mma<E>(ak, b2[ct][s], S[r][ct]);
       }
     }
+    if constexpr (DEEP) {  // the next chunk's state fragments, also to the output wave
+      state_frags();
+#pragma unroll
+      for (int s = 0; s < NGD; ++s) hs.v[(wave * NGD + s) * kWave + lane] = sb[s][0];
+    }
     if constexpr (NB == 1) {
       __syncthreads();
       if (c + 1 < ce) fetch(B, c + 1);
@@ -562,6 +699,11 @@ chunk_scan_kernel(ChunkParams p) {
 
   if (NP == 0 && ce > cb) fetch(buf0, cb);  // chunk cb (one chunk ahead)
   if constexpr (NB == 3) {
+    if constexpr (DEEP) {  // the first chunk's state fragments, for X and the output wave
+      state_frags();
+#pragma unroll
+      for (int s = 0; s < NGD; ++s) hs.v[(wave * NGD + s) * kWave + lane] = sb[s][0];
+    }
     // One copy of the step, its buffer chosen per chunk: unrolled three ways (a copy per buffer)
     // the forward measured 20-25 % slower.
     int k = 0;
@@ -609,8 +751,9 @@ hipError_t launch_wnt(const ChunkParams& p, hipStream_t stream) {
   const int64_t units = p.heads * (SEG ? p.nseg : 1);  // (head, segment) pairs
   const int64_t units8 = (units + p.xcds - 1) / p.xcds * p.xcds;
   constexpr int NP = scan_producers<E, DK, DV, W, NT, MODE>();
-  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)), dim3((W + NP) * kWave), 0,
-                     stream, p);
+  constexpr int NO = scan_outwaves<E, DK, DV, W, NT, MODE>();
+  hipLaunchKernelGGL((chunk_scan_kernel<E, DK, DV, W, NT, MODE>), dim3((unsigned)(units8 * NSA)),
+                     dim3((W + NP + NO) * kWave), 0, stream, p);
   return hipGetLastError();
 }
 

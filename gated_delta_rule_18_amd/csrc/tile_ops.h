@@ -271,12 +271,13 @@ __device__ __forceinline__ f32x4 row4(const E* M, int r, int col) {
 // One chunk's operands in LDS (16-byte chunks of every row XOR-swizzled; see swz). With the
 // per-channel decay (KDA) the buffer also holds the state-update operand K2 and the chunk's
 // state decay gamma (a 1 KiB block, of which the first DK entries are this chunk's).
-template <typename E, int DK, int DVS, bool KDA = false>
+// HASP = false: P has a ring of its own (the one-pass bf16 forward with output waves).
+template <typename E, int DK, int DVS, bool KDA = false, bool HASP = true>
 struct ScanBuf {
   alignas(16) E K[kChunk * DK];
   alignas(16) E Q[kChunk * DK];
   alignas(16) E T[kChunk * kChunk];
-  alignas(16) E P[kChunk * kChunk];
+  alignas(16) E P[HASP ? kChunk * kChunk : 8];
   alignas(16) E V[kChunk * DVS];
   alignas(16) float sc[kScRows * kChunk];
   alignas(16) E K2[KDA ? kChunk * DK : 8];

@@ -9,7 +9,8 @@ beta/decay prologue, the chunk products, the triangular solve, the state scan, t
 output and the decode step. Other workloads (--workload) time one part alone.
 --pass bwd times the chunkwise backward (kla_chunk_bwd: the gradients of a loss on the
 prefill outputs with respect to every input) on a prefill workload instead, as its own
-JSON line.
+JSON line; --pass train times a training step, the training forward (kla_chunk_fwd_train)
+and the backward from its workspace (kla_chunk_bwd_saved).
 
 Inputs are generated (seeded) and copied to HBM before the timed region. Kernels
 are launched through the C ABI with pre-marshalled pointers on torch's current
@@ -44,6 +45,7 @@ import workloads as wl  # noqa: E402
 
 METRIC = "chunked-fwd tokens/s + decode tokens/s at 1 GPU; % MFMA / HBM roofline"
 METRIC_BWD = "chunked-bwd tokens/s at 1 GPU; % MFMA / HBM roofline"
+METRIC_TRAIN = "chunked training step (fwd + bwd) tokens/s at 1 GPU; % MFMA / HBM roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
@@ -68,6 +70,14 @@ def bwd_flops_per_head_token(dk, dv, C=64):
     Q^T dO, K^T Zb) and the gradient kernel (K K^T, Q K^T, Zb Delta^T, dO Delta^T, four
     C x C x d_k products, three C x d_k x d_v products)."""
     return C * (16 * dk + 10 * dv) + 16 * dk * dv
+
+
+def train_flops_per_head_token(dk, dv, C=64):
+    """A training step: the forward's products and the backward's, less the backward's recompute
+    of the forward (K K^T and Q K^T of the per-chunk factors, K S, T R and K^T Delta of the
+    scan), which the training forward's saved workspace makes unnecessary."""
+    return chunk_flops_per_head_token(dk, dv, C) + bwd_flops_per_head_token(dk, dv, C) - (4 * C * dk + 2 * C * dv +
+                                                                                          4 * dk * dv)
 
 
 def bwd_bytes(w, es, kda=False):
@@ -267,7 +277,8 @@ def _oracle_bwd_leg(w, heads, n, kda=False):
 
 
 def run_bwd(args, w):
-    """--pass bwd: time kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd) over the workload's prefill."""
+    """--pass bwd: time kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd) over the workload's prefill.
+    --pass train: time kla_chunk_fwd_train and kla_chunk_bwd_saved (their gdn forms) per step."""
     import torch
     from gated_delta_rule_18_amd import _lib as K
     device = torch.device("cuda:0")
@@ -277,6 +288,7 @@ def run_bwd(args, w):
     L = K.lib()
     gdn = args.mode in ("gdn", "deltanet")
     kda = args.mode == "kda"
+    train = args.pass_ == "train"
     log(f"[bench] generating {w.name} ({w.note}) and its output cotangent ...")
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
     x = wl.prefill_inputs(w, GEN_WORKERS)
@@ -300,7 +312,17 @@ def run_bwd(args, w):
     dla = None if args.mode == "deltanet" else P(out["dla"])
     head = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), la, None, P(t["do"]), None, P(out["dq"]), P(out["dk"]),
             P(out["dv"]), P(out["deta"]), dla, None, w.B, w.T, w.H, w.dk, w.dv, 64)
-    if gdn:
+    if train:
+        o = torch.empty_like(t["v"])
+        fhead = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), la, None, None, P(o), w.B, w.T, w.H, w.dk, w.dv, 64)
+        if gdn:
+            call = lambda: (L.kla_gdn_chunk_fwd_train(*fhead, code, P(workspace), ws_bytes, sp) or
+                            L.kla_gdn_chunk_bwd_saved(*head, code, P(workspace), ws_bytes, sp))
+        else:
+            eps = ctypes.c_float(w.eps)
+            call = lambda: (L.kla_chunk_fwd_train(*fhead, eps, code, P(workspace), ws_bytes, sp) or
+                            L.kla_chunk_bwd_saved(*head, eps, code, P(workspace), ws_bytes, sp))
+    elif gdn:
         call = lambda: L.kla_gdn_chunk_bwd(*head, code, P(workspace), ws_bytes, sp)
     elif kda:
         call = lambda: L.kla_kda_chunk_bwd(*head, ctypes.c_float(w.eps), 0, code, P(workspace), ws_bytes, sp)
@@ -326,32 +348,35 @@ def run_bwd(args, w):
     log(f"[bench] timed region {elapsed * 1e3:.2f} ms")
     ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     tokens = w.B * w.T
-    flops = bwd_flops_per_head_token(w.dk, w.dv) * w.heads * w.T
-    nbytes = bwd_bytes(w, es, kda)
+    flops = (train_flops_per_head_token if train else bwd_flops_per_head_token)(w.dk, w.dv) * w.heads * w.T
+    nbytes = bwd_bytes(w, es, kda) + (chunk_bytes(w, es) if train else 0)
     peak_mfma = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
-    part = {"kernel": ("chunk_prep_kda_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + "
-                       "chunk_grad_kda_kernel") if kda else
-                      "chunk_prep_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + chunk_grad_kernel",
+    part = {"kernel": ("chunk_prep_kernel + chunk_scan_kernel (saving) + chunk_rscan_kernel + chunk_grad_kernel"
+                       if train else
+                       "chunk_prep_kda_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + "
+                       "chunk_grad_kda_kernel" if kda else
+                       "chunk_prep_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + chunk_grad_kernel"),
             "launches_per_step": 1, "ms_per_step": ms, "kernel_avg_us": ms * 1e3, "tokens": tokens,
             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key("chunk_bwd", args.mode))}
     part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key("chunk_bwd", args.mode))
-                                            if args.mode in ("kla", "kda") else None)
+                                            if args.mode in ("kla", "kda") and not train else None)
     roof = {"bound": "mfma", "kernel": part["kernel"], "achieved": part["mfma_tflops"], "peak": peak_mfma,
             "unit": "TFLOP/s", "frac": part["mfma_frac"], "traffic": part["hbm_traffic_bytes_per_launch"],
             "hbm_view": {"achieved": part["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": part["hbm_frac"]}}
     result = {
-        "metric": METRIC_BWD, "value": tokens * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_TRAIN if train else METRIC_BWD, "value": tokens * args.steps / elapsed, "unit": "tokens/s",
+        "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; distributions of the workload description; do ~ N(0, 1))",
-        "config": {"workload": w.name, "pass": "bwd", "mode": args.mode, "B": w.B, "H": w.H, "T": w.T,
+        "config": {"workload": w.name, "pass": args.pass_, "mode": args.mode, "B": w.B, "H": w.H, "T": w.T,
                    "d_k": w.dk, "d_v": w.dv, "chunk": 64, "parallelism": "single GPU"},
-        "parts": {"chunk_bwd": part}, "roofline": roof}
-    if not args.no_cpu_baseline and not gdn:
+        "parts": {"chunk_train" if train else "chunk_bwd": part}, "roofline": roof}
+    if not args.no_cpu_baseline and not gdn and not train:
         log("[bench] cpu baseline: gradient oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline_bwd(w, args.cpu_bwd_head_tokens, kda)
     print(json.dumps(result), flush=True)
@@ -532,8 +557,9 @@ def main():
                     help="decode steps replayed from a HIP graph (default) or launched one call at a time")
     ap.add_argument("--cpu-head-tokens", type=int, default=1048576,
                     help="size of the oracle's bounded sample, in head-tokens")
-    ap.add_argument("--pass", dest="pass_", default="fwd", choices=("fwd", "bwd"),
-                    help="fwd: the hot path (default); bwd: the chunkwise backward over a prefill workload")
+    ap.add_argument("--pass", dest="pass_", default="fwd", choices=("fwd", "bwd", "train"),
+                    help="fwd: the hot path (default); bwd: the chunkwise backward over a prefill workload; "
+                         "train: a training step (training forward and the backward from its workspace)")
     ap.add_argument("--cpu-bwd-head-tokens", type=int, default=65536,
                     help="size of the gradient oracle's bounded sample, in head-tokens")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -568,10 +594,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
         return
 
-    if args.pass_ == "bwd":
+    if args.pass_ in ("bwd", "train"):
         w = wl.WORKLOADS["fwd_b8h8_t4096" if args.workload == "mixed_b4h16" else args.workload]
         if not w.T:
-            print("--pass bwd needs a prefill workload", file=sys.stderr)
+            print(f"--pass {args.pass_} needs a prefill workload", file=sys.stderr)
+            sys.exit(2)
+        if args.pass_ == "train" and args.mode == "kda":
+            print("--pass train has no per-channel decay form (kla_kda_chunk_bwd recomputes the forward)",
+                  file=sys.stderr)
             sys.exit(2)
         return run_bwd(args, w.with_(steps=0))
 

@@ -36,6 +36,11 @@ _SIGNATURES = {
     "kla_chunk_bwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_gdn_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_chunk_fwd_train": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_gdn_chunk_fwd_train": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
+    "kla_chunk_bwd_saved": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _c_void_p, ctypes.c_size_t,
+                                                                    _c_void_p]),
+    "kla_gdn_chunk_bwd_saved": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_int, _c_void_p, ctypes.c_size_t, _c_void_p]),
     "kla_kda_chunk_fwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_kda_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
                                                                _c_void_p]),
@@ -372,6 +377,57 @@ def kla_gdn_chunk_bwd(q, k, v, beta, log_alpha, do, state_in=None, dstate_out=No
     """kla_chunk_bwd for the gated DeltaNet form (beta given, log_alpha None for alpha = 1).
     Returns dq, dk, dv, dbeta, dlog_alpha (None when log_alpha is) and dstate_in."""
     return _bwd("kla_gdn_chunk_bwd", "beta", q, k, v, beta, log_alpha, True, do, state_in, dstate_out, None,
+                want_dstate_in, chunk, workspace, stream, out)
+
+
+def _fwd_train(fn_name, gate_name, q, k, v, gate, log_alpha, log_alpha_optional, eps, state_in, return_state, o,
+               state_out, chunk, workspace, stream):
+    torch = _torch()
+    B, T, H, dk, dv, dev, o, state_out = _fwd_tensors(q, k, v, gate_name, gate, log_alpha, log_alpha_optional,
+                                                      state_in, return_state, o, state_out)
+    code = _dtype_code(q)
+    need = kla_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(log_alpha), _ptr(state_in), _ptr(state_out), _ptr(o),
+            B, T, H, dk, dv, chunk]
+    args += [float(eps)] if eps is not None else []
+    args += [code, _ptr(workspace), ws_bytes, _stream(dev, stream)]
+    check(getattr(lib(), fn_name)(*args))
+    return o, state_out, workspace
+
+
+def kla_chunk_fwd_train(q, k, v, eta, log_alpha, eps=1e-6, state_in=None, return_state=True, o=None, state_out=None,
+                        chunk=CHUNK, workspace=None, stream=None):
+    """kla_chunk_fwd for training: also fills the backward's workspace (kla_chunk_bwd_workspace_size
+    bytes; allocated when None) for kla_chunk_bwd_saved. Returns (o, final state or None, workspace)."""
+    return _fwd_train("kla_chunk_fwd_train", "eta", q, k, v, eta, log_alpha, False, eps, state_in, return_state, o,
+                      state_out, chunk, workspace, stream)
+
+
+def kla_gdn_chunk_fwd_train(q, k, v, beta, log_alpha=None, state_in=None, return_state=True, o=None,
+                            state_out=None, chunk=CHUNK, workspace=None, stream=None):
+    """kla_gdn_chunk_fwd for training (as kla_chunk_fwd_train). Returns (o, final state or None, workspace)."""
+    return _fwd_train("kla_gdn_chunk_fwd_train", "beta", q, k, v, beta, log_alpha, True, None, state_in,
+                      return_state, o, state_out, chunk, workspace, stream)
+
+
+def kla_chunk_bwd_saved(q, k, v, eta, log_alpha, do, workspace, eps=1e-6, state_in=None, dstate_out=None,
+                        want_dstate_in=True, chunk=CHUNK, stream=None, out=None):
+    """kla_chunk_bwd from the workspace kla_chunk_fwd_train filled for the same inputs (no recompute)."""
+    if workspace is None and q.shape[1] > 0:
+        raise ValueError("kla_chunk_bwd_saved needs the workspace kla_chunk_fwd_train filled")
+    return _bwd("kla_chunk_bwd_saved", "eta", q, k, v, eta, log_alpha, False, do, state_in, dstate_out, eps,
+                want_dstate_in, chunk, workspace, stream, out)
+
+
+def kla_gdn_chunk_bwd_saved(q, k, v, beta, log_alpha, do, workspace, state_in=None, dstate_out=None,
+                            want_dstate_in=True, chunk=CHUNK, stream=None, out=None):
+    """kla_gdn_chunk_bwd from the workspace kla_gdn_chunk_fwd_train filled for the same inputs."""
+    if workspace is None and q.shape[1] > 0:
+        raise ValueError("kla_gdn_chunk_bwd_saved needs the workspace kla_gdn_chunk_fwd_train filled")
+    return _bwd("kla_gdn_chunk_bwd_saved", "beta", q, k, v, beta, log_alpha, True, do, state_in, dstate_out, None,
                 want_dstate_in, chunk, workspace, stream, out)
 
 

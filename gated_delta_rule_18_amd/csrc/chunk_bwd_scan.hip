@@ -455,7 +455,7 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream) {
   bp.xcds = device_info().xcds;
   bp.bwd_off = a.kda ? (a.bf16 ? KdaSpace<bf16>::bytes(n, (int)a.d_k) : KdaSpace<float>::bytes(n, (int)a.d_k))
                      : (a.bf16 ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n));
-  if (nchunks > 0) {
+  if (nchunks > 0 && !a.saved) {  // (saved: the training forward left all of this in the workspace)
     ChunkParams fp{a.q,   a.k,       a.v, a.eta,    a.log_alpha, a.state_in, nullptr, nullptr, a.workspace,
                    a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given, a.beta_given};
     fp.xcds = bp.xcds;

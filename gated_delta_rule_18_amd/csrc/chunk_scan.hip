@@ -80,7 +80,7 @@ constexpr size_t deep_lds() {
 }
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr bool scan_deep() {
-  return is_bf16<E>() && MODE == kScanFwd && NT == 1 && deep_lds<E, DK, W, NT>() <= 160 * 1024;
+  return is_bf16<E>() && (MODE == kScanFwd || MODE == kScanFwdSave) && NT == 1 && deep_lds<E, DK, W, NT>() <= 160 * 1024;
 }
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 constexpr int scan_outwaves() {
@@ -101,13 +101,15 @@ constexpr int scan_producers() {
 // KDA workspace, the factor rows carry no decay, and the state decays per row by gamma.
 // MODE kScanKdaSeg: the segment pass with the per-channel decay (both of the above).
 // MODE kScanKdaRec: the backward's recompute with the per-channel decay.
+// MODE kScanFwdSave: kScanFwd, and, as kScanRec, every chunk's entering state and Delta are
+// stored (in kScanRec's tile order, which the backward reads) for a backward without recompute.
 // (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>() + scan_outwaves<E, DK, DV, W, NT, MODE>()) *
                              kWave) __attribute__((
     amdgpu_waves_per_eu(scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1, scan_deep<E, DK, DV, W, NT, MODE>() ? 2 : 1))) void
 chunk_scan_kernel(ChunkParams p) {
-  constexpr bool REC = scan_rec(MODE), SEG = scan_seg(MODE), KDA = scan_kda(MODE);
+  constexpr bool REC = scan_rec(MODE), SEG = scan_seg(MODE), KDA = scan_kda(MODE), SAVE = scan_save(MODE);
   constexpr bool BF = is_bf16<E>();
   // bf16 outside the backward recompute uses the whole-chunk operand layout (tile_ops.h): every
   // fragment along a row is one 16-byte LDS read. The recompute keeps the row-split layout, in
@@ -196,8 +198,8 @@ chunk_scan_kernel(ChunkParams p) {
   // Backward recompute: this head's state and Delta blocks, tile-ordered (chunk_common.h).
   constexpr uint32_t kSBytes = DK * DV * sizeof(E), kDBytes = kChunk * DV * sizeof(E);
   const BwdSpace<E> bw = BwdSpace<E>::at(p.ws, p.bwd_off, p.heads * nchunks, DK, DV);
-  const rsrc_t rsn = make_rsrc(bw.Sn + chunk0 * DK * DV, REC ? (uint32_t)(nchunks * kSBytes) : 0u);
-  const rsrc_t rdl = make_rsrc(bw.Dl + chunk0 * kChunk * DV, REC ? (uint32_t)(nchunks * kDBytes) : 0u);
+  const rsrc_t rsn = make_rsrc(bw.Sn + chunk0 * DK * DV, REC || SAVE ? (uint32_t)(nchunks * kSBytes) : 0u);
+  const rsrc_t rdl = make_rsrc(bw.Dl + chunk0 * kChunk * DV, REC || SAVE ? (uint32_t)(nchunks * kDBytes) : 0u);
   const int ct0 = (j0 + cw) / 16;  // first global 16-column tile of this wave
   // Output rows: o (the state columns; after the first segment of a segment scan these are
   // outputs from a zero entering state, corrected in place later), or, for identity columns, Y
@@ -239,7 +241,7 @@ chunk_scan_kernel(ChunkParams p) {
   // them, identical bytes), so that the wait counts below are compile-time constants. A chunk
   // past the end is clamped to the last one (loaded again, never read).
   constexpr int NDMA = (1 + !REC + KDA) * NBK + (1 + (!REC && !DEEP)) * NBT + NBV + 1 + KDA;
-  constexpr int NST = REC ? (RTK + 4) * NT : 4 * NT;  // stores per chunk and wave
+  constexpr int NST = REC ? (RTK + 4) * NT : SAVE ? (RTK + 8) * NT : 4 * NT;  // stores per chunk and wave
   auto fetch = [&](Buf& B, int64_t c) {
     c = c < ce ? c : ce - 1;
     const uint32_t t0 = (uint32_t)(c * kChunk);
@@ -279,6 +281,25 @@ chunk_scan_kernel(ChunkParams p) {
   auto dpos = [&](int wv, int idx) { return at<E, DVS, LT>(idx >> 1, 16 * wv + 8 * (idx & 1)); };
   // Slot of the T and P fragments (row tile r, group s) read early: row tiles 0, 1 need group 0.
   auto tp_slot = [](int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; };
+  // A barrier without a workgroup fence, for waves with stores of their own in flight (the fence
+  // would wait for them; the output waves): this wave's LDS accesses are complete before it.
+  auto raw_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Tile-ordered offsets (elements, kScanRec's order: tile r lane (g, c) holds rows 16 r + 4 g
+  // + 0..3 of column c) of the four state rows / four tokens this lane holds in its state tile
+  // rt / token tile r of column tile ct.
+  auto save_off_s = [&](int rt, int ct) {
+    const int r0 = PERM ? k_row(rt, g, 0) : 16 * rt + 4 * g;
+    return tile_off(r0 >> 4, ct0 + ct, DV / 16, ((r0 & 15) >> 2) * 16 + c16);
+  };
+  auto save_off_t = [&](int r, int ct) {
+    const int t = PERM ? tok_row(r, 4 * g) : 16 * r + 4 * g;
+    return tile_off(t >> 4, ct0 + ct, DV / 16, ((t & 15) >> 2) * 16 + c16);
+  };
 
   if constexpr (DEEP) {
     static_assert(NB == 3 && NP == 4 && NO == W, "four producers serve a three-buffer ring and P's ring");
@@ -316,12 +337,7 @@ chunk_scan_kernel(ChunkParams p) {
       const int ow = wave - W - NP;
       // Its LDS reads are complete before each barrier (the scan wave overwrites what it read
       // after the next one); no workgroup fence, which would also wait for its output stores.
-      auto obarrier = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-      };
+      auto obarrier = raw_barrier;
       int k = 0;
       for (int64_t c = cb; c < ce; ++c) {
         const Buf& B = k == 0 ? buf0 : k == 1 ? buf1 : buf2;
@@ -363,6 +379,29 @@ chunk_scan_kernel(ChunkParams p) {
         GV d1[NGT];
 #pragma unroll
         for (int s = 0; s < NGT; ++s) d1[s] = *reinterpret_cast<const GV*>(B.V + dpos(ow, s * kWave + lane));
+        if constexpr (SAVE) {
+          // The chunk's entering state and Delta for the backward, from the hand-over: group s of
+          // so / d1 holds state rows / tokens 32 s + 8 g + 0..7 of the lane's column, the bf16
+          // values the scan wave would store; each half goes to its place in kScanRec's order.
+#pragma unroll
+          for (int s = 0; s < NGD; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int r0 = 32 * s + 8 * g + 4 * h;
+              const uint32_t off = (uint32_t)c * kSBytes +
+                                   tile_off(r0 >> 4, ct0, DV / 16, ((r0 & 15) >> 2) * 16 + c16) * sizeof(E);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, half4(so[s], h)), rsn, off, 0, 0);
+            }
+#pragma unroll
+          for (int s = 0; s < NGT; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int r0 = 32 * s + 8 * g + 4 * h;
+              const uint32_t off = (uint32_t)c * kDBytes +
+                                   tile_off(r0 >> 4, ct0, DV / 16, ((r0 & 15) >> 2) * 16 + c16) * sizeof(E);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, half4(d1[s], h)), rdl, off, 0, 0);
+            }
+        }
         // O^T = e^G Y^T + D'^T P^T, each lane four consecutive columns of one token row
         const uint32_t t0 = (uint32_t)(c * kChunk);
 #pragma unroll
@@ -461,12 +500,12 @@ chunk_scan_kernel(ChunkParams p) {
     __syncthreads();  // chunk c's operands are in LDS; every wave is done with chunk c - 1
     if constexpr (NB > 1 && NP == 0) fetch(Bn, c + DIST);
     const uint32_t t0 = (uint32_t)(c * kChunk);
-    if constexpr (REC) {  // the state entering chunk c
+    if constexpr (REC || (SAVE && !DEEP)) {  // the state entering chunk c (DEEP: the output wave stores it)
 #pragma unroll
       for (int r = 0; r < RTK; ++r)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
-          store4_rsrc<E>(rsn, (uint32_t)c * kSBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), S[r][ct]);
+          store4_rsrc<E>(rsn, (uint32_t)c * kSBytes + save_off_s(r, ct) * sizeof(E), S[r][ct]);
     }
 
     // ---- X = K S (token rows x this wave's columns) and Y^T = S^T Q^T (DEEP: the output wave's) ----
@@ -477,7 +516,7 @@ chunk_scan_kernel(ChunkParams p) {
     // and the per-token factors. (The segment pass keeps its reads beside its products: it would
     // spill. With the per-channel decay: bit-identical outputs, within noise on B8 H8 T4096 and
     // the B4 H16 T32768 prefill.)
-    constexpr bool EARLY = PERM && (MODE == kScanFwd || MODE == kScanKda);
+    constexpr bool EARLY = PERM && (MODE == kScanFwd || MODE == kScanFwdSave || MODE == kScanKda);
     constexpr int NTF = EARLY ? 6 : 1;  // T / P fragments: row tiles 0, 1 need group 0; 2, 3 groups 0, 1
     GV ft[NTF], fp[NTF];
     f32x4 fv[4][NT], fcoef[4], feg[4];
@@ -623,12 +662,12 @@ chunk_scan_kernel(ChunkParams p) {
       }
 
     // ---- O^T = (Y^T scaled by e^G per token) + D'^T P^T; or, recomputing, Delta = D' ----
-    if constexpr (REC) {
+    if constexpr (REC || (SAVE && !DEEP)) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct)
-          store4_rsrc<E>(rdl, (uint32_t)c * kDBytes + tile_off(r, ct0 + ct, DV / 16, lane) * sizeof(E), D1[ct][r]);
+          store4_rsrc<E>(rdl, (uint32_t)c * kDBytes + save_off_t(r, ct) * sizeof(E), D1[ct][r]);
     }
     if constexpr (DEEP) {
       // D' to this wave's own V bytes of the chunk's buffer, then the chunk's second barrier: the
@@ -879,6 +918,22 @@ hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   return launch_scan_plan<true>(p, a, seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev), stream);
+}
+
+// The forward for training: the prep with the backward's factors (beta given: unbalanced, rs =
+// 1), then the one-pass scan in its saving mode, into the backward's workspace layout.
+hipError_t launch_chunk_fwd_train(const ChunkArgs& a, hipStream_t stream) {
+  const int64_t nchunks = (a.T + kChunk - 1) / kChunk, n = a.B * a.H * nchunks;
+  ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
+                a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given, a.beta_given};
+  p.xcds = device_info().xcds;
+  p.bwd_off = a.bf16 ? Workspace<bf16>::bytes(n) : Workspace<float>::bytes(n);
+  if (nchunks > 0) {
+    const hipError_t e = launch_chunk_prep(p, a.d_k, a.bf16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return a.bf16 ? launch_scan<bf16, kScanFwdSave>(p, a.d_k, a.d_v, stream)
+                : launch_scan<float, kScanFwdSave>(p, a.d_k, a.d_v, stream);
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {

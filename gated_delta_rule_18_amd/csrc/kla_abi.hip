@@ -184,7 +184,7 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
                             const float* eta, const float* log_alpha, const float* state_in, float* state_out,
                             void* o, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
                             float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream,
-                            int64_t segments = 0, bool use_scratch = false) {
+                            int64_t segments = 0, bool use_scratch = false, bool train = false) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (segments < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative segment count", fn);
@@ -211,8 +211,10 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||
       !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, kda ? 16 : 4))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
-  const size_t need = kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
-                          : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
+  // (the training forward fills the backward's workspace)
+  const size_t need = train ? kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+                      : kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+                            : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
   if (use_scratch) {
     workspace = nullptr;
     workspace_bytes = 0;
@@ -254,19 +256,21 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
   }
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
                    workspace, workspace_bytes, beta_given, segments};
-  return launched(kda ? kla::launch_chunk_kda_fwd(a, static_cast<hipStream_t>(stream))
-                      : kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)),
+  return launched(train ? kla::launch_chunk_fwd_train(a, static_cast<hipStream_t>(stream))
+                  : kda ? kla::launch_chunk_kda_fwd(a, static_cast<hipStream_t>(stream))
+                        : kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)),
                   fn);
 }
 
 // kla_chunk_bwd, kla_gdn_chunk_bwd and kla_kda_chunk_bwd (as chunk_fwd_impl; deta receives dL/dbeta
-// when beta_given; with kda, log_alpha / dlog_alpha are log a / dlog a [B, T, H, d_k] and required).
+// when beta_given; with kda, log_alpha / dlog_alpha are log a / dlog a [B, T, H, d_k] and required);
+// saved: the workspace holds what the training forward left (kla_chunk_bwd_saved and its gdn form).
 kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, bool kda, const void* q, const void* k, const void* v,
                             const float* eta, const float* log_alpha, const float* state_in, const void* dout,
                             const float* dstate_out, void* dq, void* dk, void* dv, float* deta, float* dlog_alpha,
                             float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
                             int64_t chunk, float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            void* stream, bool saved = false) {
   if (dt != KLA_F32 && dt != KLA_BF16) return fail(KLA_ERR_INVALID_VALUE, "%s: unknown dtype", fn);
   if (B < 0 || T < 0 || H < 0) return fail(KLA_ERR_INVALID_VALUE, "%s: negative size", fn);
   if (!supported_head(d_k) || !supported_head(d_v))
@@ -330,7 +334,7 @@ kla_status_t chunk_bwd_impl(const char* fn, bool beta_given, bool kda, const voi
   }
   kla::ChunkBwdArgs a{q,  k,  v,    eta,        log_alpha, state_in, dout, dstate_out, dq,  dk,
                       dv, deta, dlog_alpha, dstate_in, B,  T,        H,    d_k,        d_v, eps,
-                      dt == KLA_BF16, workspace, workspace_bytes, beta_given, kda};
+                      dt == KLA_BF16, workspace, workspace_bytes, beta_given, kda, saved};
   return launched(kla::launch_chunk_bwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -438,6 +442,43 @@ kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v, cons
   return chunk_bwd_impl("kla_gdn_chunk_bwd", true, false, q, k, v, beta, log_alpha, state_in, dout, dstate_out, dq, dk, dv,
                         dbeta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, 0.f, dt, workspace, workspace_bytes,
                         stream);
+}
+
+kla_status_t kla_chunk_fwd_train(const void* q, const void* k, const void* v, const float* eta,
+                                 const float* log_alpha, const float* state_in, float* state_out, void* o, int64_t B,
+                                 int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps,
+                                 kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_chunk_fwd_train", false, false, q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H,
+                        d_k, d_v, chunk, eps, dt, workspace, workspace_bytes, stream, 0, false, true);
+}
+
+kla_status_t kla_gdn_chunk_fwd_train(const void* q, const void* k, const void* v, const float* beta,
+                                     const float* log_alpha, const float* state_in, float* state_out, void* o,
+                                     int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                     kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl("kla_gdn_chunk_fwd_train", true, false, q, k, v, beta, log_alpha, state_in, state_out, o, B,
+                        T, H, d_k, d_v, chunk, 0.f, dt, workspace, workspace_bytes, stream, 0, false, true);
+}
+
+kla_status_t kla_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* eta, const float* log_alpha,
+                                 const float* state_in, const void* dout, const float* dstate_out, void* dq, void* dk,
+                                 void* dv, float* deta, float* dlog_alpha, float* dstate_in, int64_t B, int64_t T,
+                                 int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps, kla_dtype_t dt,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kla_chunk_bwd_saved", false, false, q, k, v, eta, log_alpha, state_in, dout, dstate_out, dq,
+                        dk, dv, deta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, eps, dt, workspace,
+                        workspace_bytes, stream, true);
+}
+
+kla_status_t kla_gdn_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* beta,
+                                     const float* log_alpha, const float* state_in, const void* dout,
+                                     const float* dstate_out, void* dq, void* dk, void* dv, float* dbeta,
+                                     float* dlog_alpha, float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                                     int64_t d_v, int64_t chunk, kla_dtype_t dt, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kla_gdn_chunk_bwd_saved", true, false, q, k, v, beta, log_alpha, state_in, dout, dstate_out,
+                        dq, dk, dv, dbeta, dlog_alpha, dstate_in, B, T, H, d_k, d_v, chunk, 0.f, dt, workspace,
+                        workspace_bytes, stream, true);
 }
 
 kla_status_t kla_kda_chunk_fwd(const void* q, const void* k, const void* v, const float* eta, const float* log_a,

@@ -86,6 +86,7 @@ struct ChunkBwdArgs {
   size_t workspace_bytes;
   bool beta_given;
   bool kda = false;  // per-channel decay: log_alpha holds log a [B, T, H, d_k], dlog_alpha d log a
+  bool saved = false;  // the workspace holds what launch_chunk_fwd_train left for these inputs
 };
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
@@ -95,6 +96,11 @@ hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,
                                  int64_t segments = 0);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
+// The forward for training (scalar gate, one pass): as launch_chunk_fwd, and a.workspace
+// (chunk_bwd_workspace_bytes) is left holding the prep's per-chunk factors, made as the
+// backward makes them, and every chunk's entering state and Delta, so that launch_chunk_bwd with
+// saved skips its prep and its recompute of the forward.
+hipError_t launch_chunk_fwd_train(const ChunkArgs& a, hipStream_t stream);
 // Per-channel decay (KDA): ChunkArgs.log_alpha / DecodeArgs.log_alpha hold log a [.., d_k].
 hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,

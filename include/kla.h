@@ -309,6 +309,67 @@ kla_status_t kla_gdn_chunk_bwd(const void* q, const void* k, const void* v,
                                kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kla_chunk_fwd_train — the chunkwise forward for training: kla_chunk_fwd, which also leaves in
+ * `workspace` what kla_chunk_bwd would otherwise recompute, so that kla_chunk_bwd_saved can skip
+ * that. Source: "Kaczmarz Linear Attention", Abstract (the chunkwise form serves training);
+ * "Deep Dive into KDA", section 3 (the chunkwise forward; its per-chunk states S[n] are what
+ * passes between chunks).
+ *   Arguments as kla_chunk_fwd (o, state_out and all inputs alike; the outputs agree with
+ *   kla_chunk_fwd's up to rounding), except:
+ *   workspace  device buffer of at least kla_chunk_bwd_workspace_size(...) bytes (NULL when
+ *              T = 0). On return it holds the per-chunk factors and every chunk's entering state
+ *              and Delta; the caller keeps it unchanged for kla_chunk_bwd_saved.
+ *   Always one pass over the sequence (no segments). Errors as kla_chunk_fwd.
+ */
+kla_status_t kla_chunk_fwd_train(const void* q, const void* k, const void* v,
+                                 const float* eta, const float* log_alpha, const float* state_in,
+                                 float* state_out, void* o,
+                                 int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                 float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * kla_gdn_chunk_fwd_train — kla_chunk_fwd_train with beta supplied by the caller (gated
+ * DeltaNet; DeltaNet when log_alpha is NULL), as kla_gdn_chunk_fwd. Source: "Deep Dive into
+ * KDA", sections 2.1-3.
+ */
+kla_status_t kla_gdn_chunk_fwd_train(const void* q, const void* k, const void* v,
+                                     const float* beta, const float* log_alpha, const float* state_in,
+                                     float* state_out, void* o,
+                                     int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                     kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kla_chunk_bwd_saved — kla_chunk_bwd from the workspace kla_chunk_fwd_train filled: the
+ * forward is not recomputed. Source: as kla_chunk_bwd.
+ *   Arguments and results as kla_chunk_bwd. The inputs (q, k, v, eta, log_alpha, state_in,
+ *   sizes, eps, dt) must be those of the kla_chunk_fwd_train call that filled `workspace`, and
+ *   the workspace unchanged since; the library cannot check this, and results are undefined
+ *   otherwise. The workspace's saved part is still valid after the call (it may be called again
+ *   for another do / dstate_out).
+ */
+kla_status_t kla_chunk_bwd_saved(const void* q, const void* k, const void* v,
+                                 const float* eta, const float* log_alpha, const float* state_in,
+                                 const void* dout, const float* dstate_out,
+                                 void* dq, void* dk, void* dv, float* deta, float* dlog_alpha,
+                                 float* dstate_in,
+                                 int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                 float eps, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * kla_gdn_chunk_bwd_saved — kla_gdn_chunk_bwd from the workspace kla_gdn_chunk_fwd_train filled
+ * (as kla_chunk_bwd_saved). Source: "Deep Dive into KDA", sections 2.1-3.
+ */
+kla_status_t kla_gdn_chunk_bwd_saved(const void* q, const void* k, const void* v,
+                                     const float* beta, const float* log_alpha, const float* state_in,
+                                     const void* dout, const float* dstate_out,
+                                     void* dq, void* dk, void* dv, float* dbeta, float* dlog_alpha,
+                                     float* dstate_in,
+                                     int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                     kla_dtype_t dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kla_kda_chunk_bwd_workspace_size — bytes of device workspace kla_kda_chunk_bwd needs (0 when
  * T = 0 or the sizes are not supported). Host-only; never fails. For bf16 and d_k = d_v = 128 it
  * is about 162 KiB per chunk of 64 tokens per head: the KDA forward's per-chunk factors and

@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol():
                           "kla_last_error", "kla_chunk_bwd_workspace_size", "kla_chunk_bwd", "kla_gdn_chunk_bwd",
                           "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step",
                           "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg", "kla_chunk_fwd_noalloc",
-                          "kla_kda_chunk_bwd_workspace_size", "kla_kda_chunk_bwd"}
+                          "kla_kda_chunk_bwd_workspace_size", "kla_kda_chunk_bwd", "kla_chunk_fwd_train",
+                          "kla_gdn_chunk_fwd_train", "kla_chunk_bwd_saved", "kla_gdn_chunk_bwd_saved"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -213,7 +214,7 @@ WS = A16 * 256  # fake workspace address, far from the tensors below
 
 def bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16, k=A16 * 2, v=A16 * 3,
         eta=A16 * 4, la=A16 * 5, s_in=0, do=A16 * 6, ds_out=0, dq=A16 * 7, dk_=A16 * 8, dv_=A16 * 9,
-        deta=A16 * 10, dla=A16 * 11, ds_in=0, ws=WS, ws_bytes=None, gdn=False):
+        deta=A16 * 10, dla=A16 * 11, ds_in=0, ws=WS, ws_bytes=None, gdn=False, saved=False):
     if ws_bytes is None:
         ws_bytes = max(K.lib().kla_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk_len, dt), 0)
     opt = lambda x: p(x) if x else None
@@ -221,8 +222,8 @@ def bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, q
             opt(deta), opt(dla), opt(ds_in), B, T, H, dk, dv, chunk_len]
     tail = [dt, opt(ws), ws_bytes, None]
     if gdn:
-        return L().kla_gdn_chunk_bwd(*head, *tail)
-    return L().kla_chunk_bwd(*head, eps, *tail)
+        return getattr(L(), "kla_gdn_chunk_bwd_saved" if saved else "kla_gdn_chunk_bwd")(*head, *tail)
+    return getattr(L(), "kla_chunk_bwd_saved" if saved else "kla_chunk_bwd")(*head, eps, *tail)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -244,6 +245,9 @@ def bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, q
 def test_chunk_bwd_rejects(kw, status):
     assert bwd(**kw) == status
     assert L().kla_last_error().startswith(b"kla_chunk_bwd")
+    # the backward from a training forward's workspace checks its arguments alike
+    assert bwd(saved=True, **kw) == status
+    assert L().kla_last_error().startswith(b"kla_chunk_bwd_saved")
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -255,6 +259,48 @@ def test_chunk_bwd_rejects(kw, status):
 def test_gdn_chunk_bwd_rejects(kw, status):
     assert bwd(gdn=True, **kw) == status
     assert L().kla_last_error().startswith(b"kla_gdn_chunk_bwd")
+    assert bwd(gdn=True, saved=True, **kw) == status
+    assert L().kla_last_error().startswith(b"kla_gdn_chunk_bwd_saved")
+
+
+def fwd_train(dk=128, dv=128, chunk_len=64, eps=1e-6, dt=K.KLA_BF16, B=1, T=64, H=1, q=A16, k=A16 * 2,
+              v=A16 * 3, eta=A16 * 4, la=A16 * 5, o=A16 * 6, ws=WS, ws_bytes=None, gdn=False):
+    """kla_chunk_fwd_train / kla_gdn_chunk_fwd_train with fake device addresses; the workspace
+    defaults to the backward's size."""
+    if ws_bytes is None:
+        ws_bytes = max(K.lib().kla_chunk_bwd_workspace_size(B, T, H, dk, dv, chunk_len, dt), 0)
+    opt = lambda x: p(x) if x else None
+    head = [p(q), p(k), p(v), opt(eta), opt(la), None, None, opt(o), B, T, H, dk, dv, chunk_len]
+    tail = [dt, opt(ws), ws_bytes, None]
+    if gdn:
+        return L().kla_gdn_chunk_fwd_train(*head, *tail)
+    return L().kla_chunk_fwd_train(*head, eps, *tail)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=96), K.KLA_ERR_NOT_SUPPORTED),
+    (dict(eps=-1.0), K.KLA_ERR_INVALID_VALUE),
+    (dict(la=0), K.KLA_ERR_INVALID_VALUE),                     # KLA needs log_alpha
+    (dict(ws=0), K.KLA_ERR_INVALID_VALUE),                     # workspace required
+    (dict(o=A16 * 2 + 64), K.KLA_ERR_INVALID_VALUE),           # o overlaps k
+])
+def test_chunk_fwd_train_rejects(kw, status):
+    assert fwd_train(**kw) == status
+    assert L().kla_last_error().startswith(b"kla_chunk_fwd_train")
+
+
+def test_chunk_fwd_train_needs_the_backward_workspace():
+    """The forward's own workspace size is not enough: the training forward fills the backward's."""
+    fwd_need = K.lib().kla_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    bwd_need = K.lib().kla_chunk_bwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    assert fwd_need < bwd_need
+    assert fwd_train(ws_bytes=fwd_need) == K.KLA_ERR_INVALID_VALUE
+    assert b"workspace" in L().kla_last_error()
+    assert fwd_train(gdn=True, la=0, ws_bytes=bwd_need - 16) == K.KLA_ERR_INVALID_VALUE
+    assert L().kla_last_error().startswith(b"kla_gdn_chunk_fwd_train")
+    assert fwd_train(gdn=True, eta=0) == K.KLA_ERR_INVALID_VALUE  # beta required
+    assert fwd_train(B=0) == K.KLA_OK
+    assert fwd_train(T=0, ws=0) == K.KLA_OK  # nothing to write without state_out
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (64, 128), (64, 64)])

@@ -315,7 +315,11 @@ def run_bwd(args, w):
     if train:
         o = torch.empty_like(t["v"])
         fhead = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), la, None, None, P(o), w.B, w.T, w.H, w.dk, w.dv, 64)
-        if gdn:
+        if kda:
+            eps = ctypes.c_float(w.eps)
+            call = lambda: (L.kla_kda_chunk_fwd_train(*fhead, eps, 0, code, P(workspace), ws_bytes, sp) or
+                            L.kla_kda_chunk_bwd_saved(*head, eps, 0, code, P(workspace), ws_bytes, sp))
+        elif gdn:
             call = lambda: (L.kla_gdn_chunk_fwd_train(*fhead, code, P(workspace), ws_bytes, sp) or
                             L.kla_gdn_chunk_bwd_saved(*head, code, P(workspace), ws_bytes, sp))
         else:
@@ -349,9 +353,13 @@ def run_bwd(args, w):
     ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     tokens = w.B * w.T
     flops = (train_flops_per_head_token if train else bwd_flops_per_head_token)(w.dk, w.dv) * w.heads * w.T
-    nbytes = bwd_bytes(w, es, kda) + (chunk_bytes(w, es) if train else 0)
+    # (a training step: both passes' bytes; the KDA forward reads log a per channel, d_k fp32)
+    nbytes = bwd_bytes(w, es, kda) + ((chunk_bytes(w, es) + (w.heads * w.T * 4 * (w.dk - 1) if kda else 0))
+                                      if train else 0)
     peak_mfma = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
-    part = {"kernel": ("chunk_prep_kernel + chunk_scan_kernel (saving) + chunk_rscan_kernel + chunk_grad_kernel"
+    part = {"kernel": ("chunk_prep_kda_kernel + chunk_scan_kernel (KDA, saving) + chunk_rscan_kernel + "
+                       "chunk_grad_kda_kernel" if train and kda else
+                       "chunk_prep_kernel + chunk_scan_kernel (saving) + chunk_rscan_kernel + chunk_grad_kernel"
                        if train else
                        "chunk_prep_kda_kernel + chunk_scan_kernel (recompute) + chunk_rscan_kernel + "
                        "chunk_grad_kda_kernel" if kda else
@@ -598,10 +606,6 @@ def main():
         w = wl.WORKLOADS["fwd_b8h8_t4096" if args.workload == "mixed_b4h16" else args.workload]
         if not w.T:
             print(f"--pass {args.pass_} needs a prefill workload", file=sys.stderr)
-            sys.exit(2)
-        if args.pass_ == "train" and args.mode == "kda":
-            print("--pass train has no per-channel decay form (kla_kda_chunk_bwd recomputes the forward)",
-                  file=sys.stderr)
             sys.exit(2)
         return run_bwd(args, w.with_(steps=0))
 

@@ -45,6 +45,10 @@ _SIGNATURES = {
     "kla_kda_chunk_fwd": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
                                                                _c_void_p]),
     "kla_kda_decode_step": (_int, [_c_void_p] * 7 + [_i64] * 4 + [_f32, _int, _int, _c_void_p]),
+    "kla_kda_chunk_fwd_train": (_int, [_c_void_p] * 8 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
+                                                                     _c_void_p]),
+    "kla_kda_chunk_bwd_saved": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _int, _c_void_p,
+                                                                         ctypes.c_size_t, _c_void_p]),
     "kla_kda_chunk_bwd_workspace_size": (ctypes.c_size_t, [_i64] * 6 + [_int]),
     "kla_kda_chunk_bwd": (_int, [_c_void_p] * 14 + [_i64] * 6 + [_f32, _int, _int, _c_void_p, ctypes.c_size_t,
                                                                    _c_void_p]),
@@ -440,19 +444,34 @@ def kla_kda_chunk_fwd(q, k, v, eta, log_a, eps=1e-6, beta_given=False, state_in=
     """Chunkwise forward with a per-channel decay (KDA's gate): log_a [B, T, H, d_k] fp32; eta
     [B, T, H] fp32 is eta of the Kaczmarz step, or beta itself when beta_given. Otherwise as
     kla_chunk_fwd. Returns (o, final state or None)."""
+    o, state_out, _ = _kda_fwd("kla_kda_chunk_fwd", kla_kda_chunk_fwd_workspace_size, q, k, v, eta, log_a, eps,
+                               beta_given, state_in, return_state, o, state_out, chunk, workspace, stream)
+    return o, state_out
+
+
+def kla_kda_chunk_fwd_train(q, k, v, eta, log_a, eps=1e-6, beta_given=False, state_in=None, return_state=True,
+                            o=None, state_out=None, chunk=CHUNK, workspace=None, stream=None):
+    """kla_kda_chunk_fwd for training: also fills the backward's workspace (kla_kda_chunk_bwd_workspace_size
+    bytes; allocated when None) for kla_kda_chunk_bwd_saved. Returns (o, final state or None, workspace)."""
+    return _kda_fwd("kla_kda_chunk_fwd_train", kla_kda_chunk_bwd_workspace_size, q, k, v, eta, log_a, eps,
+                    beta_given, state_in, return_state, o, state_out, chunk, workspace, stream)
+
+
+def _kda_fwd(fn_name, size_fn, q, k, v, eta, log_a, eps, beta_given, state_in, return_state, o, state_out, chunk,
+             workspace, stream):
     torch = _torch()
     B, T, H, dk, dv, dev, o, state_out = _fwd_tensors(q, k, v, "eta", eta, None, True, state_in, return_state, o,
                                                       state_out)
     _need(log_a, "log_a", (B, T, H, dk), torch.float32, dev)
     code = _dtype_code(q)
-    need = kla_kda_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, code)
+    need = size_fn(B, T, H, dk, dv, chunk, code)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().kla_kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in),
+    check(getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in),
                                   _ptr(state_out), _ptr(o), B, T, H, dk, dv, chunk, float(eps), int(bool(beta_given)),
                                   code, _ptr(workspace), ws_bytes, _stream(dev, stream)))
-    return o, state_out
+    return o, state_out, workspace
 
 
 def kla_kda_decode_step(q, k, v, eta, log_a, state, eps=1e-6, beta_given=False, o=None, stream=None):
@@ -491,6 +510,21 @@ def kla_kda_chunk_bwd(q, k, v, eta, log_a, do, eps=1e-6, beta_given=False, state
     kla_chunk_bwd. Returns a dict with dq, dk, dv (input dtype), deta (d beta when beta_given),
     dlog_a [B, T, H, d_k] (fp32) and dstate_in (fp32, or None when not wanted); tensors given in
     ``out`` under those names are written in place."""
+    return _kda_bwd("kla_kda_chunk_bwd", q, k, v, eta, log_a, do, eps, beta_given, state_in, dstate_out,
+                    want_dstate_in, chunk, workspace, stream, out)
+
+
+def kla_kda_chunk_bwd_saved(q, k, v, eta, log_a, do, workspace, eps=1e-6, beta_given=False, state_in=None,
+                            dstate_out=None, want_dstate_in=True, chunk=CHUNK, stream=None, out=None):
+    """kla_kda_chunk_bwd from the workspace kla_kda_chunk_fwd_train filled for the same inputs."""
+    if workspace is None and q.shape[1] > 0:
+        raise ValueError("kla_kda_chunk_bwd_saved needs the workspace kla_kda_chunk_fwd_train filled")
+    return _kda_bwd("kla_kda_chunk_bwd_saved", q, k, v, eta, log_a, do, eps, beta_given, state_in, dstate_out,
+                    want_dstate_in, chunk, workspace, stream, out)
+
+
+def _kda_bwd(fn_name, q, k, v, eta, log_a, do, eps, beta_given, state_in, dstate_out, want_dstate_in, chunk,
+             workspace, stream, out):
     torch = _torch()
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, T, H, d]")
@@ -523,7 +557,7 @@ def kla_kda_chunk_bwd(q, k, v, eta, log_a, do, eps=1e-6, beta_given=False, state
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().kla_kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in), _ptr(do),
+    check(getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(log_a), _ptr(state_in), _ptr(do),
                                   _ptr(dstate_out), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                                   _ptr(out["deta"]), _ptr(out["dlog_a"]), _ptr(out["dstate_in"]), B, T, H, dk, dv,
                                   chunk, float(eps), int(bool(beta_given)), code, _ptr(workspace), ws_bytes,

@@ -85,14 +85,18 @@ struct Workspace {
 // to the backward workspace, no outputs); the first pass of the segment scan (below); the
 // forward with the per-channel decay (KDA); the first segment pass with that decay; and the
 // backward's recompute with that decay.
-enum { kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3, kScanKdaSeg = 4, kScanKdaRec = 5, kScanFwdSave = 6 };
+enum {
+  kScanFwd = 0, kScanRec = 1, kScanSeg = 2, kScanKda = 3, kScanKdaSeg = 4, kScanKdaRec = 5, kScanFwdSave = 6,
+  kScanKdaSave = 7
+};
 __host__ __device__ constexpr bool scan_kda(int mode) {
-  return mode == kScanKda || mode == kScanKdaSeg || mode == kScanKdaRec;
+  return mode == kScanKda || mode == kScanKdaSeg || mode == kScanKdaRec || mode == kScanKdaSave;
 }
 __host__ __device__ constexpr bool scan_rec(int mode) { return mode == kScanRec || mode == kScanKdaRec; }
 __host__ __device__ constexpr bool scan_seg(int mode) { return mode == kScanSeg || mode == kScanKdaSeg; }
-// kScanFwdSave: the forward for training, which also stores what the backward's recompute would.
-__host__ __device__ constexpr bool scan_save(int mode) { return mode == kScanFwdSave; }
+// kScanFwdSave, kScanKdaSave: the forward for training, which also stores what the backward's
+// recompute would.
+__host__ __device__ constexpr bool scan_save(int mode) { return mode == kScanFwdSave || mode == kScanKdaSave; }
 
 // State columns per scan workgroup (bf16: two waves of 16 columns; fp32: four). The bf16
 // segment scan uses four waves (64 columns): with half the workgroups per segment, twice the

@@ -103,6 +103,7 @@ constexpr int scan_producers() {
 // MODE kScanKdaRec: the backward's recompute with the per-channel decay.
 // MODE kScanFwdSave: kScanFwd, and, as kScanRec, every chunk's entering state and Delta are
 // stored (in kScanRec's tile order, which the backward reads) for a backward without recompute.
+// MODE kScanKdaSave: the same for kScanKda (kScanKdaRec's order).
 // (With four producers, two waves share each of their SIMDs: at most 256 registers per wave.)
 template <typename E, int DK, int DV, int W, int NT, int MODE>
 __global__ __launch_bounds__((W + scan_producers<E, DK, DV, W, NT, MODE>() + scan_outwaves<E, DK, DV, W, NT, MODE>()) *
@@ -516,7 +517,7 @@ chunk_scan_kernel(ChunkParams p) {
     // and the per-token factors. (The segment pass keeps its reads beside its products: it would
     // spill. With the per-channel decay: bit-identical outputs, within noise on B8 H8 T4096 and
     // the B4 H16 T32768 prefill.)
-    constexpr bool EARLY = PERM && (MODE == kScanFwd || MODE == kScanFwdSave || MODE == kScanKda);
+    constexpr bool EARLY = PERM && (MODE == kScanFwd || MODE == kScanFwdSave || MODE == kScanKda || MODE == kScanKdaSave);
     constexpr int NTF = EARLY ? 6 : 1;  // T / P fragments: row tiles 0, 1 need group 0; 2, 3 groups 0, 1
     GV ft[NTF], fp[NTF];
     f32x4 fv[4][NT], fcoef[4], feg[4];
@@ -918,6 +919,22 @@ hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   return launch_scan_plan<true>(p, a, seg_plan(p.heads, p.nchunks, a.d_k, a.d_v, a.bf16, a.segments, dev), stream);
+}
+
+// The KDA forward for training (as launch_chunk_fwd_train, with the per-channel decay's prep and
+// workspace).
+hipError_t launch_chunk_kda_fwd_train(const ChunkArgs& a, hipStream_t stream) {
+  const int64_t nchunks = (a.T + kChunk - 1) / kChunk, n = a.B * a.H * nchunks;
+  ChunkParams p{a.q, a.k, a.v, a.eta, a.log_alpha, a.state_in, a.state_out, a.o, a.workspace,
+                a.B * a.H, a.H, a.T, nchunks, a.eps, a.beta_given, a.beta_given};
+  p.xcds = device_info().xcds;
+  p.bwd_off = a.bf16 ? KdaSpace<bf16>::bytes(n, (int)a.d_k) : KdaSpace<float>::bytes(n, (int)a.d_k);
+  if (nchunks > 0) {
+    const hipError_t e = launch_chunk_prep_kda(p, a.d_k, a.bf16, stream);
+    if (e != hipSuccess) return e;
+  }
+  return a.bf16 ? launch_scan<bf16, kScanKdaSave>(p, a.d_k, a.d_v, stream)
+                : launch_scan<float, kScanKdaSave>(p, a.d_k, a.d_v, stream);
 }
 
 // The forward for training: the prep with the backward's factors (beta given: unbalanced, rs =

@@ -212,7 +212,10 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
       !aligned(state_out, 16) || !aligned(eta, 4) || !aligned(log_alpha, kda ? 16 : 4))
     return fail(KLA_ERR_INVALID_VALUE, "%s: misaligned pointer", fn);
   // (the training forward fills the backward's workspace)
-  const size_t need = train ? kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+  if (train && kda && !kla::chunk_grad_kda_supported(d_k, d_v, dt == KLA_BF16))
+    return fail(KLA_ERR_NOT_SUPPORTED, "%s: fp32 gradients need d_k = d_v = 64", fn);
+  const size_t need = train ? (kda ? kla::chunk_kda_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
+                                   : kla::chunk_bwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16))
                       : kda ? kla::chunk_kda_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16)
                             : kla::chunk_fwd_workspace_bytes(B, T, H, d_k, d_v, dt == KLA_BF16, segments);
   if (use_scratch) {
@@ -256,7 +259,8 @@ kla_status_t chunk_fwd_impl(const char* fn, bool beta_given, bool kda, const voi
   }
   kla::ChunkArgs a{q, k, v, eta, log_alpha, state_in, state_out, o, B, T, H, d_k, d_v, eps, dt == KLA_BF16,
                    workspace, workspace_bytes, beta_given, segments};
-  return launched(train ? kla::launch_chunk_fwd_train(a, static_cast<hipStream_t>(stream))
+  return launched(train ? (kda ? kla::launch_chunk_kda_fwd_train(a, static_cast<hipStream_t>(stream))
+                               : kla::launch_chunk_fwd_train(a, static_cast<hipStream_t>(stream)))
                   : kda ? kla::launch_chunk_kda_fwd(a, static_cast<hipStream_t>(stream))
                         : kla::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)),
                   fn);
@@ -497,6 +501,27 @@ kla_status_t kla_kda_chunk_bwd(const void* q, const void* k, const void* v, cons
   return chunk_bwd_impl("kla_kda_chunk_bwd", beta_given != 0, true, q, k, v, eta, log_a, state_in, dout, dstate_out,
                         dq, dk, dv, deta, dlog_a, dstate_in, B, T, H, d_k, d_v, chunk, beta_given ? 0.f : eps, dt,
                         workspace, workspace_bytes, stream);
+}
+
+kla_status_t kla_kda_chunk_fwd_train(const void* q, const void* k, const void* v, const float* eta,
+                                     const float* log_a, const float* state_in, float* state_out, void* o, int64_t B,
+                                     int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk, float eps,
+                                     int beta_given, kla_dtype_t dt, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return chunk_fwd_impl("kla_kda_chunk_fwd_train", beta_given != 0, true, q, k, v, eta, log_a, state_in, state_out, o,
+                        B, T, H, d_k, d_v, chunk, beta_given ? 0.f : eps, dt, workspace, workspace_bytes, stream, 0,
+                        false, true);
+}
+
+kla_status_t kla_kda_chunk_bwd_saved(const void* q, const void* k, const void* v, const float* eta,
+                                     const float* log_a, const float* state_in, const void* dout,
+                                     const float* dstate_out, void* dq, void* dk, void* dv, float* deta, float* dlog_a,
+                                     float* dstate_in, int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                     int64_t chunk, float eps, int beta_given, kla_dtype_t dt, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl("kla_kda_chunk_bwd_saved", beta_given != 0, true, q, k, v, eta, log_a, state_in, dout,
+                        dstate_out, dq, dk, dv, deta, dlog_a, dstate_in, B, T, H, d_k, d_v, chunk,
+                        beta_given ? 0.f : eps, dt, workspace, workspace_bytes, stream, true);
 }
 
 kla_status_t kla_kda_decode_step(const void* q, const void* k, const void* v, const float* eta, const float* log_a,

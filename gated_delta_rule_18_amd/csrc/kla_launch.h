@@ -101,6 +101,8 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t stream);
 // backward makes them, and every chunk's entering state and Delta, so that launch_chunk_bwd with
 // saved skips its prep and its recompute of the forward.
 hipError_t launch_chunk_fwd_train(const ChunkArgs& a, hipStream_t stream);
+// The same for the per-channel decay (chunk_kda_bwd_workspace_bytes; launch_chunk_bwd with kda).
+hipError_t launch_chunk_kda_fwd_train(const ChunkArgs& a, hipStream_t stream);
 // Per-channel decay (KDA): ChunkArgs.log_alpha / DecodeArgs.log_alpha hold log a [.., d_k].
 hipError_t launch_chunk_kda_fwd(const ChunkArgs& a, hipStream_t stream);
 size_t chunk_kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, bool bf16,

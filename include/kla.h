@@ -412,6 +412,33 @@ kla_status_t kla_kda_chunk_bwd(const void* q, const void* k, const void* v,
                                float eps, int beta_given, kla_dtype_t dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * kla_kda_chunk_fwd_train — kla_kda_chunk_fwd for training (as kla_chunk_fwd_train): the
+ * workspace, of at least kla_kda_chunk_bwd_workspace_size(...) bytes, is left holding what
+ * kla_kda_chunk_bwd would recompute. Source: "Deep Dive into KDA", sections 2.3 and 3.
+ *   Supported as kla_kda_chunk_bwd (fp32 only with d_k = d_v = 64; else KLA_ERR_NOT_SUPPORTED);
+ *   one pass over the sequence. Otherwise arguments and errors as kla_kda_chunk_fwd.
+ */
+kla_status_t kla_kda_chunk_fwd_train(const void* q, const void* k, const void* v,
+                                     const float* eta, const float* log_a, const float* state_in,
+                                     float* state_out, void* o,
+                                     int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                     float eps, int beta_given, kla_dtype_t dt, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
+ * kla_kda_chunk_bwd_saved — kla_kda_chunk_bwd from the workspace kla_kda_chunk_fwd_train filled
+ * for the same inputs (as kla_chunk_bwd_saved). Source: "Deep Dive into KDA", sections 2.3 and 3.
+ */
+kla_status_t kla_kda_chunk_bwd_saved(const void* q, const void* k, const void* v,
+                                     const float* eta, const float* log_a, const float* state_in,
+                                     const void* dout, const float* dstate_out,
+                                     void* dq, void* dk, void* dv, float* deta, float* dlog_a,
+                                     float* dstate_in,
+                                     int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, int64_t chunk,
+                                     float eps, int beta_given, kla_dtype_t dt, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* kla_status_string(kla_status_t status);
 

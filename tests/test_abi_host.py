@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol():
                           "kla_kda_chunk_fwd_workspace_size", "kla_kda_chunk_fwd", "kla_kda_decode_step",
                           "kla_chunk_fwd_seg_workspace_size", "kla_chunk_fwd_seg", "kla_chunk_fwd_noalloc",
                           "kla_kda_chunk_bwd_workspace_size", "kla_kda_chunk_bwd", "kla_chunk_fwd_train",
-                          "kla_gdn_chunk_fwd_train", "kla_chunk_bwd_saved", "kla_gdn_chunk_bwd_saved"}
+                          "kla_gdn_chunk_fwd_train", "kla_chunk_bwd_saved", "kla_gdn_chunk_bwd_saved",
+                          "kla_kda_chunk_fwd_train", "kla_kda_chunk_bwd_saved"}
     for n in names:
         assert hasattr(L(), n), n
 
@@ -351,6 +352,25 @@ def kda_bwd(dk=128, dv=128, chunk_len=64, eps=1e-6, beta_given=0, dt=K.KLA_BF16,
 def test_kda_chunk_bwd_rejects(kw, status):
     assert kda_bwd(**kw) == status
     assert L().kla_last_error().startswith(b"kla_kda_chunk_bwd")
+
+
+def test_kda_training_pair_checks():
+    """kla_kda_chunk_fwd_train fills the KDA backward's workspace and supports what that backward
+    does; kla_kda_chunk_bwd_saved checks its arguments as kla_kda_chunk_bwd."""
+    need = K.lib().kla_kda_chunk_bwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    kfwd = K.lib().kla_kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, K.KLA_BF16)
+    lib = L()
+    args = lambda dt, dk, ws_bytes: (p(A16), p(A16 * 2), p(A16 * 3), p(A16 * 4), p(A16 * 5), None, None, p(A16 * 6),
+                                     1, 64, 1, dk, dk, 64, ctypes.c_float(1e-6), 0, dt, p(WS), ws_bytes, None)
+    assert lib.kla_kda_chunk_fwd_train(*args(K.KLA_BF16, 128, kfwd)) == K.KLA_ERR_INVALID_VALUE
+    assert lib.kla_last_error().startswith(b"kla_kda_chunk_fwd_train")
+    assert lib.kla_kda_chunk_fwd_train(*args(K.KLA_F32, 128, need)) == K.KLA_ERR_NOT_SUPPORTED
+    assert lib.kla_kda_chunk_fwd_train(*args(K.KLA_BF16, 96, need)) == K.KLA_ERR_NOT_SUPPORTED
+    a = [p(A16), p(A16 * 2), p(A16 * 3), p(A16 * 4), p(A16 * 5), None, p(A16 * 6), None, p(A16 * 7), p(A16 * 8),
+         p(A16 * 9), p(A16 * 10), p(A16 * 16), None, 1, 64, 1, 128, 128, 64, ctypes.c_float(1e-6), 0, K.KLA_BF16,
+         None, need, None]
+    assert lib.kla_kda_chunk_bwd_saved(*a) == K.KLA_ERR_INVALID_VALUE  # workspace required
+    assert lib.kla_last_error().startswith(b"kla_kda_chunk_bwd_saved")
 
 
 def test_kda_bwd_workspace_and_empty():

@@ -1,6 +1,7 @@
 """GPU parity of the training pair: kla_chunk_fwd_train (the forward that leaves the backward's
 workspace filled) and kla_chunk_bwd_saved (the backward from it, without recomputing the
-forward), and their beta-given forms. Outputs against kla_chunk_fwd (bit for bit where both run
+forward), their beta-given forms and the per-channel decay's pair (kla_kda_chunk_fwd_train,
+kla_kda_chunk_bwd_saved). Outputs against kla_chunk_fwd (bit for bit where both run
 the same arithmetic) and the fp64 oracle; gradients against the fp64 gradient oracle with the
 backward's bars (relative L2 <= 1e-4 fp32, <= 2e-2 bf16) and against kla_chunk_bwd."""
 import numpy as np
@@ -10,6 +11,7 @@ import oracle
 import workloads as wl
 from tests import oracle_pool as op
 from tests.kla_testutil import TOL, dev, heads_of, host, rel_l2, report, states_of
+from tests import test_gpu_kda_bwd as kb
 from tests.test_gpu_bwd import NAMES, _sel, _unit_keys, all_heads, compare, gpu_bwd, oracle_bwd
 
 pytestmark = pytest.mark.gpu
@@ -133,3 +135,78 @@ def test_train_pair_b8h8_t4096_all_heads():
                           "dS0": states_of(got["dS0"], hd)}
     merged, heads = op.run("backward", w, got_for, (0.0, 0.0))
     op.check("train pair b8h8_t4096", merged, heads, TOL[w.dtype])
+
+
+# ----------------------------------------------------------------------------- per-channel decay (KDA)
+
+def kda_train_pair(w, inp, la, g, beta_given=False):
+    """kla_kda_chunk_fwd_train, then kla_kda_chunk_bwd_saved: (o, S_T, gradients) on the host."""
+    q, k, v = dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype)
+    s0 = None if g["S0"] is None else dev(g["S0"])
+    dst = None if g["dST"] is None else dev(g["dST"])
+    eta, lad = dev(inp["eta"]), dev(la)
+    o, S, ws = kla.kla_kda_chunk_fwd_train(q, k, v, eta, lad, eps=w.eps, beta_given=beta_given, state_in=s0)
+    out = kla.kla_kda_chunk_bwd_saved(q, k, v, eta, lad, dev(g["do"], w.dtype), ws, eps=w.eps, beta_given=beta_given,
+                                      state_in=s0, dstate_out=dst)
+    torch.cuda.synchronize()
+    got = {"dq": host(out["dq"]), "dk": host(out["dk"]), "dv": host(out["dv"]), "deta": host(out["deta"]),
+           "dlog_a": host(out["dlog_a"]), "dS0": host(out["dstate_in"])}
+    return host(o), host(S), got
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T,beta_given", [
+    ("bf16", 128, 128, 250, False), ("bf16", 64, 64, 131, False), ("bf16", 128, 64, 100, False),
+    ("bf16", 128, 128, 190, True), ("f32", 64, 64, 77, False), ("f32", 64, 64, 130, True),
+])
+def test_kda_train_pair_shapes(dtype, dk, dv, T, beta_given):
+    """As test_train_pair_shapes, with per-channel decays: outputs against kla_kda_chunk_fwd's (bit
+    for bit with the Kaczmarz step, whose factors are the forward's; against the oracle with beta
+    given, whose factors the backward makes unbalanced), gradients against the oracle and against
+    kla_kda_chunk_bwd (fp32: bit for bit)."""
+    w = wl.custom("kda_train", 640 + T, B=2, H=2, dk=dk, dv=dv, T=T, dtype=dtype, log_alpha_range=(0.0, 0.3))
+    inp = wl.prefill_inputs(w)
+    if beta_given:
+        inp["k"] = wl.round_to_bf16(_unit_keys(inp["k"])) if dtype == "bf16" else _unit_keys(inp["k"])
+    la = wl.channel_log_decay(w)
+    g = wl.grad_inputs(w, s0_std=0.05, dst_std=1.0)
+    o, S, got = kda_train_pair(w, inp, la, g, beta_given)
+    heads = kb.all_heads(w)
+    of, Sf = kla.kla_kda_chunk_fwd(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype), dev(inp["eta"]),
+                                   dev(la), eps=w.eps, beta_given=beta_given, state_in=dev(g["S0"]))
+    torch.cuda.synchronize()
+    if beta_given:
+        eo, eS = rel_l2(o, host(of)), rel_l2(S, host(Sf))
+        report(f"kda train forward vs kla_kda_chunk_fwd {dtype} beta given", o=eo, S_T=eS)
+        assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
+    else:
+        assert np.array_equal(o, host(of)) and np.array_equal(S, host(Sf))
+    kb.compare(f"kda train pair {dtype} dk={dk} dv={dv} T={T} beta_given={beta_given}", w, got,
+               kb.oracle_bwd(w, inp, la, g, heads, beta_given), heads)
+    ref = kb.gpu_bwd(w, inp, la, g, beta_given)
+    errs = {n: rel_l2(got[n], ref[n]) for n in kb.NAMES}
+    report(f"kda train pair vs kla_kda_chunk_bwd {dtype} dk={dk} dv={dv} T={T}", **errs)
+    if dtype == "f32":
+        for n in kb.NAMES:
+            assert np.array_equal(got[n], ref[n]), n
+    else:
+        assert all(e <= TOL[dtype] for e in errs.values()), errs
+
+
+def test_kda_train_pair_b8h8_t4096_all_heads():
+    """The B8 H8 T4096 d128 bf16 shape at full size with per-channel decays, in the benchmark's
+    launch: outputs equal kla_kda_chunk_fwd's, every gradient of every head from the training
+    forward's workspace against the oracle."""
+    w = wl.WORKLOADS["fwd_b8h8_t4096"]
+    inp = wl.prefill_inputs(w)
+    la = wl.channel_log_decay(w)
+    g = wl.grad_inputs(w)
+    o, S, got = kda_train_pair(w, inp, la, g)
+    of, Sf = kla.kla_kda_chunk_fwd(dev(inp["q"], w.dtype), dev(inp["k"], w.dtype), dev(inp["v"], w.dtype),
+                                   dev(inp["eta"]), dev(la), eps=w.eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(o, host(of)) and np.array_equal(S, host(Sf))
+    del inp, g, la, o, S, of, Sf
+    got_for = lambda hd: {**{n: heads_of(got[n], hd) for n in ("dq", "dk", "dv", "deta", "dlog_a")},
+                          "dS0": states_of(got["dS0"], hd)}
+    merged, heads = op.run("kda_backward", w, got_for, (0.0, 0.0))
+    op.check("kda train pair b8h8_t4096", merged, heads, TOL[w.dtype])

@@ -242,8 +242,18 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
   store_t<E, NTH>(sm, ws, chunk_id);
 }
 
+// Waves per SIMD that the LDS of one workgroup a chunk lets a CU hold (160 KiB per CU, four SIMDs,
+// kThreads / 64 waves per workgroup).
 template <typename E, int DK>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p) {
+constexpr int prep_waves_per_simd() {
+  const int wg = (160 * 1024) / (int)sizeof(PrepSmem<E, DK>);
+  const int w = wg * (kThreads / kWave) / 4;
+  return w < 1 ? 1 : w > 8 ? 8 : w;
+}
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prep_waves_per_simd<E, DK>())))
+void chunk_prep_kernel(ChunkParams p) {
   constexpr bool BF = is_bf16<E>();
   constexpr int VN = Vec16<E>::N;
   typedef typename Vec16<E>::type V16;

@@ -217,17 +217,31 @@ __device__ __forceinline__ void store_t(const Sm& sm, const Workspace<E>& ws, in
 }
 
 // T = (I + A)^-1 (diagonal blocks in place of A in sm.Af, the others in sm.Tx), and the chunk's
-// P, T and factor rows to the workspace.
+// P, T and factor rows to the workspace (P and T with streaming stores if STREAM).
 // Called by all threads of the workgroup once A (sm.Af, fp32, zero on and above the diagonal),
 // P (sm.Ps) and the factor rows (sm.sc) are in LDS and published by a barrier.
-template <typename E, int NTH = kThreads, typename Sm>
+template <typename E, bool STREAM, int NTH = kThreads, typename Sm>
 __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, int64_t chunk_id) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // ---- diagonal blocks of T (wave 0) while the other waves store P and the factors ----
-  if (wave == 0)
-    t_diag(sm, lane);
-  else
-    store_p_sc<E>(sm, ws, chunk_id, tid - kWave, NTH - kWave);
+  // ---- diagonal blocks of T (wave 0, as t_diag; written out here: through the helper the
+  //      scheduler hoists all of the blocks' LDS reads ahead of the substitution, 92 -> 140 VGPRs
+  //      at bf16 d_k = 128) while the other waves store P and the factors ----
+  if (wave == 0) {
+    const int base = (lane >> 4) * 16, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* arow = &sm.Af[base + i][base];
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = fmaf(arow[m], x[m], s);
+      x[i] = (i == col) ? 1.f : -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.Af[base + i][base + col] = x[i];
+  } else {
+    store_p_sc<E, STREAM>(sm, ws, chunk_id, tid - kWave, NTH - kWave);
+  }
   __syncthreads();
 
   // ---- off-diagonal blocks, down each block column: wave j forms, for i = j+1 .. 3,
@@ -239,7 +253,7 @@ __device__ __forceinline__ void solve_and_store(Sm& sm, const Workspace<E>& ws, 
   __syncthreads();
 
   // ---- T to the workspace (upper off-diagonal blocks are zero) ----
-  store_t<E, NTH>(sm, ws, chunk_id);
+  store_t<E, NTH, STREAM>(sm, ws, chunk_id);
 }
 
 // Waves per SIMD that the LDS of one workgroup a chunk lets a CU hold (160 KiB per CU, four SIMDs,
@@ -251,7 +265,10 @@ constexpr int prep_waves_per_simd() {
   return w < 1 ? 1 : w > 8 ? 8 : w;
 }
 
-template <typename E, int DK>
+// STREAM: the launch's T and P blocks are larger than the last-level cache, so they go out with
+// streaming stores (the scan reads them only after the whole prep has written far more than the
+// caches hold).
+template <typename E, int DK, bool STREAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prep_waves_per_simd<E, DK>())))
 void chunk_prep_kernel(ChunkParams p) {
   constexpr bool BF = is_bf16<E>();
@@ -396,7 +413,7 @@ void chunk_prep_kernel(ChunkParams p) {
   }
   __syncthreads();
 
-  solve_and_store<E>(sm, ws, chunk_id);
+  solve_and_store<E, STREAM>(sm, ws, chunk_id);
   (void)BF;
 }
 
@@ -930,13 +947,28 @@ hipError_t launch_kda_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// T and P of a launch (two C x C blocks of E per chunk) from this many bytes on are stored with
+// streaming stores: the MI355X's last-level cache holds 256 MB. Measured (bf16, d = 128): the
+// B4 H16 T32768 prefill forward (512 MB of T and P) 1.13 -> 1.11 ms; B8 H8 T4096 (64 MB) and its
+// backward are 1-2 % slower with them.
+constexpr int64_t kStreamPrepBytes = int64_t(256) << 20;
+
+template <typename E, int DK>
+void launch_dk(const ChunkParams& p, int64_t grid, hipStream_t stream) {
+  const bool stream_tp = grid * 2 * kChunk * kChunk * (int64_t)sizeof(E) >= kStreamPrepBytes;
+  if (stream_tp)
+    hipLaunchKernelGGL((chunk_prep_kernel<E, DK, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<E, DK, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+}
+
 template <typename E>
 hipError_t launch_e(const ChunkParams& p, int64_t d_k, hipStream_t stream) {
   const int64_t grid = p.heads * p.nchunks;
   if (d_k == 128)
-    hipLaunchKernelGGL((chunk_prep_kernel<E, 128>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    launch_dk<E, 128>(p, grid, stream);
   else
-    hipLaunchKernelGGL((chunk_prep_kernel<E, 64>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    launch_dk<E, 64>(p, grid, stream);
   return hipGetLastError();
 }
 

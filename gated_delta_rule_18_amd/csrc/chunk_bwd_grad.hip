@@ -431,14 +431,19 @@ __global__ __launch_bounds__(kGradThreads) void chunk_grad_kernel(ChunkBwdParams
   }
   __syncthreads();
   // ---- dv = diag(eta rs) Zb: the transposing read of Zb^T gives four consecutive d_v
-  //      entries of one token per lane ----
+  //      entries of one token per lane. Waves 1 .. NW - 1 take its tiles, so that wave 0 can
+  //      form the per-token sums below meanwhile (which the others would wait for). ----
   constexpr int NJT = DV / 16;
+  if (wave != 0) {
 #pragma unroll
-  for (int t = 0; t < 4 * NJT / NW; ++t) {
-    const int q = wave * (4 * NJT / NW) + t, rt = q % 4, jt = q / 4;
-    const int r = 16 * rt + c16;
-    const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
-    store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
+    for (int t = 0; t < (4 * NJT + NW - 2) / (NW - 1); ++t) {
+      const int q = wave - 1 + (NW - 1) * t, rt = q % 4, jt = q / 4;
+      if (q < 4 * NJT) {
+        const int r = 16 * rt + c16;
+        const f32x4 z = col4<E, kChunk>(sm.Zt, 16 * jt, 16 * rt, g, c16);
+        store4_rsrc<E>(rdv, v0 + r * vrow + hcol_v + (16 * jt + 4 * g) * sizeof(E), sm.cr[r] * z);
+      }
+    }
   }
   // The row-major operands are read no more in this chunk: the next chunk's go into LDS now.
   // (After the transposing reads of Zb^T above: the compiler cannot tell those from the loads'

@@ -25,7 +25,7 @@ namespace {
 
 // Ks is dead once every wave holds its B fragments in registers (a barrier follows their
 // loads), so P is staged in the same bytes; once P is stored, T's off-diagonal blocks use them.
-// At 37 KiB (bf16, d_k = 128) four workgroups share a CU.
+// At 35 KiB (bf16, d_k = 128) four workgroups share a CU.
 template <typename E, int DK>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(E);

@@ -20,8 +20,9 @@ events on that stream time each part. Prints one JSON line.
 
 After the timed steps, the default run also times, each alone and outside `value`, the
 other named workloads (B8 H8 T4096 and B1 H16 T65536 prefill behind a 512 MiB cache-evicting
-write, the B64 H16 1024-step decode) and a decode whose 512 MiB state exceeds the
-last-level cache, under parts["extra:<name>"] (--no-extras skips them). The CPU baseline
+write, the B64 H16 1024-step decode), a decode whose 512 MiB state exceeds the last-level
+cache, and a B8 H8 T4096 training step with the scalar gate and with the per-channel decay,
+under parts["extra:<name>"] (--no-extras skips them). The CPU baseline
 times the fp64 oracle on the host's cores (worker processes, at most 16) on a bounded
 sample of the prefill and of the decode steps.
 """
@@ -276,9 +277,10 @@ def _oracle_bwd_leg(w, heads, n, kda=False):
     return time.perf_counter() - t0, len(heads) * n
 
 
-def run_bwd(args, w):
-    """--pass bwd: time kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd) over the workload's prefill.
-    --pass train: time kla_chunk_fwd_train and kla_chunk_bwd_saved (their gdn forms) per step."""
+def measure_bwd(w, mode, train, steps, warmup):
+    """Times kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd; mode kla, gdn, deltanet or kda)
+    over the workload's prefill, or with train the pair kla_chunk_fwd_train + kla_chunk_bwd_saved
+    (their gdn / KDA forms), for `steps` steps after `warmup`. Returns (part, elapsed seconds)."""
     import torch
     from gated_delta_rule_18_amd import _lib as K
     device = torch.device("cuda:0")
@@ -286,9 +288,8 @@ def run_bwd(args, w):
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
     L = K.lib()
-    gdn = args.mode in ("gdn", "deltanet")
-    kda = args.mode == "kda"
-    train = args.pass_ == "train"
+    gdn = mode in ("gdn", "deltanet")
+    kda = mode == "kda"
     log(f"[bench] generating {w.name} ({w.note}) and its output cotangent ...")
     on = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(device)
     x = wl.prefill_inputs(w, GEN_WORKERS)
@@ -308,8 +309,8 @@ def run_bwd(args, w):
     stream = torch.cuda.current_stream(device)
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = lambda a: ctypes.c_void_p(a.data_ptr())
-    la = None if args.mode == "deltanet" else P(t["log_alpha"])
-    dla = None if args.mode == "deltanet" else P(out["dla"])
+    la = None if mode == "deltanet" else P(t["log_alpha"])
+    dla = None if mode == "deltanet" else P(out["dla"])
     head = (P(t["q"]), P(t["k"]), P(t["v"]), P(t["eta"]), la, None, P(t["do"]), None, P(out["dq"]), P(out["dk"]),
             P(out["dv"]), P(out["deta"]), dla, None, w.B, w.T, w.H, w.dk, w.dv, 64)
     if train:
@@ -333,12 +334,12 @@ def run_bwd(args, w):
     else:
         call = lambda: L.kla_chunk_bwd(*head, ctypes.c_float(w.eps), code, P(workspace), ws_bytes, sp)
     ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    log(f"[bench] warmup {args.warmup} step(s)")
-    for _ in range(args.warmup):
+    log(f"[bench] warmup {warmup} step(s)")
+    for _ in range(warmup):
         K.check(call())
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} step(s)")
-    evs = [ev() for _ in range(args.steps)]
+    log(f"[bench] timing {steps} step(s)")
+    evs = [ev() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -350,7 +351,7 @@ def run_bwd(args, w):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed region {elapsed * 1e3:.2f} ms")
-    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     tokens = w.B * w.T
     flops = (train_flops_per_head_token if train else bwd_flops_per_head_token)(w.dk, w.dv) * w.heads * w.T
     # (a training step: both passes' bytes; the KDA forward reads log a per channel, d_k fp32)
@@ -368,9 +369,26 @@ def run_bwd(args, w):
             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key("chunk_bwd", args.mode))}
-    part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key("chunk_bwd", args.mode))
-                                            if args.mode in ("kla", "kda") and not train else None)
+            "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key("chunk_bwd", mode))}
+    part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key("chunk_bwd", mode))
+                                            if mode in ("kla", "kda") and not train else None)
+    del t, out, workspace
+    if train:
+        del o
+    torch.cuda.empty_cache()
+    return part, elapsed
+
+
+def run_bwd(args, w):
+    """--pass bwd: time kla_chunk_bwd (kla_gdn_chunk_bwd, kla_kda_chunk_bwd) over the workload's prefill.
+    --pass train: time kla_chunk_fwd_train and kla_chunk_bwd_saved (their gdn forms) per step."""
+    train = args.pass_ == "train"
+    gdn = args.mode in ("gdn", "deltanet")
+    kda = args.mode == "kda"
+    part, elapsed = measure_bwd(w, args.mode, train, args.steps, args.warmup)
+    es = 2 if w.dtype == "bf16" else 4
+    peak_mfma = PEAK_BF16_TFLOPS if es == 2 else PEAK_FP32_MFMA_TFLOPS
+    tokens = w.B * w.T
     roof = {"bound": "mfma", "kernel": part["kernel"], "achieved": part["mfma_tflops"], "peak": peak_mfma,
             "unit": "TFLOP/s", "frac": part["mfma_frac"], "traffic": part["hbm_traffic_bytes_per_launch"],
             "hbm_view": {"achieved": part["hbm_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -394,6 +412,7 @@ def run_bwd(args, w):
 # other named workloads, each in its own launch configuration, and one decode whose state exceeds
 # the 256 MB last-level cache. Prefill launches follow a 512 MiB write that evicts the caches.
 EXTRAS = ("fwd_b8h8_t4096", "fwd_long_t65536", "decode_b64h16", "decode_b512h16")
+TRAIN_EXTRAS = (("fwd_b8h8_t4096", "kla"), ("fwd_b8h8_t4096", "kda"))
 BIG_DECODE = wl.Workload("decode_b512h16", 5, B=512, H=16, dk=128, dv=128, steps=16, s0_std=0.02,
                          note="KLA decode B512 H16 d128: 512 MiB fp32 state, twice the last-level cache")
 FLUSH_BYTES = 512 << 20
@@ -795,6 +814,17 @@ def main():
             parts["extra:" + name] = time_extra(name, torch, K, L, device, stream, flush)
         del flush
         torch.cuda.empty_cache()
+        # Training steps (the forward into the backward's workspace, then the backward from it),
+        # scalar gate and per-channel decay, on the B8 H8 T4096 shape.
+        for wname, mode in TRAIN_EXTRAS:
+            tw = wl.WORKLOADS[wname]
+            log(f"[bench] extra training step {wname} ({mode})")
+            part, _ = measure_bwd(tw, mode, True, 10, 2)
+            part.update({"extra": True, "launches_timed": 10, "timing": "mean of 10 steps after 2, HIP events",
+                         "workload": tw.note + (" with per-channel decay (KDA)" if mode == "kda" else "") +
+                         ": training step, kla_" + ("kda_" if mode == "kda" else "") + "chunk_fwd_train + kla_" +
+                         ("kda_" if mode == "kda" else "") + "chunk_bwd_saved"})
+            parts["extra:train_" + wname + ("_kda" if mode == "kda" else "")] = part
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on a bounded sample ({args.cpu_head_tokens} head-tokens)")

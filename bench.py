@@ -100,7 +100,7 @@ def log(*a):
 
 
 # Source files of each timed part; the recorded HBM traffic of a part is only reported while
-# these files are byte-identical to the ones the counters were taken on.
+# the code in these files (comments and whitespace aside) is the code the counters were taken on.
 CSRC = os.path.join(ROOT, "gated_delta_rule_18_amd", "csrc")
 PART_SOURCES = {
     "chunk_fwd": ["chunk_common.h", "chunk_prep.hip", "chunk_scan.hip", "chunk_seg.hip", "tile_ops.h",
@@ -135,9 +135,9 @@ def traffic_key(part, mode):
 
 
 def recorded_traffic(workload, part):
-    """HBM bytes per launch of `part` on `workload`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs recorded in profiles/hbm_traffic.txt (each already scaled by the copy calibration),
-    or None if there is no record for the current sources."""
+    """HBM bytes per launch of `part` on `workload` (bytes read plus bytes written), from the
+    rocprofv3 request-size counter runs recorded in profiles/hbm_traffic.txt, or None if there is
+    no record for the current sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     want = sources_sha(part)

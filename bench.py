@@ -113,6 +113,9 @@ PART_SOURCES = {
 PART_SOURCES["chunk_fwd_kda"] = PART_SOURCES["chunk_fwd"]
 PART_SOURCES["decode_kda"] = PART_SOURCES["decode"]
 PART_SOURCES["chunk_bwd_kda"] = PART_SOURCES["chunk_bwd"] + ["chunk_bwd_grad_kda.hip"]
+# A training step (the saving forward, then the backward from its workspace) runs the same files.
+PART_SOURCES["chunk_train"] = PART_SOURCES["chunk_bwd"]
+PART_SOURCES["chunk_train_kda"] = PART_SOURCES["chunk_bwd_kda"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -352,6 +355,7 @@ def measure_bwd(w, mode, train, steps, warmup):
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed region {elapsed * 1e3:.2f} ms")
     ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    tkey = "chunk_train" if train else "chunk_bwd"  # name of its recorded traffic
     tokens = w.B * w.T
     flops = (train_flops_per_head_token if train else bwd_flops_per_head_token)(w.dk, w.dv) * w.heads * w.T
     # (a training step: both passes' bytes; the KDA forward reads log a per channel, d_k fp32)
@@ -369,9 +373,9 @@ def measure_bwd(w, mode, train, steps, warmup):
             "tokens_per_s": tokens / (ms * 1e-3), "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "mfma_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak_mfma,
             "hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key("chunk_bwd", mode))}
-    part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key("chunk_bwd", mode))
-                                            if mode in ("kla", "kda") and not train else None)
+            "workspace_bytes": ws_bytes, "sources_sha": sources_sha(traffic_key(tkey, mode))}
+    part["hbm_traffic_bytes_per_launch"] = (recorded_traffic(w.name, traffic_key(tkey, mode))
+                                            if mode in ("kla", "kda") else None)
     del t, out, workspace
     if train:
         del o

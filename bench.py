@@ -420,6 +420,11 @@ TRAIN_EXTRAS = (("fwd_b8h8_t4096", "kla"), ("fwd_b8h8_t4096", "kda"))
 BIG_DECODE = wl.Workload("decode_b512h16", 5, B=512, H=16, dk=128, dv=128, steps=16, s0_std=0.02,
                          note="KLA decode B512 H16 d128: 512 MiB fp32 state, twice the last-level cache")
 FLUSH_BYTES = 512 << 20
+
+
+def workload(name):
+    """A named workload, or the large-state decode (an extra, also selectable with --workload)."""
+    return BIG_DECODE if name == BIG_DECODE.name else wl.WORKLOADS[name]
 GEN_WORKERS = None  # --gen-workers
 
 
@@ -481,7 +486,7 @@ def decode_part(w, per_ms, es, launch, extra=False, launches=None):
 
 def time_extra(name, torch, K, L, device, stream, flush):
     """Times one extra workload alone (kla mode) and returns its part."""
-    w = BIG_DECODE if name == BIG_DECODE.name else wl.WORKLOADS[name]
+    w = workload(name)
     es = 2 if w.dtype == "bf16" else 4
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
@@ -575,7 +580,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--workload", default="mixed_b4h16", choices=sorted(wl.WORKLOADS) + [BIG_DECODE.name])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the chosen workload (the default run also times " + ", ".join(EXTRAS) + ")")
@@ -626,13 +631,13 @@ def main():
         return
 
     if args.pass_ in ("bwd", "train"):
-        w = wl.WORKLOADS["fwd_b8h8_t4096" if args.workload == "mixed_b4h16" else args.workload]
+        w = workload("fwd_b8h8_t4096" if args.workload == "mixed_b4h16" else args.workload)
         if not w.T:
             print(f"--pass {args.pass_} needs a prefill workload", file=sys.stderr)
             sys.exit(2)
         return run_bwd(args, w.with_(steps=0))
 
-    w = wl.WORKLOADS[args.workload]
+    w = workload(args.workload)
     es = 2 if w.dtype == "bf16" else 4
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     code = K.KLA_BF16 if w.dtype == "bf16" else K.KLA_F32
